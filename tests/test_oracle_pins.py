@@ -1,0 +1,354 @@
+"""Pins of the fp64 oracle to what the pages and the mathematics fix.
+
+Nothing here compares the oracle with itself: every check is a value the
+pages print (tests/golden/), a closed form, an invariant, a special case that
+reduces to a textbook value, or brute force through a differently written
+formulation.  Each check is chosen so that a plausible slip in the oracle (a
+dropped term, a wrong sign or index, a transposed operand, the wrong
+normalisation axes) fails it.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+
+RNG = np.random.default_rng(12345)
+
+
+def _read(golden_dir, name):
+    rows = []
+    with open(os.path.join(golden_dir, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+# ---------------------------------------------------------------- sizes
+def test_output_sizes_printed_on_pages(golden_dir):
+    for _, label, ins, k, op, exp in _read(golden_dir, "output_sizes.txt"):
+        ins = tuple(int(v) for v in ins.split(","))
+        exp = tuple(int(v) for v in exp.split(","))
+        k = int(k)
+        if op == "conv":
+            x = np.zeros((1, 1) + ins, np.float32)
+            w = np.zeros((1, 1) + (k,) * len(ins), np.float32)
+            got = oracle.conv(x, w).shape[2:]
+        elif op == "convt":
+            x = np.zeros((1, 1) + ins, np.float32)
+            w = np.zeros((1, 1, k, k), np.float32)
+            got = oracle.conv_transpose2d(x, w).shape[2:]
+        elif op == "pool2":
+            got = oracle.maxpool3d(np.zeros((1, 1) + ins), 2)[0].shape[2:]
+        else:
+            raise AssertionError(op)
+        assert got == exp, label
+
+
+def test_floor_of_floor_identity():
+    # Page l2_p6: two floor-mode 2-pools equal one floor-mode 4-pool in extent.
+    L = np.arange(0, 10000)
+    assert np.array_equal((L // 2) // 2, L // 4)
+
+
+# ---------------------------------------------------------------- convolution
+def _conv_numpy(x, w, b, groups):
+    """Independent formulation: sliding windows + tensordot per group."""
+    from numpy.lib.stride_tricks import sliding_window_view as swv
+    x = x.astype(np.float64)
+    w = w.astype(np.float64)
+    nd = x.ndim - 2
+    Co = w.shape[0]
+    cig = x.shape[1] // groups
+    cog = Co // groups
+    ks = w.shape[2:]
+    win = swv(x, ks, axis=tuple(range(2, 2 + nd)))  # N, Ci, *out, *ks
+    outs = []
+    for g in range(groups):
+        xs = win[:, g * cig:(g + 1) * cig]
+        ws = w[g * cog:(g + 1) * cog]
+        # contract over (ci, *ks)
+        axes_x = [1] + list(range(2 + nd, 2 + 2 * nd))
+        axes_w = [1] + list(range(2, 2 + nd))
+        y = np.tensordot(xs, ws, axes=(axes_x, axes_w))  # N, *out, cog
+        outs.append(np.moveaxis(y, -1, 1))
+    y = np.concatenate(outs, axis=1)
+    if b is not None:
+        y = y + b.astype(np.float64).reshape((1, Co) + (1,) * nd)
+    return y
+
+
+@pytest.mark.parametrize("shape", [
+    # (N, Ci, spatial, Co, k, groups)
+    (2, 3, (6, 7, 8), 4, 3, 1),
+    (1, 4, (5, 6, 5), 6, 2, 2),
+    (2, 8, (9, 10), 16, 3, 1),
+    (1, 6, (7, 7), 9, 3, 3),
+    (3, 2, (4, 5, 6), 2, 4, 1),
+])
+def test_conv_matches_independent_formulation(shape):
+    N, Ci, sp, Co, k, G = shape
+    x = RNG.standard_normal((N, Ci) + sp).astype(np.float32)
+    w = RNG.standard_normal((Co, Ci // G) + (k,) * len(sp)).astype(np.float32)
+    b = RNG.standard_normal(Co).astype(np.float32)
+    got = oracle.conv(x, w, b, G)
+    ref = _conv_numpy(x, w, b, G)
+    assert got.shape == ref.shape
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_conv_one_hot_kernel_is_a_shift():
+    # A kernel with a single 1 at offset (a, b, e) picks x[d+a, h+b, w+e].
+    x = RNG.standard_normal((1, 1, 6, 7, 8)).astype(np.float32)
+    for (a, bb, e) in [(0, 0, 0), (2, 1, 0), (1, 2, 3), (3, 3, 3)]:
+        w = np.zeros((1, 1, 4, 4, 4), np.float32)
+        w[0, 0, a, bb, e] = 1.0
+        y = oracle.conv(x, w)
+        np.testing.assert_array_equal(y[0, 0], x[0, 0, a:a + 3, bb:bb + 4, e:e + 5].astype(np.float64))
+
+
+def test_conv_constant_input_is_bias_plus_weight_sum():
+    x = np.ones((2, 3, 5, 5, 5), np.float32)
+    w = RNG.standard_normal((4, 3, 3, 3, 3)).astype(np.float32)
+    b = RNG.standard_normal(4).astype(np.float32)
+    y = oracle.conv(x, w, b)
+    exp = b.astype(np.float64) + w.astype(np.float64).reshape(4, -1).sum(1)
+    np.testing.assert_allclose(y, np.broadcast_to(exp[None, :, None, None, None], y.shape), rtol=1e-12)
+
+
+def test_conv_groups_do_not_mix_channels():
+    # With groups=2, output channels of group 1 must not see input group 0.
+    x = RNG.standard_normal((1, 4, 5, 5)).astype(np.float32)
+    w = RNG.standard_normal((6, 2, 3, 3)).astype(np.float32)
+    y1 = oracle.conv(x, w, None, 2)
+    x2 = x.copy()
+    x2[:, :2] += 1.0  # perturb group 0 only
+    y2 = oracle.conv(x2, w, None, 2)
+    np.testing.assert_array_equal(y1[:, 3:], y2[:, 3:])
+    assert not np.allclose(y1[:, :3], y2[:, :3])
+
+
+# ---------------------------------------------------------------- transposed conv
+def test_convt_worked_example_printed_on_page(golden_dir):
+    rows = _read(golden_dir, "convt_worked_example.txt")
+    x = np.array([[float(v) for v in r[1:]] for r in rows if r[0] == "input"], np.float32)
+    y = oracle.conv_transpose2d(x[None, None], np.ones((1, 1, 3, 3), np.float32))[0, 0]
+    assert y.shape == (4, 4)
+    for r in rows:
+        if r[0] == "printed":
+            assert y[int(r[1]), int(r[2])] == float(r[3])
+    full = np.array([[float(v) for v in r[1:]] for r in rows if r[0] == "full"])
+    np.testing.assert_array_equal(y, full)
+
+
+def test_convt_1d_adjoint_formula_from_page(golden_dir):
+    terms = [tuple(int(v) for v in r[1:]) for r in _read(golden_dir, "convt_1d_adjoint.txt")]
+    yv = np.array([2.0, 3.0], np.float32)
+    wv = np.array([5.0, 7.0, 11.0], np.float32)
+    got = oracle.conv_transpose2d(yv.reshape(1, 1, 1, 2), wv.reshape(1, 1, 1, 3))[0, 0, 0]
+    exp = np.zeros(4)
+    for i, j, k in terms:
+        exp[i] += yv[j] * wv[k]
+    np.testing.assert_array_equal(got, exp)
+
+
+@pytest.mark.parametrize("G", [1, 2, 4])
+def test_convt_is_adjoint_of_conv(G):
+    # <conv(u; W), v> == <u, convT(v; W)> with W read as [out=Ci_T][in=Co_T].
+    Ci, Co, H, W, k = 8, 4, 6, 7, 3
+    Wt = RNG.standard_normal((Ci, Co // G, k, k)).astype(np.float32)  # convT layout
+    v = RNG.standard_normal((1, Ci, H, W)).astype(np.float32)         # convT input
+    u = RNG.standard_normal((1, Co, H + k - 1, W + k - 1)).astype(np.float32)
+    lhs = np.sum(oracle.conv(u, Wt, None, G) * v.astype(np.float64))
+    rhs = np.sum(u.astype(np.float64) * oracle.conv_transpose2d(v, Wt, None, G))
+    assert abs(lhs - rhs) <= 1e-10 * max(1.0, abs(lhs))
+
+
+@pytest.mark.parametrize("G", [1, 2])
+def test_convt_equals_padded_flipped_conv(G):
+    # Page l2_p19 second trace: the transposed conv is a conv of the input
+    # zero-padded by k-1 with the kernel flipped and its channel axes swapped.
+    Ci, Co, H, W, k = 4, 6, 5, 6, 3
+    Wt = RNG.standard_normal((Ci, Co // G, k, k)).astype(np.float32)
+    x = RNG.standard_normal((2, Ci, H, W)).astype(np.float32)
+    b = RNG.standard_normal(Co).astype(np.float32)
+    cig, cog = Ci // G, Co // G
+    Wc = np.zeros((Co, cig, k, k), np.float32)
+    for g in range(G):
+        blk = Wt[g * cig:(g + 1) * cig]                      # cig, cog, k, k
+        Wc[g * cog:(g + 1) * cog] = np.flip(blk, (2, 3)).transpose(1, 0, 2, 3)
+    xp = np.pad(x, ((0, 0), (0, 0), (k - 1, k - 1), (k - 1, k - 1)))
+    np.testing.assert_allclose(oracle.conv_transpose2d(x, Wt, b, G),
+                               oracle.conv(xp, Wc, b, G), rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- activations
+def test_hardswish_special_values():
+    # Page l2_p27: 0 at and below -3, identity at and above 3, x(x+3)/6 between.
+    xs = np.array([-3.0, 3.0, -4.0, 4.0, 1.0, -1.0, 0.0, -10.0, 10.0])
+    exp = np.array([0.0, 3.0, 0.0, 4.0, 2.0 / 3.0, -1.0 / 3.0, 0.0, 0.0, 10.0])
+    np.testing.assert_allclose(oracle.hardswish(xs), exp, rtol=0, atol=1e-15)
+
+
+def test_hardswish_odd_part_is_identity():
+    x = RNG.uniform(-8, 8, 1000)
+    np.testing.assert_allclose(oracle.hardswish(x) - oracle.hardswish(-x), x, atol=1e-13)
+
+
+def test_gelu_matches_normal_table():
+    # gelu(x) = x * Phi(x); Phi(1) = 0.841344746, Phi(2) = 0.977249868 from the
+    # standard normal table; Phi(-x) = 1 - Phi(x).
+    xs = np.array([0.0, 1.0, -1.0, 2.0, -2.0])
+    exp = np.array([0.0, 0.841344746, -(1 - 0.841344746), 2 * 0.977249868,
+                    -2 * (1 - 0.977249868)])
+    np.testing.assert_allclose(oracle.gelu_erf(xs), exp, atol=2e-9)
+
+
+def test_gelu_odd_part_and_tails():
+    x = RNG.uniform(-6, 6, 2000)
+    np.testing.assert_allclose(oracle.gelu_erf(x) - oracle.gelu_erf(-x), x, atol=1e-13)
+    big = np.array([10.0, 12.0, 20.0])
+    np.testing.assert_allclose(oracle.gelu_erf(big), big, atol=1e-12)
+    np.testing.assert_allclose(oracle.gelu_erf(-big), 0.0, atol=1e-12)
+
+
+def test_gelu_tanh_form_would_break_the_tolerance():
+    # The tanh approximation differs from the erf form by more than the
+    # 2e-4 parity budget, so the path must use erf (page l2_p19 second trace
+    # claims the two agree far more closely than they do).
+    x = np.linspace(-6, 6, 120001)
+    d = np.abs(oracle.gelu_erf(x) - oracle.gelu_tanh(x))
+    assert d.max() > 2e-4
+    assert d.max() < 1e-3
+
+
+def test_softmax_rows_sum_to_one_and_closed_forms():
+    y = RNG.standard_normal((3, 16, 4, 5, 6)) * 5
+    s = oracle.softmax_channel(y)
+    np.testing.assert_allclose(s.sum(1), 1.0, atol=1e-14)
+    assert (s > 0).all() and (s < 1).all()
+    # shift invariance along the channel axis
+    np.testing.assert_allclose(oracle.softmax_channel(y + 123.0), s, atol=1e-13)
+    # equal logits -> 1/C
+    np.testing.assert_allclose(oracle.softmax_channel(np.zeros((1, 16, 3))), 1 / 16, atol=1e-16)
+    # two channels -> logistic function of the difference
+    z = RNG.standard_normal((1, 2, 50))
+    s2 = oracle.softmax_channel(z)
+    np.testing.assert_allclose(s2[0, 0], 1.0 / (1.0 + np.exp(z[0, 1] - z[0, 0])), rtol=1e-14)
+
+
+# ---------------------------------------------------------------- pooling
+def test_two_2pools_equal_one_4pool():
+    y = RNG.standard_normal((2, 3, 14, 30, 30))
+    p1, i1 = oracle.maxpool3d(y, 2)
+    p2, i2 = oracle.maxpool3d(p1, 2, i1)
+    assert p2.shape == (2, 3, 3, 7, 7)
+    # independent 4-pool by reshape over the covered region
+    c = y[:, :, :12, :28, :28].reshape(2, 3, 3, 4, 7, 4, 7, 4)
+    np.testing.assert_array_equal(p2, c.max(axis=(3, 5, 7)))
+    # the carried index names a voxel of the window holding the maximum
+    flat = y.reshape(2, 3, -1)
+    np.testing.assert_array_equal(np.take_along_axis(flat, i2.reshape(2, 3, -1), 2).reshape(p2.shape), p2)
+    d, h, w = i2 // 900, (i2 // 30) % 30, i2 % 30
+    od, oh, ow = np.indices((3, 7, 7))
+    assert ((d // 4 == od) & (h // 4 == oh) & (w // 4 == ow)).all()
+
+
+def test_pool_ties_take_the_first_scanned():
+    y = np.zeros((1, 1, 4, 4, 4))
+    p1, i1 = oracle.maxpool3d(y, 2)
+    np.testing.assert_array_equal(i1.ravel(), [0, 2, 8, 10, 32, 34, 40, 42])
+    p2, i2 = oracle.maxpool3d(p1, 2, i1)
+    assert i2.ravel().tolist() == [0]
+    # literal two-stage order: a tie between voxel (1,0,0) [first stage-1 block]
+    # and (0,2,0) [second block] goes to the first block
+    y[0, 0, 1, 0, 0] = 1.0
+    y[0, 0, 0, 2, 0] = 1.0
+    p1, i1 = oracle.maxpool3d(y, 2)
+    _, i2 = oracle.maxpool3d(p1, 2, i1)
+    assert int(i2.ravel()[0]) == 1 * 16
+
+
+def test_softmax_pool_bounds():
+    # Derived: every pooled softmax value lies in (0, 1] and the per-position
+    # channel sum of the pooled values is in [1, C] (a window max is at least
+    # the value of any single voxel of the window).
+    y = RNG.standard_normal((2, 16, 8, 8, 8)) * 3
+    s = oracle.softmax_channel(y)
+    p, _ = oracle.maxpool3d(oracle.maxpool3d(s, 2)[0], 2)
+    assert (p > 0).all() and (p <= 1).all()
+    tot = p.sum(1)
+    assert (tot >= 1 - 1e-12).all() and (tot <= 16).all()
+
+
+# ---------------------------------------------------------------- normalisation
+def _group_affine_check(y, z, G, eps):
+    """Per (n, g): z is an increasing affine map of y with mean 0 and variance
+    var/(var+eps), var taken by numpy over the group's channels and positions."""
+    N, C = y.shape[:2]
+    cg = C // G
+    for n in range(N):
+        for g in range(G):
+            a = y[n, g * cg:(g + 1) * cg].ravel()
+            b = z[n, g * cg:(g + 1) * cg].ravel()
+            var = np.var(a)
+            assert abs(b.mean()) < 1e-12
+            np.testing.assert_allclose(np.var(b), var / (var + eps), rtol=1e-12)
+            # affine: residual of the least-squares line through (a, b) is zero
+            slope = np.sum((a - a.mean()) * (b - b.mean())) / np.sum((a - a.mean()) ** 2)
+            assert slope > 0
+            resid = b - (b.mean() + slope * (a - a.mean()))
+            assert np.abs(resid).max() < 1e-11
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 16])
+def test_group_norm_invariants(G):
+    y = RNG.standard_normal((2, 16, 5, 6, 7)) * 3 + 1.5
+    z = oracle.group_norm(y, G, 1e-5)
+    _group_affine_check(y, z, G, 1e-5)
+
+
+def test_group_norm_affine_is_per_channel():
+    y = RNG.standard_normal((2, 8, 9, 9)) + 0.3
+    gamma = RNG.uniform(0.5, 1.5, 8).astype(np.float32)
+    beta = (0.1 * RNG.standard_normal(8)).astype(np.float32)
+    z = oracle.group_norm(y, 2, 1e-5, gamma, beta)
+    zn = (z - beta.astype(np.float64)[None, :, None, None]) / gamma.astype(np.float64)[None, :, None, None]
+    _group_affine_check(y, zn, 2, 1e-5)
+
+
+def test_group_norm_with_eps_dominating():
+    # var << eps: the output shrinks toward 0 by sqrt(var/(var+eps)).
+    y = 1e-4 * RNG.standard_normal((1, 4, 50))
+    z = oracle.group_norm(y, 1, 1e-2)
+    _group_affine_check(y, z, 1, 1e-2)
+
+
+def test_instance_norm_then_divide():
+    y = RNG.standard_normal((2, 16, 30, 30)) * 0.7 - 0.2
+    z = oracle.divide(oracle.instance_norm(y, 1e-5), 2.0)
+    _group_affine_check(y, 2.0 * z, 16, 1e-5)
+
+
+def test_mean_spatial_of_constant_planes():
+    y = np.broadcast_to(np.arange(6.0).reshape(2, 3, 1, 1, 1), (2, 3, 4, 5, 6))
+    np.testing.assert_array_equal(oracle.mean_spatial(y), np.arange(6.0).reshape(2, 3))
+
+
+def test_gn_mean_closed_form_equals_plain_definition():
+    # Page l2_p27: the spatial mean of the GroupNorm output depends only on
+    # per-channel means and the group statistics.  The oracle computes it both
+    # ways; the plain way materialises the normalised tensor.
+    h = oracle.hardswish(RNG.standard_normal((3, 16, 5, 7, 7)) * 0.8 + 0.1)
+    gamma = RNG.uniform(0.5, 1.5, 16).astype(np.float32)
+    beta = (0.1 * RNG.standard_normal(16)).astype(np.float32)
+    plain = oracle.mean_spatial(oracle.group_norm(h, 4, 1e-5, gamma, beta))
+    closed = oracle.gn_mean_closed_form(h, 4, 1e-5, gamma, beta)
+    np.testing.assert_allclose(closed, plain, rtol=1e-10, atol=1e-12)
+    # derived invariant: per (n, g), sum_c (out - beta_c) / gamma_c = 0
+    r = ((closed - beta.astype(np.float64)) / gamma.astype(np.float64)).reshape(3, 4, 4).sum(2)
+    np.testing.assert_allclose(r, 0.0, atol=1e-12)

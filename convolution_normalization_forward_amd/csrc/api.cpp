@@ -1,0 +1,270 @@
+// api.cpp -- the C ABI declared in include/cnf.h: descriptor validation,
+// output-shape and workspace arithmetic, kernel-family selection and the
+// launch of the chosen family on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+#include <new>
+
+#include "cnf.h"
+#include "kernels.h"
+
+namespace {
+
+enum Family : int {
+    FAM_GN_MEAN = 1,       // Conv3d k4 C_out 16 + act + GroupNorm + mean, fully fused
+    FAM_SOFTMAX_POOL = 2,  // Conv3d C_out 16 + channel softmax + 4^3 max pool
+    FAM_SMALL = 3,         // small conv C_out 16, one workgroup per sample
+    FAM_IGEMM = 4,         // Conv2d C_out 128 k3 implicit GEMM + norm pass
+    FAM_CONVT = 5          // grouped ConvTranspose2d 8x8 per group + act + GroupNorm pass
+};
+
+const char *family_name(int f)
+{
+    switch (f) {
+    case FAM_GN_MEAN: return "conv3d_k4_gn_mean(fused,1wg/sample,mfma16x16x4)";
+    case FAM_SOFTMAX_POOL: return "conv3d_softmax_pool4(1wave/window,mfma16x16x4)";
+    case FAM_SMALL: return "small_conv_norm(1wg/sample,mfma16x16x4)";
+    case FAM_IGEMM: return "conv2d_igemm(mfma32x32x2)+norm_pass";
+    case FAM_CONVT: return "convt2d_grouped8(mfma16x16x4,column-pair)+groupnorm_pass";
+    default: return "none";
+    }
+}
+
+}  // namespace
+
+struct cnf_plan {
+    cnf_desc d;
+    int family;
+    int Do, Ho, Wo;     // conv output extents (Do = 1 for 2-D)
+    int Dp, Hp, Wp;     // pooled extents
+    int64_t dims[5];
+    int32_t rank;
+    size_t workspace;
+};
+
+extern "C" {
+
+int32_t cnf_abi_version(void) { return CNF_ABI_VERSION; }
+
+const char *cnf_status_string(cnf_status s)
+{
+    switch (s) {
+    case CNF_OK: return "CNF_OK";
+    case CNF_ERR_NULL: return "CNF_ERR_NULL";
+    case CNF_ERR_INVALID_DESC: return "CNF_ERR_INVALID_DESC";
+    case CNF_ERR_UNSUPPORTED: return "CNF_ERR_UNSUPPORTED";
+    case CNF_ERR_WORKSPACE: return "CNF_ERR_WORKSPACE";
+    case CNF_ERR_ALIGNMENT: return "CNF_ERR_ALIGNMENT";
+    case CNF_ERR_HIP: return "CNF_ERR_HIP";
+    case CNF_ERR_ABI: return "CNF_ERR_ABI";
+    }
+    return "CNF_ERR_UNKNOWN";
+}
+
+cnf_status cnf_plan_create(const cnf_desc *desc, cnf_plan **plan)
+{
+    if (!plan) return CNF_ERR_NULL;
+    *plan = nullptr;
+    if (!desc) return CNF_ERR_NULL;
+    const cnf_desc &d = *desc;
+    if (d.abi_version != CNF_ABI_VERSION) return CNF_ERR_ABI;
+
+    // ---- validation (a self-inconsistent descriptor is INVALID_DESC)
+    if (d.ndim != 2 && d.ndim != 3) return CNF_ERR_INVALID_DESC;
+    if (d.kind != CNF_CONV && d.kind != CNF_CONV_TRANSPOSE) return CNF_ERR_INVALID_DESC;
+    if (d.N < 0 || d.C_in < 1 || d.C_out < 1 || d.kernel < 1 || d.groups < 1)
+        return CNF_ERR_INVALID_DESC;
+    if (d.C_in % d.groups || d.C_out % d.groups) return CNF_ERR_INVALID_DESC;
+    if (d.in_dims[0] < 1 || d.in_dims[1] < 1 || d.in_dims[2] < 1) return CNF_ERR_INVALID_DESC;
+    if (d.ndim == 2 && d.in_dims[0] != 1) return CNF_ERR_INVALID_DESC;
+    if (d.has_bias != 0 && d.has_bias != 1) return CNF_ERR_INVALID_DESC;
+    if (d.act < CNF_ACT_NONE || d.act > CNF_ACT_SOFTMAX_CHANNEL) return CNF_ERR_INVALID_DESC;
+    if (d.norm < CNF_NORM_NONE || d.norm > CNF_NORM_INSTANCE) return CNF_ERR_INVALID_DESC;
+    if (d.reduce < CNF_RED_NONE || d.reduce > CNF_RED_MAXPOOL) return CNF_ERR_INVALID_DESC;
+    if (d.affine != 0 && d.affine != 1) return CNF_ERR_INVALID_DESC;
+    if (d.want_argmax != 0 && d.want_argmax != 1) return CNF_ERR_INVALID_DESC;
+    if (d.norm == CNF_NORM_GROUP && (d.num_groups < 1 || d.C_out % d.num_groups))
+        return CNF_ERR_INVALID_DESC;
+    if (d.norm != CNF_NORM_NONE && !(d.eps > 0.0f)) return CNF_ERR_INVALID_DESC;
+    if (!(d.divide_by == d.divide_by) || d.divide_by == 0.0f) return CNF_ERR_INVALID_DESC;
+    if (d.want_argmax && d.reduce != CNF_RED_MAXPOOL) return CNF_ERR_INVALID_DESC;
+
+    cnf_plan p{};
+    p.d = d;
+    const int k = d.kernel;
+    const int D = d.in_dims[0], H = d.in_dims[1], W = d.in_dims[2];
+    if (d.kind == CNF_CONV) {
+        p.Do = d.ndim == 3 ? D - k + 1 : 1;
+        p.Ho = H - k + 1;
+        p.Wo = W - k + 1;
+    } else {
+        if (d.ndim != 2) return CNF_ERR_UNSUPPORTED;  // transposed conv is 2-D here
+        p.Do = 1;
+        p.Ho = H + k - 1;
+        p.Wo = W + k - 1;
+    }
+    if (p.Do < 1 || p.Ho < 1 || p.Wo < 1) return CNF_ERR_INVALID_DESC;
+
+    int pool_total = 1;
+    p.Dp = p.Do; p.Hp = p.Ho; p.Wp = p.Wo;
+    if (d.reduce == CNF_RED_MAXPOOL) {
+        if (d.pool_kernel < 1 || d.pool_repeats < 1 || d.pool_repeats > 8)
+            return CNF_ERR_INVALID_DESC;
+        for (int r = 0; r < d.pool_repeats; ++r) {
+            if (d.ndim == 3) p.Dp /= d.pool_kernel;
+            p.Hp /= d.pool_kernel;
+            p.Wp /= d.pool_kernel;
+            pool_total *= d.pool_kernel;
+            if (pool_total > 1 << 20) return CNF_ERR_INVALID_DESC;
+        }
+        if (p.Dp < 1 || p.Hp < 1 || p.Wp < 1) return CNF_ERR_INVALID_DESC;
+    }
+
+    if (d.reduce == CNF_RED_MEAN_SPATIAL) {
+        p.rank = 2;
+        p.dims[0] = d.N; p.dims[1] = d.C_out;
+    } else if (d.reduce == CNF_RED_MAXPOOL) {
+        p.rank = 5;
+        p.dims[0] = d.N; p.dims[1] = d.C_out;
+        p.dims[2] = p.Dp; p.dims[3] = p.Hp; p.dims[4] = p.Wp;
+    } else {
+        p.rank = d.ndim + 2;
+        p.dims[0] = d.N; p.dims[1] = d.C_out;
+        if (d.ndim == 3) { p.dims[2] = p.Do; p.dims[3] = p.Ho; p.dims[4] = p.Wo; }
+        else { p.dims[2] = p.Ho; p.dims[3] = p.Wo; }
+    }
+
+    // ---- kernel-family selection (UNSUPPORTED rather than any slow path)
+    const int norm_groups = d.norm == CNF_NORM_GROUP ? d.num_groups
+                          : d.norm == CNF_NORM_INSTANCE ? d.C_out : 0;
+    p.family = 0;
+    if (d.kind == CNF_CONV && d.groups == 1) {
+        if (d.ndim == 3 && d.reduce == CNF_RED_MEAN_SPATIAL && d.act != CNF_ACT_SOFTMAX_CHANNEL &&
+            cnf::conv3d_gn_mean_supported(d.C_in, d.C_out, k, D, H, W, d.act))
+            p.family = FAM_GN_MEAN;
+        else if (d.ndim == 3 && d.reduce == CNF_RED_MAXPOOL && d.norm == CNF_NORM_NONE &&
+                 d.divide_by == 1.0f && (d.pool_kernel == 2 || d.pool_repeats == 1) &&
+                 cnf::conv3d_softmax_pool_supported(d.C_in, d.C_out, k, d.act, pool_total))
+            p.family = FAM_SOFTMAX_POOL;
+        else if (d.reduce != CNF_RED_MAXPOOL &&
+                 cnf::small_conv_norm_supported(d.C_in, d.C_out, k, d.ndim, D, H, W, d.act))
+            p.family = FAM_SMALL;
+        else if (d.ndim == 2 && d.reduce == CNF_RED_NONE &&
+                 cnf::conv2d_igemm_supported(d.C_in, d.C_out, k, d.groups, H, W, d.act))
+            p.family = FAM_IGEMM;
+    } else if (d.kind == CNF_CONV_TRANSPOSE && d.reduce == CNF_RED_NONE) {
+        if (cnf::convt2d_supported(d.C_in, d.C_out, k, d.groups, H, W, d.act, d.norm,
+                                   d.num_groups))
+            p.family = FAM_CONVT;
+    }
+    (void)norm_groups;
+    if (!p.family) return CNF_ERR_UNSUPPORTED;
+
+    p.workspace = 0;
+    if (p.family == FAM_IGEMM) p.workspace = cnf::conv2d_igemm_workspace(d.N, d.C_in, p.Ho, p.Wo);
+    if (p.family == FAM_CONVT) p.workspace = cnf::convt2d_workspace(d.N, d.groups, p.Ho, p.Wo);
+
+    cnf_plan *np = new (std::nothrow) cnf_plan(p);
+    if (!np) return CNF_ERR_INVALID_DESC;
+    *plan = np;
+    return CNF_OK;
+}
+
+cnf_status cnf_plan_output_shape(const cnf_plan *plan, int64_t dims[5], int32_t *rank)
+{
+    if (!plan || !dims || !rank) return CNF_ERR_NULL;
+    for (int i = 0; i < 5; ++i) dims[i] = i < plan->rank ? plan->dims[i] : 0;
+    *rank = plan->rank;
+    return CNF_OK;
+}
+
+cnf_status cnf_plan_workspace_size(const cnf_plan *plan, size_t *bytes)
+{
+    if (!plan || !bytes) return CNF_ERR_NULL;
+    *bytes = plan->workspace;
+    return CNF_OK;
+}
+
+cnf_status cnf_plan_describe(const cnf_plan *plan, char *buf, size_t len)
+{
+    if (!plan || !buf) return CNF_ERR_NULL;
+    if (len == 0) return CNF_OK;
+    const cnf_desc &d = plan->d;
+    std::snprintf(buf, len, "family=%s N=%d C_in=%d C_out=%d in=%dx%dx%d k=%d groups=%d "
+                  "out_rank=%d workspace=%zu",
+                  family_name(plan->family), d.N, d.C_in, d.C_out, d.in_dims[0], d.in_dims[1],
+                  d.in_dims[2], d.kernel, d.groups, plan->rank, plan->workspace);
+    return CNF_OK;
+}
+
+void cnf_plan_destroy(cnf_plan *plan) { delete plan; }
+
+static bool misaligned(const void *p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u); }
+
+cnf_status cnf_forward(const cnf_plan *plan, const float *x, const float *w, const float *b,
+                       const float *gamma, const float *beta, float *out, int32_t *argmax,
+                       void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!plan) return CNF_ERR_NULL;
+    const cnf_desc &d = plan->d;
+    const bool need_affine = d.norm != CNF_NORM_NONE && d.affine;
+    if (!x || !w || !out) return CNF_ERR_NULL;
+    if ((b != nullptr) != (d.has_bias != 0)) return CNF_ERR_NULL;
+    if ((gamma != nullptr) != need_affine || (beta != nullptr) != need_affine) return CNF_ERR_NULL;
+    if ((argmax != nullptr) != (d.want_argmax != 0)) return CNF_ERR_NULL;
+    if (misaligned(x) || misaligned(w) || misaligned(b) || misaligned(gamma) ||
+        misaligned(beta) || misaligned(out) || misaligned(argmax) || misaligned(workspace))
+        return CNF_ERR_ALIGNMENT;
+    if (plan->workspace > 0 && (!workspace || workspace_bytes < plan->workspace))
+        return CNF_ERR_WORKSPACE;
+    if (d.N == 0) return CNF_OK;
+
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const float inv_div = 1.0f / d.divide_by;
+    const int D = d.in_dims[0], H = d.in_dims[1], W = d.in_dims[2];
+    const int norm_groups = d.norm == CNF_NORM_GROUP ? d.num_groups
+                          : d.norm == CNF_NORM_INSTANCE ? d.C_out : 0;
+    hipError_t e = hipSuccess;
+    switch (plan->family) {
+    case FAM_GN_MEAN: {
+        cnf::Conv3dGnMeanArgs a{x, w, b, gamma, beta, out, d.N, d.C_in, D, H, W, d.act,
+                                norm_groups ? norm_groups : d.C_out, d.eps, inv_div};
+        if (!norm_groups) a.num_groups = -1;  // plain mean of the activation
+        e = cnf::launch_conv3d_gn_mean(a, st);
+        break;
+    }
+    case FAM_SOFTMAX_POOL: {
+        cnf::Conv3dSoftmaxPoolArgs a{x, w, b, out, argmax, d.N, d.C_in, D, H, W, d.kernel,
+                                     plan->Do, plan->Ho, plan->Wo, plan->Dp, plan->Hp, plan->Wp,
+                                     d.act, d.pool_repeats > 1 ? 1 : 0};
+        e = cnf::launch_conv3d_softmax_pool(a, st);
+        break;
+    }
+    case FAM_SMALL: {
+        cnf::SmallConvNormArgs a{x, w, b, gamma, beta, out, d.N, d.C_in, D, H, W, d.kernel,
+                                 plan->Do, plan->Ho, plan->Wo, d.act, norm_groups, d.eps,
+                                 inv_div, d.reduce == CNF_RED_MEAN_SPATIAL ? 1 : 0};
+        e = cnf::launch_small_conv_norm(a, st);
+        break;
+    }
+    case FAM_IGEMM: {
+        cnf::Conv2dIgemmArgs a{x, w, b, gamma, beta, out, static_cast<float *>(workspace), d.N,
+                               d.C_in, H, W, plan->Ho, plan->Wo, norm_groups, d.eps, inv_div};
+        e = cnf::launch_conv2d_igemm(a, st);
+        break;
+    }
+    case FAM_CONVT: {
+        cnf::ConvT2dArgs a{x, w, b, gamma, beta, out, static_cast<float *>(workspace), d.N,
+                           d.C_in, d.C_out, H, W, d.groups, plan->Ho, plan->Wo, d.act,
+                           norm_groups, d.eps, inv_div};
+        e = cnf::launch_convt2d(a, st);
+        break;
+    }
+    default: return CNF_ERR_UNSUPPORTED;
+    }
+    return e == hipSuccess ? CNF_OK : CNF_ERR_HIP;
+}
+
+}  // extern "C"

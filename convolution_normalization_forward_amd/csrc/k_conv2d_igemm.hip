@@ -1,0 +1,300 @@
+// k_conv2d_igemm.hip -- Conv2d (C_out = 128, k = 3, C_in a multiple of 4) as
+// an implicit GEMM on fp32 MFMA, with bias and per-tile Welford partials in
+// the epilogue, followed by an in-place InstanceNorm / GroupNorm + divide pass.
+//
+// Page "Kimi-K2.6__l2_p17": Conv2d(64 -> 128, k = 3) -> InstanceNorm2d ->
+// divide by 2 on 128 x 64 x 128 x 128.  The second trace shows the conv is
+// compute-bound (arithmetic intensity ~190 FLOP/byte) and that a workgroup
+// per (sample, output channel) re-reads the input 128 times, so a tile must
+// cover every output channel.  Statistics need a whole 126 x 126 plane, which
+// no single tile sees; tiles publish Welford partials and a second pass merges
+// them and normalises in place.
+//
+// Mapping:
+//   * GEMM rows = the 128 output channels (A = weights), columns = output
+//     positions (B = im2col of x), K = C_in * 9 ordered (tap, channel).
+//   * A workgroup (8 waves) owns 128 channels x a 4-row x 64-column block of
+//     output positions of one sample; wave (wm, wn) computes channels
+//     64*wm .. +63 on output row wn as 2 x 2 tiles of v_mfma_f32_32x32x2f32.
+//   * K is walked in chunks of CC input channels: the chunk's input halo
+//     (CC x 6 x 66) and its weights (9*CC x 128, from a [ci][tap][co] copy the
+//     first kernel makes) are double-buffered in LDS; the next chunk is
+//     fetched into registers while the current one is multiplied.
+//   * Epilogue: bias, coalesced fp32 stores of y (32 consecutive positions per
+//     register), and per-channel Welford triples merged over lanes (DPP and a
+//     shuffle), waves (LDS) into one partial per (sample, tile, channel).
+#include "device.h"
+#include "kernels.h"
+
+namespace cnf {
+
+namespace {
+
+constexpr int CO = 128;
+constexpr int CC = 4;                    // input channels per K chunk
+constexpr int KC = 9 * CC;               // K per chunk
+constexpr int TR = 4, TC = 64;           // output tile: rows x cols
+constexpr int PITCH = 68;                // LDS row pitch of the input halo
+constexpr int CS = (TR + 2) * PITCH + 8; // LDS channel stride (== 32 mod 64)
+constexpr int WPITCH = CO + 32;          // LDS row pitch of the weight chunk (== 32 mod 64)
+constexpr int XS_FLOATS = CC * CS;
+constexpr int WS_FLOATS = KC * WPITCH;
+constexpr int BUF_FLOATS = XS_FLOATS + WS_FLOATS;
+constexpr int THREADS = 512;
+constexpr int XIN = CC * (TR + 2) * (TC + 2);          // halo floats per chunk
+constexpr int XPF = (XIN + THREADS - 1) / THREADS;     // per-thread prefetch (scalar)
+constexpr int WPF = (KC * CO / 4 + THREADS - 1) / THREADS;  // per-thread prefetch (float4)
+
+// w[co][ci][kh][kw] -> wt[ci][tap][co]
+__global__ void conv2d_weight_transpose_kernel(const float *__restrict__ w, float *__restrict__ wt,
+                                               int C_in)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    const int total = CO * C_in * 9;
+    if (i >= total) return;
+    const int co = i % CO, rest = i / CO;  // rest = ci * 9 + tap
+    wt[i] = w[(size_t)co * C_in * 9 + rest];
+}
+
+__device__ __forceinline__ void igemm_fetch(const float *__restrict__ xn, const float *__restrict__ wt,
+                                            int chunk, int H, int W, int tid,
+                                            const int (&xoff)[XPF], const bool (&xok)[XPF],
+                                            float (&xpf)[XPF], float4 (&wpf)[WPF])
+{
+    const float *xc = xn + (size_t)chunk * CC * H * W;
+#pragma unroll
+    for (int u = 0; u < XPF; ++u) {
+        const float v = xc[xoff[u]];
+        xpf[u] = xok[u] ? v : 0.0f;
+    }
+    const float4 *src = reinterpret_cast<const float4 *>(wt + (size_t)chunk * CC * 9 * CO);
+#pragma unroll
+    for (int u = 0; u < WPF; ++u) {
+        const int e = tid + u * THREADS;
+        wpf[u] = src[e < KC * CO / 4 ? e : 0];
+    }
+}
+
+__device__ __forceinline__ void igemm_stash(float *lds, int buf, const int (&xdst)[XPF],
+                                            const int (&wdst)[WPF], const float (&xpf)[XPF],
+                                            const float4 (&wpf)[WPF])
+{
+    float *xs = lds + buf * BUF_FLOATS;
+    float *ws = xs + XS_FLOATS;
+#pragma unroll
+    for (int u = 0; u < XPF; ++u)
+        if (xdst[u] >= 0) xs[xdst[u]] = xpf[u];
+#pragma unroll
+    for (int u = 0; u < WPF; ++u)
+        if (wdst[u] >= 0) *reinterpret_cast<float4 *>(ws + wdst[u]) = wpf[u];
+}
+
+__global__ __launch_bounds__(THREADS, 2)
+void conv2d_igemm_kernel(const float *__restrict__ x, const float *__restrict__ wt,
+                         const float *__restrict__ bias, float *__restrict__ y,
+                         float *__restrict__ partials, int C_in, int H, int W, int Ho, int Wo,
+                         int tiles_w, int tiles_per_sample)
+{
+    __shared__ float lds[2 * BUF_FLOATS];
+    float (*red)[CO][3] = reinterpret_cast<float (*)[CO][3]>(lds);  // after the K loop
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 2, wn = wave & 3;
+    const int h = lane >> 5, i32 = lane & 31;
+    const int tw = blockIdx.x, th = blockIdx.y, n = blockIdx.z;
+    const int row0 = th * TR, col0 = tw * TC;
+    const float *xn = x + (size_t)n * C_in * H * W;
+
+    // Per-thread staging slots: halo element e = tid + u*THREADS (clamped so
+    // every load is in bounds; out-of-image or surplus slots carry 0), and
+    // float4 e of the chunk's [ci][tap][co] weight rows.
+    int xoff[XPF], xdst[XPF];
+    bool xok[XPF];
+#pragma unroll
+    for (int u = 0; u < XPF; ++u) {
+        const int e = tid + u * THREADS;
+        const int ec = e < XIN ? e : XIN - 1;
+        const int cc = ec % (TC + 2), rest = ec / (TC + 2);
+        const int rr = rest % (TR + 2), c = rest / (TR + 2);
+        const int gr = row0 + rr, gc = col0 + cc;
+        xok[u] = e < XIN && gr < H && gc < W;
+        xoff[u] = xok[u] ? (c * H + gr) * W + gc : 0;
+        xdst[u] = e < XIN ? c * CS + rr * PITCH + cc : -1;
+    }
+    int wdst[WPF];
+#pragma unroll
+    for (int u = 0; u < WPF; ++u) {
+        const int e = tid + u * THREADS;
+        const int co4 = e % (CO / 4), r = e / (CO / 4);  // r = c * 9 + tap
+        const int c = r / 9, tap = r % 9;
+        wdst[u] = e < KC * CO / 4 ? (tap * CC + c) * WPITCH + co4 * 4 : -1;
+    }
+    float xpf[XPF];
+    float4 wpf[WPF];
+    v16f acc[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+
+    const int nchunks = C_in / CC;
+    igemm_fetch(xn, wt, 0, H, W, tid, xoff, xok, xpf, wpf);
+    igemm_stash(lds, 0, xdst, wdst, xpf, wpf);
+    __syncthreads();
+    for (int ch = 0; ch < nchunks; ++ch) {
+        const int buf = ch & 1;
+        if (ch + 1 < nchunks) igemm_fetch(xn, wt, ch + 1, H, W, tid, xoff, xok, xpf, wpf);
+        const float *xs = lds + buf * BUF_FLOATS;
+        const float *ws = xs + XS_FLOATS;
+        const float *wa = ws + h * WPITCH + 64 * wm + i32;
+        const float *xb = xs + h * CS + wn * PITCH + i32;
+#pragma unroll
+        for (int tap = 0; tap < 9; ++tap) {
+            const int kh = tap / 3, kw = tap % 3;
+#pragma unroll
+            for (int p = 0; p < CC / 2; ++p) {
+                const int s = tap * (CC / 2) + p;
+                const float a0 = wa[2 * s * WPITCH];
+                const float a1 = wa[2 * s * WPITCH + 32];
+                const float b0 = xb[2 * p * CS + kh * PITCH + kw];
+                const float b1 = xb[2 * p * CS + kh * PITCH + kw + 32];
+                acc[0][0] = mfma_32x32x2(a0, b0, acc[0][0]);
+                acc[0][1] = mfma_32x32x2(a0, b1, acc[0][1]);
+                acc[1][0] = mfma_32x32x2(a1, b0, acc[1][0]);
+                acc[1][1] = mfma_32x32x2(a1, b1, acc[1][1]);
+            }
+        }
+        if (ch + 1 < nchunks)  // buf^1 was last read in iteration ch-1
+            igemm_stash(lds, buf ^ 1, xdst, wdst, xpf, wpf);
+        __syncthreads();
+    }
+
+    // ---- epilogue
+    const int orow = row0 + wn;
+    const bool rvalid = orow < Ho;
+    float *yn = y + (size_t)n * CO * Ho * Wo;
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int co = 64 * wm + 32 * bi + 8 * (r >> 2) + 4 * h + (r & 3);
+            const float bc = bias ? bias[co] : 0.0f;
+            float cnt = 0.f, mean = 0.f, m2 = 0.f;
+#pragma unroll
+            for (int bj = 0; bj < 2; ++bj) {
+                const int col = col0 + 32 * bj + i32;
+                const float v = acc[bi][bj][r] + bc;
+                if (rvalid && col < Wo) {
+                    yn[((size_t)co * Ho + orow) * Wo + col] = v;
+                    cnt += 1.0f;
+                    welford_push(mean, m2, v, 1.0f / cnt);
+                }
+            }
+            row_chan16(cnt, mean, m2);
+            {
+                const float nb = __shfl_xor(cnt, 16, 64), mb = __shfl_xor(mean, 16, 64),
+                            qb = __shfl_xor(m2, 16, 64);
+                chan_merge(cnt, mean, m2, nb, mb, qb);
+            }
+            if (i32 == 0) {
+                red[wn][co][0] = cnt; red[wn][co][1] = mean; red[wn][co][2] = m2;
+            }
+        }
+    }
+    __syncthreads();
+    if (tid < CO) {
+        float cnt = 0.f, mean = 0.f, m2 = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) chan_merge(cnt, mean, m2, red[k][tid][0], red[k][tid][1], red[k][tid][2]);
+        const size_t tile = (size_t)th * tiles_w + tw;
+        float *pp = partials + (((size_t)n * tiles_per_sample + tile) * CO + tid) * 3;
+        pp[0] = cnt; pp[1] = mean; pp[2] = m2;
+    }
+}
+
+// One workgroup per (sample, channel): merge the channel's group partials in
+// a fixed order, then normalise the plane in place and divide.
+__global__ __launch_bounds__(256)
+void conv2d_norm_pass_kernel(float *__restrict__ y, const float *__restrict__ partials,
+                             const float *__restrict__ gamma, const float *__restrict__ beta,
+                             int C, int plane, int tiles_per_sample, int norm_groups, float eps,
+                             float inv_div)
+{
+    const int nc = blockIdx.x;
+    const int n = nc / C, c = nc % C;
+    __shared__ float coef[2];
+    if (threadIdx.x == 0 && norm_groups <= 0) {
+        coef[0] = inv_div;  // no norm: the divide alone
+        coef[1] = 0.0f;
+    } else if (threadIdx.x == 0) {
+        const int cg = C / norm_groups, g0 = (c / cg) * cg;
+        float cnt = 0.f, mean = 0.f, m2 = 0.f;
+        for (int j = 0; j < cg; ++j)
+            for (int t = 0; t < tiles_per_sample; ++t) {
+                const float *pp = partials + (((size_t)n * tiles_per_sample + t) * C + g0 + j) * 3;
+                chan_merge(cnt, mean, m2, pp[0], pp[1], pp[2]);
+            }
+        const float rstd = rsqrtf(m2 / cnt + eps);
+        const float ga = gamma ? gamma[c] : 1.0f, be = beta ? beta[c] : 0.0f;
+        coef[0] = rstd * ga * inv_div;
+        coef[1] = (be - mean * rstd * ga) * inv_div;
+    }
+    __syncthreads();
+    const float sc = coef[0], sh = coef[1];
+    float *p = y + (size_t)nc * plane;
+    if ((plane & 3) == 0) {
+        float4 *p4 = reinterpret_cast<float4 *>(p);
+        for (int i = threadIdx.x; i < plane / 4; i += 256) {
+            float4 v = p4[i];
+            v.x = v.x * sc + sh; v.y = v.y * sc + sh; v.z = v.z * sc + sh; v.w = v.w * sc + sh;
+            p4[i] = v;
+        }
+    } else {
+        for (int i = threadIdx.x; i < plane; i += 256) p[i] = p[i] * sc + sh;
+    }
+}
+
+}  // namespace
+
+bool conv2d_igemm_supported(int C_in, int C_out, int kernel, int groups, int H, int W, int act)
+{
+    return C_out == CO && kernel == 3 && groups == 1 && C_in % CC == 0 && C_in >= CC &&
+           H >= 3 && W >= 3 && act == ACT_NONE;
+}
+
+static size_t tiles_of(int Ho, int Wo)
+{
+    return (size_t)((Wo + TC - 1) / TC) * ((Ho + TR - 1) / TR);
+}
+
+size_t conv2d_igemm_workspace(int N, int C_in, int Ho, int Wo)
+{
+    // [N][tiles][C_out][3] Welford partials, then the [ci][tap][co] weight copy
+    return (size_t)N * tiles_of(Ho, Wo) * CO * 3 * sizeof(float) +
+           (size_t)C_in * 9 * CO * sizeof(float);
+}
+
+hipError_t launch_conv2d_igemm(const Conv2dIgemmArgs &a, hipStream_t st)
+{
+    const int tiles_w = (a.Wo + TC - 1) / TC, tiles_h = (a.Ho + TR - 1) / TR;
+    const int tps = tiles_w * tiles_h;
+    float *wt = a.partials + (size_t)a.N * tps * CO * 3;
+    {
+        const int total = CO * a.C_in * 9;
+        hipLaunchKernelGGL(conv2d_weight_transpose_kernel, dim3((total + 255) / 256), dim3(256), 0,
+                           st, a.w, wt, a.C_in);
+    }
+    hipLaunchKernelGGL(conv2d_igemm_kernel, dim3(tiles_w, tiles_h, a.N), dim3(THREADS), 0, st, a.x,
+                       wt, a.b, a.out, a.partials, a.C_in, a.H, a.W, a.Ho, a.Wo, tiles_w, tps);
+    if (a.norm_groups > 0 || a.inv_div != 1.0f) {
+        hipLaunchKernelGGL(conv2d_norm_pass_kernel, dim3(a.N * CO), dim3(256), 0, st, a.out,
+                           a.partials, a.gamma, a.beta, CO, a.Ho * a.Wo, tps, a.norm_groups,
+                           a.eps, a.inv_div);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace cnf

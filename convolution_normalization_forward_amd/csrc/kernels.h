@@ -1,0 +1,84 @@
+// kernels.h -- internal interface between the plan/dispatch layer and the
+// HIP kernel families.  Not part of the public C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace cnf {
+
+// ---- Conv3d (C_out 16, k 4) + act + GroupNorm + mean over D,H,W
+struct Conv3dGnMeanArgs {
+    const float *x, *w, *b, *gamma, *beta;
+    float *out;
+    int N, C_in, D, H, W;
+    int act, num_groups;
+    float eps, inv_div;
+};
+bool conv3d_gn_mean_supported(int C_in, int C_out, int kernel, int D, int H, int W, int act);
+size_t conv3d_gn_mean_lds_bytes(int C_in);
+hipError_t launch_conv3d_gn_mean(const Conv3dGnMeanArgs &a, hipStream_t st);
+
+// ---- Conv3d (C_out 16) + channel softmax + 4x4x4 max pool (+ argmax)
+struct Conv3dSoftmaxPoolArgs {
+    const float *x, *w, *b;
+    float *out;
+    int32_t *argmax;
+    int N, C_in, D, H, W, kernel;
+    int Do, Ho, Wo;      // conv output extents
+    int Dp, Hp, Wp;      // pooled extents
+    int act;
+    int two_stage;       // 1: tie order of two 2-pools; 0: one 4-pool
+};
+bool conv3d_softmax_pool_supported(int C_in, int C_out, int kernel, int act, int pool_total);
+hipError_t launch_conv3d_softmax_pool(const Conv3dSoftmaxPoolArgs &a, hipStream_t st);
+
+// ---- small conv (C_out 16), one workgroup per sample, norm + divide
+//      applied in registers, full output written once
+struct SmallConvNormArgs {
+    const float *x, *w, *b, *gamma, *beta;
+    float *out;
+    int N, C_in, D, H, W, kernel;
+    int Do, Ho, Wo;
+    int act, norm_groups;  // norm_groups 0: no norm
+    float eps, inv_div;
+    int reduce_mean;
+};
+bool small_conv_norm_supported(int C_in, int C_out, int kernel, int ndim, int D, int H, int W,
+                               int act);
+hipError_t launch_small_conv_norm(const SmallConvNormArgs &a, hipStream_t st);
+
+// ---- Conv2d implicit GEMM on fp32 MFMA (C_out 128, k 3) writing y and
+//      per-tile Welford partials, then in-place InstanceNorm/GroupNorm + divide
+struct Conv2dIgemmArgs {
+    const float *x, *w, *b, *gamma, *beta;
+    float *out;
+    float *partials;     // workspace: [N][tiles][C_out][3]
+    int N, C_in, H, W;
+    int Ho, Wo;
+    int norm_groups;     // 0: no norm; C_out: instance norm
+    float eps, inv_div;
+};
+bool conv2d_igemm_supported(int C_in, int C_out, int kernel, int groups, int H, int W, int act);
+size_t conv2d_igemm_workspace(int N, int C_in, int Ho, int Wo);
+hipError_t launch_conv2d_igemm(const Conv2dIgemmArgs &a, hipStream_t st);
+
+// ---- grouped ConvTranspose2d (8 in / 8 out per group, k 3, stride 1) +
+//      act writing y and per-tile Welford partials, then in-place GroupNorm
+struct ConvT2dArgs {
+    const float *x, *w, *b, *gamma, *beta;
+    float *out;
+    float *partials;     // workspace
+    int N, C_in, C_out, H, W, groups;
+    int Ho, Wo;
+    int act;
+    int norm_groups;     // 0: no norm; must equal groups otherwise
+    float eps, inv_div;
+};
+bool convt2d_supported(int C_in, int C_out, int kernel, int groups, int H, int W, int act,
+                       int norm, int num_groups);
+size_t convt2d_workspace(int N, int groups, int Ho, int Wo);
+hipError_t launch_convt2d(const ConvT2dArgs &a, hipStream_t st);
+
+}  // namespace cnf

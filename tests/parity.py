@@ -1,0 +1,61 @@
+"""Shared helpers of the GPU parity tests: run a workload through the C ABI
+on cuda:0 and compare it with the fp64 oracle element by element."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import cnf_inputs
+import convolution_normalization_forward_amd as cnf
+import oracle
+
+ATOL, RTOL = 2e-4, 1e-3   # |gpu - ref| <= ATOL + RTOL * |ref|
+
+
+def run_gpu(wl, x, p, dev="cuda:0"):
+    plan = cnf.Plan(cnf.make_desc(wl, N=x.shape[0]))
+    t = {k: (torch.from_numpy(v).to(dev) if v is not None else None) for k, v in p.items()}
+    xt = torch.from_numpy(x).to(dev)
+    out, idx = plan.forward(xt, t["w"], t["b"], t["gamma"], t["beta"])
+    torch.cuda.synchronize()
+    return plan, out, idx
+
+
+def check_close(got, ref, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    err = np.abs(got - ref)
+    bad = err > ATOL + RTOL * np.abs(ref)
+    if bad.any():
+        i = np.unravel_index(np.argmax(err - RTOL * np.abs(ref)), ref.shape)
+        raise AssertionError(f"{what}: {int(bad.sum())} of {ref.size} outside tolerance; worst at {i}: "
+                             f"gpu={got[i]!r} ref={ref[i]!r}")
+    return float(err.max())
+
+
+def check_argmax(got_idx, ref_idx, pre_pool, Pk, what=""):
+    """Argmax parity where the window's top two oracle values are separated by
+    more than the parity tolerance; returns the number of windows excluded.
+
+    pre_pool: oracle values on the conv grid (N, C, Do, Ho, Wo), float64;
+    Pk: total pool extent (4 for two 2-pools)."""
+    got_idx = np.asarray(got_idx).astype(np.int64)
+    N, C, Dp, Hp, Wp = ref_idx.shape
+    win = pre_pool[:, :, :Dp * Pk, :Hp * Pk, :Wp * Pk].reshape(N, C, Dp, Pk, Hp, Pk, Wp, Pk)
+    win = win.transpose(0, 1, 2, 4, 6, 3, 5, 7).reshape(N, C, Dp, Hp, Wp, -1)
+    top2 = np.sort(win, axis=-1)[..., -2:]
+    gap = top2[..., 1] - top2[..., 0]
+    clear = gap > ATOL + RTOL * np.abs(top2[..., 1])
+    mism = (got_idx != ref_idx) & clear
+    assert not mism.any(), f"{what}: {int(mism.sum())} argmax mismatches in clear windows"
+    # every reported index must name a voxel of its own window holding the max
+    Do, Ho, Wo = pre_pool.shape[2:]
+    d, h, w = got_idx // (Ho * Wo), (got_idx // Wo) % Ho, got_idx % Wo
+    od, oh, ow = np.indices((Dp, Hp, Wp))
+    assert ((d // Pk == od) & (h // Pk == oh) & (w // Pk == ow)).all(), f"{what}: index outside window"
+    return int((~clear).sum())
+
+
+def oracle_pre_pool(wl, x, p):
+    return oracle.pre_norm(wl, x, p["w"], p["b"])

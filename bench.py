@@ -1,0 +1,304 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused conv + norm forward path on one MI355X.
+
+A step is one call of cnf_forward on one batch of seeded synthetic input that
+is already resident in device memory.  The headline workload is the Conv3d
+3->16 k3 -> channel softmax -> MaxPool3d(2) x2 problem at batch 128
+(page "Kimi-K2.6__l2_p6"); every other workload is measured the same way and
+listed under "per_workload" in the same JSON line.
+
+Metric: effective TFLOP/s = 2 * N * C_out * |conv output grid| * (C_in/groups)
+* k^ndim / time (the nominal conv FLOPs), plus ms per step.  "roofline" puts
+the dominant kernel's ALGORITHMIC work per launch against the MI355X peak of
+the unit that bounds it, timed with HIP events on the launch stream.
+"cpu_baseline" is the fp64 oracle timed on the host cores on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP32_TFLOPS = 157.3     # MI355X dense fp32 (MFMA and packed vector)
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+HEADLINE = "conv3d_softmax_pool_n128"
+
+# Dominant kernel of each workload, as named by rocprofv3 (prefix match), its
+# bounding unit, and the ALGORITHMIC work per launch: the per-unit figure x the
+# units one launch processes (see the per-unit notes below).
+#   softmax-pool: per pooled window 64 voxels x 16 ch x C_in*k^3 MAC x 2.
+#   gn-mean:      per sample, the full conv (nothing skipped) -> nominal FLOPs.
+#   small:        the full conv -> nominal FLOPs.
+#   igemm:        the full conv -> nominal FLOPs.
+#   convt:        HBM bound: x read once + y written once (fp32).
+DOMINANT = {
+    "conv2d_in_div_n2": ("small_conv_norm_kernel", "mfma"),
+    "conv3d_softmax_pool_n128": ("conv3d_softmax_pool_kernel", "mfma"),
+    "conv3d_hswish_gn_mean_n1024": ("conv3d_k4_gn_mean_kernel", "mfma"),
+    "conv2d_in_div_n128": ("conv2d_igemm_kernel", "mfma"),
+    "convt2d_gelu_gn_n128": ("convt2d_g8_kernel", "hbm"),
+}
+
+
+def conv_out_grid(wl):
+    D, H, W = wl["in_dims"]
+    k = wl["kernel"]
+    if wl["kind"] == "conv_transpose":
+        return (1, H + k - 1, W + k - 1)
+    return ((D - k + 1) if wl["ndim"] == 3 else 1, H - k + 1, W - k + 1)
+
+
+def nominal_flops(wl):
+    Do, Ho, Wo = conv_out_grid(wl)
+    return 2.0 * wl["N"] * wl["C_out"] * Do * Ho * Wo * (wl["C_in"] // wl["groups"]) * \
+        wl["kernel"] ** wl["ndim"]
+
+
+def algorithmic_flops(wl):
+    if wl["reduce"] == "maxpool":
+        Do, Ho, Wo = conv_out_grid(wl)
+        P = wl["pool_kernel"] ** wl["pool_repeats"]
+        windows = wl["N"] * (Do // P) * (Ho // P) * (Wo // P)
+        K = (wl["C_in"] // wl["groups"]) * wl["kernel"] ** wl["ndim"]
+        return 2.0 * windows * P ** 3 * wl["C_out"] * K
+    return nominal_flops(wl)
+
+
+def algorithmic_bytes(wl):
+    """Minimum HBM bytes: read x, w, b once; write the output once."""
+    import cnf_inputs
+    n = 1
+    for v in cnf_inputs.x_shape(wl):
+        n *= v
+    w = 1
+    for v in cnf_inputs.w_shape(wl):
+        w *= v
+    Do, Ho, Wo = conv_out_grid(wl)
+    if wl["reduce"] == "mean":
+        out = wl["N"] * wl["C_out"]
+    elif wl["reduce"] == "maxpool":
+        P = wl["pool_kernel"] ** wl["pool_repeats"]
+        out = wl["N"] * wl["C_out"] * (Do // P) * (Ho // P) * (Wo // P) * (2 if wl["want_argmax"] else 1)
+    else:
+        out = wl["N"] * wl["C_out"] * Do * Ho * Wo
+    return 4.0 * (n + w + 3 * wl["C_out"] + out)
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "convolution_normalization_forward_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(name):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, or None if absent or taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(name)
+    if not e or e.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def time_workload(name, steps, warmup, dev):
+    import numpy as np
+    import torch
+
+    import cnf_inputs
+    import convolution_normalization_forward_amd as cnf
+
+    wl = cnf_inputs.workload(name)
+    plan = cnf.Plan(cnf.make_desc(wl))
+    p = cnf_inputs.gen_params(wl)
+    x = torch.from_numpy(cnf_inputs.gen_x(wl)).to(dev)
+    t = {k: (torch.from_numpy(v).to(dev) if v is not None else None) for k, v in p.items()}
+    out, idx, ws = plan.allocate(dev)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def step():
+        st = cnf.cnf_forward(plan.handle, x, t["w"], t["b"], t["gamma"], t["beta"], out, idx, ws,
+                             plan.workspace_bytes, sp)
+        if st != cnf.CNF_OK:
+            raise cnf.CnfError(st, "cnf_forward")
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = np.array([a.elapsed_time(b) for a, b in ev])  # ms
+    ms = float(per.mean())
+    fl = nominal_flops(wl)
+    afl = algorithmic_flops(wl)
+    ab = algorithmic_bytes(wl)
+    kern, bound = DOMINANT[name]
+    res = {
+        "workload": name,
+        "family": plan.describe().split()[0].split("=")[1],
+        "ms": ms,
+        "ms_min": float(per.min()),
+        "ms_wall_per_step": wall * 1e3 / steps,
+        "effective_tflops": fl / (ms * 1e-3) / 1e12,
+        "nominal_gflop": fl / 1e9,
+        "algorithmic_gflop": afl / 1e9,
+        "algorithmic_gb": ab / 1e9,
+        "frac_fp32_peak": fl / (ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS,
+        "frac_hbm_peak_algorithmic": ab / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "dominant_kernel": kern,
+        "bound": bound,
+    }
+    del x, out, idx, ws, t
+    torch.cuda.empty_cache()
+    return wl, res
+
+
+def cpu_baseline(name, seconds):
+    """The fp64 oracle, as it stands, on the host cores: whole batches of the
+    workload's first samples, repeated until `seconds` of wall time."""
+    import cnf_inputs
+    import oracle
+
+    wl = cnf_inputs.workload(name)
+    p = cnf_inputs.gen_params(wl)
+    n = min(wl["N"], 16)
+    x = cnf_inputs.gen_x(wl, range(n))
+    wl_n = dict(wl, N=n)
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.forward(wl_n, x, **p)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    fl = nominal_flops(wl_n) * done
+    return {
+        "value": fl / el / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"fp64 oracle on samples 0..{n - 1} of {name} (full conv grid), "
+                  f"{done} passes in {el:.1f} s",
+        "ms_per_sample": el * 1e3 / (done * n),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--only", action="store_true", help="measure the named workload only")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="first run 5 plain device copies of this many MiB (a known-size "
+                         "kernel for scaling HBM byte counters)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: every workload here is one GPU's whole problem "
+              "and the forward has no cross-GPU step; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import cnf_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] copy calibration: 5 copies of {args.copy_calibration_mib} MiB",
+              file=sys.stderr, flush=True)
+        del src, dst
+    names = [args.workload] if args.only else \
+        [args.workload] + [n for n in cnf_inputs.WORKLOAD_ORDER if n != args.workload]
+    per = {}
+    head_wl = None
+    for nm in names:
+        print(f"[bench] {nm}: timing {args.steps} steps after {args.warmup} warm-up",
+              file=sys.stderr, flush=True)
+        wl, r = time_workload(nm, args.steps, args.warmup, dev)
+        per[nm] = r
+        if nm == args.workload:
+            head_wl = wl
+    h = per[args.workload]
+
+    kern, bound = DOMINANT[args.workload]
+    if bound == "mfma":
+        achieved = algorithmic_flops(head_wl) / (h["ms"] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP32_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_TFLOPS}
+    else:
+        achieved = algorithmic_bytes(head_wl) / (h["ms"] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS}
+    roof["kernel"] = kern
+    roof["traffic"] = load_traffic(args.workload)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print(f"[bench] cpu baseline: oracle for ~{args.cpu_seconds:.0f} s", file=sys.stderr,
+              flush=True)
+        cpu = cpu_baseline(args.workload, args.cpu_seconds)
+
+    line = {
+        "metric": "fused conv+norm fwd effective TFLOP/s",
+        "value": h["effective_tflops"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": h["ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "N": head_wl["N"], "C_in": head_wl["C_in"],
+                   "C_out": head_wl["C_out"], "in_dims": list(head_wl["in_dims"]),
+                   "kernel": head_wl["kernel"], "parallelism": "single-gpu"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "per_workload": list(per.values()),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

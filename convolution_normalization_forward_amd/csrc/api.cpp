@@ -17,7 +17,8 @@ enum Family : int {
     FAM_SOFTMAX_POOL = 2,  // Conv3d C_out 16 + channel softmax + 4^3 max pool
     FAM_SMALL = 3,         // small conv C_out 16, one workgroup per sample
     FAM_IGEMM = 4,         // Conv2d C_out 128 k3 implicit GEMM + norm pass
-    FAM_CONVT = 5          // grouped ConvTranspose2d 8x8 per group + act + GroupNorm pass
+    FAM_CONVT = 5,         // grouped ConvTranspose2d 8x8 per group + act + GroupNorm pass
+    FAM_CONVT_FUSED = 6    // same, single write: cooperative kernel, cross-workgroup merge
 };
 
 const char *family_name(int f)
@@ -28,6 +29,7 @@ const char *family_name(int f)
     case FAM_SMALL: return "small_conv_norm(1wg/sample,mfma16x16x4)";
     case FAM_IGEMM: return "conv2d_igemm(mfma32x32x2)+norm_pass";
     case FAM_CONVT: return "convt2d_grouped8(mfma16x16x4,column-pair)+groupnorm_pass";
+    case FAM_CONVT_FUSED: return "convt2d_grouped8_gn_fused(cooperative,single-write)";
     default: return "none";
     }
 }
@@ -158,6 +160,10 @@ cnf_status cnf_plan_create(const cnf_desc *desc, cnf_plan **plan)
         if (cnf::convt2d_supported(d.C_in, d.C_out, k, d.groups, H, W, d.act, d.norm,
                                    d.num_groups))
             p.family = FAM_CONVT;
+        if (p.family == FAM_CONVT &&
+            cnf::convt2d_fused_supported(d.C_in, d.C_out, d.groups, H, W, d.act, d.norm,
+                                         d.num_groups))
+            p.family = FAM_CONVT_FUSED;
     }
     (void)norm_groups;
     if (!p.family) return CNF_ERR_UNSUPPORTED;
@@ -165,6 +171,12 @@ cnf_status cnf_plan_create(const cnf_desc *desc, cnf_plan **plan)
     p.workspace = 0;
     if (p.family == FAM_IGEMM) p.workspace = cnf::conv2d_igemm_workspace(d.N, d.C_in, p.Ho, p.Wo);
     if (p.family == FAM_CONVT) p.workspace = cnf::convt2d_workspace(d.N, d.groups, p.Ho, p.Wo);
+    if (p.family == FAM_CONVT_FUSED) {
+        // room for the two-pass fallback too (used if the grid cannot be co-resident)
+        const size_t a = cnf::convt2d_fused_workspace(d.N, d.groups, p.Ho);
+        const size_t b = cnf::convt2d_workspace(d.N, d.groups, p.Ho, p.Wo);
+        p.workspace = a > b ? a : b;
+    }
 
     cnf_plan *np = new (std::nothrow) cnf_plan(p);
     if (!np) return CNF_ERR_INVALID_DESC;
@@ -255,11 +267,18 @@ cnf_status cnf_forward(const cnf_plan *plan, const float *x, const float *w, con
         e = cnf::launch_conv2d_igemm(a, st);
         break;
     }
-    case FAM_CONVT: {
+    case FAM_CONVT:
+    case FAM_CONVT_FUSED: {
         cnf::ConvT2dArgs a{x, w, b, gamma, beta, out, static_cast<float *>(workspace), d.N,
                            d.C_in, d.C_out, H, W, d.groups, plan->Ho, plan->Wo, d.act,
                            norm_groups, d.eps, inv_div};
-        e = cnf::launch_convt2d(a, st);
+        e = hipErrorInvalidValue;
+        if (plan->family == FAM_CONVT_FUSED) {
+            e = cnf::launch_convt2d_fused(a, st);
+            if (e == hipErrorCooperativeLaunchTooLarge) (void)hipGetLastError();
+        }
+        if (plan->family == FAM_CONVT || e == hipErrorCooperativeLaunchTooLarge)
+            e = cnf::launch_convt2d(a, st);
         break;
     }
     default: return CNF_ERR_UNSUPPORTED;

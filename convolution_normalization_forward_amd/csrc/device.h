@@ -23,6 +23,30 @@ __device__ __forceinline__ v16f mfma_32x32x2(float a, float b, v16f c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
+
+// Raw buffer resource over [base, base + bytes): loads past the end return 0
+// and stores past it are dropped; offsets are 32-bit byte offsets.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, unsigned bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+__device__ __forceinline__ v4f buf_load4(__amdgpu_buffer_rsrc_t r, unsigned byte_off,
+                                         unsigned uniform_off = 0) {
+    return __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off,
+                                                                        (int)uniform_off, 0));
+}
+__device__ __forceinline__ float buf_load1(__amdgpu_buffer_rsrc_t r, unsigned byte_off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)byte_off, 0, 0));
+}
+// Non-temporal (streaming) 8-byte store.
+__device__ __forceinline__ void buf_store2_nt(v2f v, __amdgpu_buffer_rsrc_t r, unsigned byte_off,
+                                              unsigned uniform_off = 0) {
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u, v), r, (int)byte_off,
+                                          (int)uniform_off, 2);
+}
+
 // Rotate right by N lanes inside each row of 16 lanes (DPP row_ror).
 template <int N>
 __device__ __forceinline__ float row_ror(float v) {
@@ -57,9 +81,25 @@ __device__ __forceinline__ float hardswish(float x) {
     return x * fminf(fmaxf(x + 3.0f, 0.0f), 6.0f) * (1.0f / 6.0f);
 }
 
-// Exact (erf) GELU, x * Phi(x), through the device math library's erff.
+// Exact (erf) GELU, gelu(x) = x * Phi(x) = 0.5 x (1 + erf(x / sqrt 2)).
+// erf uses the rational-exponential approximation of Abramowitz & Stegun,
+// Handbook of Mathematical Functions (1964), formula 7.1.26 (|error| <= 1.5e-7
+// for x >= 0), with t = 1 / (1 + p z), z = |x| / sqrt 2.  For x < 0 the factor
+// 1 + erf(-z) = poly * exp(-z^2) is formed directly, so the negative tail keeps
+// its relative accuracy; for x >= 0 it is 2 - poly * exp(-z^2).
 __device__ __forceinline__ float gelu_erf(float x) {
-    return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
+    const float z = fabsf(x) * 0.70710678118654752f;
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
+    float poly = fmaf(t, 1.061405429f, -1.453152027f);
+    poly = fmaf(t, poly, 1.421413741f);
+    poly = fmaf(t, poly, -0.284496736f);
+    poly = fmaf(t, poly, 0.254829592f);
+    poly = poly * t;
+    // exp(-z^2) = exp2(-x^2 * log2(e) / 2)
+    const float e = __builtin_amdgcn_exp2f(x * x * -0.72134752044448170f);
+    const float pe = poly * e;
+    const float one_plus_erf = x < 0.0f ? pe : 2.0f - pe;
+    return 0.5f * x * one_plus_erf;
 }
 
 template <int ACT>

@@ -59,7 +59,7 @@ __global__ void conv2d_weight_transpose_kernel(const float *__restrict__ w, floa
 __device__ __forceinline__ void igemm_fetch(const float *__restrict__ xn, const float *__restrict__ wt,
                                             int chunk, int H, int W, int tid,
                                             const int (&xoff)[XPF], const bool (&xok)[XPF],
-                                            float (&xpf)[XPF], float4 (&wpf)[WPF])
+                                            float (&xpf)[XPF], v4f (&wpf)[WPF])
 {
     const float *xc = xn + (size_t)chunk * CC * H * W;
 #pragma unroll
@@ -67,7 +67,7 @@ __device__ __forceinline__ void igemm_fetch(const float *__restrict__ xn, const 
         const float v = xc[xoff[u]];
         xpf[u] = xok[u] ? v : 0.0f;
     }
-    const float4 *src = reinterpret_cast<const float4 *>(wt + (size_t)chunk * CC * 9 * CO);
+    const v4f *src = reinterpret_cast<const v4f *>(wt + (size_t)chunk * CC * 9 * CO);
 #pragma unroll
     for (int u = 0; u < WPF; ++u) {
         const int e = tid + u * THREADS;
@@ -77,7 +77,7 @@ __device__ __forceinline__ void igemm_fetch(const float *__restrict__ xn, const 
 
 __device__ __forceinline__ void igemm_stash(float *lds, int buf, const int (&xdst)[XPF],
                                             const int (&wdst)[WPF], const float (&xpf)[XPF],
-                                            const float4 (&wpf)[WPF])
+                                            const v4f (&wpf)[WPF])
 {
     float *xs = lds + buf * BUF_FLOATS;
     float *ws = xs + XS_FLOATS;
@@ -86,10 +86,10 @@ __device__ __forceinline__ void igemm_stash(float *lds, int buf, const int (&xds
         if (xdst[u] >= 0) xs[xdst[u]] = xpf[u];
 #pragma unroll
     for (int u = 0; u < WPF; ++u)
-        if (wdst[u] >= 0) *reinterpret_cast<float4 *>(ws + wdst[u]) = wpf[u];
+        if (wdst[u] >= 0) *reinterpret_cast<v4f *>(ws + wdst[u]) = wpf[u];
 }
 
-__global__ __launch_bounds__(THREADS, 2)
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4, 4)))
 void conv2d_igemm_kernel(const float *__restrict__ x, const float *__restrict__ wt,
                          const float *__restrict__ bias, float *__restrict__ y,
                          float *__restrict__ partials, int C_in, int H, int W, int Ho, int Wo,
@@ -131,7 +131,7 @@ void conv2d_igemm_kernel(const float *__restrict__ x, const float *__restrict__ 
         wdst[u] = e < KC * CO / 4 ? (tap * CC + c) * WPITCH + co4 * 4 : -1;
     }
     float xpf[XPF];
-    float4 wpf[WPF];
+    v4f wpf[WPF];
     v16f acc[2][2];
 #pragma unroll
     for (int a = 0; a < 2; ++a)

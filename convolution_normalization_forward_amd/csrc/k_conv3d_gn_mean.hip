@@ -146,7 +146,7 @@ void conv3d_k4_gn_mean_kernel(const float *__restrict__ x, const float *__restri
                 const int t = t0 + 4 * j;
                 if (t < T && t * 16 + c16 < P) {
                     cnt += 1.0f;
-                    const float rn = 1.0f / cnt;
+                    const float rn = __builtin_amdgcn_rcpf(cnt);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const float v = activate<ACT>(acc[j][r] + bch[r]);

@@ -31,7 +31,7 @@ namespace cnf {
 
 namespace {
 
-constexpr int WPW = 4;  // windows per wave
+constexpr int WPW = 2;  // windows per wave (the second one's patch is prefetched)
 constexpr int PP = 8;   // LDS row pitch of the patch
 
 template <int CI, int KS>
@@ -43,13 +43,6 @@ struct PatchGeom {
     static constexpr int K = CI * KS * KS * KS;
     static constexpr int NS = (K + 3) / 4;
 };
-
-__device__ __forceinline__ int tie_key(int a, int b, int c, int two_stage)
-{
-    return two_stage ? (((a >> 1) << 5) | ((b >> 1) << 4) | ((c >> 1) << 3) |
-                        ((a & 1) << 2) | ((b & 1) << 1) | (c & 1))
-                     : (a * 16 + b * 4 + c);
-}
 
 __device__ __forceinline__ void key_abc(int key, int two_stage, int &a, int &b, int &c)
 {
@@ -64,12 +57,7 @@ __device__ __forceinline__ void key_abc(int key, int two_stage, int &a, int &b, 
     }
 }
 
-__device__ __forceinline__ void better(float &best, int &bkey, float v, int key)
-{
-    if (v > best || (v == best && key < bkey)) { best = v; bkey = key; }
-}
-
-template <int CI, int KS, int ACT>
+template <int CI, int KS, int ACT, bool VEC>
 __global__ __launch_bounds__(64)
 void conv3d_softmax_pool_kernel(const float *__restrict__ x, const float *__restrict__ w,
                                 const float *__restrict__ bias, float *__restrict__ out,
@@ -77,12 +65,16 @@ void conv3d_softmax_pool_kernel(const float *__restrict__ x, const float *__rest
                                 int Ho, int Wo, int Dp, int Hp, int Wp, int two_stage)
 {
     using G = PatchGeom<CI, KS>;
-    __shared__ float patch[G::FLOATS];
+    static_assert(G::E <= 8 && G::E > 4, "patch rows are one float4 plus a tail");
+    constexpr int TAIL = G::E - 4;             // floats after the leading float4 of a row
+    constexpr int LSLOTS = (G::ROWS + 63) / 64;
+    __shared__ float patch[2][G::FLOATS + 8];  // + a dump row for surplus slots
 
     const int lane = threadIdx.x;
     const int q = lane >> 4, c16 = lane & 15;
+    const int HW = H * W;
 
-    // B operand: w[co = l%16][k = 4s + l/16], zero past K.
+    // B operand: w[co = l%16][k = 4s + l/16], zero past K; A operand offsets.
     float wreg[G::NS];
     int toff[G::NS];
 #pragma unroll
@@ -100,67 +92,120 @@ void conv3d_softmax_pool_kernel(const float *__restrict__ x, const float *__rest
     const float bc = bias ? bias[c16] : 0.0f;
     // A operand row m = l%16 is patch position (h = m/4, w = m%4)
     const int lbase = (c16 >> 2) * PP + (c16 & 3);
+    // tie keys of this lane's 16 voxels (j = depth, q = row, r = column)
+    const int kq = two_stage ? (((q >> 1) << 4) | ((q & 1) << 1)) : q * 4;
+
+    // Patch rows (ci, rd, rh) of E floats: a float4 and a TAIL part per row.
+    int gro[LSLOTS], lro[LSLOTS];
+#pragma unroll
+    for (int u = 0; u < LSLOTS; ++u) {
+        const int row = lane + 64 * u;
+        const bool rok = row < G::ROWS;
+        const int rr = rok ? row : 0;
+        const int rh = rr % G::E, rd = (rr / G::E) % G::E, ci = rr / (G::E * G::E);
+        gro[u] = (ci * D + rd) * HW + rh * W;
+        lro[u] = rok ? ci * G::CH + rd * (G::E * PP) + rh * PP : G::FLOATS;
+    }
 
     const int total = N * Dp * Hp * Wp;
-    const int HW = H * W;
-    for (int it = 0; it < WPW; ++it) {
-        const int win = blockIdx.x * WPW + it;
-        if (win >= total) break;  // wave-uniform
+    const int first = blockIdx.x * WPW;
+    auto window_base = [&](int win, int &n, int &od, int &oh, int &ow) {
         int t = win;
-        const int ow = t % Wp; t /= Wp;
-        const int oh = t % Hp; t /= Hp;
-        const int od = t % Dp;
-        const int n = t / Dp;
+        ow = t % Wp; t /= Wp;
+        oh = t % Hp; t /= Hp;
+        od = t % Dp;
+        n = t / Dp;
+        return ((size_t)n * CI * D + 4 * od) * HW + (size_t)(4 * oh) * W + 4 * ow;
+    };
 
-        // stage the input patch: rows of E floats starting at (4od+., 4oh+., 4ow)
-        const float *xs = x + (size_t)n * CI * D * HW;
-        __syncthreads();  // previous window's reads are done
-        for (int e = lane; e < G::ROWS * G::E; e += 64) {
-            const int col = e % G::E, row = e / G::E;
-            const int rh = row % G::E, rd = (row / G::E) % G::E, ci = row / (G::E * G::E);
-            patch[ci * G::CH + rd * (G::E * PP) + rh * PP + col] =
-                xs[((size_t)ci * D + 4 * od + rd) * HW + (size_t)(4 * oh + rh) * W + 4 * ow + col];
-        }
-        __syncthreads();
+    v4f pa[LSLOTS];
+    float pt[LSLOTS][TAIL];
+#define CNF_FETCH(GBASE)                                                              \
+    {                                                                                 \
+        const float *xb = x + (GBASE);                                                \
+        _Pragma("unroll") for (int u = 0; u < LSLOTS; ++u) {                          \
+            const float *src = xb + gro[u];                                           \
+            if constexpr (VEC) {                                                      \
+                pa[u] = *reinterpret_cast<const v4f *>(src);                       \
+            } else {                                                                  \
+                pa[u] = v4f{src[0], src[1], src[2], src[3]};                  \
+            }                                                                         \
+            _Pragma("unroll") for (int e = 0; e < TAIL; ++e) pt[u][e] = src[4 + e];   \
+        }                                                                             \
+    }
+#define CNF_STASH(BUF)                                                                \
+    {                                                                                 \
+        _Pragma("unroll") for (int u = 0; u < LSLOTS; ++u) {                          \
+            float *dst = &patch[BUF][lro[u]];                                         \
+            *reinterpret_cast<v4f *>(dst) = pa[u];                                 \
+            _Pragma("unroll") for (int e = 0; e < TAIL; ++e) dst[4 + e] = pt[u][e];   \
+        }                                                                             \
+    }
+
+    int n, od, oh, ow;
+    if (first >= total) return;
+    CNF_FETCH(window_base(first, n, od, oh, ow))
+    CNF_STASH(0)
+    for (int it = 0; it < WPW; ++it) {
+        const int win = first + it;
+        if (win >= total) break;  // wave-uniform
+        const int buf = it & 1;
+        int nn, od2, oh2, ow2;
+        const bool more = it + 1 < WPW && win + 1 < total;
+        window_base(win, n, od, oh, ow);
+        if (more) CNF_FETCH(window_base(win + 1, nn, od2, oh2, ow2))
+        __syncthreads();  // patch[buf] is complete
 
         v4f acc[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
+        const float *pb = patch[buf];
 #pragma unroll
         for (int s = 0; s < G::NS; ++s) {
             const int a0 = lbase + toff[s];
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                acc[j] = mfma_16x16x4(patch[a0 + j * G::E * PP], wreg[s], acc[j]);
+                acc[j] = mfma_16x16x4(pb[a0 + j * G::E * PP], wreg[s], acc[j]);
         }
 
-        float best = -1.0f;
-        int bkey = 1 << 30;
+        // activation (softmax over the 16 channels = the 16 lanes of a row)
+        float v[4][4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                float v = acc[j][r] + bc;
-                float pv;
+                float a = acc[j][r] + bc;
                 if constexpr (ACT == ACT_SOFTMAX) {
-                    const float m = row_max16(v);
-                    const float e = __expf(v - m);
+                    const float m = row_max16(a);
+                    const float e = __builtin_amdgcn_exp2f((a - m) * 1.4426950408889634f);
                     const float sum = row_sum16(e);
-                    pv = e / sum;
+                    a = e * __builtin_amdgcn_rcpf(sum);
                 } else {
-                    pv = activate<ACT>(v);
+                    a = activate<ACT>(a);
                 }
-                if (j == 0 && r == 0) { best = pv; bkey = tie_key(j, q, r, two_stage); }
-                else better(best, bkey, pv, tie_key(j, q, r, two_stage));
+                v[j][r] = a;
             }
         }
-        // across the 4 rows (h = q)
+        // window max, then the first voxel (in tie order) that attains it
+        float best = v[0][0];
 #pragma unroll
-        for (int sh = 16; sh <= 32; sh <<= 1) {
-            const float ov = __shfl_xor(best, sh, 64);
-            const int ok = __shfl_xor(bkey, sh, 64);
-            better(best, bkey, ov, ok);
-        }
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) best = fmaxf(best, v[j][r]);
+        best = fmaxf(best, __shfl_xor(best, 16, 64));
+        best = fmaxf(best, __shfl_xor(best, 32, 64));
+        int bkey = 1 << 30;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int key = two_stage ? (kq | ((j >> 1) << 5) | ((r >> 1) << 3) |
+                                             ((j & 1) << 2) | (r & 1))
+                                          : (kq | (j << 4) | r);
+                bkey = (v[j][r] == best) ? min(bkey, key) : bkey;
+            }
+        bkey = min(bkey, __shfl_xor(bkey, 16, 64));
+        bkey = min(bkey, __shfl_xor(bkey, 32, 64));
         if (q == 0) {
             int a, b, c;
             key_abc(bkey, two_stage, a, b, c);
@@ -169,7 +214,10 @@ void conv3d_softmax_pool_kernel(const float *__restrict__ x, const float *__rest
             if (argmax)
                 argmax[o] = ((4 * od + a) * Ho + (4 * oh + b)) * Wo + (4 * ow + c);
         }
+        if (more) CNF_STASH(buf ^ 1)  // buf^1 was last read in the previous iteration
     }
+#undef CNF_FETCH
+#undef CNF_STASH
 }
 
 template <int CI, int KS, int ACT>
@@ -177,9 +225,14 @@ hipError_t launch_t(const Conv3dSoftmaxPoolArgs &a, hipStream_t st)
 {
     const int total = a.N * a.Dp * a.Hp * a.Wp;
     const int grid = (total + WPW - 1) / WPW;
-    hipLaunchKernelGGL((conv3d_softmax_pool_kernel<CI, KS, ACT>), dim3(grid), dim3(64), 0, st,
-                       a.x, a.w, a.b, a.out, a.argmax, a.N, a.D, a.H, a.W, a.Ho, a.Wo, a.Dp,
-                       a.Hp, a.Wp, a.two_stage);
+    if (a.W % 4 == 0)
+        hipLaunchKernelGGL((conv3d_softmax_pool_kernel<CI, KS, ACT, true>), dim3(grid), dim3(64), 0,
+                           st, a.x, a.w, a.b, a.out, a.argmax, a.N, a.D, a.H, a.W, a.Ho, a.Wo,
+                           a.Dp, a.Hp, a.Wp, a.two_stage);
+    else
+        hipLaunchKernelGGL((conv3d_softmax_pool_kernel<CI, KS, ACT, false>), dim3(grid), dim3(64),
+                           0, st, a.x, a.w, a.b, a.out, a.argmax, a.N, a.D, a.H, a.W, a.Ho, a.Wo,
+                           a.Dp, a.Hp, a.Wp, a.two_stage);
     return hipGetLastError();
 }
 

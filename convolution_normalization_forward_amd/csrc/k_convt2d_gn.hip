@@ -91,7 +91,8 @@ void convt2d_g8_kernel(const float *__restrict__ x, const float *__restrict__ wt
     const int rows_here = min(R, Ho - i0);
     const int npairs = rows_here * PR;
     const int T = (npairs + 15) >> 4;
-    float cnt = 0.f, mean = 0.f, m2 = 0.f;
+    float s1 = 0.f, s2 = 0.f;  // per-lane sum and sum of squares (at most a few dozen values)
+    int cnt_i = 0;
     float *yg = y + ((size_t)n * C + (size_t)g * CG) * Ho * Wo;
 
     for (int t0 = wave; t0 < T; t0 += 4 * NB) {
@@ -131,15 +132,18 @@ void convt2d_g8_kernel(const float *__restrict__ x, const float *__restrict__ wt
                 v1.y = activate<ACT>(acc[j][3] + b1);
                 *reinterpret_cast<float2 *>(yg + (size_t)(2 * q) * Ho * Wo + o) = v0;
                 *reinterpret_cast<float2 *>(yg + (size_t)(2 * q + 1) * Ho * Wo + o) = v1;
-                cnt += 1.0f; welford_push(mean, m2, v0.x, 1.0f / cnt);
-                cnt += 1.0f; welford_push(mean, m2, v0.y, 1.0f / cnt);
-                cnt += 1.0f; welford_push(mean, m2, v1.x, 1.0f / cnt);
-                cnt += 1.0f; welford_push(mean, m2, v1.y, 1.0f / cnt);
+                s1 += (v0.x + v0.y) + (v1.x + v1.y);
+                s2 = fmaf(v0.x, v0.x, s2); s2 = fmaf(v0.y, v0.y, s2);
+                s2 = fmaf(v1.x, v1.x, s2); s2 = fmaf(v1.y, v1.y, s2);
+                cnt_i += 4;
             }
         }
     }
 
     // ---- one Welford triple for the whole workgroup (all 8 channels)
+    float cnt = (float)cnt_i;
+    float mean = cnt_i ? s1 / cnt : 0.0f;
+    float m2 = cnt_i ? fmaxf(s2 - s1 * mean, 0.0f) : 0.0f;
     row_chan16(cnt, mean, m2);
 #pragma unroll
     for (int sh = 16; sh <= 32; sh <<= 1) {

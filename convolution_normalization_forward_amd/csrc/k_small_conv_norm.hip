@@ -98,7 +98,7 @@ void small_conv_norm_kernel(const float *__restrict__ x, const float *__restrict
             for (int r = 0; r < 4; ++r) acc[i][r] = activate<ACT>(acc[i][r] + bch[r]);
             if (valid) {
                 cnt += 1.0f;
-                const float rn = 1.0f / cnt;
+                const float rn = __builtin_amdgcn_rcpf(cnt);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) welford_push(mean[r], m2[r], acc[i][r], rn);
             }

@@ -80,5 +80,12 @@ bool convt2d_supported(int C_in, int C_out, int kernel, int groups, int H, int W
                        int norm, int num_groups);
 size_t convt2d_workspace(int N, int groups, int Ho, int Wo);
 hipError_t launch_convt2d(const ConvT2dArgs &a, hipStream_t st);
+// single-write variant (W == 256, GroupNorm groups == conv groups): cooperative
+// persistent kernel; returns an error (and launches nothing) if the grid cannot
+// be made co-resident
+bool convt2d_fused_supported(int C_in, int C_out, int groups, int H, int W, int act, int norm,
+                             int num_groups);
+size_t convt2d_fused_workspace(int N, int groups, int Ho);
+hipError_t launch_convt2d_fused(const ConvT2dArgs &a, hipStream_t st);
 
 }  // namespace cnf

@@ -72,6 +72,13 @@ SMALL_CASES = [
     ("convt2d_gelu_gn_n128", dict(N=1, in_dims=(1, 7, 36))),
     ("convt2d_gelu_gn_n128", dict(N=2, C_in=8, C_out=8, groups=1, num_groups=1,
                                   in_dims=(1, 5, 4), act="none")),
+    # single-write cooperative transposed conv (W = 256): partial last slice,
+    # column tiles with masked rows, units that do not fill a round
+    ("convt2d_gelu_gn_n128", dict(N=2, C_in=16, C_out=16, groups=2, num_groups=2,
+                                  in_dims=(1, 30, 256))),
+    ("convt2d_gelu_gn_n128", dict(N=1, in_dims=(1, 21, 256))),
+    ("convt2d_gelu_gn_n128", dict(N=3, C_in=8, C_out=8, groups=1, num_groups=1,
+                                  in_dims=(1, 1, 256), act="hardswish")),
 ]
 
 
@@ -135,6 +142,33 @@ def test_repeatable_bitwise():
         _, a, _ = run_gpu(wl, x, p)
         _, b, _ = run_gpu(wl, x, p)
         assert torch.equal(a, b), name
+
+
+def test_fused_convt_wait_never_times_out():
+    # the single-write kernel raises a flag in its workspace (after the unit
+    # counters) if a cross-workgroup wait hit its bound; it must stay 0
+    import convolution_normalization_forward_amd as cnf
+    wl = cnf_inputs.workload("convt2d_gelu_gn_n128", N=6, in_dims=(1, 40, 256))
+    plan = cnf.Plan(cnf.make_desc(wl))
+    assert "fused" in plan.describe()
+    x = cnf_inputs.gen_x(wl)
+    p = cnf_inputs.gen_params(wl)
+    dev = "cuda:0"
+    t = {k: torch.from_numpy(v).to(dev) for k, v in p.items()}
+    out, _, ws = plan.allocate(dev)
+    ws.fill_(0xFF)
+    for _ in range(3):
+        st = cnf.cnf_forward(plan.handle, torch.from_numpy(x).to(dev), t["w"], t["b"], t["gamma"],
+                             t["beta"], out, None, ws, plan.workspace_bytes)
+        assert st == cnf.CNF_OK
+    torch.cuda.synchronize()
+    U = wl["N"] * wl["groups"]
+    words = ws[: 4 * (U + 1)].view(torch.int32).cpu()
+    assert int(words[U]) == 0, "cross-workgroup wait timed out"
+    S = -(-(wl["in_dims"][1] + 2) // 12)
+    assert (words[:U] == S).all()  # every slice of every unit arrived exactly once
+    ref, _ = oracle.forward(wl, x, **p)
+    check_close(out.cpu().numpy(), ref, "fused convt repeated")
 
 
 def test_empty_batch_is_a_noop():

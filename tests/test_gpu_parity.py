@@ -148,7 +148,7 @@ def test_fused_convt_wait_never_times_out():
     # the single-write kernel raises a flag in its workspace (after the unit
     # counters) if a cross-workgroup wait hit its bound; it must stay 0
     import convolution_normalization_forward_amd as cnf
-    wl = cnf_inputs.workload("convt2d_gelu_gn_n128", N=6, in_dims=(1, 40, 256))
+    wl = cnf_inputs.workload("convt2d_gelu_gn_n128", N=6, in_dims=(1, 70, 256))
     plan = cnf.Plan(cnf.make_desc(wl))
     assert "fused" in plan.describe()
     x = cnf_inputs.gen_x(wl)
@@ -165,7 +165,7 @@ def test_fused_convt_wait_never_times_out():
     U = wl["N"] * wl["groups"]
     words = ws[: 4 * (U + 1)].view(torch.int32).cpu()
     assert int(words[U]) == 0, "cross-workgroup wait timed out"
-    S = -(-(wl["in_dims"][1] + 2) // 12)
+    S = -(-(wl["in_dims"][1] + 2) // 26)  # 26 output rows per slice
     assert (words[:U] == S).all()  # every slice of every unit arrived exactly once
     ref, _ = oracle.forward(wl, x, **p)
     check_close(out.cpu().numpy(), ref, "fused convt repeated")

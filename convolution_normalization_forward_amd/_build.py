@@ -29,13 +29,19 @@ FLAGS = [
 ]
 
 
+# Extra flags per source.  The softmax-pool kernel's inputs and intermediates are
+# finite (softmax of finite logits), so NaN-aware min/max is not needed there and
+# the DPP row reductions fold into single v_max_f32_dpp / v_add_f32_dpp ops.
+FILE_FLAGS = {"k_conv3d_softmax_pool.hip": ["-fno-honor-nans"]}
+
+
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + FLAGS + ["-x", "hip", "-c", src, "-o", obj]
+    cmd = [HIPCC] + FLAGS + FILE_FLAGS.get(os.path.basename(src), []) + ["-x", "hip", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

@@ -48,11 +48,13 @@ __device__ __forceinline__ void buf_store2_nt(v2f v, __amdgpu_buffer_rsrc_t r, u
 }
 
 // Rotate right by N lanes inside each row of 16 lanes (DPP row_ror).
+// (bound_ctrl set: every lane of a row rotation has a source, and this form lets
+// the compiler fold the move into the consuming VALU op as a DPP operand.)
 template <int N>
 __device__ __forceinline__ float row_ror(float v) {
     static_assert(N >= 1 && N <= 15, "row_ror amount");
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v),
-                                                             0x120 + N, 0xf, 0xf, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                0x120 + N, 0xf, 0xf, true));
 }
 template <int N>
 __device__ __forceinline__ int row_ror_i(int v) {

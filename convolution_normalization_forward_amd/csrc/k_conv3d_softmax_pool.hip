@@ -9,8 +9,10 @@
 // output window needs exactly 4x4x4 conv voxels x 16 channels, and nothing
 // else is computed.
 //
-// Mapping: one wave per pooled window (n, od, oh, ow); a workgroup is one
-// wave and walks WPW consecutive windows.
+// Mapping: one wave per pooled window (n, od, oh, ow).  A workgroup is one
+// wave; the grid is one wave per resident slot (16 per CU) and each wave walks
+// the windows blockIdx, blockIdx + grid, ..., prefetching the next window's
+// input patch into registers while the current one is multiplied.
 //   * The window's input patch (C_in x (4+k-1)^3) is staged in LDS with row
 //     pitch 8.
 //   * Tile j (j = 0..3) is conv depth 4*od + j: a 16x16 MFMA result with
@@ -31,7 +33,7 @@ namespace cnf {
 
 namespace {
 
-constexpr int WPW = 2;  // windows per wave (the second one's patch is prefetched)
+constexpr int WAVES_PER_CU = 16;  // persistent grid: one wave per resident slot (4 per SIMD)
 constexpr int PP = 8;   // LDS row pitch of the patch
 
 template <int CI, int KS>
@@ -42,6 +44,12 @@ struct PatchGeom {
     static constexpr int FLOATS = CI * CH;
     static constexpr int K = CI * KS * KS * KS;
     static constexpr int NS = (K + 3) / 4;
+    // LDS offset of tap k = (ci, kd, kh, kw) inside the patch (0 past K: zero weight)
+    static constexpr int tap_off(int k) {
+        return k < K ? (k / (KS * KS * KS)) * CH + ((k / (KS * KS)) % KS) * (E * PP) +
+                           ((k / KS) % KS) * PP + k % KS
+                     : 0;
+    }
 };
 
 __device__ __forceinline__ void key_abc(int key, int two_stage, int &a, int &b, int &c)
@@ -57,12 +65,12 @@ __device__ __forceinline__ void key_abc(int key, int two_stage, int &a, int &b, 
     }
 }
 
-template <int CI, int KS, int ACT, bool VEC>
+template <int CI, int KS, int ACT, bool VEC, bool TWO>
 __global__ __launch_bounds__(64)
 void conv3d_softmax_pool_kernel(const float *__restrict__ x, const float *__restrict__ w,
                                 const float *__restrict__ bias, float *__restrict__ out,
                                 int32_t *__restrict__ argmax, int N, int D, int H, int W,
-                                int Ho, int Wo, int Dp, int Hp, int Wp, int two_stage)
+                                int Ho, int Wo, int Dp, int Hp, int Wp)
 {
     using G = PatchGeom<CI, KS>;
     static_assert(G::E <= 8 && G::E > 4, "patch rows are one float4 plus a tail");
@@ -74,26 +82,23 @@ void conv3d_softmax_pool_kernel(const float *__restrict__ x, const float *__rest
     const int q = lane >> 4, c16 = lane & 15;
     const int HW = H * W;
 
-    // B operand: w[co = l%16][k = 4s + l/16], zero past K; A operand offsets.
+    // B operand: w[co = l%16][k = 4s + l/16], zero past K.  A operand offset of
+    // tap k in the patch; the four lane rows q take compile-time values.
     float wreg[G::NS];
     int toff[G::NS];
 #pragma unroll
     for (int s = 0; s < G::NS; ++s) {
         const int k = 4 * s + q;
         wreg[s] = k < G::K ? w[c16 * G::K + k] : 0.0f;
-        int off = 0;
-        if (k < G::K) {
-            const int kw = k % KS, kh = (k / KS) % KS, kd = (k / (KS * KS)) % KS,
-                      ci = k / (KS * KS * KS);
-            off = ci * G::CH + kd * (G::E * PP) + kh * PP + kw;
-        }
-        toff[s] = off;
+        const int t0 = G::tap_off(4 * s), t1 = G::tap_off(4 * s + 1);
+        const int t2 = G::tap_off(4 * s + 2), t3 = G::tap_off(4 * s + 3);
+        toff[s] = q < 2 ? (q == 0 ? t0 : t1) : (q == 2 ? t2 : t3);
     }
     const float bc = bias ? bias[c16] : 0.0f;
     // A operand row m = l%16 is patch position (h = m/4, w = m%4)
     const int lbase = (c16 >> 2) * PP + (c16 & 3);
     // tie keys of this lane's 16 voxels (j = depth, q = row, r = column)
-    const int kq = two_stage ? (((q >> 1) << 4) | ((q & 1) << 1)) : q * 4;
+    const int kq = TWO ? (((q >> 1) << 4) | ((q & 1) << 1)) : q * 4;
 
     // Patch rows (ci, rd, rh) of E floats: a float4 and a TAIL part per row.
     int gro[LSLOTS], lro[LSLOTS];
@@ -108,7 +113,7 @@ void conv3d_softmax_pool_kernel(const float *__restrict__ x, const float *__rest
     }
 
     const int total = N * Dp * Hp * Wp;
-    const int first = blockIdx.x * WPW;
+    const int first = blockIdx.x, stride = gridDim.x;  // windows first, first+stride, ...
     auto window_base = [&](int win, int &n, int &od, int &oh, int &ow) {
         int t = win;
         ow = t % Wp; t /= Wp;
@@ -146,14 +151,12 @@ void conv3d_softmax_pool_kernel(const float *__restrict__ x, const float *__rest
     if (first >= total) return;
     CNF_FETCH(window_base(first, n, od, oh, ow))
     CNF_STASH(0)
-    for (int it = 0; it < WPW; ++it) {
-        const int win = first + it;
-        if (win >= total) break;  // wave-uniform
-        const int buf = it & 1;
+    int buf = 0;
+    for (int win = first; win < total; win += stride) {  // wave-uniform
         int nn, od2, oh2, ow2;
-        const bool more = it + 1 < WPW && win + 1 < total;
+        const bool more = win + stride < total;
         window_base(win, n, od, oh, ow);
-        if (more) CNF_FETCH(window_base(win + 1, nn, od2, oh2, ow2))
+        if (more) CNF_FETCH(window_base(win + stride, nn, od2, oh2, ow2))
         __syncthreads();  // patch[buf] is complete
 
         v4f acc[4];
@@ -199,41 +202,56 @@ void conv3d_softmax_pool_kernel(const float *__restrict__ x, const float *__rest
         for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int key = two_stage ? (kq | ((j >> 1) << 5) | ((r >> 1) << 3) |
-                                             ((j & 1) << 2) | (r & 1))
-                                          : (kq | (j << 4) | r);
+                const int key = TWO ? (kq | ((j >> 1) << 5) | ((r >> 1) << 3) |
+                                       ((j & 1) << 2) | (r & 1))
+                                    : (kq | (j << 4) | r);
                 bkey = (v[j][r] == best) ? min(bkey, key) : bkey;
             }
         bkey = min(bkey, __shfl_xor(bkey, 16, 64));
         bkey = min(bkey, __shfl_xor(bkey, 32, 64));
         if (q == 0) {
             int a, b, c;
-            key_abc(bkey, two_stage, a, b, c);
+            key_abc(bkey, TWO, a, b, c);
             const size_t o = (((size_t)n * 16 + c16) * Dp + od) * Hp * Wp + (size_t)oh * Wp + ow;
             out[o] = best;
             if (argmax)
                 argmax[o] = ((4 * od + a) * Ho + (4 * oh + b)) * Wo + (4 * ow + c);
         }
         if (more) CNF_STASH(buf ^ 1)  // buf^1 was last read in the previous iteration
+        buf ^= 1;
     }
 #undef CNF_FETCH
 #undef CNF_STASH
 }
 
+template <int CI, int KS, int ACT, bool TWO>
+hipError_t launch_t2(const Conv3dSoftmaxPoolArgs &a, hipStream_t st)
+{
+    const int total = a.N * a.Dp * a.Hp * a.Wp;
+    static int cus[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (!cus[dev & 63]) {
+        e = hipDeviceGetAttribute(&cus[dev & 63], hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+    }
+    const int grid = total < cus[dev & 63] * WAVES_PER_CU ? total : cus[dev & 63] * WAVES_PER_CU;
+    if (a.W % 4 == 0)
+        hipLaunchKernelGGL((conv3d_softmax_pool_kernel<CI, KS, ACT, true, TWO>), dim3(grid), dim3(64),
+                           0, st, a.x, a.w, a.b, a.out, a.argmax, a.N, a.D, a.H, a.W, a.Ho, a.Wo,
+                           a.Dp, a.Hp, a.Wp);
+    else
+        hipLaunchKernelGGL((conv3d_softmax_pool_kernel<CI, KS, ACT, false, TWO>), dim3(grid),
+                           dim3(64), 0, st, a.x, a.w, a.b, a.out, a.argmax, a.N, a.D, a.H, a.W,
+                           a.Ho, a.Wo, a.Dp, a.Hp, a.Wp);
+    return hipGetLastError();
+}
+
 template <int CI, int KS, int ACT>
 hipError_t launch_t(const Conv3dSoftmaxPoolArgs &a, hipStream_t st)
 {
-    const int total = a.N * a.Dp * a.Hp * a.Wp;
-    const int grid = (total + WPW - 1) / WPW;
-    if (a.W % 4 == 0)
-        hipLaunchKernelGGL((conv3d_softmax_pool_kernel<CI, KS, ACT, true>), dim3(grid), dim3(64), 0,
-                           st, a.x, a.w, a.b, a.out, a.argmax, a.N, a.D, a.H, a.W, a.Ho, a.Wo,
-                           a.Dp, a.Hp, a.Wp, a.two_stage);
-    else
-        hipLaunchKernelGGL((conv3d_softmax_pool_kernel<CI, KS, ACT, false>), dim3(grid), dim3(64),
-                           0, st, a.x, a.w, a.b, a.out, a.argmax, a.N, a.D, a.H, a.W, a.Ho, a.Wo,
-                           a.Dp, a.Hp, a.Wp, a.two_stage);
-    return hipGetLastError();
+    return a.two_stage ? launch_t2<CI, KS, ACT, true>(a, st) : launch_t2<CI, KS, ACT, false>(a, st);
 }
 
 }  // namespace

@@ -47,6 +47,18 @@ __device__ __forceinline__ void buf_store2_nt(v2f v, __amdgpu_buffer_rsrc_t r, u
                                           (int)uniform_off, 2);
 }
 
+// Workgroups are dispatched round-robin over the XCDs (linear workgroup id
+// L runs on XCD L % NXCD), and each XCD has its own L2.  xcd_remap turns L
+// into a tile index such that every XCD gets one contiguous range of tiles,
+// so neighbouring tiles (which share input halos) hit the same L2.
+// Bijective on [0, total) for any total.
+constexpr int NXCD = 8;
+__device__ __forceinline__ int xcd_remap(int L, int total) {
+    const int q = total / NXCD, r = total % NXCD;
+    const int x = L % NXCD, k = L / NXCD;
+    return x * q + (x < r ? x : r) + k;
+}
+
 // Rotate right by N lanes inside each row of 16 lanes (DPP row_ror).
 // (bound_ctrl set: every lane of a row rotation has a source, and this form lets
 // the compiler fold the move into the consuming VALU op as a DPP operand.)

@@ -102,7 +102,12 @@ void conv2d_igemm_kernel(const float *__restrict__ x, const float *__restrict__ 
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 2, wn = wave & 3;
     const int h = lane >> 5, i32 = lane & 31;
-    const int tw = blockIdx.x, th = blockIdx.y, n = blockIdx.z;
+    // XCD-aware tile order: each XCD takes a contiguous run of (n, row tile,
+    // column tile), so vertically adjacent tiles share their halo rows in L2.
+    const int tiles_h = gridDim.y;
+    const int L = blockIdx.x + gridDim.x * (blockIdx.y + tiles_h * blockIdx.z);
+    const int T = xcd_remap(L, gridDim.x * tiles_h * gridDim.z);
+    const int tw = T % tiles_w, th = (T / tiles_w) % tiles_h, n = T / (tiles_w * tiles_h);
     const int row0 = th * TR, col0 = tw * TC;
     const float *xn = x + (size_t)n * C_in * H * W;
 

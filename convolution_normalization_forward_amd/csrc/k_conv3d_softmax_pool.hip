@@ -113,7 +113,16 @@ void conv3d_softmax_pool_kernel(const float *__restrict__ x, const float *__rest
     }
 
     const int total = N * Dp * Hp * Wp;
-    const int first = blockIdx.x, stride = gridDim.x;  // windows first, first+stride, ...
+    // XCD x owns windows [lo_x, hi_x) (contiguous, so neighbouring windows share
+    // its L2); its waves (ids L = x, x + NXCD, ...) stride through that range.
+    // (A grid smaller than NXCD just strides over all windows.)
+    const int NG = gridDim.x, L = blockIdx.x;
+    const bool split = NG >= NXCD;
+    const int xcd = L % NXCD, slot = L / NXCD;
+    const int waves_here = NG / NXCD + (xcd < NG % NXCD ? 1 : 0);
+    const int lo = split ? xcd_remap(xcd, total) : 0;
+    const int hi = split ? lo + total / NXCD + (xcd < total % NXCD ? 1 : 0) : total;
+    const int first = split ? lo + slot : L, stride = split ? waves_here : NG;
     auto window_base = [&](int win, int &n, int &od, int &oh, int &ow) {
         int t = win;
         ow = t % Wp; t /= Wp;
@@ -148,13 +157,13 @@ void conv3d_softmax_pool_kernel(const float *__restrict__ x, const float *__rest
     }
 
     int n, od, oh, ow;
-    if (first >= total) return;
+    if (first >= hi) return;
     CNF_FETCH(window_base(first, n, od, oh, ow))
     CNF_STASH(0)
     int buf = 0;
-    for (int win = first; win < total; win += stride) {  // wave-uniform
+    for (int win = first; win < hi; win += stride) {  // wave-uniform
         int nn, od2, oh2, ow2;
-        const bool more = win + stride < total;
+        const bool more = win + stride < hi;
         window_base(win, n, od, oh, ow);
         if (more) CNF_FETCH(window_base(win + stride, nn, od2, oh2, ow2))
         __syncthreads();  // patch[buf] is complete

@@ -187,17 +187,22 @@ void conv2d_igemm_kernel(const float *__restrict__ x, const float *__restrict__ 
         for (int r = 0; r < 16; ++r) {
             const int co = 64 * wm + 32 * bi + 8 * (r >> 2) + 4 * h + (r & 3);
             const float bc = bias ? bias[co] : 0.0f;
-            float cnt = 0.f, mean = 0.f, m2 = 0.f;
+            float s1 = 0.f, s2 = 0.f;
+            int ni = 0;
 #pragma unroll
             for (int bj = 0; bj < 2; ++bj) {
                 const int col = col0 + 32 * bj + i32;
                 const float v = acc[bi][bj][r] + bc;
                 if (rvalid && col < Wo) {
                     yn[((size_t)co * Ho + orow) * Wo + col] = v;
-                    cnt += 1.0f;
-                    welford_push(mean, m2, v, 1.0f / cnt);
+                    s1 += v;
+                    s2 = fmaf(v, v, s2);
+                    ++ni;
                 }
             }
+            float cnt = (float)ni;
+            float mean = ni ? s1 / cnt : 0.0f;
+            float m2 = ni ? fmaxf(s2 - s1 * mean, 0.0f) : 0.0f;
             row_chan16(cnt, mean, m2);
             {
                 const float nb = __shfl_xor(cnt, 16, 64), mb = __shfl_xor(mean, 16, 64),
@@ -220,8 +225,9 @@ void conv2d_igemm_kernel(const float *__restrict__ x, const float *__restrict__ 
     }
 }
 
-// One workgroup per (sample, channel): merge the channel's group partials in
-// a fixed order, then normalise the plane in place and divide.
+// One workgroup per (sample, channel): merge the group's per-tile partials in
+// a fixed order (each thread folds a strided subset, then thread 0 folds the
+// 256 results in thread order), then normalise the plane in place and divide.
 __global__ __launch_bounds__(256)
 void conv2d_norm_pass_kernel(float *__restrict__ y, const float *__restrict__ partials,
                              const float *__restrict__ gamma, const float *__restrict__ beta,
@@ -230,35 +236,49 @@ void conv2d_norm_pass_kernel(float *__restrict__ y, const float *__restrict__ pa
 {
     const int nc = blockIdx.x;
     const int n = nc / C, c = nc % C;
+    const int tid = threadIdx.x;
+    __shared__ float tri[256][3];
     __shared__ float coef[2];
-    if (threadIdx.x == 0 && norm_groups <= 0) {
+    if (norm_groups > 0) {
+        const int cg = C / norm_groups, g0 = (c / cg) * cg;
+        const int items = cg * tiles_per_sample;  // (channel j, tile t) pairs
+        float cnt = 0.f, mean = 0.f, m2 = 0.f;
+        for (int i = tid; i < items; i += 256) {
+            const int j = i / tiles_per_sample, t = i % tiles_per_sample;
+            const float *pp = partials + (((size_t)n * tiles_per_sample + t) * C + g0 + j) * 3;
+            chan_merge(cnt, mean, m2, pp[0], pp[1], pp[2]);
+        }
+        tri[tid][0] = cnt; tri[tid][1] = mean; tri[tid][2] = m2;
+        __syncthreads();
+        if (tid == 0) {
+            float tc = 0.f, tm = 0.f, tq = 0.f;
+            for (int k = 0; k < 256; ++k) chan_merge(tc, tm, tq, tri[k][0], tri[k][1], tri[k][2]);
+            const float rstd = rsqrtf(tq / tc + eps);
+            const float ga = gamma ? gamma[c] : 1.0f, be = beta ? beta[c] : 0.0f;
+            coef[0] = rstd * ga * inv_div;
+            coef[1] = (be - tm * rstd * ga) * inv_div;
+        }
+    } else if (tid == 0) {
         coef[0] = inv_div;  // no norm: the divide alone
         coef[1] = 0.0f;
-    } else if (threadIdx.x == 0) {
-        const int cg = C / norm_groups, g0 = (c / cg) * cg;
-        float cnt = 0.f, mean = 0.f, m2 = 0.f;
-        for (int j = 0; j < cg; ++j)
-            for (int t = 0; t < tiles_per_sample; ++t) {
-                const float *pp = partials + (((size_t)n * tiles_per_sample + t) * C + g0 + j) * 3;
-                chan_merge(cnt, mean, m2, pp[0], pp[1], pp[2]);
-            }
-        const float rstd = rsqrtf(m2 / cnt + eps);
-        const float ga = gamma ? gamma[c] : 1.0f, be = beta ? beta[c] : 0.0f;
-        coef[0] = rstd * ga * inv_div;
-        coef[1] = (be - mean * rstd * ga) * inv_div;
     }
     __syncthreads();
     const float sc = coef[0], sh = coef[1];
     float *p = y + (size_t)nc * plane;
     if ((plane & 3) == 0) {
-        float4 *p4 = reinterpret_cast<float4 *>(p);
-        for (int i = threadIdx.x; i < plane / 4; i += 256) {
-            float4 v = p4[i];
-            v.x = v.x * sc + sh; v.y = v.y * sc + sh; v.z = v.z * sc + sh; v.w = v.w * sc + sh;
-            p4[i] = v;
+        v4f *p4 = reinterpret_cast<v4f *>(p);
+        const int n4 = plane / 4;
+        int i = tid;
+        for (; i + 3 * 256 < n4; i += 4 * 256) {  // four loads in flight per thread
+            v4f a0 = p4[i], a1 = p4[i + 256], a2 = p4[i + 512], a3 = p4[i + 768];
+            p4[i] = a0 * sc + sh;
+            p4[i + 256] = a1 * sc + sh;
+            p4[i + 512] = a2 * sc + sh;
+            p4[i + 768] = a3 * sc + sh;
         }
+        for (; i < n4; i += 256) p4[i] = p4[i] * sc + sh;
     } else {
-        for (int i = threadIdx.x; i < plane; i += 256) p[i] = p[i] * sc + sh;
+        for (int i = tid; i < plane; i += 256) p[i] = p[i] * sc + sh;
     }
 }
 

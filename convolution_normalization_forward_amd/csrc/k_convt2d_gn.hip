@@ -163,7 +163,8 @@ void convt2d_g8_kernel(const float *__restrict__ x, const float *__restrict__ wt
 }
 
 // One workgroup per (sample, channel): merge the group's row-block partials
-// in a fixed order, then normalise the channel's plane in place.
+// in a fixed order (strided per thread, then in thread order), then normalise
+// the channel's plane in place.
 __global__ __launch_bounds__(256)
 void convt2d_gn_pass_kernel(float *__restrict__ y, const float *__restrict__ partials,
                             const float *__restrict__ gamma, const float *__restrict__ beta,
@@ -171,28 +172,41 @@ void convt2d_gn_pass_kernel(float *__restrict__ y, const float *__restrict__ par
 {
     const int nc = blockIdx.x;
     const int n = nc / C, c = nc % C, g = c / (C / G);
+    const int tid = threadIdx.x;
+    __shared__ float tri[256][3];
     __shared__ float coef[2];
-    if (threadIdx.x == 0) {
+    {
         float cnt = 0.f, mean = 0.f, m2 = 0.f;
         const float *pp = partials + ((size_t)n * G + g) * rblocks * 3;
-        for (int r = 0; r < rblocks; ++r) chan_merge(cnt, mean, m2, pp[r * 3], pp[r * 3 + 1], pp[r * 3 + 2]);
-        const float rstd = rsqrtf(m2 / cnt + eps);
+        for (int r = tid; r < rblocks; r += 256) chan_merge(cnt, mean, m2, pp[r * 3], pp[r * 3 + 1], pp[r * 3 + 2]);
+        tri[tid][0] = cnt; tri[tid][1] = mean; tri[tid][2] = m2;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        float tc = 0.f, tm = 0.f, tq = 0.f;
+        for (int k = 0; k < 256; ++k) chan_merge(tc, tm, tq, tri[k][0], tri[k][1], tri[k][2]);
+        const float rstd = rsqrtf(tq / tc + eps);
         const float ga = gamma ? gamma[c] : 1.0f, be = beta ? beta[c] : 0.0f;
         coef[0] = rstd * ga * inv_div;
-        coef[1] = (be - mean * rstd * ga) * inv_div;
+        coef[1] = (be - tm * rstd * ga) * inv_div;
     }
     __syncthreads();
     const float sc = coef[0], sh = coef[1];
     float *p = y + (size_t)nc * plane;
     if ((plane & 3) == 0) {
-        float4 *p4 = reinterpret_cast<float4 *>(p);
-        for (int i = threadIdx.x; i < plane / 4; i += 256) {
-            float4 v = p4[i];
-            v.x = v.x * sc + sh; v.y = v.y * sc + sh; v.z = v.z * sc + sh; v.w = v.w * sc + sh;
-            p4[i] = v;
+        v4f *p4 = reinterpret_cast<v4f *>(p);
+        const int n4 = plane / 4;
+        int i = tid;
+        for (; i + 3 * 256 < n4; i += 4 * 256) {
+            v4f a0 = p4[i], a1 = p4[i + 256], a2 = p4[i + 512], a3 = p4[i + 768];
+            p4[i] = a0 * sc + sh;
+            p4[i + 256] = a1 * sc + sh;
+            p4[i + 512] = a2 * sc + sh;
+            p4[i + 768] = a3 * sc + sh;
         }
+        for (; i < n4; i += 256) p4[i] = p4[i] * sc + sh;
     } else {
-        for (int i = threadIdx.x; i < plane; i += 256) p[i] = p[i] * sc + sh;
+        for (int i = tid; i < plane; i += 256) p[i] = p[i] * sc + sh;
     }
 }
 

@@ -72,13 +72,18 @@ SMALL_CASES = [
     ("convt2d_gelu_gn_n128", dict(N=1, in_dims=(1, 7, 36))),
     ("convt2d_gelu_gn_n128", dict(N=2, C_in=8, C_out=8, groups=1, num_groups=1,
                                   in_dims=(1, 5, 4), act="none")),
-    # single-write cooperative transposed conv (W = 256): partial last slice,
-    # column tiles with masked rows, units that do not fill a round
+    # single-write cooperative transposed conv (W = 256): odd output height
+    # (last step with one row), column tiles with masked rows, units that do
+    # not fill a round, slices with an extra step, several rounds with the
+    # XCD-grouped slice mapping
     ("convt2d_gelu_gn_n128", dict(N=2, C_in=16, C_out=16, groups=2, num_groups=2,
                                   in_dims=(1, 30, 256))),
     ("convt2d_gelu_gn_n128", dict(N=1, in_dims=(1, 21, 256))),
     ("convt2d_gelu_gn_n128", dict(N=3, C_in=8, C_out=8, groups=1, num_groups=1,
                                   in_dims=(1, 1, 256), act="hardswish")),
+    ("convt2d_gelu_gn_n128", dict(N=2, in_dims=(1, 72, 256), act="none")),
+    ("convt2d_gelu_gn_n128", dict(N=3, in_dims=(1, 130, 256))),
+    ("convt2d_gelu_gn_n128", dict(N=2, in_dims=(1, 256, 256))),
 ]
 
 
@@ -144,9 +149,16 @@ def test_repeatable_bitwise():
         assert torch.equal(a, b), name
 
 
+def _fused_slices(Ho):
+    # slices per unit of the single-write kernel: at most 32, three steps each
+    nst = (Ho + 1) // 2
+    return min(32, nst // 3)
+
+
 def test_fused_convt_wait_never_times_out():
-    # the single-write kernel raises a flag in its workspace (after the unit
-    # counters) if a cross-workgroup wait hit its bound; it must stay 0
+    # the single-write kernel raises a flag (workspace word 0) if a
+    # cross-workgroup wait hit its bound; it must stay 0.  Every slice's
+    # triple (count, mean, M2, count) sits at float 4 + 4 (unit * S + slice).
     import convolution_normalization_forward_amd as cnf
     wl = cnf_inputs.workload("convt2d_gelu_gn_n128", N=6, in_dims=(1, 70, 256))
     plan = cnf.Plan(cnf.make_desc(wl))
@@ -163,10 +175,14 @@ def test_fused_convt_wait_never_times_out():
         assert st == cnf.CNF_OK
     torch.cuda.synchronize()
     U = wl["N"] * wl["groups"]
-    words = ws[: 4 * (U + 1)].view(torch.int32).cpu()
-    assert int(words[U]) == 0, "cross-workgroup wait timed out"
-    S = -(-(wl["in_dims"][1] + 2) // 26)  # 26 output rows per slice
-    assert (words[:U] == S).all()  # every slice of every unit arrived exactly once
+    Ho, Wo = plan.out_shape[2], plan.out_shape[3]
+    S = _fused_slices(Ho)
+    words = ws[:16].view(torch.int32).cpu()
+    assert int(words[0]) == 0, "cross-workgroup wait timed out"
+    tri = ws[16: 16 + 16 * U * S].view(torch.float32).cpu().numpy().reshape(U, S, 4)
+    assert (tri[:, :, 0] > 0).all() and (tri[:, :, 0] == tri[:, :, 3]).all()
+    # the slices of a unit partition its 8 x Ho x Wo outputs
+    assert (tri[:, :, 0].sum(axis=1) == 8 * Ho * Wo).all()
     ref, _ = oracle.forward(wl, x, **p)
     check_close(out.cpu().numpy(), ref, "fused convt repeated")
 

@@ -95,25 +95,25 @@ __device__ __forceinline__ float hardswish(float x) {
     return x * fminf(fmaxf(x + 3.0f, 0.0f), 6.0f) * (1.0f / 6.0f);
 }
 
-// Exact (erf) GELU, gelu(x) = x * Phi(x) = 0.5 x (1 + erf(x / sqrt 2)).
-// erf uses the rational-exponential approximation of Abramowitz & Stegun,
-// Handbook of Mathematical Functions (1964), formula 7.1.26 (|error| <= 1.5e-7
-// for x >= 0), with t = 1 / (1 + p z), z = |x| / sqrt 2.  For x < 0 the factor
-// 1 + erf(-z) = poly * exp(-z^2) is formed directly, so the negative tail keeps
-// its relative accuracy; for x >= 0 it is 2 - poly * exp(-z^2).
+// Exact (erf) GELU, gelu(x) = x * Phi(x) = 0.5 x (1 + erf(x / sqrt 2)),
+// written as relu(x) - 0.5 |x| erfc(z), z = |x| / sqrt 2, which holds for
+// both signs and keeps the negative tail's relative accuracy.  erfc uses the
+// rational-exponential approximation of Abramowitz & Stegun, Handbook of
+// Mathematical Functions (1964), formula 7.1.26 (|error| <= 1.5e-7):
+// erfc(z) = t (a1 + a2 t + ... + a5 t^4) exp(-z^2), t = 1 / (1 + p z).
+// Constants are folded so the whole activation is 11 VALU ops + rcp + exp2:
+// u = |x| sqrt(log2(e) / 2) gives exp(-z^2) = exp2(-u^2) and p z = (p / (sqrt 2
+// sqrt(log2(e) / 2))) u; the a_i carry the factor -0.5 (exact in binary).
 __device__ __forceinline__ float gelu_erf(float x) {
-    const float z = fabsf(x) * 0.70710678118654752f;
-    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
-    float poly = fmaf(t, 1.061405429f, -1.453152027f);
-    poly = fmaf(t, poly, 1.421413741f);
-    poly = fmaf(t, poly, -0.284496736f);
-    poly = fmaf(t, poly, 0.254829592f);
+    const float u = fabsf(x) * 0.849321800f;
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.272737481f, u, 1.0f));
+    float poly = fmaf(t, -0.5307027145f, 0.7265760135f);  // -a5/2, -a4/2
+    poly = fmaf(t, poly, -0.7107068705f);                 // -a3/2
+    poly = fmaf(t, poly, 0.1422483680f);                  // -a2/2
+    poly = fmaf(t, poly, -0.1274147960f);                 // -a1/2
     poly = poly * t;
-    // exp(-z^2) = exp2(-x^2 * log2(e) / 2)
-    const float e = __builtin_amdgcn_exp2f(x * x * -0.72134752044448170f);
-    const float pe = poly * e;
-    const float one_plus_erf = x < 0.0f ? pe : 2.0f - pe;
-    return 0.5f * x * one_plus_erf;
+    const float e = __builtin_amdgcn_exp2f(-(u * u));
+    return fmaf(fabsf(x), poly * e, fmaxf(x, 0.0f));
 }
 
 template <int ACT>

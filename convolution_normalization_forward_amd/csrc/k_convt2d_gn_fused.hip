@@ -8,19 +8,21 @@
 // second trace weighs a three-kernel plan (conv + GELU writing the tensor and
 // per-(n, g) sums, a finalize, a normalize pass re-reading the tensor).  Here
 // the conv output never goes to memory un-normalised:
-//   * a unit (sample, group) is cut into S row slices; S workgroups own one
-//     unit per round (units handed out round by round; the launch is
-//     cooperative, so all workgroups are resident at once);
+//   * a unit (sample, group) is cut into S slices of SPS two-row steps (the
+//     last TAIL steps of the unit are spread over the slices as single row
+//     tiles, so every slice carries the same work); S workgroups own one unit
+//     per round (units handed out round by round; the launch is cooperative,
+//     so all workgroups are resident at once);
 //   * round r: a workgroup computes its slice of unit u_r (conv + bias +
 //     activation) into an LDS bank (each lane's own values, so no barrier),
-//     keeps running sums, and at the start of round r+1 publishes the
-//     slice's (count, mean, M2) triple;
+//     keeps running sums, and early in round r+1 publishes the slice's
+//     (count, mean, M2) triple;
 //   * during round r+1 the same workgroup normalises the bank of u_r and
-//     stores it, one step behind its new MFMA work: the coefficients of u_r
-//     are needed one step into round r+1, by which time the sibling slices
-//     have normally published.  Step k of round rho lives in bank slot
-//     (k - rho) mod 6, so step k of round r+1 overwrites exactly the slot of
-//     step k-1 of round r, which it has just normalised and stored.
+//     stores it, two steps behind its new MFMA work: the coefficients of u_r
+//     are read one step into round r+1 and needed two steps in, by which time
+//     the sibling slices have normally published.  Step k of round rho lives in bank slot
+//     (k - rho) mod (SPS + 1), so step k of round r+1 goes into exactly the
+//     slot of step k-1 of round r, which has just been normalised and stored.
 // Each triple travels as two 64-bit relaxed atomics that both carry the
 // count, so a reader that sees both halves non-zero has the whole triple and
 // no fence or counter is needed.  The wait is bounded; on time-out a flag in
@@ -32,10 +34,10 @@
 // read the same input columns shifted by one, so 72 of every 96 K entries are
 // useful (zero-padded weights fill the rest).  An output row of 258 pixels is
 // 8 row tiles (pixels 0..255, one per wave) plus the last column pair; the
-// last pairs of 16 consecutive rows form one column tile.  A slice is a run
-// of 2-row steps; each step reads two input row pairs from a 3-pair LDS ring
-// that is refilled from registers loaded three events ahead.  Each step's
-// activation and sums run interleaved with the next step's MFMAs.
+// last pairs of 16 consecutive rows form one column tile.  Each step reads
+// two input row pairs from a 4-pair LDS ring refilled from registers loaded
+// three stashes ahead; waves sharing a SIMD alternate the step's MFMAs and
+// the previous step's activation.
 #include "device.h"
 #include "kernels.h"
 
@@ -51,19 +53,20 @@ constexpr int PADL = 4;            // zero columns left of x inside an LDS row
 constexpr int RP = W + PADL;       // 260: LDS row pitch (reads never pass column W - 1)
 constexpr int THREADS = 512;
 constexpr int NWAVE = THREADS / 64;          // one 32-pixel row tile per wave
-constexpr int NSLOT = 3;                     // input row pairs in the LDS ring
+constexpr int NSLOT = 4;                     // input row pairs in the LDS ring
 constexpr int PAIR_FLOATS = 2 * CG * RP;
-constexpr int MAXST = 5;                     // steps per slice
-constexpr int NEV = MAXST + 1;               // ring events per round (fixed)
-constexpr int NBANK = MAXST + 1;             // LDS bank slots (one step of two rounds overlap)
+constexpr int SPS = 4;                       // steps per slice
+constexpr int NBANK = SPS + 1;               // LDS bank slots
+constexpr int NPOS = 6;                      // ring stash positions per round (SPS + 1, padded to 3 k)
 constexpr int MAX_S = 32;                    // slices per unit
-constexpr int STRIP_ROWS = 16 + KS - 1;      // input rows behind one column tile
-constexpr int STRIP_ELEMS = CG * STRIP_ROWS; // (ci, row) entries of x columns 254..255
-constexpr int COLWAVE = NWAVE - 1;           // wave that owns the column tile
-constexpr int SPIN_LIMIT = 1 << 16;   // polls (each a memory round trip) before giving up
+constexpr int EXTWAVE = NWAVE - 2;           // wave that owns the slice's extra row tile
+constexpr int COLWAVE = NWAVE - 1;           // wave that owns the slice's column tile
+constexpr int SPIN_LIMIT = 1 << 16;          // polls (each a memory round trip) before giving up
+constexpr unsigned OOB = 0x7ff00000u;        // buffer offset past any extent: loads return 0
 static_assert(NWAVE * 32 == W, "one row tile per wave");
 static_assert(CG * 64 == THREADS, "one (channel, 64 float4) row chunk per wave");
-static_assert(STRIP_ELEMS <= THREADS, "strip staging");
+static_assert(NPOS % 3 == 0 && NPOS >= SPS + 1, "stash positions");
+static_assert((EXTWAVE & 3) != (COLWAVE & 3), "extra and column tiles on different SIMDs");
 
 struct FusedArgs {
     const float *x, *wt, *bias, *gamma, *beta;
@@ -71,27 +74,11 @@ struct FusedArgs {
     float *partials;  // [U][S][4]: (count, mean), (M2, count); zero on entry
     int *flag;        // raised if a wait timed out
     int N, C, H, G, Ho;
-    int S, SPS, TAIL, NCOL;
-    int upr;          // units per round
-    int xcd_units;    // units per XCD per round (0: plain workgroup order)
+    int S, NEXT, NCOL;  // slices, extra row tiles (16 per tail step), column tiles
+    int upr;            // units per round
+    int xcd_units;      // units per XCD per round (0: plain workgroup order)
     float eps, inv_div;
 };
-
-// Steps [k0, k0 + ns) of a unit's NST = ceil(Ho / 2) two-row steps; the
-// first TAIL slices take one step more; column tile col (or -1).
-struct Slice {
-    int k0, ns, col;
-};
-
-__device__ __forceinline__ Slice slice_of(const FusedArgs &a, int sg)
-{
-    Slice s;
-    s.k0 = sg * a.SPS + min(sg, a.TAIL);
-    s.ns = a.SPS + (sg < a.TAIL ? 1 : 0);
-    const int c = a.S - 1 - sg;
-    s.col = c < a.NCOL ? c : -1;
-    return s;
-}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t x_rsrc(const FusedArgs &a, int unit)
 {
@@ -107,29 +94,90 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t y_rsrc(const FusedArgs &a, int
 
 // One input row pair (rows row0, row0 + 1 of the group's 8 channels): this
 // thread's float4 of each row (channel = wave, column 4 * lane).  Every load
-// is issued (rows outside [0, H) are clamped; stash_pair writes zeros for
-// them): a load under a branch would leave the register a merge of two
-// values, and copying it would wait for the load.
+// is issued -- a load under a branch would leave the register a merge of two
+// values, and copying it would wait for the load -- and a row outside [0, H)
+// gets an offset past the buffer, which reads as zeros.
 __device__ __forceinline__ void load_pair(v4f (&pf)[2], __amdgpu_buffer_rsrc_t xr, int H, int row0,
                                           unsigned loff)
 {
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr) {
-        const int row = min(max(row0 + rr, 0), H - 1);
-        pf[rr] = buf_load4(xr, loff, (unsigned)(row * W * 4));
+        const int row = row0 + rr;
+        const unsigned ro = row >= 0 && row < H ? (unsigned)(row * W * 4) : OOB;
+        pf[rr] = buf_load4(xr, loff + ro);
     }
 }
 
-__device__ __forceinline__ void stash_pair(float *ring, int slot, const v4f (&pf)[2], int H, int row0,
-                                           int wave, int lane)
+__device__ __forceinline__ void stash_pair(float *ring, int slot, const v4f (&pf)[2], int wave, int lane)
 {
 #pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
-        const int row = row0 + rr;
-        const bool ok = row >= 0 && row < H;
-        *reinterpret_cast<v4f *>(ring + slot * PAIR_FLOATS + (rr * CG + wave) * RP + PADL + 4 * lane) =
-            ok ? pf[rr] : v4f{0.f, 0.f, 0.f, 0.f};
+    for (int rr = 0; rr < 2; ++rr)
+        *reinterpret_cast<v4f *>(ring + slot * PAIR_FLOATS + (rr * CG + wave) * RP + PADL + 4 * lane) = pf[rr];
+}
+
+// Ring stash positions of a round: p <= SPS-2 stashes pair p+2 at the end of
+// step p; p = SPS-1 and SPS stash the next round's pairs 0 and 1 at the end
+// of the last step; later positions stash nothing.  The loads for position
+// p + 3 are issued right after position p's stash, into register set p % 3
+// (NPOS is a multiple of 3, so every round starts on set 0).
+__device__ __forceinline__ void issue_pos(int p, v4f (&dst)[2], int k0, __amdgpu_buffer_rsrc_t xr,
+                                          bool nhas, int nk0, __amdgpu_buffer_rsrc_t nxr, int H,
+                                          unsigned loff)
+{
+    const int p3 = p + 3;
+    int pair;
+    bool next;
+    if (p3 < NPOS) {
+        next = p3 >= SPS - 1;
+        pair = p3 <= SPS - 2 ? p3 + 2 : p3 - (SPS - 1);  // past SPS: unused
+    } else {
+        next = true;  // the next round's position p3 - NPOS <= 2 <= SPS - 2
+        pair = p3 - NPOS + 2;
     }
+    const bool use_next = next && nhas;
+    load_pair(dst, use_next ? nxr : xr, H, 2 * ((use_next ? nk0 : k0) + pair) - 2, loff);
+}
+
+// Chan merge of Welford triples with the weight nb / (n + nb) from the
+// hardware reciprocal (a merge here feeds only the statistics; counts are
+// exact integers, so the weight is off by at most an ulp or so).
+__device__ __forceinline__ void merge_fast(float &n, float &mean, float &m2, float nb, float meanb, float m2b)
+{
+    const float nn = n + nb;
+    const float f = nn > 0.0f ? nb * __builtin_amdgcn_rcpf(nn) : 0.0f;
+    const float delta = meanb - mean;
+    mean = fmaf(delta, f, mean);
+    m2 = m2 + m2b + delta * delta * n * f;
+    n = nn;
+}
+
+// Every lane of a 16-lane row ends with the merge of the row's triples
+// (rotations through DPP; lane 0 of the row merges in lane order 0..15 by
+// halves, and every wave doing this on the same data gets the same bits).
+__device__ __forceinline__ void row_merge16(float &n, float &mean, float &m2)
+{
+#define CNF_ROW_STEP(S)                                                                  \
+    {                                                                                    \
+        const float nb = row_ror<S>(n), mb = row_ror<S>(mean), qb = row_ror<S>(m2);      \
+        merge_fast(n, mean, m2, nb, mb, qb);                                             \
+    }
+    CNF_ROW_STEP(8) CNF_ROW_STEP(4) CNF_ROW_STEP(2) CNF_ROW_STEP(1)
+#undef CNF_ROW_STEP
+}
+
+// Lanes 0..31 hold triples (zeros where there is nothing): merge of lanes
+// 0..15 with the merge of lanes 16..31, the same in every lane.
+__device__ __forceinline__ void merge32(float &n, float &mean, float &m2)
+{
+    row_merge16(n, mean, m2);
+    auto lane_f = [](float v, int l) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+    };
+    const float n1 = lane_f(n, 16), m1 = lane_f(mean, 16), q1 = lane_f(m2, 16);
+    n = lane_f(n, 0);
+    mean = lane_f(mean, 0);
+    m2 = lane_f(m2, 0);
+    merge_fast(n, mean, m2, n1, m1, q1);
 }
 
 // Statistics of one unit -> this lane's two channel scale / shift pairs.
@@ -169,15 +217,7 @@ __device__ __forceinline__ Coef probe_finish(const FusedArgs &a, int unit, int l
     }
     const bool mine = lane < a.S;
     float n = mine ? lo_f(p0) : 0.f, m = mine ? hi_f(p0) : 0.f, m2 = mine ? lo_f(p1) : 0.f;
-#pragma unroll
-    for (int off = 16; off >= 1; off >>= 1) {
-        const float nb = __shfl_down(n, off, 64), mb = __shfl_down(m, off, 64),
-                    qb = __shfl_down(m2, off, 64);
-        if (lane < off) chan_merge(n, m, m2, nb, mb, qb);
-    }
-    n = __shfl(n, 0, 64);
-    m = __shfl(m, 0, 64);
-    m2 = __shfl(m2, 0, 64);
+    merge32(n, m, m2);
     const float rstd = rsqrtf(m2 / n + a.eps);
     Coef c;
     c.sc0 = rstd * gb[0] * a.inv_div;
@@ -187,42 +227,43 @@ __device__ __forceinline__ Coef probe_finish(const FusedArgs &a, int unit, int l
     return c;
 }
 
-// Normalised store of one row tile (rows of the tile: channels 2q, 2q+1,
-// pixels 32 * wave + 2 * c16 + {0, 1}) of output row orow.
-__device__ __forceinline__ void store_tile(__amdgpu_buffer_rsrc_t yr, const v4f &c, const Coef &k,
-                                           unsigned vo0, unsigned vo1, int orow)
+// The slice triple from the 32 row triples in red[] (4 rows of 16 lanes per
+// wave), stored by lane 0 as two 64-bit relaxed atomics that both carry the
+// count.  Called by one whole wave.
+__device__ __forceinline__ void publish(const FusedArgs &a, const float *red, int unit, int sg, int lane)
 {
-    const unsigned so = (unsigned)(orow * WO * 4);
+    const int l = lane & 31;
+    float n = lane < 32 ? red[l * 3] : 0.f, m = lane < 32 ? red[l * 3 + 1] : 0.f,
+          m2 = lane < 32 ? red[l * 3 + 2] : 0.f;
+    merge32(n, m, m2);
+    if (lane == 0) {
+        unsigned long long *p =
+            reinterpret_cast<unsigned long long *>(a.partials + ((size_t)unit * a.S + sg) * 4);
+        const unsigned long long v0 = (unsigned long long)__float_as_uint(n) |
+                                      ((unsigned long long)__float_as_uint(m) << 32);
+        const unsigned long long v1 = (unsigned long long)__float_as_uint(m2) |
+                                      ((unsigned long long)__float_as_uint(n) << 32);
+        __hip_atomic_store(p, v0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(p + 1, v1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Normalised 8-byte stores of one tile's two channel rows (voffsets vo0 /
+// vo1 hold the lane's pixel pair; so = the uniform row offset).
+__device__ __forceinline__ void store_tile(__amdgpu_buffer_rsrc_t yr, const v4f &c, const Coef &k,
+                                           unsigned vo0, unsigned vo1, unsigned so)
+{
     buf_store2_nt(v2f{c[0] * k.sc0 + k.sh0, c[1] * k.sc0 + k.sh0}, yr, vo0, so);
     buf_store2_nt(v2f{c[2] * k.sc1 + k.sh1, c[3] * k.sc1 + k.sh1}, yr, vo1, so);
 }
 
-// Events of a round with ns steps: e = 0 (round start) stashes pair 1;
-// e = k + 1 (end of step k) stashes pair k + 2, or after the last step the
-// next round's pair 0; events ns + 1 .. NEV - 1 stash nothing.  Loads issued
-// at event e fill the register set that event e + 3 stashes (every round has
-// NEV events, so event e always uses register set e % 3, and the next
-// round's events 0..2 -- its pairs 1..3, as every slice has >= 3 steps -- are
-// loaded during this one).  Rows are picked with selects and the loads are
-// always issued; a load for an event that stashes nothing is not used.
-__device__ __forceinline__ void issue_event(int e, v4f (&dst)[2], const Slice &sl,
-                                            __amdgpu_buffer_rsrc_t xr, bool nhas, const Slice &nsl,
-                                            __amdgpu_buffer_rsrc_t nxr, int H, unsigned loff)
-{
-    const int e3 = e + 3;
-    const bool this_round = e3 < NEV && e3 < sl.ns;   // pair e3 + 1 of this round
-    const int pair = this_round ? e3 + 1 : (e3 < NEV ? 0 : e3 - NEV + 1);
-    const bool use_next = !this_round && nhas;
-    load_pair(dst, use_next ? nxr : xr, H, 2 * ((use_next ? nsl.k0 : sl.k0) + pair) - 2, loff);
-}
-
 template <int ACT>
-__device__ __forceinline__ v4f activate4(v4f c, float b0, float b1)
+__device__ __forceinline__ v4f activate4(v4f c)
 {
-    c[0] = activate<ACT>(c[0] + b0);
-    c[1] = activate<ACT>(c[1] + b0);
-    c[2] = activate<ACT>(c[2] + b1);
-    c[3] = activate<ACT>(c[3] + b1);
+    c[0] = activate<ACT>(c[0]);
+    c[1] = activate<ACT>(c[1]);
+    c[2] = activate<ACT>(c[2]);
+    c[3] = activate<ACT>(c[3]);
     return c;
 }
 
@@ -235,22 +276,46 @@ __device__ __forceinline__ void sums4(const v4f &c, float &s1, float &s2)
     s2 = fmaf(c[3], c[3], s2);
 }
 
-// Activation of a finished step's two row tiles (row 2 of them may lie past
-// Ho: then it is kept out of the sums) -> running sums and the bank slot wp.
+// Activation of a finished step's two row tiles (bias already in the
+// accumulators; the second row may lie past Ho: then it is skipped) ->
+// running sums and the bank slot wp.
 template <int ACT>
-__device__ __forceinline__ void epilogue_to_bank(const v4f &acc0, const v4f &acc1, float b0, float b1,
-                                                 bool v1, float &s1, float &s2, int &cnt, v4f *wp)
+__device__ __forceinline__ void epilogue_to_bank(const v4f &acc0, const v4f &acc1, bool v1, float &s1,
+                                                 float &s2, int &cnt, v4f *wp)
 {
-    const v4f e0 = activate4<ACT>(acc0, b0, b1);
-    const v4f e1 = activate4<ACT>(acc1, b0, b1);
-    float t1 = 0.f, t2 = 0.f;
+    const v4f e0 = activate4<ACT>(acc0);
     sums4(e0, s1, s2);
-    sums4(e1, t1, t2);
-    s1 += v1 ? t1 : 0.0f;
-    s2 += v1 ? t2 : 0.0f;
-    cnt += v1 ? 8 : 4;
     wp[0] = e0;
-    wp[THREADS] = e1;
+    cnt += 4;
+    if (v1) {
+        const v4f e1 = activate4<ACT>(acc1);
+        sums4(e1, s1, s2);
+        wp[THREADS] = e1;
+        cnt += 4;
+    }
+}
+
+// A single tile read straight from x (L2): lane (q, c16), K entry (ci, kh)
+// takes x[ci][row(c16) - kh][col(c16) - q], zero outside the input (the
+// offset is pushed past the buffer, which returns 0).  Row tile: row(c16) =
+// orow, col = 32 rt + 2 c16 + 1.  Column tile: row = 16 c + c16, col = 257.
+struct SingleTile {
+    float b[CG * KS];
+};
+
+__device__ __forceinline__ void single_load(SingleTile &t, __amdgpu_buffer_rsrc_t xr, int H, int row,
+                                            int col)
+{
+#pragma unroll
+    for (int ci = 0; ci < CG; ++ci) {
+#pragma unroll
+        for (int kh = 0; kh < KS; ++kh) {
+            const int rr = row - kh;
+            const bool ok = rr >= 0 && rr < H && col >= 0 && col < W;
+            const unsigned off = ok ? (unsigned)(((ci * H + rr) * W + col) * 4) : OOB;
+            t.b[ci * KS + kh] = buf_load1(xr, off);
+        }
+    }
 }
 
 template <int ACT>
@@ -258,8 +323,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void convt2d_gn_fused_kernel(FusedArgs a)
 {
     __shared__ float ring[NSLOT * PAIR_FLOATS];
-    __shared__ float strip[STRIP_ELEMS * 4];
-    __shared__ float red[NWAVE * 3];
+    __shared__ float red[NWAVE * 4 * 3];  // [wave][row of 16 lanes] slice triples
     __shared__ v4f bank[NBANK * 2 * THREADS];  // [slot][tile][thread], private to each thread
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -287,7 +351,6 @@ void convt2d_gn_fused_kernel(FusedArgs a)
 #pragma unroll
         for (int c = 0; c < PADL; ++c) row[c] = 0.f;
     }
-    for (int e = tid; e < STRIP_ELEMS; e += THREADS) { strip[e * 4 + 2] = 0.f; strip[e * 4 + 3] = 0.f; }
 
     const unsigned loff = (unsigned)((wave * H * W + 4 * lane) * 4);  // pair loads
     const int lb = PADL + 32 * wave + 2 * c16 + 1 - q;                // B operand column
@@ -296,58 +359,56 @@ void convt2d_gn_fused_kernel(FusedArgs a)
     v4f *const mybank = bank + tid;
     auto slot_of = [](int k, int rho) { return (k + NBANK - rho % NBANK) % NBANK; };
 
-    // ---- prologue: round 0's pair 0 in the ring, events 0..2 in flight
+    // ---- prologue: round 0's pairs 0, 1 in the ring, positions 0..2 in flight
     v4f pf[3][2];
     int base = 0;  // ring slot of the current round's pair 0
-    if (ulocal < U) {
-        const Slice s0 = slice_of(a, s_base);
+    {
+        const int k0 = s_base * SPS;
         const __amdgpu_buffer_rsrc_t xr = x_rsrc(a, ulocal);
-        v4f p0[2];
-        load_pair(p0, xr, H, 2 * s0.k0 - 2, loff);
-        stash_pair(ring, 0, p0, H, 2 * s0.k0 - 2, wave, lane);
+        v4f p0[2], p1[2];
+        load_pair(p0, xr, H, 2 * k0 - 2, loff);
+        load_pair(p1, xr, H, 2 * k0, loff);
+        stash_pair(ring, 0, p0, wave, lane);
+        stash_pair(ring, 1, p1, wave, lane);
 #pragma unroll
-        for (int e = 0; e < 3; ++e) load_pair(pf[e], xr, H, 2 * (s0.k0 + e + 1) - 2, loff);
+        for (int p = 0; p < 3; ++p) load_pair(pf[p], xr, H, 2 * (k0 + p + 2) - 2, loff);
     }
 
     float wreg[CG * KS];
-    float b0 = 0.f, b1 = 0.f;
+    v4f bias4 = v4f{0.f, 0.f, 0.f, 0.f};  // accumulator start: bias of channels 2q, 2q, 2q+1, 2q+1
     v4f gb = v4f{1.f, 0.f, 1.f, 0.f}, p_gb = gb;
-    v4f cur_col = v4f{0.f, 0.f, 0.f, 0.f}, prv_col = v4f{0.f, 0.f, 0.f, 0.f};
-    int p_unit = -1, p_sg = 0, p_k0 = 0, p_ns = 0, p_col = -1;
+    int wgroup = -1;
+    v4f cur_ext = v4f{0.f, 0.f, 0.f, 0.f}, prv_ext = cur_ext;  // extra row tile (wave EXTWAVE)
+    v4f cur_col = cur_ext, prv_col = cur_ext;                  // column tile (wave COLWAVE)
+    int p_unit = -1, p_sg = 0, p_k0 = 0, p_ext = -1, p_col = -1;
     Coef pc{0.f, 0.f, 0.f, 0.f};
 
     int r = 0;
     for (;; ++r) {
         const int unit = r * a.upr + ulocal;
-        __syncthreads();  // ring readers of the last round are done; red[] is complete
-        if (p_unit >= 0 && tid == 0) {
-            float n = 0.f, m = 0.f, m2 = 0.f;
-            for (int w = 0; w < NWAVE; ++w) chan_merge(n, m, m2, red[w * 3], red[w * 3 + 1], red[w * 3 + 2]);
-            unsigned long long *p =
-                reinterpret_cast<unsigned long long *>(a.partials + ((size_t)p_unit * S + p_sg) * 4);
-            const unsigned long long v0 = (unsigned long long)__float_as_uint(n) |
-                                          ((unsigned long long)__float_as_uint(m) << 32);
-            const unsigned long long v1 = (unsigned long long)__float_as_uint(m2) |
-                                          ((unsigned long long)__float_as_uint(n) << 32);
-            __hip_atomic_store(p, v0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(p + 1, v1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();  // pairs 0, 1 in the ring; last round's ring readers done; red[] complete
+        if (unit >= U) {
+            if (p_unit >= 0 && wave == 0) publish(a, red, p_unit, p_sg, lane);
+            break;
         }
-        if (unit >= U) break;
+        const bool has_prev = p_unit >= 0;
+        if (has_prev && wave == 0) publish(a, red, p_unit, p_sg, lane);
 
         const int sg = (s_base + r) % S;
-        const Slice sl = slice_of(a, sg);
+        const int k0 = sg * SPS;
+        const int ext = sg < a.NEXT ? sg : -1;           // extra row tile e: tail step e/16, tile e%16
+        const int col = S - 1 - sg < a.NCOL ? S - 1 - sg : -1;
         const __amdgpu_buffer_rsrc_t xr = x_rsrc(a, unit);
         const int nunit = unit + a.upr;
         const bool nhas = nunit < U;
-        const Slice nsl = slice_of(a, (sg + 1) % S);
+        const int nk0 = ((sg + 1) % S) * SPS;
         const __amdgpu_buffer_rsrc_t nxr = x_rsrc(a, nhas ? nunit : unit);
-        const int nbase = base + sl.ns + 1;  // ring slot (mod 3) of the next round's pair 0
-        const bool has_prev = p_unit >= 0;
         const __amdgpu_buffer_rsrc_t pyr = y_rsrc(a, has_prev ? p_unit : unit, plane);
 
-        // ---- weights (A operand), bias, gamma / beta of the unit's group; strip
+        // ---- weights (A operand), bias, gamma / beta of the unit's group
         const int g = unit % a.G;
-        {
+        if (g != wgroup) {
+            wgroup = g;
             const __amdgpu_buffer_rsrc_t wr =
                 make_rsrc(a.wt + (size_t)g * CG * CG * KS * KS, CG * CG * KS * KS * 4);
             const int co = c16 >> 1, t = c16 & 1;
@@ -360,166 +421,151 @@ void convt2d_gn_fused_kernel(FusedArgs a)
                 wreg[s] = kok ? v : 0.0f;
             }
             const int c0 = g * CG + 2 * q;
-            b0 = a.bias ? a.bias[c0] : 0.0f;
-            b1 = a.bias ? a.bias[c0 + 1] : 0.0f;
+            const float b0 = a.bias ? a.bias[c0] : 0.0f, b1 = a.bias ? a.bias[c0 + 1] : 0.0f;
+            bias4 = v4f{b0, b0, b1, b1};
             gb = v4f{a.gamma ? a.gamma[c0] : 1.0f, a.beta ? a.beta[c0] : 0.0f,
                      a.gamma ? a.gamma[c0 + 1] : 1.0f, a.beta ? a.beta[c0 + 1] : 0.0f};
         }
-        const int srow0 = sl.col >= 0 ? 16 * sl.col - (KS - 1) + tid % STRIP_ROWS : -1;
-        const bool sok = sl.col >= 0 && tid < STRIP_ELEMS && srow0 >= 0 && srow0 < H;
-        const v2f sv = __builtin_bit_cast(
-            v2f, __builtin_amdgcn_raw_buffer_load_b64(
-                     xr, (int)((((tid / STRIP_ROWS % CG) * H + min(max(srow0, 0), H - 1)) * W + (W - 2)) * 4),
-                     0, 0));
 
-        // ---- event 0: stash pair 1
-        stash_pair(ring, (base + 1) % NSLOT, pf[0], H, 2 * (sl.k0 + 1) - 2, wave, lane);
-        issue_event(0, pf[0], sl, xr, nhas, nsl, nxr, H, loff);
-        __syncthreads();  // pairs 0, 1 in the ring
+        // ---- this slice's single tiles: B operands straight from x (L2)
+        const int ext_row = 2 * (S * SPS + (ext >> 4)) + ((ext >> 3) & 1);
+        const bool is_ext = wave == EXTWAVE && ext >= 0, is_col = wave == COLWAVE && col >= 0;
+        SingleTile st;
+        if (is_ext || is_col)
+            single_load(st, xr, H, is_ext ? ext_row : 16 * col + c16,
+                        is_ext ? 32 * (ext & 7) + 2 * c16 + 1 - q : 2 * (W / 2) + 1 - q);
 
-        // ---- steps.  Iteration k runs the MFMAs of step k and the activation,
-        // sums and bank write of step k - 1 (before or after the MFMAs, by
-        // wave); then it stores the previous unit's step k - 1 and stashes /
-        // loads for event k + 1.
+        // ---- steps.  Iteration k stores the previous unit's step k - 2, runs the
+        // MFMAs of step k and the activation, sums and bank write of step k - 1
+        // (before or after the MFMAs, by wave), then stashes / loads ring pairs.
         float s1 = 0.f, s2 = 0.f;
         int cnt = 0;
         unsigned long long pr0 = 0ull, pr1 = 0ull;
         v4f acc0 = v4f{0.f, 0.f, 0.f, 0.f}, acc1 = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int k = 0; k < MAXST; ++k) {
-            if (k < sl.ns) {
-                if (k > 0) __syncthreads();  // pair k + 1 in the ring
-                const float *rA = ring + ((base + k) % NSLOT) * PAIR_FLOATS + lb;
-                const float *rB = ring + ((base + k + 1) % NSLOT) * PAIR_FLOATS + lb;
-                // B operands of the whole step first: input rows 2(k0+k) - 2 + m
-                float xb[CG][4];
-#pragma unroll
-                for (int ci = 0; ci < CG; ++ci) {
-                    xb[ci][0] = rA[ci * RP];
-                    xb[ci][1] = rA[(CG + ci) * RP];
-                    xb[ci][2] = rB[ci * RP];
-                    xb[ci][3] = rB[(CG + ci) * RP];
-                }
-                if (k >= 1 && late)
-                    epilogue_to_bank<ACT>(acc0, acc1, b0, b1, 2 * (sl.k0 + k - 1) + 1 < Ho, s1, s2, cnt,
-                                          mybank + slot_of(k - 1, r) * 2 * THREADS);
-                v4f n0 = v4f{0.f, 0.f, 0.f, 0.f}, n1 = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ci = 0; ci < CG; ++ci) {
-                    // output row 2(k0+k) + j reads input row 2(k0+k) + j - kh, i.e. m = 2 + j - kh
-                    n0 = mfma_16x16x4(wreg[ci * KS + 0], xb[ci][2], n0);
-                    n1 = mfma_16x16x4(wreg[ci * KS + 0], xb[ci][3], n1);
-                    n0 = mfma_16x16x4(wreg[ci * KS + 1], xb[ci][1], n0);
-                    n1 = mfma_16x16x4(wreg[ci * KS + 1], xb[ci][2], n1);
-                    n0 = mfma_16x16x4(wreg[ci * KS + 2], xb[ci][0], n0);
-                    n1 = mfma_16x16x4(wreg[ci * KS + 2], xb[ci][1], n1);
-                }
-                if (k >= 1 && !late)
-                    epilogue_to_bank<ACT>(acc0, acc1, b0, b1, 2 * (sl.k0 + k - 1) + 1 < Ho, s1, s2, cnt,
-                                          mybank + slot_of(k - 1, r) * 2 * THREADS);
-                acc0 = n0;
-                acc1 = n1;
-
-                if (k == 1 && has_prev) pc = probe_finish(a, p_unit, lane, p_gb, pr0, pr1);
-                if (k >= 1 && has_prev) {
-                    // the previous unit's step k - 1 (bank slot of this round's step k)
-                    const v4f *sp = mybank + slot_of(k, r) * 2 * THREADS;
-                    const int prow = 2 * (p_k0 + k - 1);
-                    store_tile(pyr, sp[0], pc, vo0, vo1, prow);
-                    if (prow + 1 < Ho) store_tile(pyr, sp[THREADS], pc, vo0, vo1, prow + 1);
-                }
-                if (k == 0) {
-                    if (has_prev) probe_issue(a, p_unit, lane, pr0, pr1);
-                    if (tid < STRIP_ELEMS) {
-                        strip[tid * 4 + 0] = sok ? sv[0] : 0.0f;
-                        strip[tid * 4 + 1] = sok ? sv[1] : 0.0f;
-                    }
-                }
-
-                // ---- event k + 1: stash its pair (this round's pair k + 2, or after the
-                // last step the next round's pair 0; harmless if there is none)
-                const bool last = k + 1 == sl.ns;
-                stash_pair(ring, last ? nbase % NSLOT : (base + k + 2) % NSLOT, pf[(k + 1) % 3], H,
-                           last ? 2 * nsl.k0 - 2 : 2 * (sl.k0 + k + 2) - 2, wave, lane);
-            }
-            // event k + 1's loads (also for events past the last step, which only load)
-            issue_event(k + 1, pf[(k + 1) % 3], sl, xr, nhas, nsl, nxr, H, loff);
-        }
-
-        // ---- last step: activation + sums -> bank; previous unit's step ns - 1
-        {
-            const int k = sl.ns;
-            epilogue_to_bank<ACT>(acc0, acc1, b0, b1, 2 * (sl.k0 + k - 1) + 1 < Ho, s1, s2, cnt,
-                                  mybank + slot_of(k - 1, r) * 2 * THREADS);
-            if (has_prev && k - 1 < p_ns) {
-                const v4f *sp = mybank + slot_of(k, r) * 2 * THREADS;
-                const int prow = 2 * (p_k0 + k - 1);
-                store_tile(pyr, sp[0], pc, vo0, vo1, prow);
-                if (prow + 1 < Ho) store_tile(pyr, sp[THREADS], pc, vo0, vo1, prow + 1);
-            }
-        }
-
-        // ---- column tile: pair 128 of rows 16 col + c16, read from the strip
-        if (wave == COLWAVE && sl.col >= 0) {
-            const int orow = 16 * sl.col + c16;
-            // x row orow - kh -> strip row c16 + 2 - kh; x col 257 - q -> strip col 3 - q
-            const float *sp = strip + c16 * 4 + 3 - q;
-            v4f c = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int k = 0; k < SPS; ++k) {
+            if (k > 0) __syncthreads();  // pair k + 1 in the ring
+            const float *rA = ring + ((base + k) % NSLOT) * PAIR_FLOATS + lb;
+            const float *rB = ring + ((base + k + 1) % NSLOT) * PAIR_FLOATS + lb;
+            // B operands of the whole step first: input rows 2(k0+k) - 2 + m
+            float xb[CG][4];
 #pragma unroll
             for (int ci = 0; ci < CG; ++ci) {
-#pragma unroll
-                for (int kh = 0; kh < KS; ++kh)
-                    c = mfma_16x16x4(wreg[ci * KS + kh], sp[(ci * STRIP_ROWS + 2 - kh) * 4], c);
+                xb[ci][0] = rA[ci * RP];
+                xb[ci][1] = rA[(CG + ci) * RP];
+                xb[ci][2] = rB[ci * RP];
+                xb[ci][3] = rB[(CG + ci) * RP];
             }
-            if (orow < Ho) {
-                cur_col = activate4<ACT>(c, b0, b1);
-                sums4(cur_col, s1, s2);
-                cnt += 4;
+            if (k == 1 && has_prev) probe_issue(a, p_unit, lane, pr0, pr1);
+            if (k == 2 && has_prev) pc = probe_finish(a, p_unit, lane, p_gb, pr0, pr1);
+            if (k >= 2 && has_prev) {
+                // the previous unit's step k - 2: its bank slot takes this round's step k - 1
+                const v4f *sp = mybank + slot_of(k - 1, r) * 2 * THREADS;
+                const int prow = 2 * (p_k0 + k - 2);
+                store_tile(pyr, sp[0], pc, vo0, vo1, (unsigned)(prow * WO * 4));
+                if (prow + 1 < Ho) store_tile(pyr, sp[THREADS], pc, vo0, vo1, (unsigned)((prow + 1) * WO * 4));
+            }
+            if (k >= 1 && late)
+                epilogue_to_bank<ACT>(acc0, acc1, 2 * (k0 + k - 1) + 1 < Ho, s1, s2, cnt,
+                                      mybank + slot_of(k - 1, r) * 2 * THREADS);
+            v4f n0 = bias4, n1 = bias4;
+#pragma unroll
+            for (int ci = 0; ci < CG; ++ci) {
+                // output row 2(k0+k) + j reads input row 2(k0+k) + j - kh, i.e. m = 2 + j - kh
+                n0 = mfma_16x16x4(wreg[ci * KS + 0], xb[ci][2], n0);
+                n1 = mfma_16x16x4(wreg[ci * KS + 0], xb[ci][3], n1);
+                n0 = mfma_16x16x4(wreg[ci * KS + 1], xb[ci][1], n0);
+                n1 = mfma_16x16x4(wreg[ci * KS + 1], xb[ci][2], n1);
+                n0 = mfma_16x16x4(wreg[ci * KS + 2], xb[ci][0], n0);
+                n1 = mfma_16x16x4(wreg[ci * KS + 2], xb[ci][1], n1);
+            }
+            if (k >= 1 && !late)
+                epilogue_to_bank<ACT>(acc0, acc1, 2 * (k0 + k - 1) + 1 < Ho, s1, s2, cnt,
+                                      mybank + slot_of(k - 1, r) * 2 * THREADS);
+            acc0 = n0;
+            acc1 = n1;
+
+            // ---- ring stashes at the end of step k, each followed by its loads
+            if (k <= SPS - 2) {
+                stash_pair(ring, (base + k + 2) % NSLOT, pf[k % 3], wave, lane);
+                issue_pos(k, pf[k % 3], k0, xr, nhas, nk0, nxr, H, loff);
+            } else {
+                stash_pair(ring, (base + SPS + 1) % NSLOT, pf[(SPS - 1) % 3], wave, lane);
+                issue_pos(SPS - 1, pf[(SPS - 1) % 3], k0, xr, nhas, nk0, nxr, H, loff);
+                stash_pair(ring, (base + SPS + 2) % NSLOT, pf[SPS % 3], wave, lane);
+                issue_pos(SPS, pf[SPS % 3], k0, xr, nhas, nk0, nxr, H, loff);
+#pragma unroll
+                for (int p = SPS + 1; p < NPOS; ++p) issue_pos(p, pf[p % 3], k0, xr, nhas, nk0, nxr, H, loff);
             }
         }
 
-        // ---- slice statistics -> red[wave]; published after the next barrier
+        // ---- previous unit's step SPS - 2, then the last step's activation -> bank
+        if (has_prev) {
+            const v4f *sp = mybank + slot_of(SPS - 1, r) * 2 * THREADS;
+            const int prow = 2 * (p_k0 + SPS - 2);
+            store_tile(pyr, sp[0], pc, vo0, vo1, (unsigned)(prow * WO * 4));
+            if (prow + 1 < Ho) store_tile(pyr, sp[THREADS], pc, vo0, vo1, (unsigned)((prow + 1) * WO * 4));
+        }
+        epilogue_to_bank<ACT>(acc0, acc1, 2 * (k0 + SPS - 1) + 1 < Ho, s1, s2, cnt,
+                              mybank + slot_of(SPS - 1, r) * 2 * THREADS);
+
+        // ---- single tiles
+        if (is_ext || is_col) {
+            v4f c = bias4;
+#pragma unroll
+            for (int s = 0; s < CG * KS; ++s) c = mfma_16x16x4(wreg[s], st.b[s], c);
+            const v4f e = activate4<ACT>(c);
+            // the tile's row (column tile: the lane's row) may lie past Ho
+            const bool ok = is_ext ? ext_row < Ho : 16 * col + c16 < Ho;
+            if (ok) {
+                sums4(e, s1, s2);
+                cnt += 4;
+            }
+            if (wave == EXTWAVE) cur_ext = e;
+            else cur_col = e;
+        }
+
+        // ---- slice statistics -> red[wave][row]; published after the next barrier
         {
             float fn = (float)cnt;
             float mean = cnt ? s1 / fn : 0.0f;
             float m2 = cnt ? fmaxf(s2 - s1 * mean, 0.0f) : 0.0f;
-            row_chan16(fn, mean, m2);
-#pragma unroll
-            for (int sh = 16; sh <= 32; sh <<= 1) {
-                const float nb = __shfl_xor(fn, sh, 64), mb = __shfl_xor(mean, sh, 64),
-                            qb = __shfl_xor(m2, sh, 64);
-                chan_merge(fn, mean, m2, nb, mb, qb);
+            row_merge16(fn, mean, m2);
+            if (c16 == 0) {
+                float *e = red + (wave * 4 + q) * 3;
+                e[0] = fn; e[1] = mean; e[2] = m2;
             }
-            if (lane == 0) { red[wave * 3] = fn; red[wave * 3 + 1] = mean; red[wave * 3 + 2] = m2; }
         }
 
-        // ---- the previous unit's remaining step (if it had one more) and its column tile
+        // ---- the previous unit's last step and single tiles
         if (has_prev) {
-            for (int j = sl.ns; j < p_ns; ++j) {
-                const v4f *sp = mybank + slot_of(j + 1, r) * 2 * THREADS;
-                const int prow = 2 * (p_k0 + j);
-                store_tile(pyr, sp[0], pc, vo0, vo1, prow);
-                if (prow + 1 < Ho) store_tile(pyr, sp[THREADS], pc, vo0, vo1, prow + 1);
+            const v4f *sp = mybank + slot_of(SPS, r) * 2 * THREADS;
+            const int prow = 2 * (p_k0 + SPS - 1);
+            store_tile(pyr, sp[0], pc, vo0, vo1, (unsigned)(prow * WO * 4));
+            if (prow + 1 < Ho) store_tile(pyr, sp[THREADS], pc, vo0, vo1, (unsigned)((prow + 1) * WO * 4));
+            if (wave == EXTWAVE && p_ext >= 0) {
+                const int prow_e = 2 * (S * SPS + (p_ext >> 4)) + ((p_ext >> 3) & 1);
+                const unsigned o = ((unsigned)(2 * q) * plane + 32u * (p_ext & 7) + 2u * c16) * 4u;
+                if (prow_e < Ho) store_tile(pyr, prv_ext, pc, o, o + plane * 4u, (unsigned)(prow_e * WO * 4));
             }
             if (wave == COLWAVE && p_col >= 0) {
-                const int prow = 16 * p_col + c16;
-                if (prow < Ho) {
-                    const unsigned o = ((unsigned)(2 * q) * plane + (unsigned)prow * WO + W) * 4u;
-                    buf_store2_nt(v2f{prv_col[0] * pc.sc0 + pc.sh0, prv_col[1] * pc.sc0 + pc.sh0}, pyr, o);
-                    buf_store2_nt(v2f{prv_col[2] * pc.sc1 + pc.sh1, prv_col[3] * pc.sc1 + pc.sh1}, pyr,
-                                  o + plane * 4u);
+                const int prow_c = 16 * p_col + c16;
+                if (prow_c < Ho) {
+                    const unsigned o = ((unsigned)(2 * q) * plane + (unsigned)prow_c * WO + W) * 4u;
+                    store_tile(pyr, prv_col, pc, o, o + plane * 4u, 0u);
                 }
             }
         }
 
+        prv_ext = cur_ext;
         prv_col = cur_col;
         p_gb = gb;
         p_unit = unit;
         p_sg = sg;
-        p_k0 = sl.k0;
-        p_ns = sl.ns;
-        p_col = sl.col;
-        base = nbase % NSLOT;
+        p_k0 = k0;
+        p_ext = ext;
+        p_col = col;
+        base = (base + SPS + 1) % NSLOT;
     }
 
     // ---- the last unit: its triple was published above; wait, normalise, store
@@ -528,19 +574,22 @@ void convt2d_gn_fused_kernel(FusedArgs a)
         unsigned long long pr0, pr1;
         probe_issue(a, p_unit, lane, pr0, pr1);
         pc = probe_finish(a, p_unit, lane, p_gb, pr0, pr1);
-        for (int j = 0; j < p_ns; ++j) {
+        for (int j = 0; j < SPS; ++j) {
             const v4f *sp = mybank + slot_of(j, r - 1) * 2 * THREADS;
             const int prow = 2 * (p_k0 + j);
-            store_tile(pyr, sp[0], pc, vo0, vo1, prow);
-            if (prow + 1 < Ho) store_tile(pyr, sp[THREADS], pc, vo0, vo1, prow + 1);
+            store_tile(pyr, sp[0], pc, vo0, vo1, (unsigned)(prow * WO * 4));
+            if (prow + 1 < Ho) store_tile(pyr, sp[THREADS], pc, vo0, vo1, (unsigned)((prow + 1) * WO * 4));
+        }
+        if (wave == EXTWAVE && p_ext >= 0) {
+            const int prow_e = 2 * (S * SPS + (p_ext >> 4)) + ((p_ext >> 3) & 1);
+            const unsigned o = ((unsigned)(2 * q) * plane + 32u * (p_ext & 7) + 2u * c16) * 4u;
+            if (prow_e < Ho) store_tile(pyr, prv_ext, pc, o, o + plane * 4u, (unsigned)(prow_e * WO * 4));
         }
         if (wave == COLWAVE && p_col >= 0) {
-            const int prow = 16 * p_col + c16;
-            if (prow < Ho) {
-                const unsigned o = ((unsigned)(2 * q) * plane + (unsigned)prow * WO + W) * 4u;
-                buf_store2_nt(v2f{prv_col[0] * pc.sc0 + pc.sh0, prv_col[1] * pc.sc0 + pc.sh0}, pyr, o);
-                buf_store2_nt(v2f{prv_col[2] * pc.sc1 + pc.sh1, prv_col[3] * pc.sc1 + pc.sh1}, pyr,
-                              o + plane * 4u);
+            const int prow_c = 16 * p_col + c16;
+            if (prow_c < Ho) {
+                const unsigned o = ((unsigned)(2 * q) * plane + (unsigned)prow_c * WO + W) * 4u;
+                store_tile(pyr, prv_col, pc, o, o + plane * 4u, 0u);
             }
         }
     }
@@ -553,19 +602,20 @@ __global__ void zero_words_kernel(unsigned *p, int n)
 }
 
 struct Geometry {
-    int S, SPS, TAIL, NCOL;
+    int S, NEXT, NCOL;
 };
 
-// Slices per unit: at most MAX_S and at least three steps each.
+// S slices of SPS steps; the NST - S * SPS tail steps become 16 extra row
+// tiles each, at most one per slice; at most one column tile per slice.
 bool geometry(int Ho, Geometry &g)
 {
     const int NST = (Ho + 1) / 2;
-    g.S = NST / 3 < MAX_S ? NST / 3 : MAX_S;
+    g.S = NST / SPS < MAX_S ? NST / SPS : MAX_S;
     if (g.S < 1) return false;
-    g.SPS = NST / g.S;
-    g.TAIL = NST - g.S * g.SPS;
+    const int tail = NST - g.S * SPS;
+    g.NEXT = 16 * tail;
     g.NCOL = (Ho + 15) / 16;
-    return g.SPS >= 3 && g.SPS + (g.TAIL > 0 ? 1 : 0) <= MAXST && g.NCOL <= g.S;
+    return g.NEXT <= g.S && g.NCOL <= g.S;
 }
 
 struct Occupancy {
@@ -611,7 +661,7 @@ hipError_t launch_t(const ConvT2dArgs &p, hipStream_t st)
 
     FusedArgs fa{p.x, p.w, p.b, p.gamma, p.beta, p.out, p.partials + 4,
                  reinterpret_cast<int *>(p.partials), p.N, p.C_out, p.H, p.groups, p.Ho,
-                 geo.S, geo.SPS, geo.TAIL, geo.NCOL, upr, xcd_units, p.eps, p.inv_div};
+                 geo.S, geo.NEXT, geo.NCOL, upr, xcd_units, p.eps, p.inv_div};
     void *args[] = {&fa};
     return hipLaunchCooperativeKernel(reinterpret_cast<const void *>(convt2d_gn_fused_kernel<ACT>),
                                       dim3(upr * geo.S), dim3(THREADS), args, 0, st);

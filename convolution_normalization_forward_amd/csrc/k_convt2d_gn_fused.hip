@@ -249,12 +249,15 @@ __device__ __forceinline__ void publish(const FusedArgs &a, const float *red, in
 }
 
 // Normalised 8-byte stores of one tile's two channel rows (voffsets vo0 /
-// vo1 hold the lane's pixel pair; so = the uniform row offset).
+// vo1 hold the lane's pixel pair; so = the uniform row offset).  Output rows
+// are 1032 bytes, so a tile's 128-byte run straddles two cache lines whose
+// other parts come from the neighbouring tiles of the same step: plain
+// (L2-allocating) stores let L2 merge them before they reach HBM.
 __device__ __forceinline__ void store_tile(__amdgpu_buffer_rsrc_t yr, const v4f &c, const Coef &k,
                                            unsigned vo0, unsigned vo1, unsigned so)
 {
-    buf_store2_nt(v2f{c[0] * k.sc0 + k.sh0, c[1] * k.sc0 + k.sh0}, yr, vo0, so);
-    buf_store2_nt(v2f{c[2] * k.sc1 + k.sh1, c[3] * k.sc1 + k.sh1}, yr, vo1, so);
+    buf_store2(v2f{c[0] * k.sc0 + k.sh0, c[1] * k.sc0 + k.sh0}, yr, vo0, so);
+    buf_store2(v2f{c[2] * k.sc1 + k.sh1, c[3] * k.sc1 + k.sh1}, yr, vo1, so);
 }
 
 template <int ACT>

@@ -59,14 +59,16 @@ constexpr int SPS = 4;                       // steps per slice
 constexpr int NBANK = SPS + 1;               // LDS bank slots
 constexpr int NPOS = 6;                      // ring stash positions per round (SPS + 1, padded to 3 k)
 constexpr int MAX_S = 32;                    // slices per unit
-constexpr int EXTWAVE = NWAVE - 2;           // wave that owns the slice's extra row tile
-constexpr int COLWAVE = NWAVE - 1;           // wave that owns the slice's column tile
+constexpr int SCH = CG * KS / 4;             // K entries of a single tile per wave (4 waves per tile)
+constexpr int EXTWAVE = 3;                   // wave that finishes the slice's extra row tile
+constexpr int COLWAVE = 6;                   // wave that finishes the slice's column tile
 constexpr int SPIN_LIMIT = 1 << 16;          // polls (each a memory round trip) before giving up
 constexpr unsigned OOB = 0x7ff00000u;        // buffer offset past any extent: loads return 0
 static_assert(NWAVE * 32 == W, "one row tile per wave");
 static_assert(CG * 64 == THREADS, "one (channel, 64 float4) row chunk per wave");
 static_assert(NPOS % 3 == 0 && NPOS >= SPS + 1, "stash positions");
-static_assert((EXTWAVE & 3) != (COLWAVE & 3), "extra and column tiles on different SIMDs");
+static_assert((EXTWAVE & 3) != (COLWAVE & 3), "extra and column tiles finish on different SIMDs");
+static_assert(SPS == 4, "single tiles are computed in step 2 and finished in step 3");
 
 struct FusedArgs {
     const float *x, *wt, *bias, *gamma, *beta;
@@ -298,26 +300,21 @@ __device__ __forceinline__ void epilogue_to_bank(const v4f &acc0, const v4f &acc
     }
 }
 
-// A single tile read straight from x (L2): lane (q, c16), K entry (ci, kh)
-// takes x[ci][row(c16) - kh][col(c16) - q], zero outside the input (the
-// offset is pushed past the buffer, which returns 0).  Row tile: row(c16) =
-// orow, col = 32 rt + 2 c16 + 1.  Column tile: row = 16 c + c16, col = 257.
-struct SingleTile {
-    float b[CG * KS];
-};
-
-__device__ __forceinline__ void single_load(SingleTile &t, __amdgpu_buffer_rsrc_t xr, int H, int row,
-                                            int col)
+// A single tile (the extra row tile or the column tile) is split over four
+// waves, each taking SCH = 6 of its 24 K entries (channels 2 chunk, 2 chunk
+// + 1; kh = 0..2) and reading them straight from x (L2): lane (q, c16), entry
+// (ci, kh) takes x[ci][row(c16) - kh][col(c16) - q], zero outside the input
+// (the offset is pushed past the buffer, which returns 0).  Row tile:
+// row(c16) = orow, col = 32 rt + 2 c16 + 1.  Column tile: row = 16 c + c16,
+// col = 257.  Lanes of a wave without such a tile read past the buffer.
+__device__ __forceinline__ void single_load(float (&b)[SCH], __amdgpu_buffer_rsrc_t xr, int H, int chunk,
+                                            bool has, int row, int col)
 {
 #pragma unroll
-    for (int ci = 0; ci < CG; ++ci) {
-#pragma unroll
-        for (int kh = 0; kh < KS; ++kh) {
-            const int rr = row - kh;
-            const bool ok = rr >= 0 && rr < H && col >= 0 && col < W;
-            const unsigned off = ok ? (unsigned)(((ci * H + rr) * W + col) * 4) : OOB;
-            t.b[ci * KS + kh] = buf_load1(xr, off);
-        }
+    for (int j = 0; j < SCH; ++j) {
+        const int ci = 2 * chunk + j / KS, rr = row - j % KS;
+        const bool ok = has && rr >= 0 && rr < H && col >= 0 && col < W;
+        b[j] = buf_load1(xr, ok ? (unsigned)(((ci * H + rr) * W + col) * 4) : OOB);
     }
 }
 
@@ -327,6 +324,8 @@ void convt2d_gn_fused_kernel(FusedArgs a)
 {
     __shared__ float ring[NSLOT * PAIR_FLOATS];
     __shared__ float red[NWAVE * 4 * 3];  // [wave][row of 16 lanes] slice triples
+    __shared__ v4f spart[2 * 4 * 64];     // [tile][chunk][lane] single-tile partial sums
+    __shared__ float coefs[CG * 2];       // the previous unit's (scale, shift) per channel
     __shared__ v4f bank[NBANK * 2 * THREADS];  // [slot][tile][thread], private to each thread
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -378,6 +377,7 @@ void convt2d_gn_fused_kernel(FusedArgs a)
     }
 
     float wreg[CG * KS];
+    float wsub[SCH];  // this wave's single-tile chunk of the weights
     v4f bias4 = v4f{0.f, 0.f, 0.f, 0.f};  // accumulator start: bias of channels 2q, 2q, 2q+1, 2q+1
     v4f gb = v4f{1.f, 0.f, 1.f, 0.f}, p_gb = gb;
     int wgroup = -1;
@@ -423,6 +423,12 @@ void convt2d_gn_fused_kernel(FusedArgs a)
                 const float v = buf_load1(wr, (unsigned)((((ci * CG + co) * KS + kh) * KS + (kok ? kw : 0)) * 4));
                 wreg[s] = kok ? v : 0.0f;
             }
+#pragma unroll
+            for (int j = 0; j < SCH; ++j) {
+                const int ci = 2 * (wave & 3) + j / KS, kh = j % KS;
+                const float v = buf_load1(wr, (unsigned)((((ci * CG + co) * KS + kh) * KS + (kok ? kw : 0)) * 4));
+                wsub[j] = kok ? v : 0.0f;
+            }
             const int c0 = g * CG + 2 * q;
             const float b0 = a.bias ? a.bias[c0] : 0.0f, b1 = a.bias ? a.bias[c0 + 1] : 0.0f;
             bias4 = v4f{b0, b0, b1, b1};
@@ -432,11 +438,11 @@ void convt2d_gn_fused_kernel(FusedArgs a)
 
         // ---- this slice's single tiles: B operands straight from x (L2)
         const int ext_row = 2 * (S * SPS + (ext >> 4)) + ((ext >> 3) & 1);
-        const bool is_ext = wave == EXTWAVE && ext >= 0, is_col = wave == COLWAVE && col >= 0;
-        SingleTile st;
-        if (is_ext || is_col)
-            single_load(st, xr, H, is_ext ? ext_row : 16 * col + c16,
-                        is_ext ? 32 * (ext & 7) + 2 * c16 + 1 - q : 2 * (W / 2) + 1 - q);
+        const int tsel = wave >> 2, chunk = wave & 3;  // tile (0 extra, 1 column) and K chunk
+        const bool has_t = tsel == 0 ? ext >= 0 : col >= 0;
+        float sb[SCH];
+        single_load(sb, xr, H, chunk, has_t, tsel == 0 ? ext_row : 16 * col + c16,
+                    tsel == 0 ? 32 * (ext & 7) + 2 * c16 + 1 - q : 2 * (W / 2) + 1 - q);
 
         // ---- steps.  Iteration k stores the previous unit's step k - 2, runs the
         // MFMAs of step k and the activation, sums and bank write of step k - 1
@@ -459,8 +465,26 @@ void convt2d_gn_fused_kernel(FusedArgs a)
                 xb[ci][2] = rB[ci * RP];
                 xb[ci][3] = rB[(CG + ci) * RP];
             }
-            if (k == 1 && has_prev) probe_issue(a, p_unit, lane, pr0, pr1);
-            if (k == 2 && has_prev) pc = probe_finish(a, p_unit, lane, p_gb, pr0, pr1);
+            if (k == 1 && has_prev && wave == 0) probe_issue(a, p_unit, lane, pr0, pr1);
+            if (k == 2 && has_prev) {
+                const float *cq = coefs + 4 * q;  // channels 2q, 2q+1, merged by wave 0 last step
+                pc = Coef{cq[0], cq[1], cq[2], cq[3]};
+            }
+            if (k == 3) {
+                // single tiles: the four chunk partials, summed in chunk order
+                const bool fin_e = wave == EXTWAVE && ext >= 0, fin_c = wave == COLWAVE && col >= 0;
+                if (fin_e || fin_c) {
+                    const v4f *pp = spart + (fin_e ? 0 : 4) * 64 + lane;
+                    const v4f e = activate4<ACT>(((pp[0] + pp[64]) + pp[128]) + pp[192]);
+                    // the tile's row (column tile: the lane's row) may lie past Ho
+                    if (fin_e ? ext_row < Ho : 16 * col + c16 < Ho) {
+                        sums4(e, s1, s2);
+                        cnt += 4;
+                    }
+                    if (fin_e) cur_ext = e;
+                    else cur_col = e;
+                }
+            }
             if (k >= 2 && has_prev) {
                 // the previous unit's step k - 2: its bank slot takes this round's step k - 1
                 const v4f *sp = mybank + slot_of(k - 1, r) * 2 * THREADS;
@@ -487,6 +511,21 @@ void convt2d_gn_fused_kernel(FusedArgs a)
                                       mybank + slot_of(k - 1, r) * 2 * THREADS);
             acc0 = n0;
             acc1 = n1;
+            if (k == 1 && has_prev && wave == 0) {
+                // the previous unit's coefficients for the next step (one merge per workgroup)
+                const Coef cw = probe_finish(a, p_unit, lane, p_gb, pr0, pr1);
+                if (c16 == 0) {
+                    coefs[4 * q] = cw.sc0; coefs[4 * q + 1] = cw.sh0;
+                    coefs[4 * q + 2] = cw.sc1; coefs[4 * q + 3] = cw.sh1;
+                }
+            }
+            if (k == 2 && has_t) {
+                // this wave's chunk of a single tile (chunk 0 carries the bias)
+                v4f c = chunk == 0 ? bias4 : v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int j = 0; j < SCH; ++j) c = mfma_16x16x4(wsub[j], sb[j], c);
+                spart[(tsel * 4 + chunk) * 64 + lane] = c;
+            }
 
             // ---- ring stashes at the end of step k, each followed by its loads
             if (k <= SPS - 2) {
@@ -511,22 +550,6 @@ void convt2d_gn_fused_kernel(FusedArgs a)
         }
         epilogue_to_bank<ACT>(acc0, acc1, 2 * (k0 + SPS - 1) + 1 < Ho, s1, s2, cnt,
                               mybank + slot_of(SPS - 1, r) * 2 * THREADS);
-
-        // ---- single tiles
-        if (is_ext || is_col) {
-            v4f c = bias4;
-#pragma unroll
-            for (int s = 0; s < CG * KS; ++s) c = mfma_16x16x4(wreg[s], st.b[s], c);
-            const v4f e = activate4<ACT>(c);
-            // the tile's row (column tile: the lane's row) may lie past Ho
-            const bool ok = is_ext ? ext_row < Ho : 16 * col + c16 < Ho;
-            if (ok) {
-                sums4(e, s1, s2);
-                cnt += 4;
-            }
-            if (wave == EXTWAVE) cur_ext = e;
-            else cur_col = e;
-        }
 
         // ---- slice statistics -> red[wave][row]; published after the next barrier
         {

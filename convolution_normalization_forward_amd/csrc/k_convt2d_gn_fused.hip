@@ -60,8 +60,11 @@ constexpr int NBANK = SPS + 1;               // LDS bank slots
 constexpr int NPOS = 6;                      // ring stash positions per round (SPS + 1, padded to 3 k)
 constexpr int MAX_S = 32;                    // slices per unit
 constexpr int SCH = CG * KS / 4;             // K entries of a single tile per wave (4 waves per tile)
-constexpr int EXTWAVE = 3;                   // wave that finishes the slice's extra row tile
-constexpr int COLWAVE = 6;                   // wave that finishes the slice's column tile
+// Per-round duties go to waves on different SIMDs (wave w runs on SIMD w % 4):
+constexpr int COEFWAVE = 0;                  // merges the previous unit's slice triples
+constexpr int PUBWAVE = 1;                   // publishes this workgroup's slice triple
+constexpr int EXTWAVE = 3;                   // finishes the slice's extra row tile
+constexpr int COLWAVE = 6;                   // finishes the slice's column tile
 constexpr int SPIN_LIMIT = 1 << 16;          // polls (each a memory round trip) before giving up
 constexpr unsigned OOB = 0x7ff00000u;        // buffer offset past any extent: loads return 0
 static_assert(NWAVE * 32 == W, "one row tile per wave");
@@ -391,11 +394,11 @@ void convt2d_gn_fused_kernel(FusedArgs a)
         const int unit = r * a.upr + ulocal;
         __syncthreads();  // pairs 0, 1 in the ring; last round's ring readers done; red[] complete
         if (unit >= U) {
-            if (p_unit >= 0 && wave == 0) publish(a, red, p_unit, p_sg, lane);
+            if (p_unit >= 0 && wave == PUBWAVE) publish(a, red, p_unit, p_sg, lane);
             break;
         }
         const bool has_prev = p_unit >= 0;
-        if (has_prev && wave == 0) publish(a, red, p_unit, p_sg, lane);
+        if (has_prev && wave == PUBWAVE) publish(a, red, p_unit, p_sg, lane);
 
         const int sg = (s_base + r) % S;
         const int k0 = sg * SPS;
@@ -465,9 +468,9 @@ void convt2d_gn_fused_kernel(FusedArgs a)
                 xb[ci][2] = rB[ci * RP];
                 xb[ci][3] = rB[(CG + ci) * RP];
             }
-            if (k == 1 && has_prev && wave == 0) probe_issue(a, p_unit, lane, pr0, pr1);
+            if (k == 1 && has_prev && wave == COEFWAVE) probe_issue(a, p_unit, lane, pr0, pr1);
             if (k == 2 && has_prev) {
-                const float *cq = coefs + 4 * q;  // channels 2q, 2q+1, merged by wave 0 last step
+                const float *cq = coefs + 4 * q;  // channels 2q, 2q+1, merged last step
                 pc = Coef{cq[0], cq[1], cq[2], cq[3]};
             }
             if (k == 3) {
@@ -511,7 +514,7 @@ void convt2d_gn_fused_kernel(FusedArgs a)
                                       mybank + slot_of(k - 1, r) * 2 * THREADS);
             acc0 = n0;
             acc1 = n1;
-            if (k == 1 && has_prev && wave == 0) {
+            if (k == 1 && has_prev && wave == COEFWAVE) {
                 // the previous unit's coefficients for the next step (one merge per workgroup)
                 const Coef cw = probe_finish(a, p_unit, lane, p_gb, pr0, pr1);
                 if (c16 == 0) {

@@ -33,7 +33,7 @@ CNF_ERR_HIP = 6
 CNF_ERR_ABI = 7
 
 CNF_CONV, CNF_CONV_TRANSPOSE = 0, 1
-ACT = {"none": 0, "hardswish": 1, "gelu": 2, "softmax": 3}
+ACT = {"none": 0, "hardswish": 1, "gelu": 2, "softmax": 3, "gelu_tanh": 4}
 NORM = {"none": 0, "group": 1, "instance": 2}
 REDUCE = {"none": 0, "mean": 1, "maxpool": 2}
 

@@ -82,7 +82,7 @@ cnf_status cnf_plan_create(const cnf_desc *desc, cnf_plan **plan)
     if (d.in_dims[0] < 1 || d.in_dims[1] < 1 || d.in_dims[2] < 1) return CNF_ERR_INVALID_DESC;
     if (d.ndim == 2 && d.in_dims[0] != 1) return CNF_ERR_INVALID_DESC;
     if (d.has_bias != 0 && d.has_bias != 1) return CNF_ERR_INVALID_DESC;
-    if (d.act < CNF_ACT_NONE || d.act > CNF_ACT_SOFTMAX_CHANNEL) return CNF_ERR_INVALID_DESC;
+    if (d.act < CNF_ACT_NONE || d.act > CNF_ACT_GELU_TANH) return CNF_ERR_INVALID_DESC;
     if (d.norm < CNF_NORM_NONE || d.norm > CNF_NORM_INSTANCE) return CNF_ERR_INVALID_DESC;
     if (d.reduce < CNF_RED_NONE || d.reduce > CNF_RED_MAXPOOL) return CNF_ERR_INVALID_DESC;
     if (d.affine != 0 && d.affine != 1) return CNF_ERR_INVALID_DESC;
@@ -170,11 +170,11 @@ cnf_status cnf_plan_create(const cnf_desc *desc, cnf_plan **plan)
 
     p.workspace = 0;
     if (p.family == FAM_IGEMM) p.workspace = cnf::conv2d_igemm_workspace(d.N, d.C_in, p.Ho, p.Wo);
-    if (p.family == FAM_CONVT) p.workspace = cnf::convt2d_workspace(d.N, d.groups, p.Ho, p.Wo);
+    if (p.family == FAM_CONVT) p.workspace = cnf::convt2d_workspace(d.N, d.C_out, p.Ho, p.Wo);
     if (p.family == FAM_CONVT_FUSED) {
         // room for the two-pass fallback too (used if the grid cannot be co-resident)
         const size_t a = cnf::convt2d_fused_workspace(d.N, d.groups, p.Ho);
-        const size_t b = cnf::convt2d_workspace(d.N, d.groups, p.Ho, p.Wo);
+        const size_t b = cnf::convt2d_workspace(d.N, d.C_out, p.Ho, p.Wo);
         p.workspace = a > b ? a : b;
     }
 

@@ -95,7 +95,7 @@ __device__ __forceinline__ float row_sum16(float v) {
     return v;
 }
 
-enum : int { ACT_NONE = 0, ACT_HARDSWISH = 1, ACT_GELU_ERF = 2, ACT_SOFTMAX = 3 };
+enum : int { ACT_NONE = 0, ACT_HARDSWISH = 1, ACT_GELU_ERF = 2, ACT_SOFTMAX = 3, ACT_GELU_TANH = 4 };
 
 __device__ __forceinline__ float hardswish(float x) {
     return x * fminf(fmaxf(x + 3.0f, 0.0f), 6.0f) * (1.0f / 6.0f);
@@ -122,10 +122,20 @@ __device__ __forceinline__ float gelu_erf(float x) {
     return fmaf(fabsf(x), poly * e, fmaxf(x, 0.0f));
 }
 
+// Tanh form of GELU, 0.5 x (1 + tanh(u)), u = sqrt(2/pi) (x + 0.044715 x^3).
+// With 1 + tanh(u) = 2 / (1 + exp(-2u)) it is x / (1 + exp2(x (a + b x^2))),
+// a = -2 sqrt(2/pi) log2(e), b = 0.044715 a: 6 VALU ops + exp2 + rcp.  For
+// x -> -inf the exponential overflows to +inf and the result is -0.
+__device__ __forceinline__ float gelu_tanh(float x) {
+    const float e = __builtin_amdgcn_exp2f(x * fmaf(x * x, -1.029432396e-01f, -2.302208198e+00f));
+    return x * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
 template <int ACT>
 __device__ __forceinline__ float activate(float x) {
     if constexpr (ACT == ACT_HARDSWISH) return hardswish(x);
     else if constexpr (ACT == ACT_GELU_ERF) return gelu_erf(x);
+    else if constexpr (ACT == ACT_GELU_TANH) return gelu_tanh(x);
     else return x;
 }
 

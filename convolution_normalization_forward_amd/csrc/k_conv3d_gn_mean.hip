@@ -234,7 +234,7 @@ bool conv3d_gn_mean_supported(int C_in, int C_out, int kernel, int D, int H, int
     if (C_out != 16 || kernel != KS) return false;
     if (C_in != 3 && C_in != 1) return false;
     if (W != WP || H < KS || H > HWP / WP || D < KS) return false;
-    return act == ACT_NONE || act == ACT_HARDSWISH || act == ACT_GELU_ERF;
+    return act == ACT_NONE || act == ACT_HARDSWISH || act == ACT_GELU_ERF || act == ACT_GELU_TANH;
 }
 
 hipError_t launch_conv3d_gn_mean(const Conv3dGnMeanArgs &a, hipStream_t st)
@@ -244,9 +244,11 @@ hipError_t launch_conv3d_gn_mean(const Conv3dGnMeanArgs &a, hipStream_t st)
     CNF_CASE(3, ACT_HARDSWISH)
     CNF_CASE(3, ACT_NONE)
     CNF_CASE(3, ACT_GELU_ERF)
+    CNF_CASE(3, ACT_GELU_TANH)
     CNF_CASE(1, ACT_HARDSWISH)
     CNF_CASE(1, ACT_NONE)
     CNF_CASE(1, ACT_GELU_ERF)
+    CNF_CASE(1, ACT_GELU_TANH)
 #undef CNF_CASE
     return hipErrorInvalidValue;
 }

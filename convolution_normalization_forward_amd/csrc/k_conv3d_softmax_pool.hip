@@ -267,10 +267,12 @@ hipError_t launch_t(const Conv3dSoftmaxPoolArgs &a, hipStream_t st)
 
 bool conv3d_softmax_pool_supported(int C_in, int C_out, int kernel, int act, int pool_total)
 {
+    // exactly the instantiations launch_conv3d_softmax_pool dispatches to
     if (C_out != 16 || pool_total != 4) return false;
-    if (!((C_in == 3 && (kernel == 3 || kernel == 2)) || (C_in == 1 && kernel == 3)))
-        return false;
-    return act == ACT_SOFTMAX || act == ACT_NONE || act == ACT_HARDSWISH || act == ACT_GELU_ERF;
+    if (C_in == 3 && kernel == 3)
+        return act == ACT_SOFTMAX || act == ACT_NONE || act == ACT_HARDSWISH || act == ACT_GELU_ERF ||
+               act == ACT_GELU_TANH;
+    return ((C_in == 3 && kernel == 2) || (C_in == 1 && kernel == 3)) && act == ACT_SOFTMAX;
 }
 
 hipError_t launch_conv3d_softmax_pool(const Conv3dSoftmaxPoolArgs &a, hipStream_t st)
@@ -282,6 +284,7 @@ hipError_t launch_conv3d_softmax_pool(const Conv3dSoftmaxPoolArgs &a, hipStream_
     CNF_CASE(3, 3, ACT_NONE)
     CNF_CASE(3, 3, ACT_HARDSWISH)
     CNF_CASE(3, 3, ACT_GELU_ERF)
+    CNF_CASE(3, 3, ACT_GELU_TANH)
     CNF_CASE(3, 2, ACT_SOFTMAX)
     CNF_CASE(1, 3, ACT_SOFTMAX)
 #undef CNF_CASE

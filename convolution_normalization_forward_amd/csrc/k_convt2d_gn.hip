@@ -1,15 +1,16 @@
 // k_convt2d_gn.hip -- grouped ConvTranspose2d (stride 1, no padding, k = 3,
 // 8 input and 8 output channels per group) + activation, writing y and one
-// Welford partial per (sample, group, row block); then an in-place GroupNorm
-// pass over the (sample, group) statistics.
+// Welford partial per (sample, channel, row block); then an in-place
+// GroupNorm pass over any norm grouping of the channels (InstanceNorm is
+// GroupNorm with one channel per group), so the norm groups need not be the
+// conv groups.
 //
 // Page "Kimi-K2.6__l2_p19": ConvTranspose2d(64 -> 64, k = 3, stride 1,
 // groups 8) -> GELU -> GroupNorm(8) on 128 x 64 x 256 x 256, output 258 x 258.
 // Second trace: out[i, j] = sum x[i - kh, j - kw] * W[ci, co, kh, kw] with x
 // zero outside its extent, weights laid out (C_in, C_out/groups, kh, kw);
-// first trace: GroupNorm statistics run over the 8 channels of a group and
-// all 258 x 258 positions, so they need the whole (sample, group) unit.
-// With conv groups == norm groups every (sample, group) unit is independent.
+// first trace: GroupNorm statistics run over the channels of a norm group and
+// all 258 x 258 positions, so they need the whole (sample, norm group) unit.
 //
 // Column-pair MFMA mapping.  A group has only 8 output channels, half of a
 // 16-wide MFMA operand.  Output pixels (i, 2p) and (i, 2p+1) read the same
@@ -91,8 +92,9 @@ void convt2d_g8_kernel(const float *__restrict__ x, const float *__restrict__ wt
     const int rows_here = min(R, Ho - i0);
     const int npairs = rows_here * PR;
     const int T = (npairs + 15) >> 4;
-    float s1 = 0.f, s2 = 0.f;  // per-lane sum and sum of squares (at most a few dozen values)
-    int cnt_i = 0;
+    // per-lane sums of the lane's two channels 2q (a) and 2q+1 (b)
+    float s1a = 0.f, s2a = 0.f, s1b = 0.f, s2b = 0.f;
+    int cnt_i = 0;  // values per channel
     float *yg = y + ((size_t)n * C + (size_t)g * CG) * Ho * Wo;
 
     for (int t0 = wave; t0 < T; t0 += 4 * NB) {
@@ -132,53 +134,62 @@ void convt2d_g8_kernel(const float *__restrict__ x, const float *__restrict__ wt
                 v1.y = activate<ACT>(acc[j][3] + b1);
                 *reinterpret_cast<float2 *>(yg + (size_t)(2 * q) * Ho * Wo + o) = v0;
                 *reinterpret_cast<float2 *>(yg + (size_t)(2 * q + 1) * Ho * Wo + o) = v1;
-                s1 += (v0.x + v0.y) + (v1.x + v1.y);
-                s2 = fmaf(v0.x, v0.x, s2); s2 = fmaf(v0.y, v0.y, s2);
-                s2 = fmaf(v1.x, v1.x, s2); s2 = fmaf(v1.y, v1.y, s2);
-                cnt_i += 4;
+                s1a += v0.x + v0.y;
+                s2a = fmaf(v0.x, v0.x, s2a); s2a = fmaf(v0.y, v0.y, s2a);
+                s1b += v1.x + v1.y;
+                s2b = fmaf(v1.x, v1.x, s2b); s2b = fmaf(v1.y, v1.y, s2b);
+                cnt_i += 2;
             }
         }
     }
 
-    // ---- one Welford triple for the whole workgroup (all 8 channels)
-    float cnt = (float)cnt_i;
-    float mean = cnt_i ? s1 / cnt : 0.0f;
-    float m2 = cnt_i ? fmaxf(s2 - s1 * mean, 0.0f) : 0.0f;
-    row_chan16(cnt, mean, m2);
-#pragma unroll
-    for (int sh = 16; sh <= 32; sh <<= 1) {
-        const float nb = __shfl_xor(cnt, sh, 64), mb = __shfl_xor(mean, sh, 64),
-                    qb = __shfl_xor(m2, sh, 64);
-        chan_merge(cnt, mean, m2, nb, mb, qb);
-    }
+    // ---- one Welford triple per channel: the 16 lanes of a row share channels
+    // 2q, 2q+1; rows merge in LDS, then the 4 waves in wave order
     __syncthreads();  // LDS reuse
-    if (lane == 0) { lds[wave * 3] = cnt; lds[wave * 3 + 1] = mean; lds[wave * 3 + 2] = m2; }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const float s1 = j ? s1b : s1a, s2 = j ? s2b : s2a;
+        float cnt = (float)cnt_i;
+        float mean = cnt_i ? s1 / cnt : 0.0f;
+        float m2 = cnt_i ? fmaxf(s2 - s1 * mean, 0.0f) : 0.0f;
+        row_chan16(cnt, mean, m2);
+        if (c16 == 0) {
+            float *e = lds + (wave * CG + 2 * q + j) * 3;
+            e[0] = cnt; e[1] = mean; e[2] = m2;
+        }
+    }
     __syncthreads();
-    if (tid == 0) {
+    if (tid < CG) {
         float c2 = 0.f, m = 0.f, s2 = 0.f;
-        for (int k = 0; k < 4; ++k) chan_merge(c2, m, s2, lds[k * 3], lds[k * 3 + 1], lds[k * 3 + 2]);
-        float *pp = partials + (((size_t)n * G + g) * rblocks + rb) * 3;
+        for (int k = 0; k < 4; ++k) {
+            const float *e = lds + (k * CG + tid) * 3;
+            chan_merge(c2, m, s2, e[0], e[1], e[2]);
+        }
+        float *pp = partials + (((size_t)n * C + g * CG + tid) * rblocks + rb) * 3;
         pp[0] = c2; pp[1] = m; pp[2] = s2;
     }
+    (void)G;
 }
 
-// One workgroup per (sample, channel): merge the group's row-block partials
-// in a fixed order (strided per thread, then in thread order), then normalise
-// the channel's plane in place.
+// One workgroup per (sample, channel): merge the row-block partials of every
+// channel in the channel's norm group (NG groups of C / NG channels) in a
+// fixed order (strided per thread, then in thread order), then normalise the
+// channel's plane in place.
 __global__ __launch_bounds__(256)
 void convt2d_gn_pass_kernel(float *__restrict__ y, const float *__restrict__ partials,
                             const float *__restrict__ gamma, const float *__restrict__ beta,
-                            int C, int G, int plane, int rblocks, float eps, float inv_div)
+                            int C, int NG, int plane, int rblocks, float eps, float inv_div)
 {
     const int nc = blockIdx.x;
-    const int n = nc / C, c = nc % C, g = c / (C / G);
+    const int n = nc / C, c = nc % C, cg = C / NG, c0 = (c / cg) * cg;
     const int tid = threadIdx.x;
     __shared__ float tri[256][3];
     __shared__ float coef[2];
     {
+        // the group's channels' partials are contiguous: [c0 .. c0 + cg) x rblocks
         float cnt = 0.f, mean = 0.f, m2 = 0.f;
-        const float *pp = partials + ((size_t)n * G + g) * rblocks * 3;
-        for (int r = tid; r < rblocks; r += 256) chan_merge(cnt, mean, m2, pp[r * 3], pp[r * 3 + 1], pp[r * 3 + 2]);
+        const float *pp = partials + ((size_t)n * C + c0) * rblocks * 3;
+        for (int r = tid; r < cg * rblocks; r += 256) chan_merge(cnt, mean, m2, pp[r * 3], pp[r * 3 + 1], pp[r * 3 + 2]);
         tri[tid][0] = cnt; tri[tid][1] = mean; tri[tid][2] = m2;
     }
     __syncthreads();
@@ -227,8 +238,8 @@ hipError_t launch_t(const ConvT2dArgs &a, hipStream_t st)
                        rblocks);
     if (a.norm_groups > 0) {
         hipLaunchKernelGGL(convt2d_gn_pass_kernel, dim3(a.N * a.C_out), dim3(256), 0, st, a.out,
-                           a.partials, a.gamma, a.beta, a.C_out, a.groups, a.Ho * a.Wo, rblocks,
-                           a.eps, a.inv_div);
+                           a.partials, a.gamma, a.beta, a.C_out, a.norm_groups, a.Ho * a.Wo,
+                           rblocks, a.eps, a.inv_div);
     } else if (a.inv_div != 1.0f) {
         const size_t count = (size_t)a.N * a.C_out * a.Ho * a.Wo;
         hipLaunchKernelGGL(scale_kernel, dim3(4096), dim3(256), 0, st, a.out, count, a.inv_div);
@@ -245,16 +256,16 @@ bool convt2d_supported(int C_in, int C_out, int kernel, int groups, int H, int W
     if (W % 4 != 0 || H < 1) return false;
     if ((size_t)CG * (R + KS - 1) * row_pitch(W) * sizeof(float) > 64 * 1024) return false;
     if (act == ACT_SOFTMAX) return false;
-    if (norm == 1 /* group */ && num_groups != groups) return false;
-    if (norm == 2 /* instance */) return false;
+    // any norm grouping of the channels: partials are per channel
+    if (norm == 1 /* group */ && (num_groups < 1 || C_out % num_groups != 0)) return false;
     return true;
 }
 
-size_t convt2d_workspace(int N, int groups, int Ho, int Wo)
+size_t convt2d_workspace(int N, int C_out, int Ho, int Wo)
 {
     (void)Wo;
     const size_t rblocks = (Ho + R - 1) / R;
-    return (size_t)N * groups * rblocks * 3 * sizeof(float);
+    return (size_t)N * C_out * rblocks * 3 * sizeof(float);
 }
 
 hipError_t launch_convt2d(const ConvT2dArgs &a, hipStream_t st)
@@ -263,6 +274,7 @@ hipError_t launch_convt2d(const ConvT2dArgs &a, hipStream_t st)
     case ACT_NONE: return launch_t<ACT_NONE>(a, st);
     case ACT_HARDSWISH: return launch_t<ACT_HARDSWISH>(a, st);
     case ACT_GELU_ERF: return launch_t<ACT_GELU_ERF>(a, st);
+    case ACT_GELU_TANH: return launch_t<ACT_GELU_TANH>(a, st);
     default: return hipErrorInvalidValue;
     }
 }

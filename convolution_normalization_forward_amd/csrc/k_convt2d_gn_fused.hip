@@ -649,7 +649,7 @@ bool geometry(int Ho, Geometry &g)
 
 struct Occupancy {
     int device = -1;
-    int blocks_per_cu[4] = {0, 0, 0, 0};
+    int blocks_per_cu[5] = {0, 0, 0, 0, 0};
     int cus = 0;
 };
 
@@ -710,7 +710,7 @@ bool convt2d_fused_supported(int C_in, int C_out, int groups, int H, int W_, int
     Geometry g;
     return W_ == W && C_in == CG * groups && C_out == CG * groups && H >= 1 &&
            geometry(H + KS - 1, g) && norm == 1 /* group */ && num_groups == groups &&
-           (act == ACT_NONE || act == ACT_HARDSWISH || act == ACT_GELU_ERF);
+           (act == ACT_NONE || act == ACT_HARDSWISH || act == ACT_GELU_ERF || act == ACT_GELU_TANH);
 }
 
 size_t convt2d_fused_workspace(int N, int groups, int Ho)
@@ -725,6 +725,7 @@ hipError_t launch_convt2d_fused(const ConvT2dArgs &a, hipStream_t st)
     case ACT_NONE: return launch_t<ACT_NONE>(a, st);
     case ACT_HARDSWISH: return launch_t<ACT_HARDSWISH>(a, st);
     case ACT_GELU_ERF: return launch_t<ACT_GELU_ERF>(a, st);
+    case ACT_GELU_TANH: return launch_t<ACT_GELU_TANH>(a, st);
     default: return hipErrorInvalidValue;
     }
 }

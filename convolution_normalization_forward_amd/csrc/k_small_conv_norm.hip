@@ -213,6 +213,7 @@ hipError_t launch_small_conv_norm(const SmallConvNormArgs &a, hipStream_t st)
         case ACT_NONE: return launch_t<CI, KS, ND, ACT_NONE>(a, st);                             \
         case ACT_HARDSWISH: return launch_t<CI, KS, ND, ACT_HARDSWISH>(a, st);                   \
         case ACT_GELU_ERF: return launch_t<CI, KS, ND, ACT_GELU_ERF>(a, st);                     \
+        case ACT_GELU_TANH: return launch_t<CI, KS, ND, ACT_GELU_TANH>(a, st);                   \
         default: return hipErrorInvalidValue;                                                    \
         }                                                                                        \
     }

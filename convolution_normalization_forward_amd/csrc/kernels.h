@@ -73,12 +73,12 @@ struct ConvT2dArgs {
     int N, C_in, C_out, H, W, groups;
     int Ho, Wo;
     int act;
-    int norm_groups;     // 0: no norm; must equal groups otherwise
+    int norm_groups;     // 0: no norm; else GroupNorm groups (C_out: InstanceNorm)
     float eps, inv_div;
 };
 bool convt2d_supported(int C_in, int C_out, int kernel, int groups, int H, int W, int act,
                        int norm, int num_groups);
-size_t convt2d_workspace(int N, int groups, int Ho, int Wo);
+size_t convt2d_workspace(int N, int C_out, int Ho, int Wo);  // [N][C_out][row blocks][3]
 hipError_t launch_convt2d(const ConvT2dArgs &a, hipStream_t st);
 // single-write variant (W == 256, GroupNorm groups == conv groups): cooperative
 // persistent kernel; returns an error (and launches nothing) if the grid cannot

@@ -65,7 +65,9 @@ typedef enum {
     CNF_ACT_NONE = 0,
     CNF_ACT_HARDSWISH = 1,        /* x * min(max(x + 3, 0), 6) / 6           (l2_p27) */
     CNF_ACT_GELU_ERF = 2,         /* 0.5 * x * (1 + erf(x / sqrt 2))          (l2_p19) */
-    CNF_ACT_SOFTMAX_CHANNEL = 3   /* softmax over C_out at every position     (l2_p6)  */
+    CNF_ACT_SOFTMAX_CHANNEL = 3,  /* softmax over C_out at every position     (l2_p6)  */
+    CNF_ACT_GELU_TANH = 4         /* 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))),
+                                     the tanh form of GELU   (l2_p19, first trace)      */
 } cnf_act;
 
 typedef enum {

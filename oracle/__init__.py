@@ -202,6 +202,8 @@ def pre_norm(wl: dict, x, w, b):
         y = hardswish(y)
     elif act == "gelu":
         y = gelu_erf(y)
+    elif act == "gelu_tanh":
+        y = gelu_tanh(y)
     elif act == "softmax":
         y = softmax_channel(y)
     elif act != "none":

@@ -122,5 +122,25 @@ def test_workspace_sizes_are_what_the_partials_need():
     tiles = 2 * 32   # 126 = 64 + 62 columns, 126 rows in blocks of 4
     assert p4.workspace_bytes == 128 * tiles * 128 * 3 * 4 + 64 * 9 * 128 * 4
     p5 = cnf.Plan(_desc("convt2d_gelu_gn_n128"))
-    assert p5.workspace_bytes == 128 * 8 * 65 * 3 * 4
+    # the larger of the single-write kernel's slice triples (16 B header +
+    # 1024 units x 32 slices x 16 B) and the two-pass fallback's per-channel
+    # row-block triples (128 x 64 channels x 65 row blocks x 12 B)
+    assert p5.workspace_bytes == max(16 + 1024 * 32 * 16, 128 * 64 * 65 * 3 * 4)
     assert cnf.Plan(_desc()).workspace_bytes == 0
+
+
+def test_supported_matrix_edges():
+    # combinations a family advertises are exactly the ones it launches
+    ok = [("conv3d_softmax_pool_n128", dict(act="gelu_tanh")),
+          ("convt2d_gelu_gn_n128", dict(num_groups=4)),
+          ("convt2d_gelu_gn_n128", dict(num_groups=16)),
+          ("convt2d_gelu_gn_n128", dict(norm="instance")),
+          ("convt2d_gelu_gn_n128", dict(act="gelu_tanh")),
+          ("conv2d_in_div_n128", dict(affine=1)),
+          ("conv3d_hswish_gn_mean_n1024", dict(act="gelu_tanh"))]
+    for name, over in ok:
+        assert cnf.cnf_plan_create_status(_desc(name, **over)) == cnf.CNF_OK, (name, over)
+    bad = [("conv3d_softmax_pool_n128", dict(kernel=2, act="hardswish")),
+           ("conv3d_softmax_pool_n128", dict(C_in=1, act="none"))]
+    for name, over in bad:
+        assert cnf.cnf_plan_create_status(_desc(name, **over)) == cnf.CNF_ERR_UNSUPPORTED, (name, over)

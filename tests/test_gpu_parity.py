@@ -86,6 +86,18 @@ SMALL_CASES = [
     ("convt2d_gelu_gn_n128", dict(N=3, in_dims=(1, 126, 256))),
     ("convt2d_gelu_gn_n128", dict(N=3, in_dims=(1, 128, 256), act="hardswish")),
     ("convt2d_gelu_gn_n128", dict(N=2, in_dims=(1, 256, 256))),
+    # tanh-form GELU in every family that takes an activation
+    ("conv2d_in_div_n2", dict(N=2, act="gelu_tanh")),
+    ("conv3d_softmax_pool_n128", dict(N=2, act="gelu_tanh")),
+    ("conv3d_hswish_gn_mean_n1024", dict(N=2, act="gelu_tanh")),
+    ("convt2d_gelu_gn_n128", dict(N=2, in_dims=(1, 30, 256), act="gelu_tanh")),
+    ("convt2d_gelu_gn_n128", dict(N=2, in_dims=(1, 9, 20), act="gelu_tanh")),
+    # norm groups other than the conv groups, InstanceNorm, affine InstanceNorm
+    ("convt2d_gelu_gn_n128", dict(N=2, in_dims=(1, 11, 28), num_groups=4)),
+    ("convt2d_gelu_gn_n128", dict(N=2, in_dims=(1, 11, 28), num_groups=16)),
+    ("convt2d_gelu_gn_n128", dict(N=2, in_dims=(1, 30, 256), num_groups=2)),
+    ("convt2d_gelu_gn_n128", dict(N=2, in_dims=(1, 13, 20), norm="instance", affine=1)),
+    ("conv2d_in_div_n128", dict(N=2, C_in=8, in_dims=(1, 21, 37), affine=1)),
 ]
 
 

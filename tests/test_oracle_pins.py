@@ -226,6 +226,22 @@ def test_gelu_tanh_form_would_break_the_tolerance():
     assert d.max() < 1e-3
 
 
+def test_gelu_tanh_form_pins():
+    # the tanh form (page l2_p19, first trace) keeps GELU's odd part x exactly
+    # (tanh is odd), tends to x and 0 in the tails, and stays within 5e-4 of the
+    # table-pinned erf form while differing from it by more than 4.5e-4
+    # somewhere; a wrong cubic coefficient or sqrt(2/pi) moves that maximum
+    # outside the band (0.04715 -> 1.5e-3, 0.8 -> 6.4e-4, 0 -> 3.4e-2).
+    x = RNG.uniform(-6, 6, 2000)
+    np.testing.assert_allclose(oracle.gelu_tanh(x) - oracle.gelu_tanh(-x), x, atol=1e-13)
+    big = np.array([10.0, 12.0, 20.0])
+    np.testing.assert_allclose(oracle.gelu_tanh(big), big, atol=1e-12)
+    np.testing.assert_allclose(oracle.gelu_tanh(-big), 0.0, atol=1e-12)
+    g = np.linspace(-6, 6, 120001)
+    d = np.abs(oracle.gelu_erf(g) - oracle.gelu_tanh(g)).max()
+    assert 4.5e-4 < d < 5.0e-4, d
+
+
 def test_softmax_rows_sum_to_one_and_closed_forms():
     y = RNG.standard_normal((3, 16, 4, 5, 6)) * 5
     s = oracle.softmax_channel(y)

@@ -43,8 +43,9 @@ DOMINANT = {
     "conv2d_in_div_n2": ("small_conv_norm_kernel", "mfma"),
     "conv3d_softmax_pool_n128": ("conv3d_softmax_pool_kernel", "mfma"),
     "conv3d_hswish_gn_mean_n1024": ("conv3d_k4_gn_mean_kernel", "mfma"),
-    "conv2d_in_div_n128": ("conv2d_igemm_kernel", "mfma"),
+    "conv2d_in_div_n128": ("conv2d_igemm_kernel<128", "mfma"),
     "convt2d_gelu_gn_n128": ("convt2d_gn_fused_kernel", "mfma"),
+    "convt2d_dense_gelu_gn_n128": ("conv2d_igemm_kernel<64", "mfma"),
 }
 
 

@@ -19,6 +19,9 @@ Workloads (shapes and options as the four source pages state their problems):
   * convt2d_gelu_gn_n128  ConvTranspose2d 64->64 k3 s1 groups 8 on
                           128x64x256x256, exact GELU, GroupNorm(8) with affine
                           (page l2_p19).
+  * convt2d_dense_gelu_gn_n128
+                          the same with groups = 1 (dense 64->64 transposed
+                          conv, K = 576): the other reading of l2_p19's problem.
 
 Distributions: x ~ N(0, 1) (or U[0, 1) as a second parity set, the
 distribution the pages' own harness used); conv weight and bias ~
@@ -64,6 +67,10 @@ WORKLOADS = {
     "convt2d_gelu_gn_n128": _wl(
         id=5, ndim=2, kind="conv_transpose", N=128, C_in=64, C_out=64,
         in_dims=(1, 256, 256), kernel=3, groups=8, act="gelu", norm="group",
+        num_groups=8, affine=1),
+    "convt2d_dense_gelu_gn_n128": _wl(
+        id=6, ndim=2, kind="conv_transpose", N=128, C_in=64, C_out=64,
+        in_dims=(1, 256, 256), kernel=3, groups=1, act="gelu", norm="group",
         num_groups=8, affine=1),
 }
 

@@ -16,7 +16,7 @@ enum Family : int {
     FAM_GN_MEAN = 1,       // Conv3d k4 C_out 16 + act + GroupNorm + mean, fully fused
     FAM_SOFTMAX_POOL = 2,  // Conv3d C_out 16 + channel softmax + 4^3 max pool
     FAM_SMALL = 3,         // small conv C_out 16, one workgroup per sample
-    FAM_IGEMM = 4,         // Conv2d C_out 128 k3 implicit GEMM + norm pass
+    FAM_IGEMM = 4,         // Conv2d C_out 128/64 k3 implicit GEMM (also dense stride-1 ConvTranspose2d) + norm pass
     FAM_CONVT = 5,         // grouped ConvTranspose2d 8x8 per group + act + GroupNorm pass
     FAM_CONVT_FUSED = 6    // same, single write: cooperative kernel, cross-workgroup merge
 };
@@ -157,7 +157,12 @@ cnf_status cnf_plan_create(const cnf_desc *desc, cnf_plan **plan)
                  cnf::conv2d_igemm_supported(d.C_in, d.C_out, k, d.groups, H, W, d.act))
             p.family = FAM_IGEMM;
     } else if (d.kind == CNF_CONV_TRANSPOSE && d.reduce == CNF_RED_NONE) {
-        if (cnf::convt2d_supported(d.C_in, d.C_out, k, d.groups, H, W, d.act, d.norm,
+        // dense transposed conv: the implicit GEMM on the input padded by k - 1;
+        // 8-channel groups (or a dense 8 -> 8 one): the column-pair kernels
+        if (d.groups == 1 && cnf::conv2d_igemm_supported(d.C_in, d.C_out, k, d.groups,
+                                                         H + 2 * (k - 1), W + 2 * (k - 1), d.act))
+            p.family = FAM_IGEMM;
+        else if (cnf::convt2d_supported(d.C_in, d.C_out, k, d.groups, H, W, d.act, d.norm,
                                    d.num_groups))
             p.family = FAM_CONVT;
         if (p.family == FAM_CONVT &&
@@ -169,7 +174,8 @@ cnf_status cnf_plan_create(const cnf_desc *desc, cnf_plan **plan)
     if (!p.family) return CNF_ERR_UNSUPPORTED;
 
     p.workspace = 0;
-    if (p.family == FAM_IGEMM) p.workspace = cnf::conv2d_igemm_workspace(d.N, d.C_in, p.Ho, p.Wo);
+    if (p.family == FAM_IGEMM)
+        p.workspace = cnf::conv2d_igemm_workspace(d.N, d.C_in, d.C_out, p.Ho, p.Wo);
     if (p.family == FAM_CONVT) p.workspace = cnf::convt2d_workspace(d.N, d.C_out, p.Ho, p.Wo);
     if (p.family == FAM_CONVT_FUSED) {
         // room for the two-pass fallback too (used if the grid cannot be co-resident)
@@ -262,8 +268,10 @@ cnf_status cnf_forward(const cnf_plan *plan, const float *x, const float *w, con
         break;
     }
     case FAM_IGEMM: {
+        const int tr = d.kind == CNF_CONV_TRANSPOSE;
         cnf::Conv2dIgemmArgs a{x, w, b, gamma, beta, out, static_cast<float *>(workspace), d.N,
-                               d.C_in, H, W, plan->Ho, plan->Wo, norm_groups, d.eps, inv_div};
+                               d.C_in, d.C_out, H, W, plan->Ho, plan->Wo, tr ? d.kernel - 1 : 0, tr,
+                               d.act, norm_groups, d.eps, inv_div};
         e = cnf::launch_conv2d_igemm(a, st);
         break;
     }

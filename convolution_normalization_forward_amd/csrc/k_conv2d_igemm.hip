@@ -1,6 +1,11 @@
-// k_conv2d_igemm.hip -- Conv2d (C_out = 128, k = 3, C_in a multiple of 4) as
-// an implicit GEMM on fp32 MFMA, with bias and per-tile Welford partials in
-// the epilogue, followed by an in-place InstanceNorm / GroupNorm + divide pass.
+// k_conv2d_igemm.hip -- Conv2d (C_out = 128 or 64, k = 3, C_in a multiple of
+// 4, optional zero padding) as an implicit GEMM on fp32 MFMA, with bias,
+// activation and per-tile Welford partials in the epilogue, followed by an
+// in-place InstanceNorm / GroupNorm + divide pass.  A dense (groups = 1)
+// stride-1 ConvTranspose2d is the same GEMM on the input padded by k - 1 with
+// the kernel flipped and its channel axes swapped (page "Kimi-K2.6__l2_p19",
+// second trace: out[i, j] = sum x[i - kh, j - kw] W[ci, co, kh, kw]), so it
+// runs here too: only the weight copy and the padding differ.
 //
 // Page "Kimi-K2.6__l2_p17": Conv2d(64 -> 128, k = 3) -> InstanceNorm2d ->
 // divide by 2 on 128 x 64 x 128 x 128.  The second trace shows the conv is
@@ -13,9 +18,10 @@
 // Mapping:
 //   * GEMM rows = the 128 output channels (A = weights), columns = output
 //     positions (B = im2col of x), K = C_in * 9 ordered (tap, channel).
-//   * A workgroup (8 waves) owns 128 channels x a 4-row x 64-column block of
-//     output positions of one sample; wave (wm, wn) computes channels
-//     64*wm .. +63 on output row wn as 2 x 2 tiles of v_mfma_f32_32x32x2f32.
+//   * A workgroup (8 waves) owns all CO channels x a TR-row x 64-column block
+//     of output positions of one sample (TR = 4 for 128 channels, 8 for 64);
+//     wave (wm, wn) computes channels 64*wm .. +63 on output row wn as 2 x 2
+//     tiles of v_mfma_f32_32x32x2f32.
 //   * K is walked in chunks of CC input channels: the chunk's input halo
 //     (CC x 6 x 66) and its weights (9*CC x 128, from a [ci][tap][co] copy the
 //     first kernel makes) are double-buffered in LDS; the next chunk is
@@ -30,32 +36,45 @@ namespace cnf {
 
 namespace {
 
-constexpr int CO = 128;
 constexpr int CC = 4;                    // input channels per K chunk
 constexpr int KC = 9 * CC;               // K per chunk
-constexpr int TR = 4, TC = 64;           // output tile: rows x cols
+constexpr int TC = 64;                   // output tile columns
 constexpr int PITCH = 68;                // LDS row pitch of the input halo
-constexpr int CS = (TR + 2) * PITCH + 8; // LDS channel stride (== 32 mod 64)
-constexpr int WPITCH = CO + 32;          // LDS row pitch of the weight chunk (== 32 mod 64)
-constexpr int XS_FLOATS = CC * CS;
-constexpr int WS_FLOATS = KC * WPITCH;
-constexpr int BUF_FLOATS = XS_FLOATS + WS_FLOATS;
 constexpr int THREADS = 512;
-constexpr int XIN = CC * (TR + 2) * (TC + 2);          // halo floats per chunk
-constexpr int XPF = (XIN + THREADS - 1) / THREADS;     // per-thread prefetch (scalar)
-constexpr int WPF = (KC * CO / 4 + THREADS - 1) / THREADS;  // per-thread prefetch (float4)
+constexpr int NWAVES = THREADS / 64;
 
-// w[co][ci][kh][kw] -> wt[ci][tap][co]
+// Tile geometry for CO output channels (128 or 64): 64 channels x 64 columns
+// per wave, so TR = 8 waves / (CO / 64) output rows per tile.
+template <int CO>
+struct Geo {
+    static constexpr int WM = CO / 64, TR = NWAVES / WM;
+    static constexpr int CS_BASE = (TR + 2) * PITCH;
+    static constexpr int CS = CS_BASE + ((32 - CS_BASE % 64) + 64) % 64;  // == 32 mod 64
+    static constexpr int WPITCH = CO + 32;                                // == 32 mod 64
+    static constexpr int XS_FLOATS = CC * CS;
+    static constexpr int WS_FLOATS = KC * WPITCH;
+    static constexpr int BUF_FLOATS = XS_FLOATS + WS_FLOATS;
+    static constexpr int XIN = CC * (TR + 2) * (TC + 2);           // halo floats per chunk
+    static constexpr int XPF = (XIN + THREADS - 1) / THREADS;      // per-thread prefetch (scalar)
+    static constexpr int WPF = (KC * CO / 4 + THREADS - 1) / THREADS;  // (float4)
+    static_assert(CS % 64 == 32 && WPITCH % 64 == 32, "bank spread");
+    static_assert(TR * (CO / 64) == NWAVES, "one 64 x 64 block per wave");
+};
+
+// Conv: w[co][ci][kh][kw] -> wt[ci][tap][co].  Transposed conv (weights
+// [ci][co][kh][kw]): the flipped tap, wt[ci][tap][co] = w[ci][co][8 - tap].
 __global__ void conv2d_weight_transpose_kernel(const float *__restrict__ w, float *__restrict__ wt,
-                                               int C_in)
+                                               int C_in, int CO, int transposed)
 {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     const int total = CO * C_in * 9;
     if (i >= total) return;
     const int co = i % CO, rest = i / CO;  // rest = ci * 9 + tap
-    wt[i] = w[(size_t)co * C_in * 9 + rest];
+    const int ci = rest / 9, tap = rest % 9;
+    wt[i] = transposed ? w[((size_t)ci * CO + co) * 9 + (8 - tap)] : w[(size_t)co * C_in * 9 + rest];
 }
 
+template <int CO, int XPF = Geo<CO>::XPF, int WPF = Geo<CO>::WPF>
 __device__ __forceinline__ void igemm_fetch(const float *__restrict__ xn, const float *__restrict__ wt,
                                             int chunk, int H, int W, int tid,
                                             const int (&xoff)[XPF], const bool (&xok)[XPF],
@@ -75,12 +94,13 @@ __device__ __forceinline__ void igemm_fetch(const float *__restrict__ xn, const 
     }
 }
 
+template <int CO, int XPF = Geo<CO>::XPF, int WPF = Geo<CO>::WPF>
 __device__ __forceinline__ void igemm_stash(float *lds, int buf, const int (&xdst)[XPF],
                                             const int (&wdst)[WPF], const float (&xpf)[XPF],
                                             const v4f (&wpf)[WPF])
 {
-    float *xs = lds + buf * BUF_FLOATS;
-    float *ws = xs + XS_FLOATS;
+    float *xs = lds + buf * Geo<CO>::BUF_FLOATS;
+    float *ws = xs + Geo<CO>::XS_FLOATS;
 #pragma unroll
     for (int u = 0; u < XPF; ++u)
         if (xdst[u] >= 0) xs[xdst[u]] = xpf[u];
@@ -89,18 +109,23 @@ __device__ __forceinline__ void igemm_stash(float *lds, int buf, const int (&xds
         if (wdst[u] >= 0) *reinterpret_cast<v4f *>(ws + wdst[u]) = wpf[u];
 }
 
+template <int CO, int ACT>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4, 4)))
 void conv2d_igemm_kernel(const float *__restrict__ x, const float *__restrict__ wt,
                          const float *__restrict__ bias, float *__restrict__ y,
                          float *__restrict__ partials, int C_in, int H, int W, int Ho, int Wo,
-                         int tiles_w, int tiles_per_sample)
+                         int pad, int tiles_w, int tiles_per_sample)
 {
+    using G = Geo<CO>;
+    constexpr int TR = G::TR, CS = G::CS, WPITCH = G::WPITCH, XPF = G::XPF, WPF = G::WPF;
+    constexpr int XIN = G::XIN, BUF_FLOATS = G::BUF_FLOATS, XS_FLOATS = G::XS_FLOATS;
     __shared__ float lds[2 * BUF_FLOATS];
     float (*red)[CO][3] = reinterpret_cast<float (*)[CO][3]>(lds);  // after the K loop
+    static_assert(TR * CO * 3 <= 2 * BUF_FLOATS, "reduction fits the staging buffers");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 2, wn = wave & 3;
+    const int wm = wave / TR, wn = wave % TR;
     const int h = lane >> 5, i32 = lane & 31;
     // XCD-aware tile order: each XCD takes a contiguous run of (n, row tile,
     // column tile), so vertically adjacent tiles share their halo rows in L2.
@@ -122,8 +147,9 @@ void conv2d_igemm_kernel(const float *__restrict__ x, const float *__restrict__ 
         const int ec = e < XIN ? e : XIN - 1;
         const int cc = ec % (TC + 2), rest = ec / (TC + 2);
         const int rr = rest % (TR + 2), c = rest / (TR + 2);
-        const int gr = row0 + rr, gc = col0 + cc;
-        xok[u] = e < XIN && gr < H && gc < W;
+        // input row / column of the (zero-padded by pad) halo element
+        const int gr = row0 + rr - pad, gc = col0 + cc - pad;
+        xok[u] = e < XIN && gr >= 0 && gr < H && gc >= 0 && gc < W;
         xoff[u] = xok[u] ? (c * H + gr) * W + gc : 0;
         xdst[u] = e < XIN ? c * CS + rr * PITCH + cc : -1;
     }
@@ -146,12 +172,12 @@ void conv2d_igemm_kernel(const float *__restrict__ x, const float *__restrict__ 
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
     const int nchunks = C_in / CC;
-    igemm_fetch(xn, wt, 0, H, W, tid, xoff, xok, xpf, wpf);
-    igemm_stash(lds, 0, xdst, wdst, xpf, wpf);
+    igemm_fetch<CO>(xn, wt, 0, H, W, tid, xoff, xok, xpf, wpf);
+    igemm_stash<CO>(lds, 0, xdst, wdst, xpf, wpf);
     __syncthreads();
     for (int ch = 0; ch < nchunks; ++ch) {
         const int buf = ch & 1;
-        if (ch + 1 < nchunks) igemm_fetch(xn, wt, ch + 1, H, W, tid, xoff, xok, xpf, wpf);
+        if (ch + 1 < nchunks) igemm_fetch<CO>(xn, wt, ch + 1, H, W, tid, xoff, xok, xpf, wpf);
         const float *xs = lds + buf * BUF_FLOATS;
         const float *ws = xs + XS_FLOATS;
         const float *wa = ws + h * WPITCH + 64 * wm + i32;
@@ -173,7 +199,7 @@ void conv2d_igemm_kernel(const float *__restrict__ x, const float *__restrict__ 
             }
         }
         if (ch + 1 < nchunks)  // buf^1 was last read in iteration ch-1
-            igemm_stash(lds, buf ^ 1, xdst, wdst, xpf, wpf);
+            igemm_stash<CO>(lds, buf ^ 1, xdst, wdst, xpf, wpf);
         __syncthreads();
     }
 
@@ -192,7 +218,7 @@ void conv2d_igemm_kernel(const float *__restrict__ x, const float *__restrict__ 
 #pragma unroll
             for (int bj = 0; bj < 2; ++bj) {
                 const int col = col0 + 32 * bj + i32;
-                const float v = acc[bi][bj][r] + bc;
+                const float v = activate<ACT>(acc[bi][bj][r] + bc);
                 if (rvalid && col < Wo) {
                     yn[((size_t)co * Ho + orow) * Wo + col] = v;
                     s1 += v;
@@ -218,7 +244,7 @@ void conv2d_igemm_kernel(const float *__restrict__ x, const float *__restrict__ 
     if (tid < CO) {
         float cnt = 0.f, mean = 0.f, m2 = 0.f;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) chan_merge(cnt, mean, m2, red[k][tid][0], red[k][tid][1], red[k][tid][2]);
+        for (int k = 0; k < TR; ++k) chan_merge(cnt, mean, m2, red[k][tid][0], red[k][tid][1], red[k][tid][2]);
         const size_t tile = (size_t)th * tiles_w + tw;
         float *pp = partials + (((size_t)n * tiles_per_sample + tile) * CO + tid) * 3;
         pp[0] = cnt; pp[1] = mean; pp[2] = m2;
@@ -286,34 +312,53 @@ void conv2d_norm_pass_kernel(float *__restrict__ y, const float *__restrict__ pa
 
 bool conv2d_igemm_supported(int C_in, int C_out, int kernel, int groups, int H, int W, int act)
 {
-    return C_out == CO && kernel == 3 && groups == 1 && C_in % CC == 0 && C_in >= CC &&
-           H >= 3 && W >= 3 && act == ACT_NONE;
+    return (C_out == 128 || C_out == 64) && kernel == 3 && groups == 1 && C_in % CC == 0 &&
+           C_in >= CC && H >= 1 && W >= 1 &&
+           (act == ACT_NONE || act == ACT_HARDSWISH || act == ACT_GELU_ERF || act == ACT_GELU_TANH);
 }
 
-static size_t tiles_of(int Ho, int Wo)
+static int tile_rows(int C_out) { return C_out == 128 ? Geo<128>::TR : Geo<64>::TR; }
+
+static size_t tiles_of(int C_out, int Ho, int Wo)
 {
-    return (size_t)((Wo + TC - 1) / TC) * ((Ho + TR - 1) / TR);
+    const int tr = tile_rows(C_out);
+    return (size_t)((Wo + TC - 1) / TC) * ((Ho + tr - 1) / tr);
 }
 
-size_t conv2d_igemm_workspace(int N, int C_in, int Ho, int Wo)
+size_t conv2d_igemm_workspace(int N, int C_in, int C_out, int Ho, int Wo)
 {
     // [N][tiles][C_out][3] Welford partials, then the [ci][tap][co] weight copy
-    return (size_t)N * tiles_of(Ho, Wo) * CO * 3 * sizeof(float) +
-           (size_t)C_in * 9 * CO * sizeof(float);
+    return (size_t)N * tiles_of(C_out, Ho, Wo) * C_out * 3 * sizeof(float) +
+           (size_t)C_in * 9 * C_out * sizeof(float);
+}
+
+template <int CO, int ACT>
+static void launch_gemm(const Conv2dIgemmArgs &a, const float *wt, int tiles_w, int tiles_h, int tps,
+                        hipStream_t st)
+{
+    hipLaunchKernelGGL((conv2d_igemm_kernel<CO, ACT>), dim3(tiles_w, tiles_h, a.N), dim3(THREADS), 0, st,
+                       a.x, wt, a.b, a.out, a.partials, a.C_in, a.H, a.W, a.Ho, a.Wo, a.pad, tiles_w,
+                       tps);
 }
 
 hipError_t launch_conv2d_igemm(const Conv2dIgemmArgs &a, hipStream_t st)
 {
-    const int tiles_w = (a.Wo + TC - 1) / TC, tiles_h = (a.Ho + TR - 1) / TR;
+    const int CO = a.C_out, tr = tile_rows(CO);
+    const int tiles_w = (a.Wo + TC - 1) / TC, tiles_h = (a.Ho + tr - 1) / tr;
     const int tps = tiles_w * tiles_h;
     float *wt = a.partials + (size_t)a.N * tps * CO * 3;
     {
         const int total = CO * a.C_in * 9;
         hipLaunchKernelGGL(conv2d_weight_transpose_kernel, dim3((total + 255) / 256), dim3(256), 0,
-                           st, a.w, wt, a.C_in);
+                           st, a.w, wt, a.C_in, CO, a.transposed);
     }
-    hipLaunchKernelGGL(conv2d_igemm_kernel, dim3(tiles_w, tiles_h, a.N), dim3(THREADS), 0, st, a.x,
-                       wt, a.b, a.out, a.partials, a.C_in, a.H, a.W, a.Ho, a.Wo, tiles_w, tps);
+#define CNF_CASE(C, A) \
+    if (CO == C && a.act == A) launch_gemm<C, A>(a, wt, tiles_w, tiles_h, tps, st); else
+    CNF_CASE(128, ACT_NONE) CNF_CASE(128, ACT_HARDSWISH) CNF_CASE(128, ACT_GELU_ERF)
+    CNF_CASE(128, ACT_GELU_TANH) CNF_CASE(64, ACT_NONE) CNF_CASE(64, ACT_HARDSWISH)
+    CNF_CASE(64, ACT_GELU_ERF) CNF_CASE(64, ACT_GELU_TANH)
+    return hipErrorInvalidValue;
+#undef CNF_CASE
     if (a.norm_groups > 0 || a.inv_div != 1.0f) {
         hipLaunchKernelGGL(conv2d_norm_pass_kernel, dim3(a.N * CO), dim3(256), 0, st, a.out,
                            a.partials, a.gamma, a.beta, CO, a.Ho * a.Wo, tps, a.norm_groups,

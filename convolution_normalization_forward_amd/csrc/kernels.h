@@ -49,19 +49,23 @@ bool small_conv_norm_supported(int C_in, int C_out, int kernel, int ndim, int D,
                                int act);
 hipError_t launch_small_conv_norm(const SmallConvNormArgs &a, hipStream_t st);
 
-// ---- Conv2d implicit GEMM on fp32 MFMA (C_out 128, k 3) writing y and
-//      per-tile Welford partials, then in-place InstanceNorm/GroupNorm + divide
+// ---- Conv2d implicit GEMM on fp32 MFMA (C_out 128 or 64, k 3) writing y and
+//      per-tile Welford partials, then in-place InstanceNorm/GroupNorm + divide;
+//      also a dense stride-1 ConvTranspose2d (input padded by 2, kernel flipped)
 struct Conv2dIgemmArgs {
     const float *x, *w, *b, *gamma, *beta;
     float *out;
-    float *partials;     // workspace: [N][tiles][C_out][3]
-    int N, C_in, H, W;
+    float *partials;     // workspace: [N][tiles][C_out][3], then the weight copy
+    int N, C_in, C_out, H, W;
     int Ho, Wo;
+    int pad;             // zero padding of the input on every side
+    int transposed;      // weights are [C_in][C_out][k][k] (transposed conv)
+    int act;
     int norm_groups;     // 0: no norm; C_out: instance norm
     float eps, inv_div;
 };
 bool conv2d_igemm_supported(int C_in, int C_out, int kernel, int groups, int H, int W, int act);
-size_t conv2d_igemm_workspace(int N, int C_in, int Ho, int Wo);
+size_t conv2d_igemm_workspace(int N, int C_in, int C_out, int Ho, int Wo);
 hipError_t launch_conv2d_igemm(const Conv2dIgemmArgs &a, hipStream_t st);
 
 // ---- grouped ConvTranspose2d (8 in / 8 out per group, k 3, stride 1) +

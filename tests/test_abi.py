@@ -44,6 +44,7 @@ def test_every_workload_plans_with_expected_shape(name):
         "conv3d_hswish_gn_mean_n1024": (1024, 16),
         "conv2d_in_div_n128": (128, 128, 126, 126),
         "convt2d_gelu_gn_n128": (128, 64, 258, 258),
+        "convt2d_dense_gelu_gn_n128": (128, 64, 258, 258),
     }[name]
     assert plan.out_shape == exp
     assert "family=" in plan.describe()

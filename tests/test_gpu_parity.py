@@ -98,6 +98,15 @@ SMALL_CASES = [
     ("convt2d_gelu_gn_n128", dict(N=2, in_dims=(1, 30, 256), num_groups=2)),
     ("convt2d_gelu_gn_n128", dict(N=2, in_dims=(1, 13, 20), norm="instance", affine=1)),
     ("conv2d_in_div_n128", dict(N=2, C_in=8, in_dims=(1, 21, 37), affine=1)),
+    # implicit GEMM with 64 output channels (8-row tiles) and with an activation
+    ("conv2d_in_div_n128", dict(N=2, C_in=8, C_out=64, in_dims=(1, 19, 70), norm="group",
+                                num_groups=8, affine=1)),
+    ("conv2d_in_div_n128", dict(N=1, C_in=12, in_dims=(1, 13, 40), act="hardswish")),
+    # dense transposed conv (groups 1) on the implicit GEMM: padded input, flipped kernel
+    ("convt2d_dense_gelu_gn_n128", dict(N=2, C_in=8, C_out=64, in_dims=(1, 9, 20))),
+    ("convt2d_dense_gelu_gn_n128", dict(N=2, C_in=16, C_out=128, in_dims=(1, 14, 61),
+                                        norm="instance", act="gelu_tanh")),
+    ("convt2d_dense_gelu_gn_n128", dict(N=1, C_in=64, in_dims=(1, 33, 66))),
 ]
 
 
@@ -125,6 +134,7 @@ FULL_SUBSET = {
     "conv3d_hswish_gn_mean_n1024": 8,
     "conv2d_in_div_n128": 2,
     "convt2d_gelu_gn_n128": 2,
+    "convt2d_dense_gelu_gn_n128": 2,
 }
 
 

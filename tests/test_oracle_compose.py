@@ -81,6 +81,7 @@ SMALL = {
     "conv2d_in_div_n128": dict(N=1, C_in=8, C_out=16, in_dims=(1, 12, 11)),
     "convt2d_gelu_gn_n128": dict(N=2, C_in=16, C_out=16, in_dims=(1, 9, 10), groups=8,
                                  num_groups=8),
+    "convt2d_dense_gelu_gn_n128": dict(N=2, C_in=6, C_out=8, in_dims=(1, 7, 9), num_groups=4),
 }
 
 

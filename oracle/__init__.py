@@ -53,7 +53,11 @@ def _load():
     lib.orc_group_norm.argtypes = [P, I, I, L, I, D, P, P]
     lib.orc_divide.argtypes = [P, L, D]
     lib.orc_mean_spatial.argtypes = [P, I, I, L, P]
-    lib.orc_maxpool3d.argtypes = [P, P, I, I, I, I, I, I, P, P]
+    lib.orc_conv_general.argtypes = [I] * 10 + [P] * 7
+    lib.orc_conv_general.restype = I
+    lib.orc_conv_transpose_general.argtypes = [I] * 10 + [P] * 8
+    lib.orc_conv_transpose_general.restype = I
+    lib.orc_maxpool3d.argtypes = [P, P, I, I, I, I, I, I, I, I, P, P]
     lib.orc_maxpool3d.restype = I
     lib.orc_gn_mean_closed_form.argtypes = [P, I, I, L, I, D, P, P, P]
     lib.orc_num_threads.restype = I
@@ -76,11 +80,35 @@ def num_threads() -> int:
 
 
 # ---------------------------------------------------------------- primitives
-def conv(x, w, b=None, groups=1):
-    """Stride-1, unpadded, grouped cross-correlation (2-D or 3-D).
+def _axes3(v, two_d, neutral):
+    """Per-axis (D, H, W) parameters; a 2-D problem has the neutral value on D."""
+    v = (v,) * (2 if two_d else 3) if isinstance(v, int) else tuple(v)
+    if two_d:
+        v = (neutral,) + v
+    return (ctypes.c_int * 3)(*v)
+
+
+def conv_extent(L, k, stride=1, padding=0, dilation=1):
+    """floor((L + 2p - d(k-1) - 1) / s) + 1 ([p6] integer output-size passage)."""
+    num = L + 2 * padding - dilation * (k - 1) - 1
+    return num // stride + 1 if num >= 0 else 0
+
+
+def conv_transpose_extent(L, k, stride=1, padding=0, dilation=1, output_padding=0):
+    """(L - 1)s - 2p + d(k - 1) + op + 1 ([p19] first trace, output-size formula)."""
+    return (L - 1) * stride - 2 * padding + dilation * (k - 1) + output_padding + 1
+
+
+def conv(x, w, b=None, groups=1, stride=1, padding=0, dilation=1):
+    """Grouped cross-correlation (2-D or 3-D).
 
     x: (N, Ci, [D,] H, W); w: (Co, Ci/groups, [kd,] kh, kw).  Returns float64.
+    Stride 1, no padding, dilation 1 runs orc_conv; anything else runs
+    orc_conv_general (stride, zero padding, dilation; an int applies to every
+    spatial axis, a tuple gives one value per axis).
     """
+    if (stride, padding, dilation) != (1, 0, 1):
+        return _conv_general(x, w, b, groups, stride, padding, dilation)
     x, w, b = _f32(x), _f32(w), _f32(b)
     two_d = x.ndim == 4
     if two_d:
@@ -96,6 +124,52 @@ def conv(x, w, b=None, groups=1):
                           _ptr(b), _ptr(y))
     if rc != 0:
         raise ValueError("orc_conv: bad shape")
+    return y[:, :, 0] if two_d else y
+
+
+def _conv_general(x, w, b, groups, stride, padding, dilation):
+    x, w, b = _f32(x), _f32(w), _f32(b)
+    two_d = x.ndim == 4
+    x5 = x[:, :, None] if two_d else x
+    w5 = w[:, :, None] if two_d else w
+    N, Ci, D, H, W = x5.shape
+    Co, _, kd, kh, kw = w5.shape
+    s, p, dl = _axes3(stride, two_d, 1), _axes3(padding, two_d, 0), _axes3(dilation, two_d, 1)
+    dims = [conv_extent(L, k, s[i], p[i], dl[i]) for i, (L, k) in enumerate(((D, kd), (H, kh), (W, kw)))]
+    y = np.empty((N, Co, *dims), dtype=np.float64)
+    rc = _load().orc_conv_general(N, Ci, D, H, W, Co, groups, kd, kh, kw, s, p, dl,
+                                  _ptr(np.ascontiguousarray(x5)), _ptr(np.ascontiguousarray(w5)),
+                                  _ptr(b), _ptr(y))
+    if rc != 0:
+        raise ValueError("orc_conv_general: bad shape")
+    return y[:, :, 0] if two_d else y
+
+
+def conv_transpose(x, w, b=None, groups=1, stride=1, padding=0, dilation=1, output_padding=0):
+    """Grouped transposed conv, 2-D or 3-D, w: (Ci, Co/groups, [kd,] kh, kw).
+
+    2-D with stride 1, no padding, dilation 1 runs orc_conv_transpose2d;
+    anything else runs orc_conv_transpose_general.
+    """
+    x, w, b = _f32(x), _f32(w), _f32(b)
+    two_d = x.ndim == 4
+    if two_d and (stride, padding, dilation, output_padding) == (1, 0, 1, 0):
+        return conv_transpose2d(x, w, b, groups)
+    x5 = x[:, :, None] if two_d else x
+    w5 = w[:, :, None] if two_d else w
+    N, Ci, D, H, W = x5.shape
+    _, cog, kd, kh, kw = w5.shape
+    Co = cog * groups
+    s, p = _axes3(stride, two_d, 1), _axes3(padding, two_d, 0)
+    dl, op = _axes3(dilation, two_d, 1), _axes3(output_padding, two_d, 0)
+    dims = [conv_transpose_extent(L, k, s[i], p[i], dl[i], op[i])
+            for i, (L, k) in enumerate(((D, kd), (H, kh), (W, kw)))]
+    y = np.empty((N, Co, *dims), dtype=np.float64)
+    rc = _load().orc_conv_transpose_general(N, Ci, D, H, W, Co, groups, kd, kh, kw, s, p, dl, op,
+                                            _ptr(np.ascontiguousarray(x5)),
+                                            _ptr(np.ascontiguousarray(w5)), _ptr(b), _ptr(y))
+    if rc != 0:
+        raise ValueError("orc_conv_transpose_general: bad shape")
     return y[:, :, 0] if two_d else y
 
 
@@ -166,15 +240,18 @@ def mean_spatial(y):
 
 
 def maxpool3d(y, k, idx=None):
-    """One floor-mode max pool with kernel = stride = k; returns (out, argmax)."""
+    """One floor-mode max pool with kernel = stride = k on (N, C, D, H, W);
+    k is an int (every axis) or a (kd, kh, kw) tuple.  Returns (out, argmax)."""
     y = np.ascontiguousarray(y, dtype=np.float64)
     N, C, D, H, W = y.shape
-    shp = (N, C, D // k, H // k, W // k)
+    kd, kh, kw = (k, k, k) if isinstance(k, int) else tuple(k)
+    shp = (N, C, D // kd, H // kh, W // kw)
     out = np.empty(shp, dtype=np.float64)
     oidx = np.empty(shp, dtype=np.int64)
     if idx is not None:
         idx = np.ascontiguousarray(idx, dtype=np.int64)
-    rc = _load().orc_maxpool3d(_ptr(y), _ptr(idx), N, C, D, H, W, k, _ptr(out), _ptr(oidx))
+    rc = _load().orc_maxpool3d(_ptr(y), _ptr(idx), N, C, D, H, W, kd, kh, kw,
+                               _ptr(out), _ptr(oidx))
     if rc != 0:
         raise ValueError("orc_maxpool3d: bad kernel")
     return out, oidx
@@ -193,10 +270,12 @@ def gn_mean_closed_form(h, num_groups, eps=1e-5, gamma=None, beta=None):
 # ---------------------------------------------------------------- composition
 def pre_norm(wl: dict, x, w, b):
     """Conv (or transposed conv) followed by the activation, in float64."""
+    geo = dict(stride=wl.get("stride", 1), padding=wl.get("padding", 0),
+               dilation=wl.get("dilation", 1))
     if wl["kind"] == "conv_transpose":
-        y = conv_transpose2d(x, w, b, wl["groups"])
+        y = conv_transpose(x, w, b, wl["groups"], output_padding=wl.get("output_padding", 0), **geo)
     else:
-        y = conv(x, w, b, wl["groups"])
+        y = conv(x, w, b, wl["groups"], **geo)
     act = wl["act"]
     if act == "hardswish":
         y = hardswish(y)
@@ -236,10 +315,13 @@ def forward(wl: dict, x, w, b=None, gamma=None, beta=None, closed_form_mean=Fals
     if red == "mean":
         return mean_spatial(y), None
     if red == "maxpool":
-        if y.ndim == 4:
+        p = wl["pool_kernel"]
+        k = (p, p, p)
+        if y.ndim == 4:  # 2-D: pool H and W only, keep D = 1
             y = y[:, :, None]
+            k = (1, p, p)
         idx = None
         for _ in range(wl["pool_repeats"]):
-            y, idx = maxpool3d(y, wl["pool_kernel"], idx)
+            y, idx = maxpool3d(y, k, idx)
         return y, idx
     raise ValueError(red)

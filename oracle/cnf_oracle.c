@@ -124,6 +124,138 @@ int orc_conv_transpose2d(int N, int Ci, int H, int W, int Co, int G,
     return 0;
 }
 
+/* --------------------------------------------------------------------------
+ * Convolution with stride s, zero padding p and dilation d along each axis
+ * (s, p, dl are 3-entry arrays for D, H, W), groups G:
+ *   y[n,co,o] = b[co] + sum_{c<Ci/G} sum_{a} x[n, g*Ci/G + c, o*s - p + a*dl]
+ *                                           * wt[co, c, a]
+ * per axis, with x taken as 0 outside [0, L).  Output extent per axis is
+ * floor((L + 2p - dl*(k-1) - 1) / s) + 1.
+ * [p6] the trace's integer output-size passage, which states this extent for
+ *      Conv3d and MaxPool3d; [p19] the fix sequence's adjoint derivation,
+ *      which writes the strided, padded, dilated conv as this gather.
+ * A 2-D conv is the D = 1, kd = 1, s[0] = dl[0] = 1, p[0] = 0 case.
+ * x: [N][Ci][D][H][W], wt: [Co][Ci/G][kd][kh][kw], b: [Co] or NULL,
+ * y: [N][Co][Do][Ho][Wo].  Returns 0, or -1 on a bad shape.
+ * ------------------------------------------------------------------------ */
+static int conv_extent(int L, int k, int s, int p, int dl)
+{
+    const int num = L + 2 * p - dl * (k - 1) - 1;
+    if (num < 0) return 0;
+    return num / s + 1;
+}
+
+int orc_conv_general(int N, int Ci, int D, int H, int W, int Co, int G,
+                     int kd, int kh, int kw, const int *s, const int *p, const int *dl,
+                     const float *x, const float *wt, const float *b, double *y)
+{
+    if (N < 0 || Ci < 1 || Co < 1 || G < 1 || Ci % G || Co % G) return -1;
+    if (kd < 1 || kh < 1 || kw < 1) return -1;
+    for (int i = 0; i < 3; ++i)
+        if (s[i] < 1 || p[i] < 0 || dl[i] < 1) return -1;
+    const int Do = conv_extent(D, kd, s[0], p[0], dl[0]);
+    const int Ho = conv_extent(H, kh, s[1], p[1], dl[1]);
+    const int Wo = conv_extent(W, kw, s[2], p[2], dl[2]);
+    if (Do < 1 || Ho < 1 || Wo < 1) return -1;
+    const int cig = Ci / G, cog = Co / G;
+    const int64_t in_plane = (int64_t)D * H * W;
+    const int64_t out_plane = (int64_t)Do * Ho * Wo;
+
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int n = 0; n < N; ++n) {
+        for (int co = 0; co < Co; ++co) {
+            const int g = co / cog;
+            double *yp = y + ((int64_t)n * Co + co) * out_plane;
+            for (int od = 0; od < Do; ++od)
+            for (int oh = 0; oh < Ho; ++oh)
+            for (int ow = 0; ow < Wo; ++ow) {
+                double acc = b ? (double)b[co] : 0.0;
+                for (int c = 0; c < cig; ++c) {
+                    const int ci = g * cig + c;
+                    const float *xp = x + ((int64_t)n * Ci + ci) * in_plane;
+                    const float *wp = wt + ((int64_t)co * cig + c) * kd * kh * kw;
+                    for (int a = 0; a < kd; ++a)
+                    for (int bb = 0; bb < kh; ++bb)
+                    for (int e = 0; e < kw; ++e) {
+                        const int id = od * s[0] - p[0] + a * dl[0];
+                        const int ih = oh * s[1] - p[1] + bb * dl[1];
+                        const int iw = ow * s[2] - p[2] + e * dl[2];
+                        if (id < 0 || id >= D || ih < 0 || ih >= H || iw < 0 || iw >= W)
+                            continue;  /* zero padding */
+                        acc += (double)xp[((int64_t)id * H + ih) * W + iw] *
+                               (double)wp[(a * kh + bb) * kw + e];
+                    }
+                }
+                yp[((int64_t)od * Ho + oh) * Wo + ow] = acc;
+            }
+        }
+    }
+    return 0;
+}
+
+/* --------------------------------------------------------------------------
+ * Transposed convolution with stride s, padding p, dilation dl and
+ * output_padding op along each axis, groups G, written as the adjoint of
+ * orc_conv_general: input position i, tap a sends x[i] * wt[ci, co, a] to the
+ * output position o = i*s - p + a*dl, and contributions falling outside
+ * [0, Lo) are dropped.  Output extent per axis is
+ *   Lo = (L - 1)*s - 2p + dl*(k - 1) + op + 1.
+ * [p19] first trace, the output-size formula with all five parameters; the
+ *       fix sequence's statement that the transposed conv is the adjoint of
+ *       the conv, and the conv gather it takes the adjoint of.  Weight
+ *       layout as the page states: wt: [Ci][Co/G][kd][kh][kw].
+ * x: [N][Ci][D][H][W], b: [Co] or NULL, y: [N][Co][Do][Ho][Wo].
+ * ------------------------------------------------------------------------ */
+int orc_conv_transpose_general(int N, int Ci, int D, int H, int W, int Co, int G,
+                               int kd, int kh, int kw, const int *s, const int *p,
+                               const int *dl, const int *op,
+                               const float *x, const float *wt, const float *b, double *y)
+{
+    if (N < 0 || Ci < 1 || Co < 1 || G < 1 || Ci % G || Co % G) return -1;
+    if (kd < 1 || kh < 1 || kw < 1 || D < 1 || H < 1 || W < 1) return -1;
+    for (int i = 0; i < 3; ++i)
+        if (s[i] < 1 || p[i] < 0 || dl[i] < 1 || op[i] < 0) return -1;
+    const int Do = (D - 1) * s[0] - 2 * p[0] + dl[0] * (kd - 1) + op[0] + 1;
+    const int Ho = (H - 1) * s[1] - 2 * p[1] + dl[1] * (kh - 1) + op[1] + 1;
+    const int Wo = (W - 1) * s[2] - 2 * p[2] + dl[2] * (kw - 1) + op[2] + 1;
+    if (Do < 1 || Ho < 1 || Wo < 1) return -1;
+    const int cig = Ci / G, cog = Co / G;
+    const int64_t in_plane = (int64_t)D * H * W;
+    const int64_t out_plane = (int64_t)Do * Ho * Wo;
+
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int n = 0; n < N; ++n) {
+        for (int co = 0; co < Co; ++co) {
+            const int g = co / cog, col = co % cog;
+            double *yp = y + ((int64_t)n * Co + co) * out_plane;
+            const double bias = b ? (double)b[co] : 0.0;
+            for (int64_t q = 0; q < out_plane; ++q) yp[q] = bias;
+            for (int c = 0; c < cig; ++c) {
+                const int ci = g * cig + c;
+                const float *xp = x + ((int64_t)n * Ci + ci) * in_plane;
+                const float *wp = wt + ((int64_t)ci * cog + col) * kd * kh * kw;
+                for (int i0 = 0; i0 < D; ++i0)
+                for (int i1 = 0; i1 < H; ++i1)
+                for (int i2 = 0; i2 < W; ++i2) {
+                    const double v = (double)xp[((int64_t)i0 * H + i1) * W + i2];
+                    for (int a = 0; a < kd; ++a)
+                    for (int bb = 0; bb < kh; ++bb)
+                    for (int e = 0; e < kw; ++e) {
+                        const int od = i0 * s[0] - p[0] + a * dl[0];
+                        const int oh = i1 * s[1] - p[1] + bb * dl[1];
+                        const int ow = i2 * s[2] - p[2] + e * dl[2];
+                        if (od < 0 || od >= Do || oh < 0 || oh >= Ho || ow < 0 || ow >= Wo)
+                            continue;
+                        yp[((int64_t)od * Ho + oh) * Wo + ow] +=
+                            v * (double)wp[(a * kh + bb) * kw + e];
+                    }
+                }
+            }
+        }
+    }
+    return 0;
+}
+
 /* HardSwish h(x) = x * min(max(x + 3, 0), 6) / 6.
  * [p27] first trace, its statement of the activation and its piecewise
  *       reading (0 below -3, x above 3). */
@@ -231,22 +363,24 @@ void orc_mean_spatial(const double *y, int N, int C, int64_t S, double *out)
     }
 }
 
-/* One max-pool pass, kernel = stride = k along D, H, W, no padding, floor
- * mode: out extent floor(L / k).  Each window is scanned in row-major
- * (d, h, w) order and a later value replaces the running maximum only when
- * strictly larger, so among equal values the first one scanned wins.
+/* One max-pool pass, kernel = stride = (kd, kh, kw), no padding, floor
+ * mode: out extent floor(L / k) per axis.  Each window is scanned in
+ * row-major (d, h, w) order and a later value replaces the running maximum
+ * only when strictly larger, so among equal values the first one scanned wins.
  * The argmax of every output is carried as a flat index into the grid the
  * first pass saw: in_idx NULL means "this is the first pass" and the index
  * of an input voxel is d*H*W + h*W + w; otherwise the index is copied from
  * in_idx.  [p6] the problem statement (MaxPool3d(kernel_size=2) twice) and
- * the trace's floor-mode size chain 14x30x30 -> 7x15x15 -> 3x7x7.
- * in: [N][C][D][H][W]; out, out_idx: [N][C][D/k][H/k][W/k]. */
+ * the trace's floor-mode size chain 14x30x30 -> 7x15x15 -> 3x7x7, and its
+ * output-size formula with padding 0, dilation 1, stride = kernel.  A 2-D
+ * pool is the D = 1, kd = 1 case (it pools H and W only).
+ * in: [N][C][D][H][W]; out, out_idx: [N][C][D/kd][H/kh][W/kw]. */
 int orc_maxpool3d(const double *in, const int64_t *in_idx,
-                  int N, int C, int D, int H, int W, int k,
+                  int N, int C, int D, int H, int W, int kd, int kh, int kw,
                   double *out, int64_t *out_idx)
 {
-    if (k < 1) return -1;
-    const int Dp = D / k, Hp = H / k, Wp = W / k;
+    if (kd < 1 || kh < 1 || kw < 1) return -1;
+    const int Dp = D / kd, Hp = H / kh, Wp = W / kw;
     const int64_t in_plane = (int64_t)D * H * W, out_plane = (int64_t)Dp * Hp * Wp;
     for (int64_t nc = 0; nc < (int64_t)N * C; ++nc) {
         const double *ip = in + nc * in_plane;
@@ -256,10 +390,10 @@ int orc_maxpool3d(const double *in, const int64_t *in_idx,
         for (int ow = 0; ow < Wp; ++ow) {
             double best = 0.0;
             int64_t best_i = -1;
-            for (int a = 0; a < k; ++a)
-            for (int bb = 0; bb < k; ++bb)
-            for (int e = 0; e < k; ++e) {
-                const int64_t off = ((int64_t)(od * k + a) * H + (oh * k + bb)) * W + (ow * k + e);
+            for (int a = 0; a < kd; ++a)
+            for (int bb = 0; bb < kh; ++bb)
+            for (int e = 0; e < kw; ++e) {
+                const int64_t off = ((int64_t)(od * kd + a) * H + (oh * kh + bb)) * W + (ow * kw + e);
                 const double v = ip[off];
                 if (best_i < 0 || v > best) {
                     best = v;

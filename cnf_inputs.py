@@ -41,7 +41,8 @@ _TID_X, _TID_W, _TID_B, _TID_GAMMA, _TID_BETA = 1, 2, 3, 4, 5
 
 _BASE = dict(ndim=2, kind="conv", groups=1, has_bias=1, act="none", norm="none",
              num_groups=1, eps=1e-5, affine=0, divide_by=1.0, reduce="none",
-             pool_kernel=0, pool_repeats=0, want_argmax=0)
+             pool_kernel=0, pool_repeats=0, want_argmax=0, stride=1, padding=0, dilation=1,
+             output_padding=0)
 
 
 def _wl(**kw):

@@ -20,7 +20,7 @@ import torch  # noqa: F401  (loads the HIP runtime first; see module docstring)
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libcnf.so")
 
-CNF_ABI_VERSION = 1
+CNF_ABI_VERSION = 2
 
 # cnf_status
 CNF_OK = 0
@@ -64,6 +64,10 @@ class cnf_desc(ctypes.Structure):
         ("pool_kernel", ctypes.c_int32),
         ("pool_repeats", ctypes.c_int32),
         ("want_argmax", ctypes.c_int32),
+        ("stride", ctypes.c_int32),
+        ("padding", ctypes.c_int32),
+        ("dilation", ctypes.c_int32),
+        ("output_padding", ctypes.c_int32),
     ]
 
 
@@ -202,6 +206,8 @@ def make_desc(wl: dict, N: int | None = None) -> cnf_desc:
     d.reduce = REDUCE[wl["reduce"]]
     d.pool_kernel, d.pool_repeats = wl["pool_kernel"], wl["pool_repeats"]
     d.want_argmax = wl["want_argmax"]
+    d.stride, d.padding = wl.get("stride", 1), wl.get("padding", 0)
+    d.dilation, d.output_padding = wl.get("dilation", 1), wl.get("output_padding", 0)
     return d
 
 

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 
@@ -18,7 +19,8 @@ enum Family : int {
     FAM_SMALL = 3,         // small conv C_out 16, one workgroup per sample
     FAM_IGEMM = 4,         // Conv2d C_out 128/64 k3 implicit GEMM (also dense stride-1 ConvTranspose2d) + norm pass
     FAM_CONVT = 5,         // grouped ConvTranspose2d 8x8 per group + act + GroupNorm pass
-    FAM_CONVT_FUSED = 6    // same, single write: cooperative kernel, cross-workgroup merge
+    FAM_CONVT_FUSED = 6,   // same, single write: cooperative kernel, cross-workgroup merge
+    FAM_GENERIC = 7        // any validated descriptor: gathered implicit GEMM + passes
 };
 
 const char *family_name(int f)
@@ -30,6 +32,7 @@ const char *family_name(int f)
     case FAM_IGEMM: return "conv2d_igemm(mfma32x32x2)+norm_pass";
     case FAM_CONVT: return "convt2d_grouped8(mfma16x16x4,column-pair)+groupnorm_pass";
     case FAM_CONVT_FUSED: return "convt2d_grouped8_gn_fused(cooperative,single-write)";
+    case FAM_GENERIC: return "generic(gathered-igemm mfma16x16x4 + softmax/finalize/apply/pool passes)";
     default: return "none";
     }
 }
@@ -45,6 +48,39 @@ struct cnf_plan {
     int32_t rank;
     size_t workspace;
 };
+
+namespace {
+
+// The general family's arguments for a plan (pointers may be null when only
+// the workspace size or the limits are wanted).
+cnf::GenericArgs generic_args(const cnf_plan &p, const float *x, const float *w, const float *b,
+                              const float *gamma, const float *beta, float *out, int32_t *argmax,
+                              void *workspace, int norm_groups)
+{
+    const cnf_desc &d = p.d;
+    const bool three = d.ndim == 3;
+    cnf::GenericArgs a{};
+    a.x = x; a.w = w; a.b = b; a.gamma = gamma; a.beta = beta;
+    a.out = out; a.argmax = argmax; a.workspace = workspace;
+    a.N = d.N; a.C_in = d.C_in; a.C_out = d.C_out; a.groups = d.groups; a.ndim = d.ndim;
+    a.transposed = d.kind == CNF_CONV_TRANSPOSE;
+    a.D = d.in_dims[0]; a.H = d.in_dims[1]; a.W = d.in_dims[2];
+    a.Do = p.Do; a.Ho = p.Ho; a.Wo = p.Wo;
+    a.kd = three ? d.kernel : 1; a.kh = d.kernel; a.kw = d.kernel;
+    a.sd = three ? d.stride : 1; a.sh = d.stride; a.sw = d.stride;
+    a.pd = three ? d.padding : 0; a.ph = d.padding; a.pw = d.padding;
+    a.dd = three ? d.dilation : 1; a.dh = d.dilation; a.dw = d.dilation;
+    a.act = d.act;
+    a.norm_groups = norm_groups;
+    a.eps = d.eps;
+    a.inv_div = 1.0f / d.divide_by;
+    a.reduce = d.reduce;
+    a.pool_kernel = d.pool_kernel; a.pool_repeats = d.pool_repeats;
+    a.argmax_wanted = d.want_argmax;
+    return a;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -92,22 +128,31 @@ cnf_status cnf_plan_create(const cnf_desc *desc, cnf_plan **plan)
     if (d.norm != CNF_NORM_NONE && !(d.eps > 0.0f)) return CNF_ERR_INVALID_DESC;
     if (!(d.divide_by == d.divide_by) || d.divide_by == 0.0f) return CNF_ERR_INVALID_DESC;
     if (d.want_argmax && d.reduce != CNF_RED_MAXPOOL) return CNF_ERR_INVALID_DESC;
+    if (d.stride < 1 || d.dilation < 1 || d.padding < 0 || d.output_padding < 0)
+        return CNF_ERR_INVALID_DESC;
+    if (d.kind == CNF_CONV && d.output_padding != 0) return CNF_ERR_INVALID_DESC;
+    if (d.kind == CNF_CONV_TRANSPOSE &&
+        d.output_padding >= (d.stride > d.dilation ? d.stride : d.dilation))
+        return CNF_ERR_INVALID_DESC;
 
     cnf_plan p{};
     p.d = d;
     const int k = d.kernel;
     const int D = d.in_dims[0], H = d.in_dims[1], W = d.in_dims[2];
-    if (d.kind == CNF_CONV) {
-        p.Do = d.ndim == 3 ? D - k + 1 : 1;
-        p.Ho = H - k + 1;
-        p.Wo = W - k + 1;
-    } else {
-        if (d.ndim != 2) return CNF_ERR_UNSUPPORTED;  // transposed conv is 2-D here
-        p.Do = 1;
-        p.Ho = H + k - 1;
-        p.Wo = W + k - 1;
-    }
-    if (p.Do < 1 || p.Ho < 1 || p.Wo < 1) return CNF_ERR_INVALID_DESC;
+    // Output extent per axis (64-bit, so huge descriptors are rejected, not wrapped).
+    auto extent = [&](int L) -> long long {
+        const long long s = d.stride, pd = d.padding, dl = d.dilation;
+        if (d.kind == CNF_CONV) {
+            const long long num = L + 2 * pd - dl * (k - 1) - 1;
+            return num < 0 ? 0 : num / s + 1;
+        }
+        return (L - 1LL) * s - 2 * pd + dl * (k - 1) + d.output_padding + 1;
+    };
+    const long long eD = d.ndim == 3 ? extent(D) : 1, eH = extent(H), eW = extent(W);
+    if (eD < 1 || eH < 1 || eW < 1) return CNF_ERR_INVALID_DESC;
+    if (eD > (1 << 30) || eH > (1 << 30) || eW > (1 << 30) || eD * eH * eW > (1LL << 40))
+        return CNF_ERR_UNSUPPORTED;
+    p.Do = (int)eD; p.Ho = (int)eH; p.Wo = (int)eW;
 
     int pool_total = 1;
     p.Dp = p.Do; p.Hp = p.Ho; p.Wp = p.Wo;
@@ -142,7 +187,15 @@ cnf_status cnf_plan_create(const cnf_desc *desc, cnf_plan **plan)
     const int norm_groups = d.norm == CNF_NORM_GROUP ? d.num_groups
                           : d.norm == CNF_NORM_INSTANCE ? d.C_out : 0;
     p.family = 0;
-    if (d.kind == CNF_CONV && d.groups == 1) {
+    // The specialised families assume stride 1, no padding, dilation 1; the
+    // CNF_FORCE_GENERIC environment variable (tests) sends everything to the
+    // general family.
+    const char *force = std::getenv("CNF_FORCE_GENERIC");
+    const bool basic = d.stride == 1 && d.padding == 0 && d.dilation == 1 &&
+                       d.output_padding == 0 && !(force && force[0] == '1');
+    if (!basic) {
+        // no specialised family
+    } else if (d.kind == CNF_CONV && d.groups == 1) {
         if (d.ndim == 3 && d.reduce == CNF_RED_MEAN_SPATIAL && d.act != CNF_ACT_SOFTMAX_CHANNEL &&
             cnf::conv3d_gn_mean_supported(d.C_in, d.C_out, k, D, H, W, d.act))
             p.family = FAM_GN_MEAN;
@@ -156,7 +209,7 @@ cnf_status cnf_plan_create(const cnf_desc *desc, cnf_plan **plan)
         else if (d.ndim == 2 && d.reduce == CNF_RED_NONE &&
                  cnf::conv2d_igemm_supported(d.C_in, d.C_out, k, d.groups, H, W, d.act))
             p.family = FAM_IGEMM;
-    } else if (d.kind == CNF_CONV_TRANSPOSE && d.reduce == CNF_RED_NONE) {
+    } else if (d.kind == CNF_CONV_TRANSPOSE && d.ndim == 2 && d.reduce == CNF_RED_NONE) {
         // dense transposed conv: the implicit GEMM on the input padded by k - 1;
         // 8-channel groups (or a dense 8 -> 8 one): the column-pair kernels
         if (d.groups == 1 && cnf::conv2d_igemm_supported(d.C_in, d.C_out, k, d.groups,
@@ -170,13 +223,21 @@ cnf_status cnf_plan_create(const cnf_desc *desc, cnf_plan **plan)
                                          d.num_groups))
             p.family = FAM_CONVT_FUSED;
     }
-    (void)norm_groups;
-    if (!p.family) return CNF_ERR_UNSUPPORTED;
+    if (!p.family) {
+        const cnf::GenericArgs ga = generic_args(p, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                                 nullptr, nullptr, nullptr, norm_groups);
+        if (!cnf::generic_supported(ga)) return CNF_ERR_UNSUPPORTED;
+        p.family = FAM_GENERIC;
+    }
 
     p.workspace = 0;
     if (p.family == FAM_IGEMM)
         p.workspace = cnf::conv2d_igemm_workspace(d.N, d.C_in, d.C_out, p.Ho, p.Wo);
     if (p.family == FAM_CONVT) p.workspace = cnf::convt2d_workspace(d.N, d.C_out, p.Ho, p.Wo);
+    if (p.family == FAM_GENERIC)
+        p.workspace = cnf::generic_workspace(generic_args(p, nullptr, nullptr, nullptr, nullptr,
+                                                          nullptr, nullptr, nullptr, nullptr,
+                                                          norm_groups));
     if (p.family == FAM_CONVT_FUSED) {
         // room for the two-pass fallback too (used if the grid cannot be co-resident)
         const size_t a = cnf::convt2d_fused_workspace(d.N, d.groups, p.Ho);
@@ -211,9 +272,10 @@ cnf_status cnf_plan_describe(const cnf_plan *plan, char *buf, size_t len)
     if (len == 0) return CNF_OK;
     const cnf_desc &d = plan->d;
     std::snprintf(buf, len, "family=%s N=%d C_in=%d C_out=%d in=%dx%dx%d k=%d groups=%d "
-                  "out_rank=%d workspace=%zu",
+                  "stride=%d padding=%d dilation=%d output_padding=%d out_rank=%d workspace=%zu",
                   family_name(plan->family), d.N, d.C_in, d.C_out, d.in_dims[0], d.in_dims[1],
-                  d.in_dims[2], d.kernel, d.groups, plan->rank, plan->workspace);
+                  d.in_dims[2], d.kernel, d.groups, d.stride, d.padding, d.dilation,
+                  d.output_padding, plan->rank, plan->workspace);
     return CNF_OK;
 }
 
@@ -289,6 +351,11 @@ cnf_status cnf_forward(const cnf_plan *plan, const float *x, const float *w, con
             e = cnf::launch_convt2d(a, st);
         break;
     }
+    case FAM_GENERIC:
+        e = cnf::launch_generic(generic_args(*plan, x, w, b, gamma, beta, out, argmax, workspace,
+                                             norm_groups),
+                                st);
+        break;
     default: return CNF_ERR_UNSUPPORTED;
     }
     return e == hipSuccess ? CNF_OK : CNF_ERR_HIP;

@@ -92,4 +92,32 @@ bool convt2d_fused_supported(int C_in, int C_out, int groups, int H, int W, int 
 size_t convt2d_fused_workspace(int N, int groups, int Ho);
 hipError_t launch_convt2d_fused(const ConvT2dArgs &a, hipStream_t st);
 
+// ---- general family: any validated descriptor (2-D or 3-D, conv or
+//      transposed conv, groups, stride, padding, dilation, output_padding,
+//      every activation / norm / reduction).  Up to five launches: conv
+//      (MFMA implicit GEMM, gathered from L2) + act + per-tile statistics,
+//      channel softmax, statistics finalize, in-place normalise, max-pool passes.
+struct GenericArgs {
+    const float *x, *w, *b, *gamma, *beta;
+    float *out;
+    int32_t *argmax;
+    void *workspace;
+    int N, C_in, C_out, groups, ndim, transposed;
+    int D, H, W;                 // input extents (D = 1 for 2-D)
+    int Do, Ho, Wo;              // conv output extents
+    int kd, kh, kw;              // kernel extents (kd = 1 for 2-D)
+    int sd, sh, sw;              // stride per axis
+    int pd, ph, pw;              // zero padding per axis (transposed: the conv's padding)
+    int dd, dh, dw;              // dilation per axis
+    int act;
+    int norm_groups;             // 0: no norm; C_out: instance norm
+    float eps, inv_div;
+    int reduce;                  // cnf_reduce
+    int pool_kernel, pool_repeats;
+    int argmax_wanted;
+};
+bool generic_supported(const GenericArgs &a);
+size_t generic_workspace(const GenericArgs &a);
+hipError_t launch_generic(const GenericArgs &a, hipStream_t st);
+
 }  // namespace cnf

@@ -4,8 +4,10 @@
  *
  * The library computes, in one call on one HIP stream, the forward pass
  *
- *     y   = conv(x; w, b)           stride 1, no padding, dilation 1, groups
- *     a   = act(y)                  none | HardSwish | exact GELU | channel softmax
+ *     y   = conv(x; w, b)           groups, stride, zero padding, dilation
+ *                                   (transposed conv: also output_padding)
+ *     a   = act(y)                  none | HardSwish | exact GELU | tanh GELU |
+ *                                   channel softmax
  *     z   = norm(a)                 none | GroupNorm | InstanceNorm (eps inside sqrt)
  *     z   = z / divide_by
  *     out = reduce(z)               none | mean over D,H,W | p-max-pool applied r times
@@ -19,8 +21,13 @@
  *   "Kimi-K2.6__l2_p6"   Conv3d -> softmax over channels -> MaxPool3d(2) twice
  *                        (the trace's problem statement and floor-mode size chain);
  *   "Kimi-K2.6__l2_p19"  ConvTranspose2d (stride 1, groups) -> GELU -> GroupNorm
- *                        (first trace: shapes and output size; second trace:
- *                        transposed-conv definition and weight layout).
+ *                        (first trace: shapes and the output-size formula with
+ *                        stride, padding, dilation and output_padding; second
+ *                        trace: transposed-conv definition and weight layout;
+ *                        the fix sequence: the transposed conv as the adjoint
+ *                        of the strided, padded, dilated conv).
+ * The conv output-size formula with stride, padding and dilation is the one
+ * "Kimi-K2.6__l2_p6" states in its integer output-size passage.
  *
  * Conventions for every entry point:
  *   - Tensors are fp32, dense and contiguous, batch-major NC(D)HW.  2-D
@@ -46,7 +53,7 @@
 extern "C" {
 #endif
 
-#define CNF_ABI_VERSION 1
+#define CNF_ABI_VERSION 2
 
 typedef enum {
     CNF_OK = 0,
@@ -105,6 +112,13 @@ typedef struct {
     int32_t pool_kernel;   /* maxpool kernel = stride (>= 1) */
     int32_t pool_repeats;  /* number of successive pools (>= 1) */
     int32_t want_argmax;   /* maxpool only: 1 = also write int32 argmax */
+    /* Conv geometry, the same on every spatial axis (added in ABI version 2). */
+    int32_t stride;        /* >= 1 */
+    int32_t padding;       /* >= 0; conv: zeros around the input; transposed conv:
+                              rows/cols dropped from each side of the full output */
+    int32_t dilation;      /* >= 1; spacing of the kernel taps */
+    int32_t output_padding;/* transposed conv: 0 <= output_padding < max(stride,
+                              dilation), extra extent at the high end; conv: 0 */
 } cnf_desc;
 
 typedef struct cnf_plan cnf_plan;
@@ -113,19 +127,26 @@ typedef struct cnf_plan cnf_plan;
  * an immutable plan in *plan (host memory, freed by cnf_plan_destroy).
  * Checks: abi_version; ndim in {2,3}; N >= 0; C_in, C_out, kernel >= 1;
  * groups divides C_in and C_out; num_groups divides C_out (GroupNorm);
+ * stride, dilation >= 1; padding >= 0; output_padding as stated above;
  * every conv output extent >= 1; pooled extents >= 1; eps > 0 when a norm is
- * requested; divide_by != 0; enum fields in range.  Returns
- * CNF_ERR_UNSUPPORTED for valid descriptors no kernel family covers (the
- * supported families are listed in cnf_plan_describe's output).
+ * requested; divide_by != 0; enum fields in range.  Shapes the specialised
+ * kernel families cover take them; every other valid descriptor takes the
+ * general family (cnf_plan_describe names the choice).  Returns
+ * CNF_ERR_UNSUPPORTED only past the general family's size limits: a sample's
+ * input or output, or the weights, at or above 2 GiB - 16 MiB; an extent,
+ * padding or dilated kernel extent at or above 2^20; more than 2048 channels
+ * per norm group; more than 2^27 output positions per channel.
  * On failure *plan is set to NULL. */
 cnf_status cnf_plan_create(const cnf_desc *desc, cnf_plan **plan);
 
 /* Output shape of cnf_forward's `out`: dims[0..rank-1], rank <= 5.
- *   reduce NONE    -> (N, C_out, [Do,] Ho, Wo) with Do/Ho/Wo = L - k + 1
- *                     (L + k - 1 for the transposed conv)
+ *   reduce NONE    -> (N, C_out, [Do,] Ho, Wo) with, per axis,
+ *                     conv:       floor((L + 2p - d(k-1) - 1) / s) + 1
+ *                     transposed: (L - 1)s - 2p + d(k-1) + output_padding + 1
  *   reduce MEAN    -> (N, C_out)
  *   reduce MAXPOOL -> (N, C_out, Dp, Hp, Wp), each extent floor-divided by
- *                     pool_kernel pool_repeats times (2-D: Dp = 1 is kept).
+ *                     pool_kernel pool_repeats times (2-D: H and W are pooled,
+ *                     Dp = 1 is kept).
  * argmax, when requested, has the same shape as out. */
 cnf_status cnf_plan_output_shape(const cnf_plan *plan, int64_t dims[5], int32_t *rank);
 

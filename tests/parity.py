@@ -38,24 +38,31 @@ def check_argmax(got_idx, ref_idx, pre_pool, Pk, what=""):
     """Argmax parity where the window's top two oracle values are separated by
     more than the parity tolerance; returns the number of windows excluded.
 
-    pre_pool: oracle values on the conv grid (N, C, Do, Ho, Wo), float64;
-    Pk: total pool extent (4 for two 2-pools)."""
+    pre_pool: oracle values the first pool sees, on the conv grid, float64,
+    (N, C, Do, Ho, Wo) or (N, C, Ho, Wo) for a 2-D problem (whose pools leave
+    D alone); Pk: total pool extent per pooled axis (4 for two 2-pools)."""
     got_idx = np.asarray(got_idx).astype(np.int64)
+    if pre_pool.ndim == 4:
+        pre_pool = pre_pool[:, :, None]
+        kd = 1
+    else:
+        kd = Pk
     N, C, Dp, Hp, Wp = ref_idx.shape
-    win = pre_pool[:, :, :Dp * Pk, :Hp * Pk, :Wp * Pk].reshape(N, C, Dp, Pk, Hp, Pk, Wp, Pk)
+    win = pre_pool[:, :, :Dp * kd, :Hp * Pk, :Wp * Pk].reshape(N, C, Dp, kd, Hp, Pk, Wp, Pk)
     win = win.transpose(0, 1, 2, 4, 6, 3, 5, 7).reshape(N, C, Dp, Hp, Wp, -1)
     top2 = np.sort(win, axis=-1)[..., -2:]
     gap = top2[..., 1] - top2[..., 0]
     clear = gap > ATOL + RTOL * np.abs(top2[..., 1])
     mism = (got_idx != ref_idx) & clear
     assert not mism.any(), f"{what}: {int(mism.sum())} argmax mismatches in clear windows"
-    # every reported index must name a voxel of its own window holding the max
+    # every reported index must name a voxel of its own window
     Do, Ho, Wo = pre_pool.shape[2:]
     d, h, w = got_idx // (Ho * Wo), (got_idx // Wo) % Ho, got_idx % Wo
     od, oh, ow = np.indices((Dp, Hp, Wp))
-    assert ((d // Pk == od) & (h // Pk == oh) & (w // Pk == ow)).all(), f"{what}: index outside window"
+    assert ((d // kd == od) & (h // Pk == oh) & (w // Pk == ow)).all(), f"{what}: index outside window"
     return int((~clear).sum())
 
 
 def oracle_pre_pool(wl, x, p):
-    return oracle.pre_norm(wl, x, p["w"], p["b"])
+    """The oracle's values entering the first pool: conv, activation, norm, divide."""
+    return oracle.forward(dict(wl, reduce="none", want_argmax=0), x, **p)[0]

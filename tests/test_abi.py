@@ -69,8 +69,16 @@ def _desc(name="conv3d_hswish_gn_mean_n1024", **over):
     (lambda d: setattr(d, "act", 9), cnf.CNF_ERR_INVALID_DESC),
     (lambda d: setattr(d, "reduce", 7), cnf.CNF_ERR_INVALID_DESC),
     (lambda d: setattr(d, "want_argmax", 1), cnf.CNF_ERR_INVALID_DESC),  # argmax without a pool
-    (lambda d: setattr(d, "C_out", 24), cnf.CNF_ERR_UNSUPPORTED),        # valid, no kernel family
-    (lambda d: setattr(d, "kernel", 5), cnf.CNF_ERR_UNSUPPORTED),
+    (lambda d: setattr(d, "stride", 0), cnf.CNF_ERR_INVALID_DESC),
+    (lambda d: setattr(d, "dilation", 0), cnf.CNF_ERR_INVALID_DESC),
+    (lambda d: setattr(d, "padding", -1), cnf.CNF_ERR_INVALID_DESC),
+    (lambda d: setattr(d, "output_padding", 1), cnf.CNF_ERR_INVALID_DESC),  # conv: must be 0
+    (lambda d: setattr(d, "dilation", 9), cnf.CNF_ERR_INVALID_DESC),        # dilated kernel > input
+    (lambda d: setattr(d, "C_out", 24), cnf.CNF_OK),          # no specialised family: general one
+    (lambda d: setattr(d, "kernel", 5), cnf.CNF_OK),
+    (lambda d: setattr(d, "stride", 3), cnf.CNF_OK),
+    (lambda d: (setattr(d, "padding", 2), setattr(d, "dilation", 2)), cnf.CNF_OK),
+    (lambda d: [d.in_dims.__setitem__(i, 1024) for i in range(3)], cnf.CNF_ERR_UNSUPPORTED),
 ])
 def test_descriptor_validation(mutate, status):
     d = _desc()
@@ -141,7 +149,92 @@ def test_supported_matrix_edges():
           ("conv3d_hswish_gn_mean_n1024", dict(act="gelu_tanh"))]
     for name, over in ok:
         assert cnf.cnf_plan_create_status(_desc(name, **over)) == cnf.CNF_OK, (name, over)
-    bad = [("conv3d_softmax_pool_n128", dict(kernel=2, act="hardswish")),
-           ("conv3d_softmax_pool_n128", dict(C_in=1, act="none"))]
-    for name, over in bad:
-        assert cnf.cnf_plan_create_status(_desc(name, **over)) == cnf.CNF_ERR_UNSUPPORTED, (name, over)
+    # ... and the combinations no specialised family takes go to the general one
+    other = [("conv3d_softmax_pool_n128", dict(kernel=2, act="hardswish")),
+             ("conv3d_softmax_pool_n128", dict(C_in=1, act="none"))]
+    for name, over in other:
+        assert "family=generic" in cnf.Plan(_desc(name, **over)).describe(), (name, over)
+
+
+def test_transposed_conv_output_padding_rule():
+    # 0 <= output_padding < max(stride, dilation)
+    d = _desc("convt2d_gelu_gn_n128", output_padding=1)
+    assert cnf.cnf_plan_create_status(d) == cnf.CNF_ERR_INVALID_DESC
+    for s, dl, op, st in [(2, 1, 1, cnf.CNF_OK), (2, 1, 2, cnf.CNF_ERR_INVALID_DESC),
+                          (1, 3, 2, cnf.CNF_OK), (1, 3, 3, cnf.CNF_ERR_INVALID_DESC)]:
+        d = _desc("convt2d_gelu_gn_n128", stride=s, dilation=dl, output_padding=op)
+        assert cnf.cnf_plan_create_status(d) == st, (s, dl, op)
+
+
+@pytest.mark.parametrize("name,over,shape", [
+    # conv: floor((L + 2p - d(k-1) - 1) / s) + 1
+    ("conv2d_in_div_n128", dict(stride=2, padding=1), (128, 128, 64, 64)),
+    ("conv2d_in_div_n128", dict(dilation=2, padding=2), (128, 128, 128, 128)),
+    ("conv3d_hswish_gn_mean_n1024", dict(stride=2, reduce="none"), (1024, 16, 7, 15, 15)),
+    # transposed: (L - 1)s - 2p + d(k-1) + op + 1
+    ("convt2d_gelu_gn_n128", dict(stride=2, padding=1, output_padding=1), (128, 64, 512, 512)),
+    ("convt2d_gelu_gn_n128", dict(stride=3, dilation=2), (128, 64, 770, 770)),
+    ("convt2d_gelu_gn_n128", dict(ndim=3, in_dims=(4, 8, 8), stride=2), (128, 64, 9, 17, 17)),
+    # 2-D pool of a strided conv: H and W pooled, D = 1 kept
+    ("conv2d_in_div_n2", dict(stride=2, reduce="maxpool", pool_kernel=3, pool_repeats=1),
+     (2, 16, 1, 5, 5)),
+])
+def test_general_geometry_output_shapes(name, over, shape):
+    plan = cnf.Plan(_desc(name, **over))
+    assert plan.out_shape == shape
+    assert "family=generic" in plan.describe()
+
+
+def test_family_routing():
+    # the page configurations keep their specialised families ...
+    fams = {n: cnf.Plan(_desc(n)).describe().split()[0] for n in cnf_inputs.WORKLOAD_ORDER}
+    assert not any("generic" in f for f in fams.values()), fams
+    # ... and CNF_FORCE_GENERIC=1 sends them to the general one
+    os.environ["CNF_FORCE_GENERIC"] = "1"
+    try:
+        for n in cnf_inputs.WORKLOAD_ORDER:
+            assert "family=generic" in cnf.Plan(_desc(n)).describe(), n
+    finally:
+        del os.environ["CNF_FORCE_GENERIC"]
+    assert "generic" not in cnf.Plan(_desc("conv2d_in_div_n2")).describe()
+
+
+def _align(v):
+    return (v + 255) // 256 * 256
+
+
+def test_general_workspace_layout_sizes():
+    # InstanceNorm, no reduction: per-tile triples (16 B) + per-channel scale/shift (8 B)
+    p = cnf.Plan(_desc("conv2d_in_div_n128", stride=2, padding=1))
+    S = 64 * 64
+    T = (S + 63) // 64
+    assert p.workspace_bytes == _align(128 * 128 * T * 16) + _align(128 * 128 * 8)
+    # plain conv, nothing after it: no workspace
+    p = cnf.Plan(_desc("conv2d_in_div_n2", stride=2, norm="none", divide_by=1.0))
+    assert p.workspace_bytes == 0
+    # softmax + two 2-pools with argmax: staged conv output, then two ping-pong
+    # value + index buffers of the first pool's size
+    p = cnf.Plan(_desc("conv3d_softmax_pool_n128", padding=1))
+    S = 16 * 32 * 32
+    pool1 = 128 * 16 * 8 * 16 * 16
+    assert p.workspace_bytes == _align(128 * 16 * S * 4) + 4 * _align(pool1 * 4)
+
+
+def test_descriptor_layout_matches_the_c_header(tmp_path):
+    """sizeof and every field offset of cnf_desc, as gcc lays it out from the
+    header, equal the ctypes mirror."""
+    import ctypes
+    import subprocess
+    fields = [f for f, _ in cnf.cnf_desc._fields_]
+    src = tmp_path / "layout.c"
+    body = "".join(f'    printf("{f} %zu\\n", offsetof(cnf_desc, {f}));\n' for f in fields)
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "cnf.h"\n'
+                   'int main(void) {\n    printf("size %zu\\n", sizeof(cnf_desc));\n'
+                   + body + "    return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.check_call(["gcc", "-std=c11", f"-I{os.path.join(ROOT, 'include')}", str(src),
+                           "-o", str(exe)])
+    got = dict(l.split() for l in subprocess.check_output([str(exe)], text=True).splitlines())
+    assert int(got["size"]) == ctypes.sizeof(cnf.cnf_desc)
+    for f in fields:
+        assert int(got[f]) == getattr(cnf.cnf_desc, f).offset, f

@@ -46,21 +46,31 @@ DOMINANT = {
     "conv2d_in_div_n128": ("conv2d_igemm_kernel<128", "mfma"),
     "convt2d_gelu_gn_n128": ("convt2d_gn_fused_kernel", "mfma"),
     "convt2d_dense_gelu_gn_n128": ("conv2d_igemm_kernel<64", "mfma"),
+    "conv2d_s2p1_in_div_n128": ("gen_conv_kernel<0, false>", "mfma"),
+    "convt2d_s2_gelu_gn_n128": ("gen_conv_kernel<2, true>", "mfma"),
 }
 
 
 def conv_out_grid(wl):
+    """Conv output extents (D = 1 for 2-D), with stride, padding, dilation."""
+    k, s, p, d = wl["kernel"], wl["stride"], wl["padding"], wl["dilation"]
+
+    def ext(L):
+        if wl["kind"] == "conv_transpose":
+            return (L - 1) * s - 2 * p + d * (k - 1) + wl["output_padding"] + 1
+        return (L + 2 * p - d * (k - 1) - 1) // s + 1
     D, H, W = wl["in_dims"]
-    k = wl["kernel"]
-    if wl["kind"] == "conv_transpose":
-        return (1, H + k - 1, W + k - 1)
-    return ((D - k + 1) if wl["ndim"] == 3 else 1, H - k + 1, W - k + 1)
+    return (ext(D) if wl["ndim"] == 3 else 1, ext(H), ext(W))
 
 
 def nominal_flops(wl):
+    """2 x outputs x (C_in/groups) x taps per output.  A transposed conv with
+    stride s reaches each output with k^ndim / s^ndim taps on average."""
     Do, Ho, Wo = conv_out_grid(wl)
-    return 2.0 * wl["N"] * wl["C_out"] * Do * Ho * Wo * (wl["C_in"] // wl["groups"]) * \
-        wl["kernel"] ** wl["ndim"]
+    taps = wl["kernel"] ** wl["ndim"]
+    if wl["kind"] == "conv_transpose":
+        taps /= wl["stride"] ** wl["ndim"]
+    return 2.0 * wl["N"] * wl["C_out"] * Do * Ho * Wo * (wl["C_in"] // wl["groups"]) * taps
 
 
 def algorithmic_flops(wl):

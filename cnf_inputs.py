@@ -22,6 +22,16 @@ Workloads (shapes and options as the four source pages state their problems):
   * convt2d_dense_gelu_gn_n128
                           the same with groups = 1 (dense 64->64 transposed
                           conv, K = 576): the other reading of l2_p19's problem.
+  * conv2d_s2p1_in_div_n128
+                          l2_p17's chain with a strided, padded conv: Conv2d
+                          64->128 k3 stride 2 padding 1 on 128x64x128x128
+                          (-> 64x64), InstanceNorm2d, /2.
+  * convt2d_s2_gelu_gn_n128
+                          l2_p19's chain as an upsampling layer:
+                          ConvTranspose2d 64->64 k3 stride 2 padding 1
+                          output_padding 1 groups 8 on 128x64x128x128
+                          (-> 256x256, the page's output size), GELU,
+                          GroupNorm(8) with affine.
 
 Distributions: x ~ N(0, 1) (or U[0, 1) as a second parity set, the
 distribution the pages' own harness used); conv weight and bias ~
@@ -73,7 +83,17 @@ WORKLOADS = {
         id=6, ndim=2, kind="conv_transpose", N=128, C_in=64, C_out=64,
         in_dims=(1, 256, 256), kernel=3, groups=1, act="gelu", norm="group",
         num_groups=8, affine=1),
+    "conv2d_s2p1_in_div_n128": _wl(
+        id=7, ndim=2, N=128, C_in=64, C_out=128, in_dims=(1, 128, 128), kernel=3,
+        stride=2, padding=1, norm="instance", num_groups=128, divide_by=2.0),
+    "convt2d_s2_gelu_gn_n128": _wl(
+        id=8, ndim=2, kind="conv_transpose", N=128, C_in=64, C_out=64,
+        in_dims=(1, 128, 128), kernel=3, groups=8, stride=2, padding=1,
+        output_padding=1, act="gelu", norm="group", num_groups=8, affine=1),
 }
+
+# The workloads the pages state (the others vary their geometry).
+PAGE_WORKLOADS = [n for n in WORKLOADS if WORKLOADS[n]["id"] <= 6]
 
 # Order in which the workloads are listed (smallest first).
 WORKLOAD_ORDER = list(WORKLOADS)

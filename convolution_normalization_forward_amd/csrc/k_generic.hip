@@ -28,10 +28,14 @@
 //                          gathered straight from the input through L1/L2 with
 //                          per-lane bounds checks (no LDS staging: the access
 //                          pattern depends on stride and dilation).  A wave owns
-//                          16 channels x 64 positions (four column tiles share
-//                          each weight operand); + bias + activation; writes the
-//                          conv output and, for each (sample, channel, 64-position
-//                          tile), (count, mean, M2) from two passes over the tile.
+//                          up to 4 x 16 channels x a 4-row x 16-column block of
+//                          positions (row coordinates are wave-uniform; each
+//                          gathered operand feeds up to 16 MFMAs); a strided transposed
+//                          conv is split into stride^ndim phases so only the taps
+//                          that reach a phase are issued; + bias + activation;
+//                          writes the conv output and, for each (sample, channel,
+//                          64-position tile), (count, mean, M2) from two passes
+//                          over the tile.
 //   2. gen_softmax_kernel  softmax over the channels at each position, in place,
 //                          and the same per-tile statistics of its result.
 //   3. gen_finalize_kernel per (sample, norm group): merges the tile triples in
@@ -67,137 +71,249 @@ constexpr unsigned GOOB = 0x7ff00000u;   // an offset past the end of every reso
 constexpr unsigned RES_MAX = 0x7f000000u;
 
 struct GenConv {
-    const float *x, *w, *b;
+    const float *x, *wp, *b;   // wp: weights packed by gen_weight_pack_kernel
     float *y;          // conv output [N][C_out][S] or nullptr
     v4f *part;         // [N][C_out][T] (count, mean, M2, 0) or nullptr
-    long long tasks;   // N * T * G * cob
-    int C_in, C_out, Cgi, Cgo, G, cob, T;
+    int tasks;         // N * nph * Tq * GTn * cobN (below 2^31)
+    int tpw;           // tasks per wave
+    int C_in, C_out, Cgi, Cgo, G, cobN, T, Tq, CT;  // CT: column tiles per phase
+    // P conv groups share one 16-row tile (groups of at most 8 output channels):
+    // RPG = 16/P rows and KPG = 4/P K entries per group; GTn = ceil(G/P) group
+    // tiles; steps = ceil(Cgi/KPG) K steps per tap; KP = 4*steps.
+    int P, RPG, KPG, GTn, steps, KP;
     int D, H, W, Do, Ho, Wo, S;
     int kd, kh, kw;
     int sd, sh, sw, pd, ph, pw, dd, dh, dw;
-    float rsd, rsh, rsw;  // 1 / stride (transposed gather)
-    unsigned in_plane, w_elems;
+    unsigned in_plane, wp_elems;
     float out_scale;
 };
 
-// Transposed gather: t = o + p - a*d names input position t / s when s divides
-// t and the quotient lies in [0, L).  The quotient comes from a float product:
-// for 0 <= t < 2^21 the fraction of (t + 0.5)/s is at least 0.5/s away from an
-// integer while the float error is below 0.25/s, so the floor is exact.
-__device__ __forceinline__ bool gather_src(int t, int s, float rs, int L, int &q) {
-    q = (int)floorf(((float)t + 0.5f) * rs);
-    return t >= 0 && q * s == t && q < L;
-}
-
-template <int ACT, bool TR>
-__global__ __launch_bounds__(GT) void gen_conv_kernel(GenConv g) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// A wave's 64 output positions are ROWS rows x (64 / ROWS) consecutive
+// columns (four MFMA column tiles u; tile u is row u / CW, columns
+// (u % CW)*16 + col).  Row coordinates are wave-uniform; columns are per lane.
+// Wide outputs use one row of 64 columns, so each store instruction of a wave
+// writes whole runs of a row.
+//
+// A conv gathers input x[o*s - p + a*d].  A transposed conv (the adjoint) reaches
+// output o from input (o + p - a*d)/s where s divides o + p - a*d.  Along z and y
+// the outputs are visited in phases: rows o = q*s + r with the same residue r
+// are reached by the same taps (those with s | r + p - a*d) from input rows
+// q + (r + p - a*d)/s, so a wave works inside one phase and skips the other taps
+// with a uniform branch.  Along x each lane checks its own column: the exact
+// quotient comes from a float product, exact for 0 <= t < 2^21 (the fraction of
+// (t + 0.5)/s is at least 0.5/s from an integer, the float error below 0.25/s).
+//
+// One wave owns NB blocks of 16 output channels of one conv group: each
+// gathered input operand feeds NB MFMAs, each weight operand 4.
+template <int ACT, bool TR, int NB, int ROWS>
+__device__ __forceinline__ void gen_conv_task(const GenConv &g, int task, int lane) {
+    constexpr int CW = 4 / ROWS;  // 16-column tiles per row
     const int col = lane & 15, kq = lane >> 4;
-    const long long task = (long long)xcd_remap(blockIdx.x, gridDim.x) * 4 + wave;
-    if (task >= g.tasks) return;  // whole waves leave; the kernel has no barriers
-    long long t = task;
-    const int cb = (int)(t % g.cob); t /= g.cob;
-    const int grp = (int)(t % g.G); t /= g.G;
-    const int pt = (int)(t % g.T);
-    const int n = (int)(t / g.T);
+    // Task order (fastest first): channel blocks, phase, group, tile, sample.
+    const int nph = TR ? g.sd * g.sh : 1;
+    int t = task;
+    const int cbn = t % g.cobN; t /= g.cobN;
+    const int phs = t % nph; t /= nph;
+    const int gt = t % g.GTn; t /= g.GTn;
+    const int pt = t % g.Tq;
+    const int n = t / g.Tq;
 
-    const auto xr = make_rsrc(g.x + (size_t)n * g.C_in * g.in_plane, g.C_in * g.in_plane * 4u);
-    const auto wr = make_rsrc(g.w, g.w_elems * 4u);
+    // Phase residues (z, y) and the phase's row grid (all rows for a conv).
+    int rz = 0, ry = 0, Qz = g.Do, Qy = g.Ho;
+    if (TR) {
+        ry = phs % g.sh;
+        rz = phs / g.sh;
+        Qz = (g.Do - rz + g.sd - 1) / g.sd;
+        Qy = (g.Ho - ry + g.sh - 1) / g.sh;
+    }
+    const int rt = pt / g.CT, ct = pt - rt * g.CT;
+    const int row0 = rt * ROWS, col0 = ct * 16 * CW;
+    const int nrows = min(ROWS, Qz * Qy - row0), ncols = min(16 * CW, g.Wo - col0);
+    const int cnt = nrows > 0 && ncols > 0 ? nrows * ncols : 0;
+    const int tile = phs * g.Tq + pt;
 
-    // This lane's output position in each of the four column tiles.
-    const int HWo = g.Ho * g.Wo;
-    int bz[4], by[4], bx[4], pos[4];
+    // Output channel of accumulator row `row` of block b (tile rows are split
+    // into P groups of RPG rows); false for padding rows.
+    auto out_channel = [&](int b, int row, int &cgl) -> bool {
+        const int grp = gt * g.P + row / g.RPG;
+        const int co = (cbn * NB + b) * 16 + row % g.RPG;
+        cgl = grp * g.Cgo + co;
+        return co < g.Cgo && grp < g.G;
+    };
+
+    if (cnt <= 0) {  // this phase has fewer rows than the largest: empty statistics
+        if (g.part && col == 0) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    int cgl;
+                    if (out_channel(b, 4 * kq + r, cgl))
+                        g.part[((size_t)n * g.C_out + cgl) * g.T + tile] = v4f{0.f, 0.f, 0.f, 0.f};
+                }
+        }
+        return;
+    }
+
+    // Rows (uniform): gather base along z and y, output row offset.
+    int bz[ROWS], by[ROWS], orow[ROWS];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+        const bool rv = r < nrows;
+        const int rq = rv ? row0 + r : 0;
+        const int qz = rq / Qy, qy = rq - qz * Qy;
+        const int oz = TR ? qz * g.sd + rz : qz, oy = TR ? qy * g.sh + ry : qy;
+        bz[r] = TR ? qz : oz * g.sd - g.pd;
+        by[r] = TR ? qy : oy * g.sh - g.ph;
+        if (!rv) bz[r] = -(1 << 29);  // every tap falls outside the input
+        orow[r] = (oz * g.Ho + oy) * g.Wo;
+    }
+    const float rsw = 1.0f / (float)g.sw;
+    // Columns (per lane): output column and the x term of the gather.  For a
+    // transposed conv, (ox + pw) = bq * sw + bm; tap kx with kx*dw = kq' * sw + km
+    // reaches the lane iff bm == km, from input column bq - kq'.
+    int ox[4], bx[4], bm[4];
     bool pv[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-        pos[u] = pt * PTILE + u * 16 + col;
-        pv[u] = pos[u] < g.S;
-        const int p2 = pv[u] ? pos[u] : 0;
-        const int oz = p2 / HWo, rem = p2 - oz * HWo;
-        const int oy = rem / g.Wo, ox = rem - oy * g.Wo;
-        if (TR) { bz[u] = oz + g.pd; by[u] = oy + g.ph; bx[u] = ox + g.pw; }
-        else { bz[u] = oz * g.sd - g.pd; by[u] = oy * g.sh - g.ph; bx[u] = ox * g.sw - g.pw; }
-        if (!pv[u]) bz[u] = -(1 << 29);  // every tap falls outside the input
+        ox[u] = col0 + (u % CW) * 16 + col;
+        pv[u] = (u / CW) < nrows && ox[u] < g.Wo;
+        if (TR) {
+            const int num = ox[u] + g.pw;  // >= 0, below 2^21
+            bx[u] = (int)floorf(((float)num + 0.5f) * rsw);
+            bm[u] = num - bx[u] * g.sw;
+        } else {
+            bx[u] = ox[u] * g.sw - g.pw;
+            bm[u] = 0;
+        }
     }
 
-    // A operand: row col = output channel co_l of the group, K entry kq = input channel.
-    const int co_l = cb * 16 + col;
-    const bool arow = co_l < g.Cgo;
+    // A operands: row col = output channel (cbn*NB + b)*16 + col, K entry kq =
+    // input channel c0 + kq.  In the packed weights those NB values are adjacent
+    // and a (tap, channel chunk) is one contiguous run of 64*NB floats, zero where
+    // the channel or the output channel is padding.
     const int taps = g.kd * g.kh * g.kw;
-    unsigned wbase, wci;
-    if (TR) {  // w[C_in][Cgo][taps]
-        wbase = ((unsigned)(grp * g.Cgi) * g.Cgo + co_l) * taps;
-        wci = (unsigned)g.Cgo * taps;
-    } else {   // w[C_out][Cgi][taps]
-        wbase = (unsigned)(grp * g.Cgo + co_l) * g.Cgi * taps;
-        wci = taps;
-    }
-    const unsigned xch0 = (unsigned)(grp * g.Cgi) * g.in_plane;
+    const unsigned wrow = (unsigned)g.cobN * 16 * NB;   // floats per K entry
+    const unsigned woff = ((unsigned)kq * wrow + ((unsigned)cbn * 16 + col) * NB) * 4u;
+    // B operand: K entry kq is channel c0 + kq % KPG of group gt*P + kq / KPG.
+    const float *xs = g.x + ((size_t)n * g.C_in + (size_t)gt * g.P * g.Cgi) * g.in_plane;
+    const unsigned xbytes = (unsigned)(g.C_in - gt * g.P * g.Cgi) * g.in_plane * 4u;
+    const unsigned kq_off = (unsigned)((kq / g.KPG) * g.Cgi + kq % g.KPG) * g.in_plane * 4u;
 
-    v4f acc[4];
+    // Bias of this lane's output channels, fetched before the MFMA loop so its
+    // latency overlaps the gathers.
+    float bias[NB][4];
+    const auto br = make_rsrc(g.b ? g.b : g.x, g.b ? (unsigned)g.C_out * 4u : 0u);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc[u] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            int cgl;
+            const bool cv = out_channel(b, 4 * kq + r, cgl);
+            bias[b][r] = buf_load1(br, cv ? (unsigned)cgl * 4u : GOOB);
+        }
 
-    int tap = 0;
-    for (int kz = 0; kz < g.kd; ++kz)
-    for (int ky = 0; ky < g.kh; ++ky)
-    for (int kx = 0; kx < g.kw; ++kx, ++tap) {
-        unsigned sp[4];
-        bool ok[4];
+    v4f acc[NB][4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            int iz, iy, ix;
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc[b][u] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    for (int kz = 0; kz < g.kd; ++kz) {
+        int tz = kz * g.dd;
+        if (TR) {
+            const int num = rz + g.pd - kz * g.dd;
+            if (num % g.sd) continue;
+            tz = num / g.sd;
+        }
+        for (int ky = 0; ky < g.kh; ++ky) {
+            int ty = ky * g.dh;
             if (TR) {
-                const bool a = gather_src(bz[u] - kz * g.dd, g.sd, g.rsd, g.D, iz);
-                const bool b = gather_src(by[u] - ky * g.dh, g.sh, g.rsh, g.H, iy);
-                const bool c = gather_src(bx[u] - kx * g.dw, g.sw, g.rsw, g.W, ix);
-                ok[u] = a && b && c;
-            } else {
-                iz = bz[u] + kz * g.dd;
-                iy = by[u] + ky * g.dh;
-                ix = bx[u] + kx * g.dw;
-                ok[u] = (unsigned)iz < (unsigned)g.D && (unsigned)iy < (unsigned)g.H &&
-                        (unsigned)ix < (unsigned)g.W;
+                const int num = ry + g.ph - ky * g.dh;
+                if (num % g.sh) continue;
+                ty = num / g.sh;
             }
-            sp[u] = ((unsigned)iz * g.H + (unsigned)iy) * g.W + (unsigned)ix;
-        }
-        for (int c0 = 0; c0 < g.Cgi; c0 += 4) {
-            const int ci = c0 + kq;
-            const bool cok = ci < g.Cgi;
-            const float a = buf_load1(wr, (arow && cok) ? (wbase + ci * wci + tap) * 4u : GOOB);
-            float bv[4];
+            bool okzy[ROWS];
+            unsigned rowb[ROWS];
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
-                bv[u] = buf_load1(xr, (ok[u] && cok) ? (xch0 + ci * g.in_plane + sp[u]) * 4u : GOOB);
+            for (int r = 0; r < ROWS; ++r) {
+                const int iz = bz[r] + tz, iy = by[r] + ty;
+                okzy[r] = (unsigned)iz < (unsigned)g.D && (unsigned)iy < (unsigned)g.H;
+                rowb[r] = ((unsigned)iz * g.H + (unsigned)iy) * g.W * 4u;
+            }
+            for (int kx = 0; kx < g.kw; ++kx) {
+                const int tap = (kz * g.kh + ky) * g.kw + kx;
+                const int kxd = kx * g.dw;
+                const int kxq = TR ? kxd / g.sw : 0, kxm = TR ? kxd - kxq * g.sw : 0;
+                unsigned xo[4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) acc[u] = mfma_16x16x4(a, bv[u], acc[u]);
+                for (int u = 0; u < 4; ++u) {
+                    int ix;
+                    bool okx;
+                    if (TR) {
+                        ix = bx[u] - kxq;
+                        okx = bm[u] == kxm && (unsigned)ix < (unsigned)g.W;
+                    } else {
+                        ix = bx[u] + kxd;
+                        okx = (unsigned)ix < (unsigned)g.W;
+                    }
+                    xo[u] = (okzy[u / CW] && okx) ? rowb[u / CW] + (unsigned)ix * 4u + kq_off : GOOB;
+                }
+                const unsigned wtap = ((unsigned)(gt * taps + tap) * g.KP) * wrow;
+                for (int st = 0; st < g.steps; ++st) {
+                    // buffers rebased on the step's first channel (scalar work);
+                    // padding channels and other groups' rows meet zero weights
+                    const int c0 = st * g.KPG;
+                    const auto xr = make_rsrc(xs + (size_t)c0 * g.in_plane,
+                                              xbytes - (unsigned)c0 * g.in_plane * 4u);
+                    const unsigned wsh = wtap + (unsigned)st * 4u * wrow;
+                    const auto wr = make_rsrc(g.wp + wsh, (g.wp_elems - wsh) * 4u);
+                    float a[NB];
+                    if constexpr (NB == 4) {
+                        const v4f v = buf_load4(wr, woff);
+                        a[0] = v[0]; a[1] = v[1]; a[2] = v[2]; a[3] = v[3];
+                    } else if constexpr (NB == 2) {
+                        const v2f v = buf_load2(wr, woff);
+                        a[0] = v[0]; a[1] = v[1];
+                    } else {
+                        a[0] = buf_load1(wr, woff);
+                    }
+                    float bv[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) bv[u] = buf_load1(xr, xo[u]);
+#pragma unroll
+                    for (int b = 0; b < NB; ++b)
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) acc[b][u] = mfma_16x16x4(a[b], bv[u], acc[b][u]);
+                }
+            }
         }
     }
 
-    // Epilogue: lane holds channels 4*kq + r of the block at position col of each tile.
-    const int cnt = min(PTILE, g.S - pt * PTILE);
+    // Epilogue: lane holds channels 4*kq + r of block b at column tile u.
     const auto yr = make_rsrc(g.y ? g.y + (size_t)n * g.C_out * g.S : g.x,
                               g.y ? (unsigned)g.C_out * g.S * 4u : 0u);
+    const float rcnt = 1.0f / (float)cnt;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const int co = cb * 16 + 4 * kq + r;
-        const bool cv = co < g.Cgo;
-        const int cgl = grp * g.Cgo + co;
-        const float bias = (g.b && cv) ? g.b[cgl] : 0.0f;
+        int cgl;
+        const bool cv = out_channel(b, 4 * kq + r, cgl);
         float v[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = activate<ACT>(acc[u][r] + bias);
+        for (int u = 0; u < 4; ++u) v[u] = activate<ACT>(acc[b][u][r] + bias[b][r]);
         if (g.y) {
 #pragma unroll
             for (int u = 0; u < 4; ++u)
                 buf_store1(v[u] * g.out_scale, yr,
-                           (cv && pv[u]) ? ((unsigned)cgl * g.S + pos[u]) * 4u : GOOB);
+                           (cv && pv[u]) ? ((unsigned)cgl * g.S + orow[u / CW] + ox[u]) * 4u : GOOB);
         }
         if (g.part) {
-            float s = 0.0f;
+            float sm = 0.0f;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) s += pv[u] ? v[u] : 0.0f;
-            const float mean = row_sum16(s) / (float)cnt;
+            for (int u = 0; u < 4; ++u) sm += pv[u] ? v[u] : 0.0f;
+            const float mean = row_sum16(sm) * rcnt;
             float q = 0.0f;
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
@@ -206,9 +322,55 @@ __global__ __launch_bounds__(GT) void gen_conv_kernel(GenConv g) {
             }
             q = row_sum16(q);
             if (col == 0 && cv)
-                g.part[((size_t)n * g.C_out + cgl) * g.T + pt] = v4f{(float)cnt, mean, q, 0.0f};
+                g.part[((size_t)n * g.C_out + cgl) * g.T + tile] = v4f{(float)cnt, mean, q, 0.0f};
         }
     }
+}
+
+// Each wave runs g.tpw consecutive tasks (the host sizes it so a wave issues a
+// few hundred MFMAs).
+template <int ACT, bool TR, int NB, int ROWS>
+__global__ __launch_bounds__(GT) void gen_conv_kernel(GenConv g) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int first = (xcd_remap(blockIdx.x, gridDim.x) * 4 + wave) * g.tpw;
+    for (int j = 0; j < g.tpw; ++j) {
+        const int task = first + j;
+        if (task >= g.tasks) return;  // whole waves leave; the kernel has no barriers
+        gen_conv_task<ACT, TR, NB, ROWS>(g, task, lane);
+    }
+}
+
+// Packed weights for gen_conv_kernel: wp[gt][tap][st][kq][cbn][col][b] is the
+// A operand entry (row (cbn*NB + b)*16 + col, K entry kq) of K step st at that
+// tap for group tile gt: with P groups per tile, row belongs to group gt*P +
+// row / RPG (output channel row % RPG) and kq to group gt*P + kq / KPG (input
+// channel st*KPG + kq % KPG); the entry is the weight when both name the same
+// existing group and real channels, else 0 (block-diagonal A, zero padding).
+// Source layout: conv w[C_out][Cgi][taps], transposed conv w[C_in][Cgo][taps].
+__global__ __launch_bounds__(GT) void gen_weight_pack_kernel(const float *w, float *wp, int G,
+                                                             int Cgi, int Cgo, int taps,
+                                                             int steps, int P, int cobN, int NB,
+                                                             int transposed, unsigned total) {
+    const unsigned i = blockIdx.x * GT + threadIdx.x;
+    if (i >= total) return;
+    const int RPG = 16 / P, KPG = 4 / P;
+    unsigned r = i;
+    const int b = r % NB; r /= NB;
+    const int col = r % 16; r /= 16;
+    const int cbn = r % cobN; r /= cobN;
+    const int kq = r % 4; r /= 4;
+    const int st = r % steps; r /= steps;
+    const int tap = r % taps;
+    const int gt = r / taps;
+    const int grp = gt * P + col / RPG;
+    const int co = (cbn * NB + b) * 16 + col % RPG;
+    const int ci = st * KPG + kq % KPG;
+    float v = 0.0f;
+    if (grp == gt * P + kq / KPG && grp < G && co < Cgo && ci < Cgi)
+        v = transposed ? w[((size_t)(grp * Cgi + ci) * Cgo + co) * taps + tap]
+                       : w[((size_t)(grp * Cgo + co) * Cgi + ci) * taps + tap];
+    wp[i] = v;
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -315,13 +477,25 @@ __global__ __launch_bounds__(GT) void gen_finalize_kernel(const v4f *part, int C
     }
 }
 
-// y[plane][i] = y * scale[plane] + shift[plane]; blockIdx.x = plane.
-constexpr int APPLY_CHUNK = GT * 8;
+// y[plane][i] = y * scale[plane] + shift[plane]; blockIdx.x = plane, blockIdx.y =
+// chunk of APPLY_CHUNK elements.  Planes of a multiple of 4 elements are 16-byte
+// aligned and go by 16-byte accesses.
+constexpr int APPLY_CHUNK = GT * 16;
 __global__ __launch_bounds__(GT) void gen_apply_kernel(float *y, const v2f *ss, int S) {
     const v2f sc = ss[blockIdx.x];
     float *p = y + (size_t)blockIdx.x * S;
-    const int end = min(S, (int)(blockIdx.y + 1) * APPLY_CHUNK);
-    for (int i = blockIdx.y * APPLY_CHUNK + threadIdx.x; i < end; i += GT) p[i] = fmaf(p[i], sc[0], sc[1]);
+    const int lo = blockIdx.y * APPLY_CHUNK, hi = min(S, lo + APPLY_CHUNK);
+    if ((S & 3) == 0) {
+        v4f *q = reinterpret_cast<v4f *>(p);
+        for (int i = lo / 4 + threadIdx.x; i < hi / 4; i += GT) {
+            v4f v = q[i];
+            v[0] = fmaf(v[0], sc[0], sc[1]); v[1] = fmaf(v[1], sc[0], sc[1]);
+            v[2] = fmaf(v[2], sc[0], sc[1]); v[3] = fmaf(v[3], sc[0], sc[1]);
+            q[i] = v;
+        }
+    } else {
+        for (int i = lo + threadIdx.x; i < hi; i += GT) p[i] = fmaf(p[i], sc[0], sc[1]);
+    }
 }
 
 // One floor-mode max-pool pass over [N*C][Di][Hi][Wi] with kernel = stride =
@@ -364,9 +538,18 @@ __global__ __launch_bounds__(GT) void gen_pool_kernel(const float *in, const int
     if (out_idx) out_idx[i] = best_i;
 }
 
+int blocks_per_wave(int Cgo) {
+    const int cob = (Cgo + 15) / 16;
+    return cob >= 4 ? 4 : cob >= 2 ? 2 : 1;
+}
+
 struct GenLayout {
     bool stats, stage, softmax, finalize, apply;
-    int T;
+    int nph, Tq, CT;  // conv phases (z, y), tiles per phase, column tiles per row
+    int ROWS;         // rows per tile: 1 (64 columns) or 4 (16 columns)
+    int NB, cobN, P, KPG, GTn, steps;
+    size_t off_wp, wp_elems;
+    int T;            // statistics tiles per (sample, channel)
     size_t off_stage, off_part, off_ss, off_pv[2], off_pi[2], total;
     long long pool1;  // elements after the first pool pass
 };
@@ -381,8 +564,36 @@ void layout(const GenericArgs &a, GenLayout &L) {
     L.stage = a.reduce == 2 || (a.reduce == 1 && L.softmax);
     L.finalize = L.stats;
     L.apply = a.reduce == 0 && a.norm_groups > 0;
-    L.T = (int)((S + PTILE - 1) / PTILE);
+    // A transposed conv visits its outputs in stride^ndim phases (see
+    // gen_conv_kernel); each phase gets as many tiles as the largest needs.
+    // Tiles are ROWS rows (over z, y) x 64/ROWS columns; a transposed conv's
+    // rows are split into sd*sh phases (the largest phase has the most rows).
+    L.nph = 1;
+    long long Qzy = (long long)a.Do * a.Ho;
+    if (a.transposed) {
+        L.nph = a.sd * a.sh;
+        Qzy = (long long)((a.Do + a.sd - 1) / a.sd) * ((a.Ho + a.sh - 1) / a.sh);
+    }
+    L.ROWS = a.Wo >= 48 ? 1 : 4;
+    const int tw = PTILE / L.ROWS;
+    L.CT = (a.Wo + tw - 1) / tw;
+    L.Tq = (int)((Qzy + L.ROWS - 1) / L.ROWS) * L.CT;
+    // the softmax pass writes the statistics over contiguous positions instead
+    L.T = L.softmax ? (int)((S + PTILE - 1) / PTILE) : L.nph * L.Tq;
+    const int Cgi = a.C_in / a.groups, Cgo = a.C_out / a.groups;
+    // Groups of at most 8 output channels share a 16-row tile, P per tile.
+    int pw2 = 1;
+    while (pw2 < Cgo) pw2 <<= 1;
+    L.P = (Cgo <= 8 && a.groups >= 2) ? (16 / pw2 < 4 ? 16 / pw2 : 4) : 1;
+    L.KPG = 4 / L.P;
+    L.GTn = (a.groups + L.P - 1) / L.P;
+    L.steps = (Cgi + L.KPG - 1) / L.KPG;
+    L.NB = L.P > 1 ? 1 : blocks_per_wave(Cgo);
+    L.cobN = L.P > 1 ? 1 : ((Cgo + 15) / 16 + L.NB - 1) / L.NB;
+    L.wp_elems = (size_t)L.GTn * a.kd * a.kh * a.kw * 4 * L.steps * L.cobN * 16 * L.NB;
     size_t off = 0;
+    L.off_wp = off;
+    off = align256(off + L.wp_elems * 4);
     L.off_stage = off;
     if (L.stage) off = align256(off + (size_t)NC * S * 4);
     L.off_part = off;
@@ -403,10 +614,19 @@ void layout(const GenericArgs &a, GenLayout &L) {
     L.total = off;
 }
 
+template <int ACT, bool TR, int ROWS>
+void launch_conv_rows(const GenConv &g, int NB, dim3 grid, hipStream_t st) {
+    if (NB == 4) gen_conv_kernel<ACT, TR, 4, ROWS><<<grid, dim3(GT), 0, st>>>(g);
+    else if (NB == 2) gen_conv_kernel<ACT, TR, 2, ROWS><<<grid, dim3(GT), 0, st>>>(g);
+    else gen_conv_kernel<ACT, TR, 1, ROWS><<<grid, dim3(GT), 0, st>>>(g);
+}
+
 template <int ACT, bool TR>
-hipError_t launch_conv(const GenConv &g, hipStream_t st) {
-    const long long blocks = (g.tasks + 3) / 4;
-    gen_conv_kernel<ACT, TR><<<dim3((unsigned)blocks), dim3(GT), 0, st>>>(g);
+hipError_t launch_conv(const GenConv &g, int NB, int ROWS, hipStream_t st) {
+    const long long waves = ((long long)g.tasks + g.tpw - 1) / g.tpw;
+    const dim3 grid((unsigned)((waves + 3) / 4));
+    if (ROWS == 1) launch_conv_rows<ACT, TR, 1>(g, NB, grid, st);
+    else launch_conv_rows<ACT, TR, 4>(g, NB, grid, st);
     return hipGetLastError();
 }
 
@@ -434,9 +654,10 @@ bool generic_supported(const GenericArgs &a) {
     if (a.reduce == 2 && (long long)a.pool_kernel * a.pool_kernel * a.pool_kernel > (1 << 20)) return false;
     // launch grids: the apply kernel's chunk axis, and 32-bit block counts
     if (S >= (1LL << 27)) return false;
-    const long long T = (S + PTILE - 1) / PTILE;
-    const long long cob = (Cgo + 15) / 16;
-    if ((long long)a.N * T * a.groups * cob / 4 >= (1LL << 31) - 1) return false;
+    GenLayout L;
+    layout(a, L);
+    if ((long long)a.N * L.nph * L.Tq * L.GTn * L.cobN >= (1LL << 31) - 64) return false;
+    if (L.wp_elems * 4 >= RES_MAX) return false;
     if ((long long)a.N * a.C_out * S / GT >= (1LL << 31) - 1) return false;
     return true;
 }
@@ -460,27 +681,51 @@ hipError_t launch_generic(const GenericArgs &a, hipStream_t st) {
 
     // 1. conv (+ bias + elementwise activation)
     GenConv g{};
-    g.x = a.x; g.w = a.w; g.b = a.b;
+    g.x = a.x; g.b = a.b;
+    float *wp = reinterpret_cast<float *>(ws + L.off_wp);
+    g.wp = wp;
+    g.wp_elems = (unsigned)L.wp_elems;
+    g.P = L.P; g.RPG = 16 / L.P; g.KPG = L.KPG; g.GTn = L.GTn; g.steps = L.steps;
+    g.KP = 4 * L.steps;
     g.y = y;
     g.part = L.softmax ? nullptr : part;
     g.C_in = a.C_in; g.C_out = a.C_out; g.G = a.groups;
     g.Cgi = a.C_in / a.groups; g.Cgo = a.C_out / a.groups;
-    g.cob = (g.Cgo + 15) / 16;
+    const int NB = L.NB;
+    g.cobN = L.cobN;
     g.T = L.T;
-    g.tasks = (long long)a.N * L.T * a.groups * g.cob;
+    g.Tq = L.Tq;
+    g.CT = L.CT;
+    g.tasks = (int)((long long)a.N * L.nph * L.Tq * L.GTn * g.cobN);
     g.D = a.D; g.H = a.H; g.W = a.W; g.Do = a.Do; g.Ho = a.Ho; g.Wo = a.Wo; g.S = S;
     g.kd = a.kd; g.kh = a.kh; g.kw = a.kw;
     g.sd = a.sd; g.sh = a.sh; g.sw = a.sw; g.pd = a.pd; g.ph = a.ph; g.pw = a.pw;
     g.dd = a.dd; g.dh = a.dh; g.dw = a.dw;
-    g.rsd = 1.0f / a.sd; g.rsh = 1.0f / a.sh; g.rsw = 1.0f / a.sw;
     g.in_plane = (unsigned)a.D * a.H * a.W;
-    const unsigned taps = (unsigned)a.kd * a.kh * a.kw;
-    g.w_elems = a.transposed ? (unsigned)a.C_in * g.Cgo * taps : (unsigned)a.C_out * g.Cgi * taps;
+    {
+        // ~256 MFMAs per wave, but at least 16K waves in flight
+        const double taps_issued = (double)a.kd * a.kh * a.kw / L.nph;  // x taps all issued
+        const double mfma = taps_issued * L.steps * 4.0 * NB;
+        long long tpw = (long long)(256.0 / (mfma > 1.0 ? mfma : 1.0));
+        const long long cap = g.tasks / 16384;
+        if (tpw > cap) tpw = cap;
+        g.tpw = (int)(tpw < 1 ? 1 : tpw > 64 ? 64 : tpw);
+    }
+    {
+        const unsigned total = (unsigned)L.wp_elems;
+        gen_weight_pack_kernel<<<dim3((total + GT - 1) / GT), dim3(GT), 0, st>>>(
+            a.w, wp, a.groups, g.Cgi, g.Cgo, a.kd * a.kh * a.kw, L.steps, L.P, L.cobN, NB,
+            a.transposed, total);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     // the conv writes the final values when nothing follows but the divide
     g.out_scale = (!L.softmax && a.norm_groups == 0 && a.reduce == 0) ? a.inv_div : 1.0f;
     const int act = L.softmax ? ACT_NONE : a.act;
 #define CNF_GEN_CASE(A)                                                             \
-    case A: e = a.transposed ? launch_conv<A, true>(g, st) : launch_conv<A, false>(g, st); break;
+    case A:                                                                         \
+        e = a.transposed ? launch_conv<A, true>(g, NB, L.ROWS, st)                  \
+                         : launch_conv<A, false>(g, NB, L.ROWS, st);                \
+        break;
     switch (act) {
         CNF_GEN_CASE(ACT_NONE)
         CNF_GEN_CASE(ACT_HARDSWISH)

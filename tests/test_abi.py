@@ -45,6 +45,8 @@ def test_every_workload_plans_with_expected_shape(name):
         "conv2d_in_div_n128": (128, 128, 126, 126),
         "convt2d_gelu_gn_n128": (128, 64, 258, 258),
         "convt2d_dense_gelu_gn_n128": (128, 64, 258, 258),
+        "conv2d_s2p1_in_div_n128": (128, 128, 64, 64),
+        "convt2d_s2_gelu_gn_n128": (128, 64, 256, 256),
     }[name]
     assert plan.out_shape == exp
     assert "family=" in plan.describe()
@@ -187,8 +189,10 @@ def test_general_geometry_output_shapes(name, over, shape):
 
 def test_family_routing():
     # the page configurations keep their specialised families ...
-    fams = {n: cnf.Plan(_desc(n)).describe().split()[0] for n in cnf_inputs.WORKLOAD_ORDER}
+    fams = {n: cnf.Plan(_desc(n)).describe().split()[0] for n in cnf_inputs.PAGE_WORKLOADS}
     assert not any("generic" in f for f in fams.values()), fams
+    for n in set(cnf_inputs.WORKLOAD_ORDER) - set(cnf_inputs.PAGE_WORKLOADS):
+        assert "family=generic" in cnf.Plan(_desc(n)).describe(), n
     # ... and CNF_FORCE_GENERIC=1 sends them to the general one
     os.environ["CNF_FORCE_GENERIC"] = "1"
     try:
@@ -203,21 +207,43 @@ def _align(v):
     return (v + 255) // 256 * 256
 
 
+def _packed_weights(G, taps, Cgi, Cgo):
+    # [group tiles][taps][K steps x 4][channel blocks of 16, NB per wave] floats;
+    # groups of at most 8 output channels go P to a tile, 4/P K entries each
+    pw2 = 1
+    while pw2 < Cgo:
+        pw2 *= 2
+    P = min(4, 16 // pw2) if (Cgo <= 8 and G >= 2) else 1
+    steps = -(-Cgi // (4 // P))
+    cob = (Cgo + 15) // 16
+    NB = 1 if P > 1 else 4 if cob >= 4 else 2 if cob >= 2 else 1
+    cobN = 1 if P > 1 else (cob + NB - 1) // NB
+    return _align(-(-G // P) * taps * 4 * steps * cobN * 16 * NB * 4)
+
+
 def test_general_workspace_layout_sizes():
-    # InstanceNorm, no reduction: per-tile triples (16 B) + per-channel scale/shift (8 B)
+    # InstanceNorm, no reduction: packed weights, per-tile triples (16 B),
+    # per-channel scale/shift (8 B)
     p = cnf.Plan(_desc("conv2d_in_div_n128", stride=2, padding=1))
     S = 64 * 64
     T = (S + 63) // 64
-    assert p.workspace_bytes == _align(128 * 128 * T * 16) + _align(128 * 128 * 8)
-    # plain conv, nothing after it: no workspace
+    assert p.workspace_bytes == (_packed_weights(1, 9, 64, 128) + _align(128 * 128 * T * 16)
+                                 + _align(128 * 128 * 8))
+    # plain conv, nothing after it: the packed weights only
     p = cnf.Plan(_desc("conv2d_in_div_n2", stride=2, norm="none", divide_by=1.0))
-    assert p.workspace_bytes == 0
+    assert p.workspace_bytes == _packed_weights(1, 9, 8, 16)
     # softmax + two 2-pools with argmax: staged conv output, then two ping-pong
     # value + index buffers of the first pool's size
     p = cnf.Plan(_desc("conv3d_softmax_pool_n128", padding=1))
     S = 16 * 32 * 32
     pool1 = 128 * 16 * 8 * 16 * 16
-    assert p.workspace_bytes == _align(128 * 16 * S * 4) + 4 * _align(pool1 * 4)
+    assert p.workspace_bytes == (_packed_weights(1, 27, 3, 16) + _align(128 * 16 * S * 4)
+                                 + 4 * _align(pool1 * 4))
+    # strided transposed conv: stride^2 phases of ceil(256/2)^2 positions each
+    p = cnf.Plan(_desc("convt2d_s2_gelu_gn_n128"))
+    T = 4 * (128 * 128 // 64)
+    assert p.workspace_bytes == (_packed_weights(8, 9, 8, 8) + _align(128 * 64 * T * 16)
+                                 + _align(128 * 64 * 8))
 
 
 def test_descriptor_layout_matches_the_c_header(tmp_path):

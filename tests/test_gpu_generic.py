@@ -103,6 +103,24 @@ GENERAL_CASES = [
     ("convt2d_gelu_gn_n128", dict(N=1, C_in=8, C_out=8, groups=1, in_dims=(1, 10, 11), stride=2,
                                   num_groups=1, reduce="maxpool", pool_kernel=2, pool_repeats=2,
                                   want_argmax=1)),
+    # phases of unequal size (output extents not multiples of the stride), 3-D dilated
+    ("convt2d_gelu_gn_n128", dict(N=1, in_dims=(1, 7, 9), stride=3, padding=2, output_padding=1)),
+    ("convt2d_gelu_gn_n128", dict(N=1, ndim=3, C_in=8, C_out=8, groups=1, num_groups=2,
+                                  in_dims=(3, 4, 5), stride=2, dilation=2, output_padding=1)),
+    # wide outputs (one-row, 64-column tiles) with ragged last column tiles
+    ("convt2d_s2_gelu_gn_n128", dict(N=2, in_dims=(1, 9, 30))),
+    ("convt2d_s2_gelu_gn_n128", dict(N=1, C_in=8, C_out=8, groups=1, num_groups=2,
+                                     in_dims=(1, 5, 40), stride=3, output_padding=2)),
+    ("conv2d_s2p1_in_div_n128", dict(N=2, C_in=12, in_dims=(1, 7, 130))),
+    # several conv groups per 16-row MFMA tile (block-diagonal weights): 3 channels
+    # per group with 3 groups, depthwise with 5 groups (last tile partly empty),
+    # a transposed conv with 7 groups of 1 output channel
+    ("conv2d_in_div_n2", dict(N=2, C_in=9, C_out=9, groups=3, in_dims=(1, 11, 13), padding=1,
+                              norm="group", num_groups=3, affine=1)),
+    ("conv2d_in_div_n2", dict(N=2, C_in=5, C_out=5, groups=5, in_dims=(1, 12, 50), stride=2,
+                              norm="none", divide_by=1.0, act="hardswish")),
+    ("convt2d_gelu_gn_n128", dict(N=2, C_in=14, C_out=7, groups=7, num_groups=7,
+                                  in_dims=(1, 6, 9), stride=2)),
     # stride-1 page shapes through non-default padding (the specialised families decline)
     ("convt2d_gelu_gn_n128", dict(N=1, in_dims=(1, 20, 30), padding=1)),
     ("conv2d_in_div_n128", dict(N=1, C_in=16, in_dims=(1, 25, 40), padding=1)),

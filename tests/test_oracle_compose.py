@@ -40,8 +40,25 @@ def _convt_numpy(x, w, b, G):
     return y
 
 
-def _reference_numpy(wl, x, p):
+def _conv_torch(wl, x, p):
+    # strided / padded / dilated geometry: torch's float64 CPU routines
+    import torch
+    import torch.nn.functional as F
+    t = lambda a: None if a is None else torch.from_numpy(a.astype(np.float64))  # noqa: E731
+    geo = dict(stride=wl["stride"], padding=wl["padding"], dilation=wl["dilation"],
+               groups=wl["groups"])
+    nd = wl["ndim"]
     if wl["kind"] == "conv_transpose":
+        fn = F.conv_transpose2d if nd == 2 else F.conv_transpose3d
+        return fn(t(x), t(p["w"]), t(p["b"]), output_padding=wl["output_padding"], **geo).numpy()
+    fn = F.conv2d if nd == 2 else F.conv3d
+    return fn(t(x), t(p["w"]), t(p["b"]), **geo).numpy()
+
+
+def _reference_numpy(wl, x, p):
+    if (wl["stride"], wl["padding"], wl["dilation"], wl["output_padding"]) != (1, 0, 1, 0):
+        y = _conv_torch(wl, x, p)
+    elif wl["kind"] == "conv_transpose":
         y = _convt_numpy(x, p["w"], p["b"], wl["groups"])
     else:
         y = _conv_numpy(x, p["w"], p["b"], wl["groups"])
@@ -82,6 +99,8 @@ SMALL = {
     "convt2d_gelu_gn_n128": dict(N=2, C_in=16, C_out=16, in_dims=(1, 9, 10), groups=8,
                                  num_groups=8),
     "convt2d_dense_gelu_gn_n128": dict(N=2, C_in=6, C_out=8, in_dims=(1, 7, 9), num_groups=4),
+    "conv2d_s2p1_in_div_n128": dict(N=1, C_in=8, C_out=16, in_dims=(1, 13, 12)),
+    "convt2d_s2_gelu_gn_n128": dict(N=2, C_in=16, C_out=16, in_dims=(1, 6, 7)),
 }
 
 

@@ -46,8 +46,8 @@ DOMINANT = {
     "conv2d_in_div_n128": ("conv2d_igemm_kernel<128", "mfma"),
     "convt2d_gelu_gn_n128": ("convt2d_gn_fused_kernel", "mfma"),
     "convt2d_dense_gelu_gn_n128": ("conv2d_igemm_kernel<64", "mfma"),
-    "conv2d_s2p1_in_div_n128": ("gen_conv_kernel<0, false>", "mfma"),
-    "convt2d_s2_gelu_gn_n128": ("gen_conv_kernel<2, true>", "mfma"),
+    "conv2d_s2p1_in_div_n128": ("gen_conv_kernel<0, false,", "mfma"),
+    "convt2d_s2_gelu_gn_n128": ("gen_conv_kernel<2, true,", "mfma"),
 }
 
 

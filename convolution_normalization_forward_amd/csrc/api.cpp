@@ -47,6 +47,7 @@ struct cnf_plan {
     int64_t dims[5];
     int32_t rank;
     size_t workspace;
+    int igemm_pad;      // zero padding the implicit GEMM applies to the input
 };
 
 namespace {
@@ -191,10 +192,22 @@ cnf_status cnf_plan_create(const cnf_desc *desc, cnf_plan **plan)
     // CNF_FORCE_GENERIC environment variable (tests) sends everything to the
     // general family.
     const char *force = std::getenv("CNF_FORCE_GENERIC");
-    const bool basic = d.stride == 1 && d.padding == 0 && d.dilation == 1 &&
-                       d.output_padding == 0 && !(force && force[0] == '1');
+    const bool unit = d.stride == 1 && d.dilation == 1 && d.output_padding == 0 &&
+                      !(force && force[0] == '1');
+    const bool basic = unit && d.padding == 0;
+    p.igemm_pad = d.kind == CNF_CONV_TRANSPOSE ? k - 1 : 0;
     if (!basic) {
-        // no specialised family
+        // Stride-1, dilation-1 2-D convs with padding up to k - 1 are the implicit
+        // GEMM with that padding; a dense transposed conv with padding p is the
+        // GEMM of the flipped kernel with padding k - 1 - p.
+        const int gp = d.kind == CNF_CONV ? d.padding : k - 1 - d.padding;
+        if (unit && d.ndim == 2 && d.groups == 1 && d.reduce == CNF_RED_NONE &&
+            d.padding <= k - 1 &&
+            cnf::conv2d_igemm_supported(d.C_in, d.C_out, k, d.groups, H + 2 * gp, W + 2 * gp,
+                                        d.act)) {
+            p.family = FAM_IGEMM;
+            p.igemm_pad = gp;
+        }
     } else if (d.kind == CNF_CONV && d.groups == 1) {
         if (d.ndim == 3 && d.reduce == CNF_RED_MEAN_SPATIAL && d.act != CNF_ACT_SOFTMAX_CHANNEL &&
             cnf::conv3d_gn_mean_supported(d.C_in, d.C_out, k, D, H, W, d.act))
@@ -332,7 +345,7 @@ cnf_status cnf_forward(const cnf_plan *plan, const float *x, const float *w, con
     case FAM_IGEMM: {
         const int tr = d.kind == CNF_CONV_TRANSPOSE;
         cnf::Conv2dIgemmArgs a{x, w, b, gamma, beta, out, static_cast<float *>(workspace), d.N,
-                               d.C_in, d.C_out, H, W, plan->Ho, plan->Wo, tr ? d.kernel - 1 : 0, tr,
+                               d.C_in, d.C_out, H, W, plan->Ho, plan->Wo, plan->igemm_pad, tr,
                                d.act, norm_groups, d.eps, inv_div};
         e = cnf::launch_conv2d_igemm(a, st);
         break;

@@ -187,6 +187,19 @@ def test_general_geometry_output_shapes(name, over, shape):
     assert "family=generic" in plan.describe()
 
 
+def test_padded_stride1_convs_use_the_implicit_gemm():
+    for name, over, shape in [("conv2d_in_div_n128", dict(padding=1), (128, 128, 128, 128)),
+                              ("conv2d_in_div_n128", dict(padding=2), (128, 128, 130, 130)),
+                              ("convt2d_dense_gelu_gn_n128", dict(padding=1), (128, 64, 256, 256)),
+                              ("convt2d_dense_gelu_gn_n128", dict(padding=2), (128, 64, 254, 254))]:
+        plan = cnf.Plan(_desc(name, **over))
+        assert "conv2d_igemm" in plan.describe(), (name, over)
+        assert plan.out_shape == shape
+    # beyond k - 1, or strided / dilated: the general family
+    for over in (dict(padding=3), dict(padding=1, dilation=2), dict(padding=1, stride=2)):
+        assert "family=generic" in cnf.Plan(_desc("conv2d_in_div_n128", **over)).describe(), over
+
+
 def test_family_routing():
     # the page configurations keep their specialised families ...
     fams = {n: cnf.Plan(_desc(n)).describe().split()[0] for n in cnf_inputs.PAGE_WORKLOADS}

@@ -107,6 +107,14 @@ SMALL_CASES = [
     ("convt2d_dense_gelu_gn_n128", dict(N=2, C_in=16, C_out=128, in_dims=(1, 14, 61),
                                         norm="instance", act="gelu_tanh")),
     ("convt2d_dense_gelu_gn_n128", dict(N=1, C_in=64, in_dims=(1, 33, 66))),
+    # zero-padded stride-1 convs ("same" padding) and padded dense transposed convs on
+    # the implicit GEMM
+    ("conv2d_in_div_n128", dict(N=2, C_in=8, in_dims=(1, 20, 70), padding=1)),
+    ("conv2d_in_div_n128", dict(N=1, C_in=12, C_out=64, in_dims=(1, 9, 33), padding=2,
+                                act="gelu", norm="group", num_groups=8, affine=1)),
+    ("convt2d_dense_gelu_gn_n128", dict(N=2, C_in=8, in_dims=(1, 11, 19), padding=1)),
+    ("convt2d_dense_gelu_gn_n128", dict(N=1, C_in=8, C_out=128, in_dims=(1, 12, 40), padding=2,
+                                        norm="instance")),
 ]
 
 

@@ -8,7 +8,10 @@ is already resident in device memory.  The headline workload is the Conv3d
 listed under "per_workload" in the same JSON line.
 
 Metric: effective TFLOP/s = 2 * N * C_out * |conv output grid| * (C_in/groups)
-* k^ndim / time (the nominal conv FLOPs), plus ms per step.  "roofline" puts
+* k^ndim / time (the nominal conv FLOPs), plus ms per step.  `value` and
+`ms_per_step` time K back-to-back steps (inputs resident; whatever the 256 MB
+MALL keeps between steps); each workload also reports cold single steps
+(ms_cold_*), each after a 512 MB write that evicts L2 and MALL.  "roofline" puts
 the dominant kernel's ALGORITHMIC work per launch against the MI355X peak of
 the unit that bounds it, timed with HIP events on the launch stream.
 "cpu_baseline" is the fp64 oracle timed on the host cores on a bounded sample.
@@ -127,7 +130,7 @@ def load_traffic(name):
     return e.get("hbm_bytes_per_launch")
 
 
-def time_workload(name, steps, warmup, dev):
+def time_workload(name, steps, warmup, dev, flush=None, cold_reps=10):
     import numpy as np
     import torch
 
@@ -174,6 +177,19 @@ def time_workload(name, steps, warmup, dev):
         b.record(stream)
     torch.cuda.synchronize()
     per = np.array([a.elapsed_time(b) for a, b in ev])
+    # cold steps: before each, overwrite a buffer larger than the MALL (256 MB) so
+    # no input, weight or output line is left in L2 / MALL; then time one step
+    cold = []
+    if flush is not None:
+        for i in range(cold_reps):
+            flush.fill_(float(i))
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            step()
+            b.record(stream)
+            b.synchronize()
+            cold.append(a.elapsed_time(b))
+    cold = np.array(cold) if cold else None
     fl = nominal_flops(wl)
     afl = algorithmic_flops(wl)
     ab = algorithmic_bytes(wl)
@@ -185,6 +201,8 @@ def time_workload(name, steps, warmup, dev):
         "ms_single_launch_mean": float(per.mean()),
         "ms_single_launch_min": float(per.min()),
         "ms_wall_per_step": wall * 1e3 / steps,
+        "ms_cold_median": float(np.median(cold)) if cold is not None else None,
+        "ms_cold_min": float(cold.min()) if cold is not None else None,
         "effective_tflops": fl / (ms * 1e-3) / 1e12,
         "nominal_gflop": fl / 1e9,
         "algorithmic_gflop": afl / 1e9,
@@ -219,6 +237,14 @@ def cpu_baseline(name, seconds):
         if el >= seconds:
             break
     fl = nominal_flops(wl_n) * done
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")),
+                         None)
+    except OSError:
+        pass
+    per_sample = el / (done * n)
     return {
         "value": fl / el / 1e12,
         "unit": "TFLOP/s",
@@ -226,7 +252,10 @@ def cpu_baseline(name, seconds):
         "kind": "oracle",
         "sample": f"fp64 oracle on samples 0..{n - 1} of {name} (full conv grid), "
                   f"{done} passes in {el:.1f} s",
-        "ms_per_sample": el * 1e3 / (done * n),
+        "subset_seconds": el,
+        "ms_per_sample": per_sample * 1e3,
+        "full_batch_seconds_extrapolated": per_sample * wl["N"],
+        "cpu_model": model,
     }
 
 
@@ -268,6 +297,7 @@ def main():
         print(f"[bench] copy calibration: 5 copies of {args.copy_calibration_mib} MiB",
               file=sys.stderr, flush=True)
         del src, dst
+    flush = torch.empty(512 * (1 << 20) // 4, dtype=torch.float32, device=dev)
     names = [args.workload] if args.only else \
         [args.workload] + [n for n in cnf_inputs.WORKLOAD_ORDER if n != args.workload]
     per = {}
@@ -275,7 +305,7 @@ def main():
     for nm in names:
         print(f"[bench] {nm}: timing {args.steps} steps after {args.warmup} warm-up",
               file=sys.stderr, flush=True)
-        wl, r = time_workload(nm, args.steps, args.warmup, dev)
+        wl, r = time_workload(nm, args.steps, args.warmup, dev, flush)
         per[nm] = r
         if nm == args.workload:
             head_wl = wl

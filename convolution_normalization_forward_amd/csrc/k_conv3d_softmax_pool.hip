@@ -16,15 +16,19 @@
 //   * The window's input patch (C_in x (4+k-1)^3) is staged in LDS with row
 //     pitch 8.
 //   * Tile j (j = 0..3) is conv depth 4*od + j: a 16x16 MFMA result with
-//     rows = the 16 positions of the 4x4 (h, w) patch and columns = the 16
-//     output channels (v_mfma_f32_16x16x4f32, K = C_in*k^3 padded to a
-//     multiple of 4 with zero weights).  Weights (B operand) live in registers;
-//     the im2col operand (A) is read from LDS through a per-lane offset table.
-//   * Lane l holds positions (h = l/16, w = r) of channel l%16, so the softmax
-//     over channels is a max and a sum across the 16 lanes of a DPP row.
-//   * The window maximum and its argmax are reduced in-lane over (depth, w),
-//     then across the four rows with lane shuffles.  Ties resolve as the
-//     literal sequence of pools would (first 2x2x2 block in scan order, then
+//     rows = the 16 output channels and columns = the 16 positions of the 4x4
+//     (h, w) patch (v_mfma_f32_16x16x4f32, K = C_in*k^3 padded to a multiple
+//     of 4 with zero weights).  Weights (A operand) live in registers; the
+//     im2col operand (B) is read from LDS through a per-lane offset table.
+//     The accumulator starts at the bias.
+//   * Lane l holds channels 4*(l/16) + r (r = 0..3) of position l%16, so the
+//     softmax over the 16 channels is 3 in-lane steps and two cross-row
+//     exchanges (xor 16, xor 32) per reduction, instead of a 16-lane DPP
+//     reduction per value.  For the softmax, weights and bias carry the factor
+//     log2(e), so each exponential is one exp2 of (logit - max).
+//   * The window maximum of channel c and its argmax are reduced in-lane over
+//     depth, then across the 16 lanes (positions) of the row.  Ties resolve as
+//     the literal sequence of pools would (first 2x2x2 block in scan order, then
 //     first voxel inside it), or in plain row-major order for a single 4-pool.
 #include "device.h"
 #include "kernels.h"
@@ -82,23 +86,31 @@ void conv3d_softmax_pool_kernel(const float *__restrict__ x, const float *__rest
     const int q = lane >> 4, c16 = lane & 15;
     const int HW = H * W;
 
-    // B operand: w[co = l%16][k = 4s + l/16], zero past K.  A operand offset of
-    // tap k in the patch; the four lane rows q take compile-time values.
+    // A operand: w[co = l%16][k = 4s + l/16], zero past K (times log2 e for the
+    // softmax).  B operand offset of tap k in the patch; the four lane rows q
+    // take compile-time values.
+    constexpr float LSCALE = ACT == ACT_SOFTMAX ? 1.4426950408889634f : 1.0f;
     float wreg[G::NS];
     int toff[G::NS];
 #pragma unroll
     for (int s = 0; s < G::NS; ++s) {
         const int k = 4 * s + q;
-        wreg[s] = k < G::K ? w[c16 * G::K + k] : 0.0f;
+        wreg[s] = k < G::K ? w[c16 * G::K + k] * LSCALE : 0.0f;
         const int t0 = G::tap_off(4 * s), t1 = G::tap_off(4 * s + 1);
         const int t2 = G::tap_off(4 * s + 2), t3 = G::tap_off(4 * s + 3);
         toff[s] = q < 2 ? (q == 0 ? t0 : t1) : (q == 2 ? t2 : t3);
     }
-    const float bc = bias ? bias[c16] : 0.0f;
-    // A operand row m = l%16 is patch position (h = m/4, w = m%4)
+    // accumulator rows 4q + r start at their channel's bias
+    v4f bias4;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) bias4[r] = bias ? bias[4 * q + r] * LSCALE : 0.0f;
+    // B operand column m = l%16 is patch position (h = m/4, w = m%4)
     const int lbase = (c16 >> 2) * PP + (c16 & 3);
-    // tie keys of this lane's 16 voxels (j = depth, q = row, r = column)
-    const int kq = TWO ? (((q >> 1) << 4) | ((q & 1) << 1)) : q * 4;
+    // tie key of this lane's position (h, w) = (c16 / 4, c16 % 4); depth j adds
+    // its own bits
+    const int ph = c16 >> 2, pw = c16 & 3;
+    const int kpos = TWO ? (((ph >> 1) << 4) | ((pw >> 1) << 3) | ((ph & 1) << 1) | (pw & 1))
+                         : ((ph << 2) | pw);
 
     // Patch rows (ci, rd, rh) of E floats: a float4 and a TAIL part per row.
     int gro[LSLOTS], lro[LSLOTS];
@@ -170,59 +182,69 @@ void conv3d_softmax_pool_kernel(const float *__restrict__ x, const float *__rest
 
         v4f acc[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < 4; ++j) acc[j] = bias4;
         const float *pb = patch[buf];
 #pragma unroll
         for (int s = 0; s < G::NS; ++s) {
             const int a0 = lbase + toff[s];
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                acc[j] = mfma_16x16x4(pb[a0 + j * G::E * PP], wreg[s], acc[j]);
+                acc[j] = mfma_16x16x4(wreg[s], pb[a0 + j * G::E * PP], acc[j]);
         }
 
-        // activation (softmax over the 16 channels = the 16 lanes of a row)
+        // activation; the softmax at position (j, c16) runs over the lane's 4
+        // channels and the same position in the other three lane rows
         float v[4][4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
+            if constexpr (ACT == ACT_SOFTMAX) {
+                float m = fmaxf(fmaxf(acc[j][0], acc[j][1]), fmaxf(acc[j][2], acc[j][3]));
+                m = fmaxf(m, __shfl_xor(m, 16, 64));
+                m = fmaxf(m, __shfl_xor(m, 32, 64));
+                float e[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float a = acc[j][r] + bc;
-                if constexpr (ACT == ACT_SOFTMAX) {
-                    const float m = row_max16(a);
-                    const float e = __builtin_amdgcn_exp2f((a - m) * 1.4426950408889634f);
-                    const float sum = row_sum16(e);
-                    a = e * __builtin_amdgcn_rcpf(sum);
-                } else {
-                    a = activate<ACT>(a);
-                }
-                v[j][r] = a;
+                for (int r = 0; r < 4; ++r) e[r] = __builtin_amdgcn_exp2f(acc[j][r] - m);
+                float sum = (e[0] + e[1]) + (e[2] + e[3]);
+                sum += __shfl_xor(sum, 16, 64);
+                sum += __shfl_xor(sum, 32, 64);
+                const float inv = __builtin_amdgcn_rcpf(sum);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) v[j][r] = e[r] * inv;
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) v[j][r] = activate<ACT>(acc[j][r]);
             }
         }
-        // window max, then the first voxel (in tie order) that attains it
-        float best = v[0][0];
+        // per channel row 4q + r: window max over depth (in-lane) and the 16
+        // positions (lanes of the row), then the first voxel in tie order
+        float best[4];
+        int bkey[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int r = 0; r < 4; ++r) {
+            float b = fmaxf(fmaxf(v[0][r], v[1][r]), fmaxf(v[2][r], v[3][r]));
+            b = row_max16(b);
+            int k = 1 << 30;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) best = fmaxf(best, v[j][r]);
-        best = fmaxf(best, __shfl_xor(best, 16, 64));
-        best = fmaxf(best, __shfl_xor(best, 32, 64));
-        int bkey = 1 << 30;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int key = TWO ? (kq | ((j >> 1) << 5) | ((r >> 1) << 3) |
-                                       ((j & 1) << 2) | (r & 1))
-                                    : (kq | (j << 4) | r);
-                bkey = (v[j][r] == best) ? min(bkey, key) : bkey;
+            for (int j = 0; j < 4; ++j) {
+                const int key = kpos | (TWO ? (((j >> 1) << 5) | ((j & 1) << 2)) : (j << 4));
+                k = (v[j][r] == b) ? min(k, key) : k;
             }
-        bkey = min(bkey, __shfl_xor(bkey, 16, 64));
-        bkey = min(bkey, __shfl_xor(bkey, 32, 64));
-        if (q == 0) {
+            k = min(k, row_ror_i<8>(k));
+            k = min(k, row_ror_i<4>(k));
+            k = min(k, row_ror_i<2>(k));
+            k = min(k, row_ror_i<1>(k));
+            best[r] = b;
+            bkey[r] = k;
+        }
+        // lanes c16 = 0..3 of row q store channel 4q + c16
+        if (c16 < 4) {
+            const float bv = c16 == 0 ? best[0] : c16 == 1 ? best[1] : c16 == 2 ? best[2] : best[3];
+            const int bk = c16 == 0 ? bkey[0] : c16 == 1 ? bkey[1] : c16 == 2 ? bkey[2] : bkey[3];
             int a, b, c;
-            key_abc(bkey, TWO, a, b, c);
-            const size_t o = (((size_t)n * 16 + c16) * Dp + od) * Hp * Wp + (size_t)oh * Wp + ow;
-            out[o] = best;
+            key_abc(bk, TWO, a, b, c);
+            const size_t o = (((size_t)n * 16 + 4 * q + c16) * Dp + od) * Hp * Wp +
+                             (size_t)oh * Wp + ow;
+            out[o] = bv;
             if (argmax)
                 argmax[o] = ((4 * od + a) * Ho + (4 * oh + b)) * Wo + (4 * ow + c);
         }

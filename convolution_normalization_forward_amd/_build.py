@@ -32,7 +32,7 @@ FLAGS = [
 # Extra flags per source.  The softmax-pool kernel's inputs and intermediates are
 # finite (softmax of finite logits), so NaN-aware min/max is not needed there and
 # the DPP row reductions fold into single v_max_f32_dpp / v_add_f32_dpp ops.
-FILE_FLAGS = {"k_conv3d_softmax_pool.hip": ["-fno-honor-nans"],
+FILE_FLAGS = {"k_conv3d_softmax_pool.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
               # the general conv's accumulators are loop-carried VGPRs; the default
               # heuristic put the MFMAs on AGPRs and copied every accumulator both
               # ways around each group of MFMAs

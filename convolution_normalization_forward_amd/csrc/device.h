@@ -85,6 +85,19 @@ template <int N>
 __device__ __forceinline__ int row_ror_i(int v) {
     return __builtin_amdgcn_mov_dpp(v, 0x120 + N, 0xf, 0xf, false);
 }
+// Every lane of a 16-lane row gets the row's minimum (int).  bound_ctrl is set,
+// as in row_ror, so each rotation folds into v_min_i32 as a DPP operand.
+template <int N>
+__device__ __forceinline__ int row_ror_ib(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, 0x120 + N, 0xf, 0xf, true);
+}
+__device__ __forceinline__ int row_min16_i(int v) {
+    v = min(v, row_ror_ib<8>(v));
+    v = min(v, row_ror_ib<4>(v));
+    v = min(v, row_ror_ib<2>(v));
+    v = min(v, row_ror_ib<1>(v));
+    return v;
+}
 
 // Every lane of a 16-lane row gets the row's max / sum.
 __device__ __forceinline__ float row_max16(float v) {

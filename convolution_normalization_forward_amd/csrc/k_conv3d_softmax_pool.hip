@@ -30,6 +30,8 @@
 //     depth, then across the 16 lanes (positions) of the row.  Ties resolve as
 //     the literal sequence of pools would (first 2x2x2 block in scan order, then
 //     first voxel inside it), or in plain row-major order for a single 4-pool.
+#include <type_traits>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -172,18 +174,20 @@ void conv3d_softmax_pool_kernel(const float *__restrict__ x, const float *__rest
     if (first >= hi) return;
     CNF_FETCH(window_base(first, n, od, oh, ow))
     CNF_STASH(0)
-    int buf = 0;
-    for (int win = first; win < hi; win += stride) {  // wave-uniform
+    // One window on patch buffer BUF (a compile-time constant, so every LDS
+    // operand address is a per-lane base plus an immediate offset).
+    auto window = [&](int win, auto bufc) {
+        constexpr int BUF = decltype(bufc)::value;
         int nn, od2, oh2, ow2;
         const bool more = win + stride < hi;
         window_base(win, n, od, oh, ow);
         if (more) CNF_FETCH(window_base(win + stride, nn, od2, oh2, ow2))
-        __syncthreads();  // patch[buf] is complete
+        __syncthreads();  // patch[BUF] is complete
 
         v4f acc[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[j] = bias4;
-        const float *pb = patch[buf];
+        const float *pb = patch[BUF];
 #pragma unroll
         for (int s = 0; s < G::NS; ++s) {
             const int a0 = lbase + toff[s];
@@ -223,16 +227,14 @@ void conv3d_softmax_pool_kernel(const float *__restrict__ x, const float *__rest
         for (int r = 0; r < 4; ++r) {
             float b = fmaxf(fmaxf(v[0][r], v[1][r]), fmaxf(v[2][r], v[3][r]));
             b = row_max16(b);
+            // keys grow with depth j: the first depth holding the max wins in-lane
             int k = 1 << 30;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 3; j >= 0; --j) {
                 const int key = kpos | (TWO ? (((j >> 1) << 5) | ((j & 1) << 2)) : (j << 4));
-                k = (v[j][r] == b) ? min(k, key) : k;
+                k = (v[j][r] == b) ? key : k;
             }
-            k = min(k, row_ror_i<8>(k));
-            k = min(k, row_ror_i<4>(k));
-            k = min(k, row_ror_i<2>(k));
-            k = min(k, row_ror_i<1>(k));
+            k = row_min16_i(k);
             best[r] = b;
             bkey[r] = k;
         }
@@ -248,8 +250,14 @@ void conv3d_softmax_pool_kernel(const float *__restrict__ x, const float *__rest
             if (argmax)
                 argmax[o] = ((4 * od + a) * Ho + (4 * oh + b)) * Wo + (4 * ow + c);
         }
-        if (more) CNF_STASH(buf ^ 1)  // buf^1 was last read in the previous iteration
-        buf ^= 1;
+        if (more) CNF_STASH(BUF ^ 1)  // BUF^1 was last read in the previous window
+    };
+    for (int win = first; win < hi;) {  // wave-uniform
+        window(win, std::integral_constant<int, 0>{});
+        win += stride;
+        if (win >= hi) break;
+        window(win, std::integral_constant<int, 1>{});
+        win += stride;
     }
 #undef CNF_FETCH
 #undef CNF_STASH

@@ -42,6 +42,9 @@
  *   - cnf_forward is asynchronous on `stream` (a hipStream_t; NULL is the
  *     null stream).  Calls on different streams may run concurrently if each
  *     has its own workspace and output.
+ *   - Inputs and parameters must be finite: padded contraction entries and
+ *     conv groups that share a matrix tile multiply zero weights by real
+ *     inputs, so an Inf or NaN may reach outputs outside its receptive field.
  */
 #ifndef CNF_H_
 #define CNF_H_

@@ -31,6 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_FP32_TFLOPS = 157.3     # MI355X dense fp32 (MFMA and packed vector)
+PEAK_MFMA_TFLOPS = {"f32": 157.3, "bf16": 2500.0, "f16": 2500.0}  # dense MFMA per input type
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 HEADLINE = "conv3d_softmax_pool_n128"
 
@@ -49,8 +50,10 @@ DOMINANT = {
     "conv2d_in_div_n128": ("conv2d_igemm_kernel<128", "mfma"),
     "convt2d_gelu_gn_n128": ("convt2d_gn_fused_kernel", "mfma"),
     "convt2d_dense_gelu_gn_n128": ("conv2d_igemm_kernel<64", "mfma"),
-    "conv2d_s2p1_in_div_n128": ("gen_conv_kernel<0, false,", "mfma"),
-    "convt2d_s2_gelu_gn_n128": ("gen_conv_kernel<2, true,", "mfma"),
+    "conv2d_s2p1_in_div_n128": ("gen_conv_kernel<false, 4, 1, 0>", "mfma"),
+    "convt2d_s2_gelu_gn_n128": ("gen_conv_kernel<true, 1, 1, 0>", "mfma"),
+    "conv2d_in_div_n128_bf16": ("gen_conv_kernel<false, 4, 1, 1>", "mfma"),
+    "convt2d_gelu_gn_n128_bf16": ("gen_conv_kernel<true, 1, 1, 1>", "mfma"),
 }
 
 
@@ -140,8 +143,10 @@ def time_workload(name, steps, warmup, dev, flush=None, cold_reps=10):
     wl = cnf_inputs.workload(name)
     plan = cnf.Plan(cnf.make_desc(wl))
     p = cnf_inputs.gen_params(wl)
-    x = torch.from_numpy(cnf_inputs.gen_x(wl)).to(dev)
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[wl.get("dtype", "f32")]
+    x = torch.from_numpy(cnf_inputs.gen_x(wl)).to(dev).to(dt)
     t = {k: (torch.from_numpy(v).to(dev) if v is not None else None) for k, v in p.items()}
+    t["w"] = t["w"].to(dt)
     out, idx, ws = plan.allocate(dev)
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
@@ -208,7 +213,9 @@ def time_workload(name, steps, warmup, dev, flush=None, cold_reps=10):
         "algorithmic_gflop": afl / 1e9,
         "algorithmic_gb": ab / 1e9,
         "frac_fp32_peak": fl / (ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS,
+        "frac_mfma_peak_own_dtype": fl / (ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS[wl.get("dtype", "f32")],
         "frac_hbm_peak_algorithmic": ab / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "dtype": wl.get("dtype", "f32"),
         "dominant_kernel": kern,
         "bound": bound,
     }

@@ -26,12 +26,20 @@ Workloads (shapes and options as the four source pages state their problems):
                           l2_p17's chain with a strided, padded conv: Conv2d
                           64->128 k3 stride 2 padding 1 on 128x64x128x128
                           (-> 64x64), InstanceNorm2d, /2.
+  * conv2d_in_div_n128_bf16, convt2d_gelu_gn_n128_bf16
+                          the l2_p17 and l2_p19 problems with x and w in bf16
+                          (fp32 accumulation and epilogue).
   * convt2d_s2_gelu_gn_n128
                           l2_p19's chain as an upsampling layer:
                           ConvTranspose2d 64->64 k3 stride 2 padding 1
                           output_padding 1 groups 8 on 128x64x128x128
                           (-> 256x256, the page's output size), GELU,
                           GroupNorm(8) with affine.
+
+Element types: with dtype "bf16" or "f16", x and the conv weight are drawn as
+above and rounded to that type (round to nearest even); they are returned as
+float32 arrays holding exactly the rounded values, so the oracle and the
+library see the same numbers (bias, gamma and beta stay fp32).
 
 Distributions: x ~ N(0, 1) (or U[0, 1) as a second parity set, the
 distribution the pages' own harness used); conv weight and bias ~
@@ -52,7 +60,7 @@ _TID_X, _TID_W, _TID_B, _TID_GAMMA, _TID_BETA = 1, 2, 3, 4, 5
 _BASE = dict(ndim=2, kind="conv", groups=1, has_bias=1, act="none", norm="none",
              num_groups=1, eps=1e-5, affine=0, divide_by=1.0, reduce="none",
              pool_kernel=0, pool_repeats=0, want_argmax=0, stride=1, padding=0, dilation=1,
-             output_padding=0)
+             output_padding=0, dtype="f32")
 
 
 def _wl(**kw):
@@ -92,7 +100,13 @@ WORKLOADS = {
         output_padding=1, act="gelu", norm="group", num_groups=8, affine=1),
 }
 
-# The workloads the pages state (the others vary their geometry).
+# 16-bit-input forms of the l2_p17 and l2_p19 problems (x and w in bf16, fp32
+# accumulation and epilogue): the second input precision.
+WORKLOADS["conv2d_in_div_n128_bf16"] = dict(WORKLOADS["conv2d_in_div_n128"], id=9, dtype="bf16")
+WORKLOADS["convt2d_gelu_gn_n128_bf16"] = dict(WORKLOADS["convt2d_gelu_gn_n128"], id=10,
+                                              dtype="bf16")
+
+# The workloads the pages state (the others vary their geometry or precision).
 PAGE_WORKLOADS = [n for n in WORKLOADS if WORKLOADS[n]["id"] <= 6]
 
 # Order in which the workloads are listed (smallest first).
@@ -120,6 +134,20 @@ def w_shape(wl: dict) -> tuple:
     if wl["kind"] == "conv_transpose":
         return (wl["C_in"], wl["C_out"] // g) + ks
     return (wl["C_out"], wl["C_in"] // g) + ks
+
+
+def round_to(a: np.ndarray, dtype: str) -> np.ndarray:
+    """float32 array rounded to bf16 / fp16 (nearest even), returned as float32."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    if dtype == "f32":
+        return a
+    if dtype == "f16":
+        return a.astype(np.float16).astype(np.float32)
+    if dtype == "bf16":
+        u = a.view(np.uint32).astype(np.uint64)
+        u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+        return u.astype(np.uint32).view(np.float32)
+    raise ValueError(dtype)
 
 
 def fan_in(wl: dict) -> int:
@@ -150,13 +178,14 @@ def gen_x(wl: dict, samples=None, dist: str = "normal", seed_offset: int = 0) ->
             out[i] = r.random(per, dtype=np.float32)
         else:
             raise ValueError(dist)
-    return out
+    return round_to(out, wl.get("dtype", "f32"))
 
 
 def gen_params(wl: dict, seed_offset: int = 0) -> dict:
     """Conv weight and bias, and the norm's gamma / beta (None when unused)."""
     bound = 1.0 / math.sqrt(fan_in(wl))
     w = _rng(wl, _TID_W, seed_offset).uniform(-bound, bound, w_shape(wl)).astype(np.float32)
+    w = round_to(w, wl.get("dtype", "f32"))
     b = None
     if wl["has_bias"]:
         b = _rng(wl, _TID_B, seed_offset).uniform(-bound, bound, (wl["C_out"],)).astype(np.float32)

@@ -20,7 +20,7 @@ import torch  # noqa: F401  (loads the HIP runtime first; see module docstring)
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libcnf.so")
 
-CNF_ABI_VERSION = 2
+CNF_ABI_VERSION = 3
 
 # cnf_status
 CNF_OK = 0
@@ -36,6 +36,7 @@ CNF_CONV, CNF_CONV_TRANSPOSE = 0, 1
 ACT = {"none": 0, "hardswish": 1, "gelu": 2, "softmax": 3, "gelu_tanh": 4}
 NORM = {"none": 0, "group": 1, "instance": 2}
 REDUCE = {"none": 0, "mean": 1, "maxpool": 2}
+DTYPE = {"f32": 0, "bf16": 1, "f16": 2}
 
 EXPORTED = ("cnf_plan_create", "cnf_plan_output_shape", "cnf_plan_workspace_size",
             "cnf_forward", "cnf_plan_destroy", "cnf_status_string", "cnf_plan_describe",
@@ -68,6 +69,7 @@ class cnf_desc(ctypes.Structure):
         ("padding", ctypes.c_int32),
         ("dilation", ctypes.c_int32),
         ("output_padding", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
     ]
 
 
@@ -208,6 +210,7 @@ def make_desc(wl: dict, N: int | None = None) -> cnf_desc:
     d.want_argmax = wl["want_argmax"]
     d.stride, d.padding = wl.get("stride", 1), wl.get("padding", 0)
     d.dilation, d.output_padding = wl.get("dilation", 1), wl.get("output_padding", 0)
+    d.dtype = DTYPE[wl.get("dtype", "f32")]
     return d
 
 

@@ -54,7 +54,7 @@ namespace {
 
 // The general family's arguments for a plan (pointers may be null when only
 // the workspace size or the limits are wanted).
-cnf::GenericArgs generic_args(const cnf_plan &p, const float *x, const float *w, const float *b,
+cnf::GenericArgs generic_args(const cnf_plan &p, const void *x, const void *w, const float *b,
                               const float *gamma, const float *beta, float *out, int32_t *argmax,
                               void *workspace, int norm_groups)
 {
@@ -78,6 +78,7 @@ cnf::GenericArgs generic_args(const cnf_plan &p, const float *x, const float *w,
     a.reduce = d.reduce;
     a.pool_kernel = d.pool_kernel; a.pool_repeats = d.pool_repeats;
     a.argmax_wanted = d.want_argmax;
+    a.dtype = d.dtype;
     return a;
 }
 
@@ -132,6 +133,8 @@ cnf_status cnf_plan_create(const cnf_desc *desc, cnf_plan **plan)
     if (d.stride < 1 || d.dilation < 1 || d.padding < 0 || d.output_padding < 0)
         return CNF_ERR_INVALID_DESC;
     if (d.kind == CNF_CONV && d.output_padding != 0) return CNF_ERR_INVALID_DESC;
+    if (d.dtype != CNF_DTYPE_F32 && d.dtype != CNF_DTYPE_BF16 && d.dtype != CNF_DTYPE_F16)
+        return CNF_ERR_INVALID_DESC;
     if (d.kind == CNF_CONV_TRANSPOSE &&
         d.output_padding >= (d.stride > d.dilation ? d.stride : d.dilation))
         return CNF_ERR_INVALID_DESC;
@@ -192,8 +195,9 @@ cnf_status cnf_plan_create(const cnf_desc *desc, cnf_plan **plan)
     // CNF_FORCE_GENERIC environment variable (tests) sends everything to the
     // general family.
     const char *force = std::getenv("CNF_FORCE_GENERIC");
+    // (16-bit inputs: the general family only)
     const bool unit = d.stride == 1 && d.dilation == 1 && d.output_padding == 0 &&
-                      !(force && force[0] == '1');
+                      d.dtype == CNF_DTYPE_F32 && !(force && force[0] == '1');
     const bool basic = unit && d.padding == 0;
     p.igemm_pad = d.kind == CNF_CONV_TRANSPOSE ? k - 1 : 0;
     if (!basic) {
@@ -285,10 +289,13 @@ cnf_status cnf_plan_describe(const cnf_plan *plan, char *buf, size_t len)
     if (len == 0) return CNF_OK;
     const cnf_desc &d = plan->d;
     std::snprintf(buf, len, "family=%s N=%d C_in=%d C_out=%d in=%dx%dx%d k=%d groups=%d "
-                  "stride=%d padding=%d dilation=%d output_padding=%d out_rank=%d workspace=%zu",
+                  "stride=%d padding=%d dilation=%d output_padding=%d dtype=%s out_rank=%d "
+                  "workspace=%zu",
                   family_name(plan->family), d.N, d.C_in, d.C_out, d.in_dims[0], d.in_dims[1],
                   d.in_dims[2], d.kernel, d.groups, d.stride, d.padding, d.dilation,
-                  d.output_padding, plan->rank, plan->workspace);
+                  d.output_padding,
+                  d.dtype == CNF_DTYPE_BF16 ? "bf16" : d.dtype == CNF_DTYPE_F16 ? "f16" : "f32",
+                  plan->rank, plan->workspace);
     return CNF_OK;
 }
 
@@ -296,12 +303,14 @@ void cnf_plan_destroy(cnf_plan *plan) { delete plan; }
 
 static bool misaligned(const void *p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u); }
 
-cnf_status cnf_forward(const cnf_plan *plan, const float *x, const float *w, const float *b,
+cnf_status cnf_forward(const cnf_plan *plan, const void *xv, const void *wv, const float *b,
                        const float *gamma, const float *beta, float *out, int32_t *argmax,
                        void *workspace, size_t workspace_bytes, void *stream)
 {
     if (!plan) return CNF_ERR_NULL;
     const cnf_desc &d = plan->d;
+    // fp32 views for the fp32-only families (16-bit inputs only reach the general one)
+    const float *x = static_cast<const float *>(xv), *w = static_cast<const float *>(wv);
     const bool need_affine = d.norm != CNF_NORM_NONE && d.affine;
     if (!x || !w || !out) return CNF_ERR_NULL;
     if ((b != nullptr) != (d.has_bias != 0)) return CNF_ERR_NULL;
@@ -365,8 +374,8 @@ cnf_status cnf_forward(const cnf_plan *plan, const float *x, const float *w, con
         break;
     }
     case FAM_GENERIC:
-        e = cnf::launch_generic(generic_args(*plan, x, w, b, gamma, beta, out, argmax, workspace,
-                                             norm_groups),
+        e = cnf::launch_generic(generic_args(*plan, xv, wv, b, gamma, beta, out, argmax,
+                                             workspace, norm_groups),
                                 st);
         break;
     default: return CNF_ERR_UNSUPPORTED;

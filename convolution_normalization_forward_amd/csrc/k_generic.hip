@@ -71,16 +71,19 @@ constexpr unsigned GOOB = 0x7ff00000u;   // an offset past the end of every reso
 constexpr unsigned RES_MAX = 0x7f000000u;
 
 struct GenConv {
-    const float *x, *wp, *b;   // wp: weights packed by gen_weight_pack_kernel
+    const void *x, *wp;        // element type DT; wp: weights packed by gen_weight_pack_kernel
+    const float *b;
     float *y;          // conv output [N][C_out][S] or nullptr
     v4f *part;         // [N][C_out][T] (count, mean, M2, 0) or nullptr
     int tasks;         // N * nph * Tq * GTn * cobN (below 2^31)
     int tpw;           // tasks per wave
     int C_in, C_out, Cgi, Cgo, G, cobN, T, Tq, CT;  // CT: column tiles per phase
     // P conv groups share one 16-row tile (groups of at most 8 output channels):
-    // RPG = 16/P rows and KPG = 4/P K entries per group; GTn = ceil(G/P) group
-    // tiles; steps = ceil(Cgi/KPG) K steps per tap; KP = 4*steps.
+    // RPG = 16/P rows and KPG = KS/P K entries per group per step (KS = 4 K
+    // entries per step for fp32, 16 for the 16-bit types); GTn = ceil(G/P)
+    // group tiles; steps = ceil(Cgi/KPG) K steps per tap; KP = KS*steps.
     int P, RPG, KPG, GTn, steps, KP;
+    int act;
     int D, H, W, Do, Ho, Wo, S;
     int kd, kh, kw;
     int sd, sh, sw, pd, ph, pw, dd, dh, dw;
@@ -105,8 +108,38 @@ struct GenConv {
 //
 // One wave owns NB blocks of 16 output channels of one conv group: each
 // gathered input operand feeds NB MFMAs, each weight operand 4.
-template <int ACT, bool TR, int NB, int ROWS>
+//
+// DT selects the input element type: 0 fp32 (v_mfma_f32_16x16x4f32, one K
+// entry per lane per step), 1 bf16 / 2 fp16 (v_mfma_f32_16x16x16_{bf16,f16},
+// four consecutive K entries per lane per step; products are exact in fp32 and
+// accumulate in fp32).
+typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+typedef unsigned short v4us __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float activate_rt(float x, int act) {
+    switch (act) {
+    case ACT_HARDSWISH: return hardswish(x);
+    case ACT_GELU_ERF: return gelu_erf(x);
+    case ACT_GELU_TANH: return gelu_tanh(x);
+    default: return x;
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ v4f mfma16(v4us a, v4us b, v4f c) {
+    if constexpr (DT == 1)
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4bf, a),
+                                                         __builtin_bit_cast(v4bf, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(v4h, a),
+                                                     __builtin_bit_cast(v4h, b), c, 0, 0, 0);
+}
+
+template <bool TR, int NB, int ROWS, int DT>
 __device__ __forceinline__ void gen_conv_task(const GenConv &g, int task, int lane) {
+    constexpr unsigned ES = DT ? 2u : 4u;   // element size of x and the packed weights
+    constexpr int KL = DT ? 4 : 1;          // K entries a lane supplies per step
     constexpr int CW = 4 / ROWS;  // 16-column tiles per row
     const int col = lane & 15, kq = lane >> 4;
     // Task order (fastest first): channel blocks, phase, group, tile, sample.
@@ -188,22 +221,28 @@ __device__ __forceinline__ void gen_conv_task(const GenConv &g, int task, int la
         }
     }
 
-    // A operands: row col = output channel (cbn*NB + b)*16 + col, K entry kq =
-    // input channel c0 + kq.  In the packed weights those NB values are adjacent
-    // and a (tap, channel chunk) is one contiguous run of 64*NB floats, zero where
-    // the channel or the output channel is padding.
+    // A operands: row col = output channel (cbn*NB + b)*16 + col, K entries
+    // KL*kq .. KL*kq + KL-1.  In the packed weights a lane's NB*KL values are
+    // adjacent and a (tap, K step) is one contiguous run of 64*NB*KL elements,
+    // zero where the channel or the output channel is padding.
     const int taps = g.kd * g.kh * g.kw;
-    const unsigned wrow = (unsigned)g.cobN * 16 * NB;   // floats per K entry
-    const unsigned woff = ((unsigned)kq * wrow + ((unsigned)cbn * 16 + col) * NB) * 4u;
-    // B operand: K entry kq is channel c0 + kq % KPG of group gt*P + kq / KPG.
-    const float *xs = g.x + ((size_t)n * g.C_in + (size_t)gt * g.P * g.Cgi) * g.in_plane;
-    const unsigned xbytes = (unsigned)(g.C_in - gt * g.P * g.Cgi) * g.in_plane * 4u;
-    const unsigned kq_off = (unsigned)((kq / g.KPG) * g.Cgi + kq % g.KPG) * g.in_plane * 4u;
+    const unsigned wrow = (unsigned)g.cobN * 16 * NB * KL;   // elements per lane row kq
+    const unsigned woff = ((unsigned)kq * wrow + ((unsigned)cbn * 16 + col) * NB * KL) * ES;
+    // B operand: K entry e of a step is channel c0 + e % KPG of group gt*P + e / KPG.
+    const char *xs = static_cast<const char *>(g.x) +
+                     ((size_t)n * g.C_in + (size_t)gt * g.P * g.Cgi) * g.in_plane * ES;
+    const unsigned xbytes = (unsigned)(g.C_in - gt * g.P * g.Cgi) * g.in_plane * ES;
+    unsigned koff[KL];
+#pragma unroll
+    for (int i = 0; i < KL; ++i) {
+        const int e = KL * kq + i;
+        koff[i] = (unsigned)((e / g.KPG) * g.Cgi + e % g.KPG) * g.in_plane * ES;
+    }
 
     // Bias of this lane's output channels, fetched before the MFMA loop so its
     // latency overlaps the gathers.
     float bias[NB][4];
-    const auto br = make_rsrc(g.b ? g.b : g.x, g.b ? (unsigned)g.C_out * 4u : 0u);
+    const auto br = make_rsrc(g.b ? (const void *)g.b : g.x, g.b ? (unsigned)g.C_out * 4u : 0u);
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -239,7 +278,7 @@ __device__ __forceinline__ void gen_conv_task(const GenConv &g, int task, int la
             for (int r = 0; r < ROWS; ++r) {
                 const int iz = bz[r] + tz, iy = by[r] + ty;
                 okzy[r] = (unsigned)iz < (unsigned)g.D && (unsigned)iy < (unsigned)g.H;
-                rowb[r] = ((unsigned)iz * g.H + (unsigned)iy) * g.W * 4u;
+                rowb[r] = ((unsigned)iz * g.H + (unsigned)iy) * g.W * ES;
             }
             for (int kx = 0; kx < g.kw; ++kx) {
                 const int tap = (kz * g.kh + ky) * g.kw + kx;
@@ -257,34 +296,63 @@ __device__ __forceinline__ void gen_conv_task(const GenConv &g, int task, int la
                         ix = bx[u] + kxd;
                         okx = (unsigned)ix < (unsigned)g.W;
                     }
-                    xo[u] = (okzy[u / CW] && okx) ? rowb[u / CW] + (unsigned)ix * 4u + kq_off : GOOB;
+                    // (a lane's K entries add koff[i]; GOOB + koff stays past the end)
+                    xo[u] = (okzy[u / CW] && okx) ? rowb[u / CW] + (unsigned)ix * ES : GOOB;
                 }
-                const unsigned wtap = ((unsigned)(gt * taps + tap) * g.KP) * wrow;
+                const unsigned wtap = ((unsigned)(gt * taps + tap) * g.KP) * (wrow / KL);
                 for (int st = 0; st < g.steps; ++st) {
                     // buffers rebased on the step's first channel (scalar work);
                     // padding channels and other groups' rows meet zero weights
                     const int c0 = st * g.KPG;
-                    const auto xr = make_rsrc(xs + (size_t)c0 * g.in_plane,
-                                              xbytes - (unsigned)c0 * g.in_plane * 4u);
-                    const unsigned wsh = wtap + (unsigned)st * 4u * wrow;
-                    const auto wr = make_rsrc(g.wp + wsh, (g.wp_elems - wsh) * 4u);
-                    float a[NB];
-                    if constexpr (NB == 4) {
-                        const v4f v = buf_load4(wr, woff);
-                        a[0] = v[0]; a[1] = v[1]; a[2] = v[2]; a[3] = v[3];
-                    } else if constexpr (NB == 2) {
-                        const v2f v = buf_load2(wr, woff);
-                        a[0] = v[0]; a[1] = v[1];
+                    const auto xr = make_rsrc(xs + (size_t)c0 * g.in_plane * ES,
+                                              xbytes - (unsigned)c0 * g.in_plane * ES);
+                    const unsigned wsh = wtap + (unsigned)st * 4u * wrow;   // elements
+                    const auto wr = make_rsrc(static_cast<const char *>(g.wp) + (size_t)wsh * ES,
+                                              (g.wp_elems - wsh) * ES);
+                    if constexpr (DT == 0) {
+                        float a[NB];
+                        if constexpr (NB == 4) {
+                            const v4f v = buf_load4(wr, woff);
+                            a[0] = v[0]; a[1] = v[1]; a[2] = v[2]; a[3] = v[3];
+                        } else if constexpr (NB == 2) {
+                            const v2f v = buf_load2(wr, woff);
+                            a[0] = v[0]; a[1] = v[1];
+                        } else {
+                            a[0] = buf_load1(wr, woff);
+                        }
+                        float bv[4];
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) bv[u] = buf_load1(xr, xo[u] + koff[0]);
+#pragma unroll
+                        for (int b = 0; b < NB; ++b)
+#pragma unroll
+                            for (int u = 0; u < 4; ++u) acc[b][u] = mfma_16x16x4(a[b], bv[u], acc[b][u]);
                     } else {
-                        a[0] = buf_load1(wr, woff);
+                        // A: NB blocks x 4 consecutive K entries (8*NB bytes per lane)
+                        v4us a[NB];
+                        if constexpr (NB == 1) {
+                            a[0] = __builtin_bit_cast(v4us, buf_load2(wr, woff));
+                        } else {
+#pragma unroll
+                            for (int h = 0; h < NB / 2; ++h) {
+                                const v4f v = buf_load4(wr, woff + 16u * h);
+                                a[2 * h] = __builtin_bit_cast(v4us, v2f{v[0], v[1]});
+                                a[2 * h + 1] = __builtin_bit_cast(v4us, v2f{v[2], v[3]});
+                            }
+                        }
+                        // B: the lane's 4 K entries (channels) at each column tile
+                        v4us bv[4];
+#pragma unroll
+                        for (int u = 0; u < 4; ++u)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                bv[u][i] = __builtin_amdgcn_raw_buffer_load_b16(
+                                    xr, (int)(xo[u] + koff[i]), 0, 0);
+#pragma unroll
+                        for (int b = 0; b < NB; ++b)
+#pragma unroll
+                            for (int u = 0; u < 4; ++u) acc[b][u] = mfma16<DT>(a[b], bv[u], acc[b][u]);
                     }
-                    float bv[4];
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) bv[u] = buf_load1(xr, xo[u]);
-#pragma unroll
-                    for (int b = 0; b < NB; ++b)
-#pragma unroll
-                        for (int u = 0; u < 4; ++u) acc[b][u] = mfma_16x16x4(a[b], bv[u], acc[b][u]);
                 }
             }
         }
@@ -302,7 +370,7 @@ __device__ __forceinline__ void gen_conv_task(const GenConv &g, int task, int la
         const bool cv = out_channel(b, 4 * kq + r, cgl);
         float v[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = activate<ACT>(acc[b][u][r] + bias[b][r]);
+        for (int u = 0; u < 4; ++u) v[u] = activate_rt(acc[b][u][r] + bias[b][r], g.act);
         if (g.y) {
 #pragma unroll
             for (int u = 0; u < 4; ++u)
@@ -329,7 +397,7 @@ __device__ __forceinline__ void gen_conv_task(const GenConv &g, int task, int la
 
 // Each wave runs g.tpw consecutive tasks (the host sizes it so a wave issues a
 // few hundred MFMAs).
-template <int ACT, bool TR, int NB, int ROWS>
+template <bool TR, int NB, int ROWS, int DT>
 __global__ __launch_bounds__(GT) void gen_conv_kernel(GenConv g) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -337,25 +405,29 @@ __global__ __launch_bounds__(GT) void gen_conv_kernel(GenConv g) {
     for (int j = 0; j < g.tpw; ++j) {
         const int task = first + j;
         if (task >= g.tasks) return;  // whole waves leave; the kernel has no barriers
-        gen_conv_task<ACT, TR, NB, ROWS>(g, task, lane);
+        gen_conv_task<TR, NB, ROWS, DT>(g, task, lane);
     }
 }
 
-// Packed weights for gen_conv_kernel: wp[gt][tap][st][kq][cbn][col][b] is the
-// A operand entry (row (cbn*NB + b)*16 + col, K entry kq) of K step st at that
-// tap for group tile gt: with P groups per tile, row belongs to group gt*P +
-// row / RPG (output channel row % RPG) and kq to group gt*P + kq / KPG (input
-// channel st*KPG + kq % KPG); the entry is the weight when both name the same
-// existing group and real channels, else 0 (block-diagonal A, zero padding).
-// Source layout: conv w[C_out][Cgi][taps], transposed conv w[C_in][Cgo][taps].
-__global__ __launch_bounds__(GT) void gen_weight_pack_kernel(const float *w, float *wp, int G,
-                                                             int Cgi, int Cgo, int taps,
-                                                             int steps, int P, int cobN, int NB,
+// Packed weights for gen_conv_kernel: wp[gt][tap][st][kq][cbn][col][b][i] is
+// the A operand entry (row (cbn*NB + b)*16 + col, K entry e = KL*kq + i) of K
+// step st at that tap for group tile gt: with P groups per tile, the row
+// belongs to group gt*P + row / RPG (output channel row % RPG) and the K entry
+// to group gt*P + e / KPG (input channel st*KPG + e % KPG); the entry is the
+// weight when both name the same existing group and real channels, else 0
+// (block-diagonal A, zero padding).  KL = 1 K entry per lane for fp32, 4 for
+// the 16-bit types (copied bit for bit).  Source layout: conv w[C_out][Cgi][taps],
+// transposed conv w[C_in][Cgo][taps].
+template <typename E>
+__global__ __launch_bounds__(GT) void gen_weight_pack_kernel(const E *w, E *wp, int G, int Cgi,
+                                                             int Cgo, int taps, int steps, int P,
+                                                             int KL, int cobN, int NB,
                                                              int transposed, unsigned total) {
-    const unsigned i = blockIdx.x * GT + threadIdx.x;
-    if (i >= total) return;
-    const int RPG = 16 / P, KPG = 4 / P;
-    unsigned r = i;
+    const unsigned idx = blockIdx.x * GT + threadIdx.x;
+    if (idx >= total) return;
+    const int RPG = 16 / P, KPG = 4 * KL / P;
+    unsigned r = idx;
+    const int i = r % KL; r /= KL;
     const int b = r % NB; r /= NB;
     const int col = r % 16; r /= 16;
     const int cbn = r % cobN; r /= cobN;
@@ -363,14 +435,15 @@ __global__ __launch_bounds__(GT) void gen_weight_pack_kernel(const float *w, flo
     const int st = r % steps; r /= steps;
     const int tap = r % taps;
     const int gt = r / taps;
+    const int e = KL * kq + i;
     const int grp = gt * P + col / RPG;
     const int co = (cbn * NB + b) * 16 + col % RPG;
-    const int ci = st * KPG + kq % KPG;
-    float v = 0.0f;
-    if (grp == gt * P + kq / KPG && grp < G && co < Cgo && ci < Cgi)
+    const int ci = st * KPG + e % KPG;
+    E v = E(0);
+    if (grp == gt * P + e / KPG && grp < G && co < Cgo && ci < Cgi)
         v = transposed ? w[((size_t)(grp * Cgi + ci) * Cgo + co) * taps + tap]
                        : w[((size_t)(grp * Cgo + co) * Cgi + ci) * taps + tap];
-    wp[i] = v;
+    wp[idx] = v;
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -548,6 +621,7 @@ struct GenLayout {
     int nph, Tq, CT;  // conv phases (z, y), tiles per phase, column tiles per row
     int ROWS;         // rows per tile: 1 (64 columns) or 4 (16 columns)
     int NB, cobN, P, KPG, GTn, steps;
+    int KL, ES;       // K entries per lane per step (1 fp32, 4 16-bit); element bytes
     size_t off_wp, wp_elems;
     int T;            // statistics tiles per (sample, channel)
     size_t off_stage, off_part, off_ss, off_pv[2], off_pi[2], total;
@@ -585,15 +659,17 @@ void layout(const GenericArgs &a, GenLayout &L) {
     int pw2 = 1;
     while (pw2 < Cgo) pw2 <<= 1;
     L.P = (Cgo <= 8 && a.groups >= 2) ? (16 / pw2 < 4 ? 16 / pw2 : 4) : 1;
-    L.KPG = 4 / L.P;
+    L.KL = a.dtype ? 4 : 1;
+    L.ES = a.dtype ? 2 : 4;
+    L.KPG = 4 * L.KL / L.P;
     L.GTn = (a.groups + L.P - 1) / L.P;
     L.steps = (Cgi + L.KPG - 1) / L.KPG;
     L.NB = L.P > 1 ? 1 : blocks_per_wave(Cgo);
     L.cobN = L.P > 1 ? 1 : ((Cgo + 15) / 16 + L.NB - 1) / L.NB;
-    L.wp_elems = (size_t)L.GTn * a.kd * a.kh * a.kw * 4 * L.steps * L.cobN * 16 * L.NB;
+    L.wp_elems = (size_t)L.GTn * a.kd * a.kh * a.kw * 4 * L.steps * L.cobN * 16 * L.NB * L.KL;
     size_t off = 0;
     L.off_wp = off;
-    off = align256(off + L.wp_elems * 4);
+    off = align256(off + L.wp_elems * L.ES);
     L.off_stage = off;
     if (L.stage) off = align256(off + (size_t)NC * S * 4);
     L.off_part = off;
@@ -614,19 +690,24 @@ void layout(const GenericArgs &a, GenLayout &L) {
     L.total = off;
 }
 
-template <int ACT, bool TR, int ROWS>
-void launch_conv_rows(const GenConv &g, int NB, dim3 grid, hipStream_t st) {
-    if (NB == 4) gen_conv_kernel<ACT, TR, 4, ROWS><<<grid, dim3(GT), 0, st>>>(g);
-    else if (NB == 2) gen_conv_kernel<ACT, TR, 2, ROWS><<<grid, dim3(GT), 0, st>>>(g);
-    else gen_conv_kernel<ACT, TR, 1, ROWS><<<grid, dim3(GT), 0, st>>>(g);
+template <bool TR, int ROWS, int DT>
+void launch_conv_nb(const GenConv &g, int NB, dim3 grid, hipStream_t st) {
+    if (NB == 4) gen_conv_kernel<TR, 4, ROWS, DT><<<grid, dim3(GT), 0, st>>>(g);
+    else if (NB == 2) gen_conv_kernel<TR, 2, ROWS, DT><<<grid, dim3(GT), 0, st>>>(g);
+    else gen_conv_kernel<TR, 1, ROWS, DT><<<grid, dim3(GT), 0, st>>>(g);
 }
 
-template <int ACT, bool TR>
-hipError_t launch_conv(const GenConv &g, int NB, int ROWS, hipStream_t st) {
+template <int DT>
+hipError_t launch_conv(const GenConv &g, bool tr, int NB, int ROWS, hipStream_t st) {
     const long long waves = ((long long)g.tasks + g.tpw - 1) / g.tpw;
     const dim3 grid((unsigned)((waves + 3) / 4));
-    if (ROWS == 1) launch_conv_rows<ACT, TR, 1>(g, NB, grid, st);
-    else launch_conv_rows<ACT, TR, 4>(g, NB, grid, st);
+    if (tr) {
+        if (ROWS == 1) launch_conv_nb<true, 1, DT>(g, NB, grid, st);
+        else launch_conv_nb<true, 4, DT>(g, NB, grid, st);
+    } else {
+        if (ROWS == 1) launch_conv_nb<false, 1, DT>(g, NB, grid, st);
+        else launch_conv_nb<false, 4, DT>(g, NB, grid, st);
+    }
     return hipGetLastError();
 }
 
@@ -657,7 +738,7 @@ bool generic_supported(const GenericArgs &a) {
     GenLayout L;
     layout(a, L);
     if ((long long)a.N * L.nph * L.Tq * L.GTn * L.cobN >= (1LL << 31) - 64) return false;
-    if (L.wp_elems * 4 >= RES_MAX) return false;
+    if (L.wp_elems * L.ES >= RES_MAX) return false;
     if ((long long)a.N * a.C_out * S / GT >= (1LL << 31) - 1) return false;
     return true;
 }
@@ -682,11 +763,11 @@ hipError_t launch_generic(const GenericArgs &a, hipStream_t st) {
     // 1. conv (+ bias + elementwise activation)
     GenConv g{};
     g.x = a.x; g.b = a.b;
-    float *wp = reinterpret_cast<float *>(ws + L.off_wp);
+    void *wp = ws + L.off_wp;
     g.wp = wp;
     g.wp_elems = (unsigned)L.wp_elems;
     g.P = L.P; g.RPG = 16 / L.P; g.KPG = L.KPG; g.GTn = L.GTn; g.steps = L.steps;
-    g.KP = 4 * L.steps;
+    g.KP = 4 * L.KL * L.steps;
     g.y = y;
     g.part = L.softmax ? nullptr : part;
     g.C_in = a.C_in; g.C_out = a.C_out; g.G = a.groups;
@@ -705,35 +786,32 @@ hipError_t launch_generic(const GenericArgs &a, hipStream_t st) {
     {
         // ~256 MFMAs per wave, but at least 16K waves in flight
         const double taps_issued = (double)a.kd * a.kh * a.kw / L.nph;  // x taps all issued
-        const double mfma = taps_issued * L.steps * 4.0 * NB;
+        const double mfma = taps_issued * L.steps * 4.0 * NB * (a.dtype ? 0.5 : 1.0);
         long long tpw = (long long)(256.0 / (mfma > 1.0 ? mfma : 1.0));
         const long long cap = g.tasks / 16384;
         if (tpw > cap) tpw = cap;
         g.tpw = (int)(tpw < 1 ? 1 : tpw > 64 ? 64 : tpw);
     }
     {
-        const unsigned total = (unsigned)L.wp_elems;
-        gen_weight_pack_kernel<<<dim3((total + GT - 1) / GT), dim3(GT), 0, st>>>(
-            a.w, wp, a.groups, g.Cgi, g.Cgo, a.kd * a.kh * a.kw, L.steps, L.P, L.cobN, NB,
-            a.transposed, total);
+        const unsigned total = (unsigned)L.wp_elems, blocks = (total + GT - 1) / GT;
+        const int taps = a.kd * a.kh * a.kw;
+        if (a.dtype)
+            gen_weight_pack_kernel<unsigned short><<<dim3(blocks), dim3(GT), 0, st>>>(
+                static_cast<const unsigned short *>(a.w), static_cast<unsigned short *>(wp),
+                a.groups, g.Cgi, g.Cgo, taps, L.steps, L.P, L.KL, L.cobN, NB, a.transposed,
+                total);
+        else
+            gen_weight_pack_kernel<float><<<dim3(blocks), dim3(GT), 0, st>>>(
+                static_cast<const float *>(a.w), static_cast<float *>(wp), a.groups, g.Cgi,
+                g.Cgo, taps, L.steps, L.P, L.KL, L.cobN, NB, a.transposed, total);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     // the conv writes the final values when nothing follows but the divide
     g.out_scale = (!L.softmax && a.norm_groups == 0 && a.reduce == 0) ? a.inv_div : 1.0f;
-    const int act = L.softmax ? ACT_NONE : a.act;
-#define CNF_GEN_CASE(A)                                                             \
-    case A:                                                                         \
-        e = a.transposed ? launch_conv<A, true>(g, NB, L.ROWS, st)                  \
-                         : launch_conv<A, false>(g, NB, L.ROWS, st);                \
-        break;
-    switch (act) {
-        CNF_GEN_CASE(ACT_NONE)
-        CNF_GEN_CASE(ACT_HARDSWISH)
-        CNF_GEN_CASE(ACT_GELU_ERF)
-        CNF_GEN_CASE(ACT_GELU_TANH)
-    default: return hipErrorInvalidValue;
-    }
-#undef CNF_GEN_CASE
+    g.act = L.softmax ? ACT_NONE : a.act;
+    if (a.dtype == 1) e = launch_conv<1>(g, a.transposed, NB, L.ROWS, st);
+    else if (a.dtype == 2) e = launch_conv<2>(g, a.transposed, NB, L.ROWS, st);
+    else e = launch_conv<0>(g, a.transposed, NB, L.ROWS, st);
     if (e != hipSuccess) return e;
 
     // 2. channel softmax

@@ -98,7 +98,8 @@ hipError_t launch_convt2d_fused(const ConvT2dArgs &a, hipStream_t st);
 //      (MFMA implicit GEMM, gathered from L2) + act + per-tile statistics,
 //      channel softmax, statistics finalize, in-place normalise, max-pool passes.
 struct GenericArgs {
-    const float *x, *w, *b, *gamma, *beta;
+    const void *x, *w;           // element type `dtype` (cnf_dtype)
+    const float *b, *gamma, *beta;
     float *out;
     int32_t *argmax;
     void *workspace;
@@ -115,6 +116,7 @@ struct GenericArgs {
     int reduce;                  // cnf_reduce
     int pool_kernel, pool_repeats;
     int argmax_wanted;
+    int dtype;                   // 0 fp32, 1 bf16, 2 fp16 (x and w)
 };
 bool generic_supported(const GenericArgs &a);
 size_t generic_workspace(const GenericArgs &a);

@@ -30,8 +30,11 @@
  * "Kimi-K2.6__l2_p6" states in its integer output-size passage.
  *
  * Conventions for every entry point:
- *   - Tensors are fp32, dense and contiguous, batch-major NC(D)HW.  2-D
- *     problems set ndim = 2 and in_dims[0] = 1.
+ *   - Tensors are dense and contiguous, batch-major NC(D)HW.  2-D problems set
+ *     ndim = 2 and in_dims[0] = 1.  x and w have the element type
+ *     desc->dtype (fp32, bf16 or fp16); b, gamma, beta and out are always fp32.
+ *     The contraction accumulates in fp32 whatever the input type; every
+ *     step after it (activation, statistics, norm, divide, reduction) is fp32.
  *   - Every tensor pointer passed to cnf_forward is a DEVICE pointer owned by
  *     the caller (for example a torch tensor's data_ptr()); the library never
  *     allocates device memory, never frees caller memory and never
@@ -56,7 +59,7 @@
 extern "C" {
 #endif
 
-#define CNF_ABI_VERSION 2
+#define CNF_ABI_VERSION 3
 
 typedef enum {
     CNF_OK = 0,
@@ -70,6 +73,12 @@ typedef enum {
 } cnf_status;
 
 typedef enum { CNF_CONV = 0, CNF_CONV_TRANSPOSE = 1 } cnf_conv_kind;
+
+/* Element type of x and w.  The 16-bit types feed the 16-bit matrix
+ * instructions (products exact in fp32, fp32 accumulation); the pages use
+ * fp32 throughout, and name tensor-core input precisions only as what a
+ * vendor library would pick. */
+typedef enum { CNF_DTYPE_F32 = 0, CNF_DTYPE_BF16 = 1, CNF_DTYPE_F16 = 2 } cnf_dtype;
 
 typedef enum {
     CNF_ACT_NONE = 0,
@@ -122,6 +131,7 @@ typedef struct {
     int32_t dilation;      /* >= 1; spacing of the kernel taps */
     int32_t output_padding;/* transposed conv: 0 <= output_padding < max(stride,
                               dilation), extra extent at the high end; conv: 0 */
+    int32_t dtype;         /* cnf_dtype of x and w (added in ABI version 3) */
 } cnf_desc;
 
 typedef struct cnf_plan cnf_plan;
@@ -131,6 +141,7 @@ typedef struct cnf_plan cnf_plan;
  * Checks: abi_version; ndim in {2,3}; N >= 0; C_in, C_out, kernel >= 1;
  * groups divides C_in and C_out; num_groups divides C_out (GroupNorm);
  * stride, dilation >= 1; padding >= 0; output_padding as stated above;
+ * dtype in range;
  * every conv output extent >= 1; pooled extents >= 1; eps > 0 when a norm is
  * requested; divide_by != 0; enum fields in range.  Shapes the specialised
  * kernel families cover take them; every other valid descriptor takes the
@@ -159,9 +170,10 @@ cnf_status cnf_plan_output_shape(const cnf_plan *plan, int64_t dims[5], int32_t 
 cnf_status cnf_plan_workspace_size(const cnf_plan *plan, size_t *bytes);
 
 /* Run the whole forward path on `stream`.
- *   x      [N][C_in][D][H][W]                         (D absent for 2-D)
+ *   x      [N][C_in][D][H][W]  (D absent for 2-D), element type desc->dtype
  *   w      conv: [C_out][C_in/groups][k]^ndim; transposed conv:
- *          [C_in][C_out/groups][k]^ndim (the layout l2_p19 states)
+ *          [C_in][C_out/groups][k]^ndim (the layout l2_p19 states), element
+ *          type desc->dtype
  *   b      [C_out] iff has_bias, else NULL
  *   gamma, beta  [C_out] iff a norm with affine = 1, else NULL
  *   out    the shape cnf_plan_output_shape reports
@@ -173,7 +185,7 @@ cnf_status cnf_plan_workspace_size(const cnf_plan *plan, size_t *bytes);
  * Returns CNF_ERR_NULL / CNF_ERR_ALIGNMENT / CNF_ERR_WORKSPACE before any
  * launch, or CNF_ERR_HIP if a launch failed. */
 cnf_status cnf_forward(const cnf_plan *plan,
-                       const float *x, const float *w, const float *b,
+                       const void *x, const void *w, const float *b,
                        const float *gamma, const float *beta,
                        float *out, int32_t *argmax,
                        void *workspace, size_t workspace_bytes,

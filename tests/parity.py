@@ -12,10 +12,16 @@ import oracle
 ATOL, RTOL = 2e-4, 1e-3   # |gpu - ref| <= ATOL + RTOL * |ref|
 
 
+_TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+
+
 def run_gpu(wl, x, p, dev="cuda:0"):
     plan = cnf.Plan(cnf.make_desc(wl, N=x.shape[0]))
     t = {k: (torch.from_numpy(v).to(dev) if v is not None else None) for k, v in p.items()}
-    xt = torch.from_numpy(x).to(dev)
+    # x and w hold values exact in the workload's element type; hand them over in it
+    dt = _TORCH_DTYPE[wl.get("dtype", "f32")]
+    t["w"] = t["w"].to(dt)
+    xt = torch.from_numpy(x).to(dev).to(dt)
     out, idx = plan.forward(xt, t["w"], t["b"], t["gamma"], t["beta"])
     torch.cuda.synchronize()
     return plan, out, idx

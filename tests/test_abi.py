@@ -47,6 +47,8 @@ def test_every_workload_plans_with_expected_shape(name):
         "convt2d_dense_gelu_gn_n128": (128, 64, 258, 258),
         "conv2d_s2p1_in_div_n128": (128, 128, 64, 64),
         "convt2d_s2_gelu_gn_n128": (128, 64, 256, 256),
+        "conv2d_in_div_n128_bf16": (128, 128, 126, 126),
+        "convt2d_gelu_gn_n128_bf16": (128, 64, 258, 258),
     }[name]
     assert plan.out_shape == exp
     assert "family=" in plan.describe()
@@ -198,6 +200,22 @@ def test_padded_stride1_convs_use_the_implicit_gemm():
     # beyond k - 1, or strided / dilated: the general family
     for over in (dict(padding=3), dict(padding=1, dilation=2), dict(padding=1, stride=2)):
         assert "family=generic" in cnf.Plan(_desc("conv2d_in_div_n128", **over)).describe(), over
+
+
+def test_sixteen_bit_inputs_plan_on_the_general_family():
+    d = _desc("conv2d_in_div_n128")
+    d.dtype = 3
+    assert cnf.cnf_plan_create_status(d) == cnf.CNF_ERR_INVALID_DESC
+    for dt in ("bf16", "f16"):
+        for name in cnf_inputs.PAGE_WORKLOADS:
+            plan = cnf.Plan(_desc(name, dtype=dt))
+            assert "family=generic" in plan.describe() and f"dtype={dt}" in plan.describe()
+    # 16-bit packed weights: 16 K entries per step (4 per lane), 2-byte elements
+    p = cnf.Plan(_desc("conv2d_in_div_n128", dtype="bf16"))
+    S = 126 * 126
+    T = -(-126 // 1) * -(-126 // 64)   # one-row tiles of 64 columns
+    wp = 1 * 9 * 16 * (64 // 16) * 2 * 16 * 4 * 2   # taps x 16 x steps x cobN x 16 x NB x 2 B
+    assert p.workspace_bytes == _align(wp) + _align(128 * 128 * T * 16) + _align(128 * 128 * 8)
 
 
 def test_family_routing():

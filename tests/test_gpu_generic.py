@@ -147,6 +147,40 @@ def test_page_configurations_through_the_general_family(name, over):
     _case(name, force=True, **over)
 
 
+# 16-bit inputs (x and w rounded to bf16 / fp16 by the input generator, so the
+# oracle sees the same values); the products are exact in fp32 and accumulate in
+# fp32, so the same tolerance applies.
+SIXTEEN_BIT_CASES = [
+    ("conv2d_in_div_n2", {}),
+    ("conv2d_in_div_n128", dict(N=1, C_in=16, in_dims=(1, 30, 70))),
+    ("conv3d_hswish_gn_mean_n1024", dict(N=2)),
+    ("conv3d_softmax_pool_n128", dict(N=2)),
+    ("convt2d_gelu_gn_n128", dict(N=1, in_dims=(1, 19, 33))),
+    ("convt2d_dense_gelu_gn_n128", dict(N=1, C_in=24, in_dims=(1, 12, 20))),
+    ("conv2d_s2p1_in_div_n128", dict(N=2, C_in=40, in_dims=(1, 21, 70))),
+    ("convt2d_s2_gelu_gn_n128", dict(N=2, in_dims=(1, 9, 30))),
+    ("conv2d_in_div_n2", dict(C_in=6, C_out=24, groups=3, in_dims=(1, 23, 29), dilation=2,
+                              padding=2, act="hardswish", norm="group", num_groups=4, affine=1,
+                              divide_by=1.0)),
+    ("conv2d_in_div_n2", dict(C_in=8, C_out=8, groups=8, kernel=5, stride=2, in_dims=(1, 31, 26),
+                              act="gelu", norm="none", divide_by=3.0)),
+    ("conv2d_in_div_n2", dict(C_in=70, C_out=1, kernel=1, stride=3, in_dims=(1, 20, 22),
+                              norm="none", divide_by=1.0)),
+    ("convt2d_gelu_gn_n128", dict(N=2, ndim=3, C_in=8, C_out=16, groups=2, in_dims=(3, 5, 6),
+                                  stride=2, output_padding=1, act="hardswish", num_groups=4,
+                                  reduce="mean", divide_by=2.0)),
+    ("conv2d_in_div_n2", dict(in_dims=(1, 30, 27), stride=1, padding=1, reduce="maxpool",
+                              pool_kernel=2, pool_repeats=2, want_argmax=1, norm="group",
+                              num_groups=4, affine=1)),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("name,over", SIXTEEN_BIT_CASES)
+def test_sixteen_bit_inputs_every_element(name, over, dtype):
+    _case(name, dtype=dtype, **over)
+
+
 def test_general_family_uniform_inputs():
     _case("conv2d_in_div_n2", dist="uniform", stride=2, padding=1, norm="group", num_groups=2,
           affine=1)

@@ -145,6 +145,8 @@ FULL_SUBSET = {
     "convt2d_dense_gelu_gn_n128": 2,
     "conv2d_s2p1_in_div_n128": 2,
     "convt2d_s2_gelu_gn_n128": 2,
+    "conv2d_in_div_n128_bf16": 2,
+    "convt2d_gelu_gn_n128_bf16": 2,
 }
 
 

@@ -101,6 +101,9 @@ SMALL = {
     "convt2d_dense_gelu_gn_n128": dict(N=2, C_in=6, C_out=8, in_dims=(1, 7, 9), num_groups=4),
     "conv2d_s2p1_in_div_n128": dict(N=1, C_in=8, C_out=16, in_dims=(1, 13, 12)),
     "convt2d_s2_gelu_gn_n128": dict(N=2, C_in=16, C_out=16, in_dims=(1, 6, 7)),
+    "conv2d_in_div_n128_bf16": dict(N=1, C_in=8, C_out=16, in_dims=(1, 12, 11)),
+    "convt2d_gelu_gn_n128_bf16": dict(N=2, C_in=16, C_out=16, in_dims=(1, 9, 10), groups=8,
+                                      num_groups=8),
 }
 
 
@@ -117,6 +120,28 @@ def test_oracle_chain_matches_independent_numpy(name, dist):
     if wl["reduce"] == "mean":
         cf, _ = oracle.forward(wl, x, **p, closed_form_mean=True)
         np.testing.assert_allclose(cf, out, rtol=1e-10, atol=1e-12)
+
+
+def test_sixteen_bit_rounding_matches_torch():
+    """round_to (the input generator's bf16 / fp16 rounding) equals torch's
+    conversions bit for bit, including exact ties (round half to even)."""
+    import torch
+    r = np.random.Generator(np.random.PCG64(5))
+    a = (r.standard_normal(4096) * np.exp2(r.integers(-20, 12, 4096))).astype(np.float32)
+    # exact bf16 ties: low 16 bits = 0x8000, both parities of the kept part
+    u = a.view(np.uint32).copy()
+    u[:64] = (u[:64] & 0xFFFF0000) | 0x8000
+    u[64:128] = (u[64:128] & 0xFFFE0000) | 0x00018000
+    a = u.view(np.float32)
+    for dt, tt in (("bf16", torch.bfloat16), ("f16", torch.float16)):
+        got = cnf_inputs.round_to(a, dt)
+        ref = torch.from_numpy(a).to(tt).to(torch.float32).numpy()
+        np.testing.assert_array_equal(got.view(np.uint32), ref.view(np.uint32))
+    wl = cnf_inputs.workload("conv2d_in_div_n2", dtype="bf16")
+    x = cnf_inputs.gen_x(wl)
+    assert (x.view(np.uint32) & 0xFFFF == 0).all()      # representable in bf16
+    w = cnf_inputs.gen_params(wl)["w"]
+    assert (w.view(np.uint32) & 0xFFFF == 0).all()
 
 
 def test_inputs_are_per_sample_streams():

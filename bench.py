@@ -90,7 +90,8 @@ def algorithmic_flops(wl):
 
 
 def algorithmic_bytes(wl):
-    """Minimum HBM bytes: read x, w, b once; write the output once."""
+    """Minimum HBM bytes: read x, w (in their element type), b, gamma, beta once;
+    write the fp32 output once."""
     import cnf_inputs
     n = 1
     for v in cnf_inputs.x_shape(wl):
@@ -106,7 +107,8 @@ def algorithmic_bytes(wl):
         out = wl["N"] * wl["C_out"] * (Do // P) * (Ho // P) * (Wo // P) * (2 if wl["want_argmax"] else 1)
     else:
         out = wl["N"] * wl["C_out"] * Do * Ho * Wo
-    return 4.0 * (n + w + 3 * wl["C_out"] + out)
+    es = 2.0 if wl.get("dtype", "f32") in ("bf16", "f16") else 4.0   # x and w element size
+    return es * (n + w) + 4.0 * (3 * wl["C_out"] + out)
 
 
 def kernel_source_digest():

@@ -27,6 +27,16 @@ def test_library_exports_every_declared_symbol():
     assert set(cnf.EXPORTED) == names
 
 
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    # no CPU fallback: without libcnf.so the binding raises instead of computing
+    monkeypatch.setattr(cnf, "_lib", None)
+    monkeypatch.setattr(cnf, "LIB_PATH", str(tmp_path / "libcnf.so"))
+    with pytest.raises(ImportError):
+        cnf.load_library()
+    with pytest.raises(ImportError):
+        cnf.Plan(cnf.make_desc(cnf_inputs.workload("conv2d_in_div_n2")))
+
+
 def test_abi_version_and_status_strings():
     assert cnf.cnf_abi_version() == cnf.CNF_ABI_VERSION
     for s in range(8):

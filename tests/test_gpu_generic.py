@@ -181,6 +181,28 @@ def test_sixteen_bit_inputs_every_element(name, over, dtype):
     _case(name, dtype=dtype, **over)
 
 
+import random_descriptors  # noqa: E402
+
+RANDOM_CASES = random_descriptors.cases(48) + random_descriptors.cases(48, seed=77, first_id=950)
+
+
+@pytest.mark.parametrize("wl", RANDOM_CASES, ids=[w["name"] for w in RANDOM_CASES])
+def test_random_descriptor_sweep(wl):
+    """48 seeded random small descriptors (geometry, groups, activation, norm,
+    reduction, input type), every element against the oracle."""
+    _say(f"[random] {wl}")
+    x = cnf_inputs.gen_x(wl)
+    p = cnf_inputs.gen_params(wl)
+    plan, out, idx = run_gpu(wl, x, p)
+    ref, ref_idx = oracle.forward(wl, x, **p)
+    err = check_close(out.cpu().numpy(), ref, wl["name"])
+    if wl["want_argmax"]:
+        Pk = wl["pool_kernel"] ** wl["pool_repeats"]
+        excl = check_argmax(idx.cpu().numpy(), ref_idx, oracle_pre_pool(wl, x, p), Pk, wl["name"])
+        _say(f"    argmax ok, {excl} near-tie windows excluded")
+    _say(f"    {plan.describe().split()[0][:20]} max_abs_err={err:.3e}")
+
+
 def test_general_family_uniform_inputs():
     _case("conv2d_in_div_n2", dist="uniform", stride=2, padding=1, norm="group", num_groups=2,
           affine=1)

@@ -61,3 +61,62 @@ def cases(n: int, seed: int = 2024, first_id: int = 900) -> list:
                   dtype=str(r.choice(["f32", "f32", "bf16", "f16"])), name=f"random{seed}_{len(out)}")
         out.append(wl)
     return out
+
+
+def specialised_cases(n: int, seed: int = 31) -> list:
+    """Seeded random shapes inside the specialised families' supported sets
+    (implicit GEMM, single-write and two-pass transposed conv, softmax-pool,
+    GroupNorm-mean, small conv), all at stride 1 and no padding unless the
+    family takes padding."""
+    r = np.random.Generator(np.random.PCG64(seed))
+    base = dict(eps=1e-5, has_bias=1, stride=1, padding=0, dilation=1, output_padding=0,
+                dtype="f32", pool_kernel=0, pool_repeats=0, want_argmax=0, divide_by=1.0,
+                affine=0, norm="none", num_groups=1, reduce="none", act="none", groups=1)
+    acts = ["none", "hardswish", "gelu", "gelu_tanh"]
+    out = []
+    i = 0
+    while len(out) < n:
+        fam = ["igemm", "convt_fused", "convt", "softmax_pool", "gn_mean", "small"][i % 6]
+        i += 1
+        wl = dict(base, id=1100 + len(out), name=f"spec{seed}_{len(out)}_{fam}")
+        act = str(r.choice(acts))
+        if fam == "igemm":
+            co = int(r.choice([64, 128]))
+            norm = str(r.choice(["none", "group", "instance"]))
+            wl.update(ndim=2, kind=str(r.choice(["conv", "conv_transpose"])), N=int(r.integers(1, 3)),
+                      C_in=int(r.choice([4, 8, 12, 16, 32])), C_out=co,
+                      in_dims=(1, int(r.integers(3, 40)), int(r.integers(3, 90))), kernel=3,
+                      act=act, norm=norm, num_groups=int(r.choice([1, 8, 16])) if norm == "group" else co,
+                      affine=int(norm != "none" and r.random() < 0.5), padding=int(r.integers(0, 3)),
+                      divide_by=float(r.choice([1.0, 2.0])))
+        elif fam in ("convt_fused", "convt"):
+            G = int(r.choice([1, 2, 4, 8]))
+            W = 256 if fam == "convt_fused" else int(r.integers(3, 60))
+            wl.update(ndim=2, kind="conv_transpose", N=int(r.integers(1, 3)), C_in=8 * G, C_out=8 * G,
+                      in_dims=(1, int(r.integers(1, 40)), W), kernel=3, groups=G, act=act,
+                      norm="group", num_groups=G, affine=int(r.random() < 0.5))
+        elif fam == "softmax_pool":
+            two = bool(r.random() < 0.7)
+            wl.update(ndim=3, kind="conv", N=int(r.integers(1, 3)), C_in=3, C_out=16,
+                      in_dims=tuple(int(r.integers(6, 20)) for _ in range(3)), kernel=3,
+                      act=str(r.choice(["softmax", "softmax", "none", "gelu_tanh"])), reduce="maxpool",
+                      pool_kernel=2 if two else 4, pool_repeats=2 if two else 1,
+                      want_argmax=int(r.random() < 0.7))
+        elif fam == "gn_mean":
+            wl.update(ndim=3, kind="conv", N=int(r.integers(1, 4)), C_in=3, C_out=16,
+                      in_dims=(int(r.integers(4, 12)), int(r.integers(4, 20)), int(r.integers(4, 33))),
+                      kernel=4, act=act, norm="group", num_groups=int(r.choice([1, 2, 4, 8, 16])),
+                      affine=int(r.random() < 0.5), reduce="mean")
+        else:
+            nd = int(r.choice([2, 3]))
+            dims = (1, int(r.integers(3, 33)), int(r.integers(3, 33))) if nd == 2 else \
+                tuple(int(r.integers(3, 11)) for _ in range(3))
+            wl.update(ndim=nd, kind="conv", N=int(r.integers(1, 3)),
+                      C_in=int(r.choice([1, 3, 4, 8])) if nd == 2 else int(r.choice([1, 3])),
+                      C_out=16, in_dims=dims, kernel=3, act=act,
+                      norm=str(r.choice(["instance", "group", "none"])), num_groups=4,
+                      reduce=str(r.choice(["none", "mean"])), divide_by=float(r.choice([1.0, 2.0])))
+            if wl["norm"] == "instance":
+                wl["num_groups"] = 16
+        out.append(wl)
+    return out

@@ -203,6 +203,26 @@ def test_random_descriptor_sweep(wl):
     _say(f"    {plan.describe().split()[0][:20]} max_abs_err={err:.3e}")
 
 
+SPECIALISED_CASES = random_descriptors.specialised_cases(36)
+
+
+@pytest.mark.parametrize("wl", SPECIALISED_CASES, ids=[w["name"] for w in SPECIALISED_CASES])
+def test_random_specialised_family_sweep(wl):
+    """36 seeded random shapes inside the specialised families' supported sets
+    (whichever family the planner picks), every element against the oracle."""
+    _say(f"[random-spec] {wl}")
+    x = cnf_inputs.gen_x(wl)
+    p = cnf_inputs.gen_params(wl)
+    plan, out, idx = run_gpu(wl, x, p)
+    ref, ref_idx = oracle.forward(wl, x, **p)
+    err = check_close(out.cpu().numpy(), ref, wl["name"])
+    if wl["want_argmax"]:
+        Pk = wl["pool_kernel"] ** wl["pool_repeats"]
+        excl = check_argmax(idx.cpu().numpy(), ref_idx, oracle_pre_pool(wl, x, p), Pk, wl["name"])
+        _say(f"    argmax ok, {excl} near-tie windows excluded")
+    _say(f"    {plan.describe().split()[0][:40]} max_abs_err={err:.3e}")
+
+
 def test_general_family_uniform_inputs():
     _case("conv2d_in_div_n2", dist="uniform", stride=2, padding=1, norm="group", num_groups=2,
           affine=1)

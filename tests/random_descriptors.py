@@ -92,8 +92,12 @@ def specialised_cases(n: int, seed: int = 31) -> list:
         elif fam in ("convt_fused", "convt"):
             G = int(r.choice([1, 2, 4, 8]))
             W = 256 if fam == "convt_fused" else int(r.integers(3, 60))
+            # the single-write kernel takes heights whose (H + 3) // 2 two-row steps
+            # split into whole 4-step slices: H = 8m - 3 or 8m - 2
+            H = (8 * int(r.integers(1, 6)) - int(r.choice([2, 3])) if fam == "convt_fused"
+                 else int(r.integers(1, 40)))
             wl.update(ndim=2, kind="conv_transpose", N=int(r.integers(1, 3)), C_in=8 * G, C_out=8 * G,
-                      in_dims=(1, int(r.integers(1, 40)), W), kernel=3, groups=G, act=act,
+                      in_dims=(1, H, W), kernel=3, groups=G, act=act,
                       norm="group", num_groups=G, affine=int(r.random() < 0.5))
         elif fam == "softmax_pool":
             two = bool(r.random() < 0.7)

@@ -32,6 +32,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, un
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
                                              0x00020000);
 }
+// Resources built here span fewer than RES_MAX bytes, so GOOB is past the end of
+// every one of them: a lane that must not touch memory passes GOOB as its offset.
+constexpr unsigned GOOB = 0x7ff00000u;
+constexpr unsigned RES_MAX = 0x7f000000u;
 __device__ __forceinline__ v4f buf_load4(__amdgpu_buffer_rsrc_t r, unsigned byte_off,
                                          unsigned uniform_off = 0) {
     return __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off,

@@ -27,8 +27,10 @@
 //     first kernel makes) are double-buffered in LDS; the next chunk is
 //     fetched into registers while the current one is multiplied.
 //   * Epilogue: bias, coalesced fp32 stores of y (32 consecutive positions per
-//     register), and per-channel Welford triples merged over lanes (DPP and a
-//     shuffle), waves (LDS) into one partial per (sample, tile, channel).
+//     register), and per-channel (count, mean, M2) of each 16-lane row taken in
+//     two passes over the registers (DPP row sums, no division per lane); one
+//     Chan merge per channel over the rows (LDS) leaves one partial per
+//     (sample, tile, channel).
 #include "device.h"
 #include "kernels.h"
 
@@ -120,8 +122,6 @@ void conv2d_igemm_kernel(const float *__restrict__ x, const float *__restrict__ 
     constexpr int TR = G::TR, CS = G::CS, WPITCH = G::WPITCH, XPF = G::XPF, WPF = G::WPF;
     constexpr int XIN = G::XIN, BUF_FLOATS = G::BUF_FLOATS, XS_FLOATS = G::XS_FLOATS;
     __shared__ float lds[2 * BUF_FLOATS];
-    float (*red)[CO][3] = reinterpret_cast<float (*)[CO][3]>(lds);  // after the K loop
-    static_assert(TR * CO * 3 <= 2 * BUF_FLOATS, "reduction fits the staging buffers");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -204,50 +204,62 @@ void conv2d_igemm_kernel(const float *__restrict__ x, const float *__restrict__ 
     }
 
     // ---- epilogue
+    // Register r of acc[bi][bj] holds channel co(bi, r) (fixed per 32-lane half
+    // h) at column col0 + 32 * bj + lane % 32.  Statistics are taken per 16-lane
+    // row s16 = (lane / 16) % 2, which covers the tile columns 16 * s16 + 32 * bj
+    // + lane % 16: mean and then summed squared deviations (two passes over the
+    // registers), giving 2 * TR (count, mean, M2) partials per channel that one
+    // Chan merge per channel folds into the tile's partial.
     const int orow = row0 + wn;
-    const bool rvalid = orow < Ho;
-    float *yn = y + (size_t)n * CO * Ho * Wo;
+    const int rem = orow < Ho ? Wo - col0 : 0;  // valid columns of this wave's row
+    const int s16 = (lane >> 4) & 1;
+    const int cnt = min(max(rem - 16 * s16, 0), 16) + min(max(rem - 16 * s16 - 32, 0), 16);
+    const float rcnt = cnt ? 1.0f / (float)cnt : 0.0f;
+    const unsigned plane = (unsigned)Ho * Wo;
+    const auto yr = make_rsrc(y + (size_t)n * CO * plane, CO * plane * 4u);
+    bool ok[2];
+    unsigned off[2];
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj) {
+        ok[bj] = 32 * bj + i32 < rem;
+        off[bj] = ((unsigned)(64 * wm + 4 * h) * plane + (unsigned)orow * Wo + col0 + 32 * bj + i32) * 4u;
+    }
+    float (*red)[2][CO][3] = reinterpret_cast<float (*)[2][CO][3]>(lds);
+    static_assert(TR * 2 * CO * 3 <= 2 * BUF_FLOATS, "row partials fit the staging buffers");
 #pragma unroll
     for (int bi = 0; bi < 2; ++bi) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int co = 64 * wm + 32 * bi + 8 * (r >> 2) + 4 * h + (r & 3);
+            const int dc = 32 * bi + 8 * (r >> 2) + (r & 3);  // co - 64 * wm - 4 * h
+            const int co = 64 * wm + 4 * h + dc;
             const float bc = bias ? bias[co] : 0.0f;
-            float s1 = 0.f, s2 = 0.f;
-            int ni = 0;
+            float v[2];
 #pragma unroll
             for (int bj = 0; bj < 2; ++bj) {
-                const int col = col0 + 32 * bj + i32;
-                const float v = activate<ACT>(acc[bi][bj][r] + bc);
-                if (rvalid && col < Wo) {
-                    yn[((size_t)co * Ho + orow) * Wo + col] = v;
-                    s1 += v;
-                    s2 = fmaf(v, v, s2);
-                    ++ni;
-                }
+                v[bj] = activate<ACT>(acc[bi][bj][r] + bc);
+                buf_store1(v[bj], yr, ok[bj] ? off[bj] + (unsigned)dc * plane * 4u : GOOB);
             }
-            float cnt = (float)ni;
-            float mean = ni ? s1 / cnt : 0.0f;
-            float m2 = ni ? fmaxf(s2 - s1 * mean, 0.0f) : 0.0f;
-            row_chan16(cnt, mean, m2);
-            {
-                const float nb = __shfl_xor(cnt, 16, 64), mb = __shfl_xor(mean, 16, 64),
-                            qb = __shfl_xor(m2, 16, 64);
-                chan_merge(cnt, mean, m2, nb, mb, qb);
-            }
-            if (i32 == 0) {
-                red[wn][co][0] = cnt; red[wn][co][1] = mean; red[wn][co][2] = m2;
+            const float mean = row_sum16((ok[0] ? v[0] : 0.0f) + (ok[1] ? v[1] : 0.0f)) * rcnt;
+            const float d0 = v[0] - mean, d1 = v[1] - mean;
+            const float m2 = row_sum16((ok[0] ? d0 * d0 : 0.0f) + (ok[1] ? d1 * d1 : 0.0f));
+            if ((lane & 15) == 0) {
+                red[wn][s16][co][0] = (float)cnt;
+                red[wn][s16][co][1] = mean;
+                red[wn][s16][co][2] = m2;
             }
         }
     }
     __syncthreads();
     if (tid < CO) {
-        float cnt = 0.f, mean = 0.f, m2 = 0.f;
+        float tc = 0.f, tm = 0.f, tq = 0.f;
 #pragma unroll
-        for (int k = 0; k < TR; ++k) chan_merge(cnt, mean, m2, red[k][tid][0], red[k][tid][1], red[k][tid][2]);
+        for (int k = 0; k < TR; ++k)
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                chan_merge(tc, tm, tq, red[k][q][tid][0], red[k][q][tid][1], red[k][q][tid][2]);
         const size_t tile = (size_t)th * tiles_w + tw;
         float *pp = partials + (((size_t)n * tiles_per_sample + tile) * CO + tid) * 3;
-        pp[0] = cnt; pp[1] = mean; pp[2] = m2;
+        pp[0] = tc; pp[1] = tm; pp[2] = tq;
     }
 }
 
@@ -312,8 +324,12 @@ void conv2d_norm_pass_kernel(float *__restrict__ y, const float *__restrict__ pa
 
 bool conv2d_igemm_supported(int C_in, int C_out, int kernel, int groups, int H, int W, int act)
 {
+    // (H, W: the padded input; one sample's output planes are addressed with
+    // 32-bit byte offsets and its input planes with 32-bit element offsets)
     return (C_out == 128 || C_out == 64) && kernel == 3 && groups == 1 && C_in % CC == 0 &&
-           C_in >= CC && H >= 1 && W >= 1 &&
+           C_in >= CC && H >= 3 && W >= 3 &&
+           (long long)C_out * (H - 2) * (W - 2) * 4 < (long long)RES_MAX &&
+           (long long)C_in * H * W < (1LL << 31) &&
            (act == ACT_NONE || act == ACT_HARDSWISH || act == ACT_GELU_ERF || act == ACT_GELU_TANH);
 }
 

@@ -67,8 +67,6 @@ namespace {
 
 constexpr int GT = 256;                  // threads per workgroup (4 waves)
 constexpr int PTILE = 64;                // output positions per wave task
-constexpr unsigned GOOB = 0x7ff00000u;   // an offset past the end of every resource
-constexpr unsigned RES_MAX = 0x7f000000u;
 
 struct GenConv {
     const void *x, *wp;        // element type DT; wp: weights packed by gen_weight_pack_kernel

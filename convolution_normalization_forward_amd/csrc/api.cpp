@@ -29,7 +29,7 @@ const char *family_name(int f)
     case FAM_GN_MEAN: return "conv3d_k4_gn_mean(fused,1wg/sample,mfma16x16x4)";
     case FAM_SOFTMAX_POOL: return "conv3d_softmax_pool4(1wave/window,mfma16x16x4)";
     case FAM_SMALL: return "small_conv_norm(1wg/sample,mfma16x16x4)";
-    case FAM_IGEMM: return "conv2d_igemm(mfma32x32x2)+norm_pass";
+    case FAM_IGEMM: return "conv2d_igemm(mfma32x32x2)+norm_finalize+apply";
     case FAM_CONVT: return "convt2d_grouped8(mfma16x16x4,column-pair)+groupnorm_pass";
     case FAM_CONVT_FUSED: return "convt2d_grouped8_gn_fused(cooperative,single-write)";
     case FAM_GENERIC: return "generic(gathered-igemm mfma16x16x4 + softmax/finalize/apply/pool passes)";

@@ -1,7 +1,8 @@
 // k_conv2d_igemm.hip -- Conv2d (C_out = 128 or 64, k = 3, C_in a multiple of
 // 4, optional zero padding) as an implicit GEMM on fp32 MFMA, with bias,
-// activation and per-tile Welford partials in the epilogue, followed by an
-// in-place InstanceNorm / GroupNorm + divide pass.  A dense (groups = 1)
+// activation and per-tile Welford partials in the epilogue, followed by a
+// statistics finalize (scale and shift per channel) and an in-place
+// InstanceNorm / GroupNorm + divide pass.  A dense (groups = 1)
 // stride-1 ConvTranspose2d is the same GEMM on the input padded by k - 1 with
 // the kernel flipped and its channel axes swapped (page "Kimi-K2.6__l2_p19",
 // second trace: out[i, j] = sum x[i - kh, j - kw] W[ci, co, kh, kw]), so it
@@ -263,61 +264,69 @@ void conv2d_igemm_kernel(const float *__restrict__ x, const float *__restrict__ 
     }
 }
 
-// One workgroup per (sample, channel): merge the group's per-tile partials in
-// a fixed order (each thread folds a strided subset, then thread 0 folds the
-// 256 results in thread order), then normalise the plane in place and divide.
+// Statistics -> per-channel scale and shift.  One wave per (sample, norm
+// group): lane l folds the group's (channel, tile) partials l, l + 64, ... in
+// order, the 64 lane results are merged by a fixed tree (DPP rows, then the two
+// row pairs, then the halves), and lane 0's result is the group's, so every
+// channel of the group uses the same mean and variance.
 __global__ __launch_bounds__(256)
-void conv2d_norm_pass_kernel(float *__restrict__ y, const float *__restrict__ partials,
-                             const float *__restrict__ gamma, const float *__restrict__ beta,
-                             int C, int plane, int tiles_per_sample, int norm_groups, float eps,
-                             float inv_div)
+void conv2d_norm_finalize_kernel(const float *__restrict__ partials, const float *__restrict__ gamma,
+                                 const float *__restrict__ beta, v2f *__restrict__ ss, int N, int C,
+                                 int tiles, int norm_groups, float eps, float inv_div)
 {
-    const int nc = blockIdx.x;
-    const int n = nc / C, c = nc % C;
-    const int tid = threadIdx.x;
-    __shared__ float tri[256][3];
-    __shared__ float coef[2];
-    if (norm_groups > 0) {
-        const int cg = C / norm_groups, g0 = (c / cg) * cg;
-        const int items = cg * tiles_per_sample;  // (channel j, tile t) pairs
-        float cnt = 0.f, mean = 0.f, m2 = 0.f;
-        for (int i = tid; i < items; i += 256) {
-            const int j = i / tiles_per_sample, t = i % tiles_per_sample;
-            const float *pp = partials + (((size_t)n * tiles_per_sample + t) * C + g0 + j) * 3;
-            chan_merge(cnt, mean, m2, pp[0], pp[1], pp[2]);
-        }
-        tri[tid][0] = cnt; tri[tid][1] = mean; tri[tid][2] = m2;
-        __syncthreads();
-        if (tid == 0) {
-            float tc = 0.f, tm = 0.f, tq = 0.f;
-            for (int k = 0; k < 256; ++k) chan_merge(tc, tm, tq, tri[k][0], tri[k][1], tri[k][2]);
-            const float rstd = rsqrtf(tq / tc + eps);
-            const float ga = gamma ? gamma[c] : 1.0f, be = beta ? beta[c] : 0.0f;
-            coef[0] = rstd * ga * inv_div;
-            coef[1] = (be - tm * rstd * ga) * inv_div;
-        }
-    } else if (tid == 0) {
-        coef[0] = inv_div;  // no norm: the divide alone
-        coef[1] = 0.0f;
+    const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (wid >= N * norm_groups) return;  // whole waves; the kernel has no barriers
+    const int n = wid / norm_groups, g = wid % norm_groups;
+    const int cg = C / norm_groups, c0 = g * cg;
+    const int items = cg * tiles;
+    float cnt = 0.f, mean = 0.f, m2 = 0.f;
+    for (int i = lane; i < items; i += 64) {
+        const int j = i / tiles, t = i % tiles;
+        const float *pp = partials + (((size_t)n * tiles + t) * C + c0 + j) * 3;
+        chan_merge(cnt, mean, m2, pp[0], pp[1], pp[2]);
     }
-    __syncthreads();
-    const float sc = coef[0], sh = coef[1];
-    float *p = y + (size_t)nc * plane;
-    if ((plane & 3) == 0) {
-        v4f *p4 = reinterpret_cast<v4f *>(p);
-        const int n4 = plane / 4;
-        int i = tid;
-        for (; i + 3 * 256 < n4; i += 4 * 256) {  // four loads in flight per thread
-            v4f a0 = p4[i], a1 = p4[i + 256], a2 = p4[i + 512], a3 = p4[i + 768];
-            p4[i] = a0 * sc + sh;
-            p4[i + 256] = a1 * sc + sh;
-            p4[i + 512] = a2 * sc + sh;
-            p4[i + 768] = a3 * sc + sh;
-        }
-        for (; i < n4; i += 256) p4[i] = p4[i] * sc + sh;
-    } else {
-        for (int i = tid; i < plane; i += 256) p[i] = p[i] * sc + sh;
+    row_chan16(cnt, mean, m2);
+#pragma unroll
+    for (int sh = 16; sh <= 32; sh *= 2) {
+        const float nb = __shfl_xor(cnt, sh, 64), mb = __shfl_xor(mean, sh, 64),
+                    qb = __shfl_xor(m2, sh, 64);
+        chan_merge(cnt, mean, m2, nb, mb, qb);
     }
+    cnt = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, cnt)));
+    mean = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, mean)));
+    m2 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, m2)));
+    const float rstd = rsqrtf(m2 / cnt + eps);
+    for (int j = lane; j < cg; j += 64) {
+        const int c = c0 + j;
+        const float ga = gamma ? gamma[c] : 1.0f, be = beta ? beta[c] : 0.0f;
+        ss[(size_t)n * C + c] = v2f{rstd * ga * inv_div, (be - mean * rstd * ga) * inv_div};
+    }
+}
+
+// y = y * scale + shift in place, with (scale, shift) per (sample, channel)
+// plane (ss) or uniform (ss null: the divide alone).  Workgroup b covers chunk
+// b % chunks of plane b / chunks: APPLY_V vectors of VEC floats per thread,
+// all loads issued before the stores.  VEC = 4 needs plane % 4 == 0.
+constexpr int APPLY_V = 4;
+template <int VEC>
+__global__ __launch_bounds__(256)
+void conv2d_apply_kernel(float *__restrict__ y, const v2f *__restrict__ ss, float uscale,
+                         int plane, int chunks)
+{
+    typedef float vt __attribute__((ext_vector_type(VEC)));
+    const int p = blockIdx.x / chunks, chunk = blockIdx.x - p * chunks;
+    const v2f s = ss ? ss[p] : v2f{uscale, 0.0f};
+    const int nv = plane / VEC;
+    vt *yp = reinterpret_cast<vt *>(y + (size_t)p * plane);
+    const int i0 = chunk * (256 * APPLY_V) + threadIdx.x;
+    vt v[APPLY_V];
+#pragma unroll
+    for (int k = 0; k < APPLY_V; ++k)
+        if (i0 + k * 256 < nv) v[k] = yp[i0 + k * 256];
+#pragma unroll
+    for (int k = 0; k < APPLY_V; ++k)
+        if (i0 + k * 256 < nv) yp[i0 + k * 256] = v[k] * s[0] + s[1];
 }
 
 }  // namespace
@@ -343,9 +352,10 @@ static size_t tiles_of(int C_out, int Ho, int Wo)
 
 size_t conv2d_igemm_workspace(int N, int C_in, int C_out, int Ho, int Wo)
 {
-    // [N][tiles][C_out][3] Welford partials, then the [ci][tap][co] weight copy
+    // [N][tiles][C_out][3] Welford partials, the [ci][tap][co] weight copy, then
+    // [N][C_out] (scale, shift) pairs
     return (size_t)N * tiles_of(C_out, Ho, Wo) * C_out * 3 * sizeof(float) +
-           (size_t)C_in * 9 * C_out * sizeof(float);
+           (size_t)C_in * 9 * C_out * sizeof(float) + (size_t)N * C_out * 2 * sizeof(float);
 }
 
 template <int CO, int ACT>
@@ -376,9 +386,25 @@ hipError_t launch_conv2d_igemm(const Conv2dIgemmArgs &a, hipStream_t st)
     return hipErrorInvalidValue;
 #undef CNF_CASE
     if (a.norm_groups > 0 || a.inv_div != 1.0f) {
-        hipLaunchKernelGGL(conv2d_norm_pass_kernel, dim3(a.N * CO), dim3(256), 0, st, a.out,
-                           a.partials, a.gamma, a.beta, CO, a.Ho * a.Wo, tps, a.norm_groups,
-                           a.eps, a.inv_div);
+        v2f *ss = nullptr;
+        if (a.norm_groups > 0) {
+            ss = reinterpret_cast<v2f *>(wt + (size_t)a.C_in * 9 * CO);
+            const int waves = a.N * a.norm_groups;
+            hipLaunchKernelGGL(conv2d_norm_finalize_kernel, dim3((waves + 3) / 4), dim3(256), 0, st,
+                               a.partials, a.gamma, a.beta, ss, a.N, CO, tps, a.norm_groups, a.eps,
+                               a.inv_div);
+        }
+        const int plane = a.Ho * a.Wo;
+        const int vec = plane % 4 == 0 ? 4 : 1;
+        const int chunks = (plane / vec + 256 * APPLY_V - 1) / (256 * APPLY_V);
+        if ((long long)a.N * CO * chunks > 0x7fffffffLL) return hipErrorInvalidValue;
+        const dim3 grid((unsigned)(a.N * CO * chunks));
+        if (vec == 4)
+            hipLaunchKernelGGL(conv2d_apply_kernel<4>, grid, dim3(256), 0, st, a.out, ss, a.inv_div,
+                               plane, chunks);
+        else
+            hipLaunchKernelGGL(conv2d_apply_kernel<1>, grid, dim3(256), 0, st, a.out, ss, a.inv_div,
+                               plane, chunks);
     }
     return hipGetLastError();
 }

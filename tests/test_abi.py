@@ -143,7 +143,8 @@ def test_forward_rejects_bad_pointers_before_launch():
 def test_workspace_sizes_are_what_the_partials_need():
     p4 = cnf.Plan(_desc("conv2d_in_div_n128"))
     tiles = 2 * 32   # 126 = 64 + 62 columns, 126 rows in blocks of 4
-    assert p4.workspace_bytes == 128 * tiles * 128 * 3 * 4 + 64 * 9 * 128 * 4
+    # partials, the [ci][tap][co] weight copy, one (scale, shift) per (n, c)
+    assert p4.workspace_bytes == 128 * tiles * 128 * 3 * 4 + 64 * 9 * 128 * 4 + 128 * 128 * 8
     p5 = cnf.Plan(_desc("convt2d_gelu_gn_n128"))
     # the larger of the single-write kernel's slice triples (16 B header +
     # 1024 units x 32 slices x 16 B) and the two-pass fallback's per-channel

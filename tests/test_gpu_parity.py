@@ -102,6 +102,13 @@ SMALL_CASES = [
     ("conv2d_in_div_n128", dict(N=2, C_in=8, C_out=64, in_dims=(1, 19, 70), norm="group",
                                 num_groups=8, affine=1)),
     ("conv2d_in_div_n128", dict(N=1, C_in=12, in_dims=(1, 13, 40), act="hardswish")),
+    # implicit GEMM second pass: the divide alone (uniform scale), no pass at all, and
+    # one GroupNorm group over all 128 channels (each lane folds many tile partials)
+    ("conv2d_in_div_n128", dict(N=2, C_in=8, in_dims=(1, 17, 45), norm="none")),
+    ("conv2d_in_div_n128", dict(N=1, C_in=8, in_dims=(1, 12, 66), norm="none", divide_by=1.0,
+                                act="gelu")),
+    ("conv2d_in_div_n128", dict(N=2, C_in=8, in_dims=(1, 30, 140), norm="group", num_groups=1,
+                                affine=1)),
     # dense transposed conv (groups 1) on the implicit GEMM: padded input, flipped kernel
     ("convt2d_dense_gelu_gn_n128", dict(N=2, C_in=8, C_out=64, in_dims=(1, 9, 20))),
     ("convt2d_dense_gelu_gn_n128", dict(N=2, C_in=16, C_out=128, in_dims=(1, 14, 61),

@@ -548,24 +548,42 @@ __global__ __launch_bounds__(GT) void gen_finalize_kernel(const v4f *part, int C
     }
 }
 
-// y[plane][i] = y * scale[plane] + shift[plane]; blockIdx.x = plane, blockIdx.y =
-// chunk of APPLY_CHUNK elements.  Planes of a multiple of 4 elements are 16-byte
-// aligned and go by 16-byte accesses.
-constexpr int APPLY_CHUNK = GT * 16;
-__global__ __launch_bounds__(GT) void gen_apply_kernel(float *y, const v2f *ss, int S) {
-    const v2f sc = ss[blockIdx.x];
-    float *p = y + (size_t)blockIdx.x * S;
-    const int lo = blockIdx.y * APPLY_CHUNK, hi = min(S, lo + APPLY_CHUNK);
-    if ((S & 3) == 0) {
-        v4f *q = reinterpret_cast<v4f *>(p);
-        for (int i = lo / 4 + threadIdx.x; i < hi / 4; i += GT) {
-            v4f v = q[i];
-            v[0] = fmaf(v[0], sc[0], sc[1]); v[1] = fmaf(v[1], sc[0], sc[1]);
-            v[2] = fmaf(v[2], sc[0], sc[1]); v[3] = fmaf(v[3], sc[0], sc[1]);
-            q[i] = v;
+// y[plane][i] = y * scale[plane] + shift[plane]; workgroup b takes chunk
+// b % chunks (of APPLY_CHUNK elements) of plane b / chunks, so consecutive
+// workgroups stream consecutive addresses.  Planes of a multiple of 4 elements
+// are 16-byte aligned and go by 16-byte accesses.  Each thread issues all its
+// loads before its stores (a load-store loop kept one load in flight per thread).
+constexpr int APPLY_PER = 4;                    // accesses per thread
+constexpr int APPLY_CHUNK = GT * APPLY_PER * 4;
+template <int VEC>
+__device__ __forceinline__ void apply_chunk(float *p, int lo, int hi, v2f sc) {
+    typedef float vt __attribute__((ext_vector_type(VEC)));
+    vt *q = reinterpret_cast<vt *>(p);
+    const int i0 = lo / VEC + threadIdx.x, n = hi / VEC;
+    vt v[APPLY_PER];
+#pragma unroll
+    for (int k = 0; k < APPLY_PER; ++k)
+        if (i0 + k * GT < n) v[k] = q[i0 + k * GT];
+#pragma unroll
+    for (int k = 0; k < APPLY_PER; ++k) {
+        if (i0 + k * GT < n) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) v[k][e] = fmaf(v[k][e], sc[0], sc[1]);
+            q[i0 + k * GT] = v[k];
         }
+    }
+}
+__global__ __launch_bounds__(GT) void gen_apply_kernel(float *y, const v2f *ss, int S, int chunks) {
+    const int plane = blockIdx.x / chunks, chunk = blockIdx.x - plane * chunks;
+    const v2f sc = ss[plane];
+    float *p = y + (size_t)plane * S;
+    const int lo = chunk * APPLY_CHUNK, hi = min(S, lo + APPLY_CHUNK);
+    if ((S & 3) == 0) {
+        apply_chunk<4>(p, lo, hi, sc);
     } else {
-        for (int i = lo + threadIdx.x; i < hi; i += GT) p[i] = fmaf(p[i], sc[0], sc[1]);
+        // scalar accesses: the chunk in APPLY_CHUNK / (GT * APPLY_PER) passes
+        for (int part = lo; part < hi; part += GT * APPLY_PER)
+            apply_chunk<1>(p, part, min(hi, part + GT * APPLY_PER), sc);
     }
 }
 
@@ -738,6 +756,8 @@ bool generic_supported(const GenericArgs &a) {
     if ((long long)a.N * L.nph * L.Tq * L.GTn * L.cobN >= (1LL << 31) - 64) return false;
     if (L.wp_elems * L.ES >= RES_MAX) return false;
     if ((long long)a.N * a.C_out * S / GT >= (1LL << 31) - 1) return false;
+    if ((long long)a.N * a.C_out * ((S + APPLY_CHUNK - 1) / APPLY_CHUNK) >= (1LL << 31) - 1)
+        return false;
     return true;
 }
 
@@ -835,8 +855,8 @@ hipError_t launch_generic(const GenericArgs &a, hipStream_t st) {
     // 4. in-place normalisation of the output
     if (L.apply) {
         const unsigned chunks = (unsigned)((S + APPLY_CHUNK - 1) / APPLY_CHUNK);
-        gen_apply_kernel<<<dim3((unsigned)((long long)a.N * a.C_out), chunks), dim3(GT), 0, st>>>(
-            a.out, ss, S);
+        gen_apply_kernel<<<dim3((unsigned)((long long)a.N * a.C_out * chunks)), dim3(GT), 0, st>>>(
+            a.out, ss, S, (int)chunks);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
 

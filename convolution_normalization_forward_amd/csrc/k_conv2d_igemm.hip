@@ -19,12 +19,15 @@
 // Mapping:
 //   * GEMM rows = the 128 output channels (A = weights), columns = output
 //     positions (B = im2col of x), K = C_in * 9 ordered (tap, channel).
-//   * A workgroup (8 waves) owns all CO channels x a TR-row x 64-column block
-//     of output positions of one sample (TR = 4 for 128 channels, 8 for 64);
-//     wave (wm, wn) computes channels 64*wm .. +63 on output row wn as 2 x 2
-//     tiles of v_mfma_f32_32x32x2f32.
+//   * A workgroup (8 waves) owns all CO channels x a TR-row x 32-column block
+//     of output positions of one sample (TR = 8 for 128 channels, 16 for 64);
+//     wave (wm, wn) computes channels 64*wm .. +63 on output rows 2*wn and
+//     2*wn + 1 as 2 x 2 tiles of v_mfma_f32_32x32x2f32 (channel half x row).
+//     32-column tiles keep the padding of the last column tile small for
+//     widths just past a multiple of 64 (258 = 4 * 64 + 2 wasted a quarter of
+//     the MFMA work with 64-column tiles).
 //   * K is walked in chunks of CC input channels: the chunk's input halo
-//     (CC x 6 x 66) and its weights (9*CC x 128, from a [ci][tap][co] copy the
+//     (CC x (TR + 2) x 34) and its weights (9*CC x CO, from a [ci][tap][co] copy the
 //     first kernel makes) are double-buffered in LDS; the next chunk is
 //     fetched into registers while the current one is multiplied.
 //   * Epilogue: bias, coalesced fp32 stores of y (32 consecutive positions per
@@ -41,16 +44,17 @@ namespace {
 
 constexpr int CC = 4;                    // input channels per K chunk
 constexpr int KC = 9 * CC;               // K per chunk
-constexpr int TC = 64;                   // output tile columns
-constexpr int PITCH = 68;                // LDS row pitch of the input halo
+constexpr int TC = 32;                   // output tile columns
+constexpr int PITCH = 36;                // LDS row pitch of the input halo
 constexpr int THREADS = 512;
 constexpr int NWAVES = THREADS / 64;
 
 // Tile geometry for CO output channels (128 or 64): 64 channels x 64 columns
-// per wave, so TR = 8 waves / (CO / 64) output rows per tile.
+// (two rows of 32) per wave, so NR = 8 waves / (CO / 64) waves along the rows
+// and TR = 2 * NR output rows per tile.
 template <int CO>
 struct Geo {
-    static constexpr int WM = CO / 64, TR = NWAVES / WM;
+    static constexpr int WM = CO / 64, NR = NWAVES / WM, TR = 2 * NR;
     static constexpr int CS_BASE = (TR + 2) * PITCH;
     static constexpr int CS = CS_BASE + ((32 - CS_BASE % 64) + 64) % 64;  // == 32 mod 64
     static constexpr int WPITCH = CO + 32;                                // == 32 mod 64
@@ -61,7 +65,7 @@ struct Geo {
     static constexpr int XPF = (XIN + THREADS - 1) / THREADS;      // per-thread prefetch (scalar)
     static constexpr int WPF = (KC * CO / 4 + THREADS - 1) / THREADS;  // (float4)
     static_assert(CS % 64 == 32 && WPITCH % 64 == 32, "bank spread");
-    static_assert(TR * (CO / 64) == NWAVES, "one 64 x 64 block per wave");
+    static_assert(NR * WM == NWAVES, "one 64-channel x 64-position block per wave");
 };
 
 // Conv: w[co][ci][kh][kw] -> wt[ci][tap][co].  Transposed conv (weights
@@ -120,13 +124,13 @@ void conv2d_igemm_kernel(const float *__restrict__ x, const float *__restrict__ 
                          int pad, int tiles_w, int tiles_per_sample)
 {
     using G = Geo<CO>;
-    constexpr int TR = G::TR, CS = G::CS, WPITCH = G::WPITCH, XPF = G::XPF, WPF = G::WPF;
+    constexpr int TR = G::TR, NR = G::NR, CS = G::CS, WPITCH = G::WPITCH, XPF = G::XPF, WPF = G::WPF;
     constexpr int XIN = G::XIN, BUF_FLOATS = G::BUF_FLOATS, XS_FLOATS = G::XS_FLOATS;
     __shared__ float lds[2 * BUF_FLOATS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / TR, wn = wave % TR;
+    const int wm = wave / NR, wn = wave % NR;
     const int h = lane >> 5, i32 = lane & 31;
     // XCD-aware tile order: each XCD takes a contiguous run of (n, row tile,
     // column tile), so vertically adjacent tiles share their halo rows in L2.
@@ -182,7 +186,7 @@ void conv2d_igemm_kernel(const float *__restrict__ x, const float *__restrict__ 
         const float *xs = lds + buf * BUF_FLOATS;
         const float *ws = xs + XS_FLOATS;
         const float *wa = ws + h * WPITCH + 64 * wm + i32;
-        const float *xb = xs + h * CS + wn * PITCH + i32;
+        const float *xb = xs + h * CS + 2 * wn * PITCH + i32;
 #pragma unroll
         for (int tap = 0; tap < 9; ++tap) {
             const int kh = tap / 3, kw = tap % 3;
@@ -192,7 +196,7 @@ void conv2d_igemm_kernel(const float *__restrict__ x, const float *__restrict__ 
                 const float a0 = wa[2 * s * WPITCH];
                 const float a1 = wa[2 * s * WPITCH + 32];
                 const float b0 = xb[2 * p * CS + kh * PITCH + kw];
-                const float b1 = xb[2 * p * CS + kh * PITCH + kw + 32];
+                const float b1 = xb[2 * p * CS + (kh + 1) * PITCH + kw];
                 acc[0][0] = mfma_32x32x2(a0, b0, acc[0][0]);
                 acc[0][1] = mfma_32x32x2(a0, b1, acc[0][1]);
                 acc[1][0] = mfma_32x32x2(a1, b0, acc[1][0]);
@@ -206,15 +210,16 @@ void conv2d_igemm_kernel(const float *__restrict__ x, const float *__restrict__ 
 
     // ---- epilogue
     // Register r of acc[bi][bj] holds channel co(bi, r) (fixed per 32-lane half
-    // h) at column col0 + 32 * bj + lane % 32.  Statistics are taken per 16-lane
-    // row s16 = (lane / 16) % 2, which covers the tile columns 16 * s16 + 32 * bj
-    // + lane % 16: mean and then summed squared deviations (two passes over the
-    // registers), giving 2 * TR (count, mean, M2) partials per channel that one
-    // Chan merge per channel folds into the tile's partial.
-    const int orow = row0 + wn;
-    const int rem = orow < Ho ? Wo - col0 : 0;  // valid columns of this wave's row
+    // h) at row row0 + 2 * wn + bj, column col0 + lane % 32.  Statistics are
+    // taken per 16-lane row s16 = (lane / 16) % 2, which covers the tile columns
+    // 16 * s16 + lane % 16 of both rows: mean and then summed squared deviations
+    // (two passes over the registers), giving 2 * NR (count, mean, M2) partials
+    // per channel that one Chan merge per channel folds into the tile's partial.
     const int s16 = (lane >> 4) & 1;
-    const int cnt = min(max(rem - 16 * s16, 0), 16) + min(max(rem - 16 * s16 - 32, 0), 16);
+    int rem[2];  // valid columns of each of the wave's two rows
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj) rem[bj] = row0 + 2 * wn + bj < Ho ? Wo - col0 : 0;
+    const int cnt = min(max(rem[0] - 16 * s16, 0), 16) + min(max(rem[1] - 16 * s16, 0), 16);
     const float rcnt = cnt ? 1.0f / (float)cnt : 0.0f;
     const unsigned plane = (unsigned)Ho * Wo;
     const auto yr = make_rsrc(y + (size_t)n * CO * plane, CO * plane * 4u);
@@ -222,11 +227,12 @@ void conv2d_igemm_kernel(const float *__restrict__ x, const float *__restrict__ 
     unsigned off[2];
 #pragma unroll
     for (int bj = 0; bj < 2; ++bj) {
-        ok[bj] = 32 * bj + i32 < rem;
-        off[bj] = ((unsigned)(64 * wm + 4 * h) * plane + (unsigned)orow * Wo + col0 + 32 * bj + i32) * 4u;
+        ok[bj] = i32 < rem[bj];
+        off[bj] = ((unsigned)(64 * wm + 4 * h) * plane + (unsigned)(row0 + 2 * wn + bj) * Wo + col0 +
+                   i32) * 4u;
     }
     float (*red)[2][CO][3] = reinterpret_cast<float (*)[2][CO][3]>(lds);
-    static_assert(TR * 2 * CO * 3 <= 2 * BUF_FLOATS, "row partials fit the staging buffers");
+    static_assert(NR * 2 * CO * 3 <= 2 * BUF_FLOATS, "row partials fit the staging buffers");
 #pragma unroll
     for (int bi = 0; bi < 2; ++bi) {
 #pragma unroll
@@ -254,7 +260,7 @@ void conv2d_igemm_kernel(const float *__restrict__ x, const float *__restrict__ 
     if (tid < CO) {
         float tc = 0.f, tm = 0.f, tq = 0.f;
 #pragma unroll
-        for (int k = 0; k < TR; ++k)
+        for (int k = 0; k < NR; ++k)
 #pragma unroll
             for (int q = 0; q < 2; ++q)
                 chan_merge(tc, tm, tq, red[k][q][tid][0], red[k][q][tid][1], red[k][q][tid][2]);

@@ -142,7 +142,7 @@ def test_forward_rejects_bad_pointers_before_launch():
 
 def test_workspace_sizes_are_what_the_partials_need():
     p4 = cnf.Plan(_desc("conv2d_in_div_n128"))
-    tiles = 2 * 32   # 126 = 64 + 62 columns, 126 rows in blocks of 4
+    tiles = 4 * 16   # 126 columns in tiles of 32, 126 rows in tiles of 8
     # partials, the [ci][tap][co] weight copy, one (scale, shift) per (n, c)
     assert p4.workspace_bytes == 128 * tiles * 128 * 3 * 4 + 64 * 9 * 128 * 4 + 128 * 128 * 8
     p5 = cnf.Plan(_desc("convt2d_gelu_gn_n128"))

@@ -23,9 +23,12 @@
 //     The accumulator starts at the bias.
 //   * Lane l holds channels 4*(l/16) + r (r = 0..3) of position l%16, so the
 //     softmax over the 16 channels is 3 in-lane steps and two cross-row
-//     exchanges (xor 16, xor 32) per reduction, instead of a 16-lane DPP
-//     reduction per value.  For the softmax, weights and bias carry the factor
-//     log2(e), so each exponential is one exp2 of (logit - max).
+//     exchanges (xor 16, xor 32, on the LDS pipe) per reduction, instead of a
+//     16-lane DPP reduction per value.  (gfx950's permlane swaps would do the
+//     exchange on the VALU, but each costs a copy and the swap there, and
+//     this kernel is bound by VALU + MFMA issue: measured slower.)  For the
+//     softmax, weights and bias carry the factor log2(e), so each
+//     exponential is one exp2 of (logit - max).
 //   * The window maximum of channel c and its argmax are reduced in-lane over
 //     depth, then across the 16 lanes (positions) of the row.  Ties resolve as
 //     the literal sequence of pools would (first 2x2x2 block in scan order, then
@@ -188,12 +191,24 @@ void conv3d_softmax_pool_kernel(const float *__restrict__ x, const float *__rest
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[j] = bias4;
         const float *pb = patch[BUF];
+        // B operands one K step ahead: the reads of step s + 1 are issued before
+        // the four MFMAs of step s (pinned by the scheduling groups), so a step
+        // waits only for reads issued a step earlier.
+        float bop[2][4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bop[0][j] = pb[lbase + toff[0] + j * G::E * PP];
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);          // step 0's LDS reads
 #pragma unroll
         for (int s = 0; s < G::NS; ++s) {
-            const int a0 = lbase + toff[s];
+            if (s + 1 < G::NS) {
+                const int a1 = lbase + toff[s + 1];
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[j] = mfma_16x16x4(wreg[s], pb[a0 + j * G::E * PP], acc[j]);
+                for (int j = 0; j < 4; ++j) bop[(s + 1) & 1][j] = pb[a1 + j * G::E * PP];
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // the step's LDS reads
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[j] = mfma_16x16x4(wreg[s], bop[s & 1][j], acc[j]);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);      // then its MFMAs
         }
 
         // activation; the softmax at position (j, c16) runs over the lane's 4

@@ -99,8 +99,6 @@ void conv3d_softmax_pool_kernel(const float *__restrict__ x, const float *__rest
     int toff[G::NS];
 #pragma unroll
     for (int s = 0; s < G::NS; ++s) {
-        const int k = 4 * s + q;
-        wreg[s] = k < G::K ? w[c16 * G::K + k] * LSCALE : 0.0f;
         const int t0 = G::tap_off(4 * s), t1 = G::tap_off(4 * s + 1);
         const int t2 = G::tap_off(4 * s + 2), t3 = G::tap_off(4 * s + 3);
         toff[s] = q < 2 ? (q == 0 ? t0 : t1) : (q == 2 ? t2 : t3);
@@ -176,6 +174,27 @@ void conv3d_softmax_pool_kernel(const float *__restrict__ x, const float *__rest
     int n, od, oh, ow;
     if (first >= hi) return;
     CNF_FETCH(window_base(first, n, od, oh, ow))
+    // Weights: every wave of the grid needs the whole (16 x K) tensor at once,
+    // and per-lane 4-byte gathers from it (lane l wants w[l%16][4s + l/16])
+    // pile ~20 requests per wave onto the same few L2 lines at kernel start.
+    // Instead the wave reads it with contiguous float4 loads (16 * K is a
+    // multiple of 4 and w is 16-byte aligned), parks it in the patch buffers
+    // (not yet in use), and picks its A operands from LDS.
+    {
+        constexpr int WN = 16 * G::K;
+        static_assert(WN % 4 == 0 && WN <= 2 * (G::FLOATS + 8), "weights fit the patch buffers");
+        float *wl = &patch[0][0];
+#pragma unroll
+        for (int i = 4 * lane; i < WN; i += 256)
+            *reinterpret_cast<v4f *>(wl + i) = *reinterpret_cast<const v4f *>(w + i);
+        __syncthreads();
+#pragma unroll
+        for (int s = 0; s < G::NS; ++s) {
+            const int k = 4 * s + q;
+            wreg[s] = k < G::K ? wl[c16 * G::K + k] * LSCALE : 0.0f;
+        }
+        __syncthreads();  // every lane has its weights before the patch overwrites them
+    }
     CNF_STASH(0)
     // One window on patch buffer BUF (a compile-time constant, so every LDS
     // operand address is a per-lane base plus an immediate offset).

@@ -55,9 +55,41 @@ void small_conv_norm_kernel(const float *__restrict__ x, const float *__restrict
     const int T = (P + 15) >> 4;
     const int in_floats = CI * D * HW;
 
-    // stage the whole sample
+    // Stage the whole sample, every load of a thread in flight before its LDS
+    // stores (a load-then-store loop waits out one memory latency per element
+    // group).  float4 when the sample size keeps every sample 16-byte aligned
+    // (x itself is), else batches of 8 scalars.
     const float *xs = x + (size_t)n * in_floats;
-    for (int e = tid; e < in_floats; e += THREADS) lds[e] = xs[e];
+    if ((in_floats & 3) == 0) {
+        constexpr int MAXV = (MAX_LDS_FLOATS / 4 + THREADS - 1) / THREADS;
+        const int nv = in_floats >> 2;
+        const v4f *xs4 = reinterpret_cast<const v4f *>(xs);
+        v4f buf[MAXV];
+#pragma unroll
+        for (int u = 0; u < MAXV; ++u) {
+            const int e = tid + u * THREADS;
+            buf[u] = e < nv ? xs4[e] : v4f{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int u = 0; u < MAXV; ++u) {
+            const int e = tid + u * THREADS;
+            if (e < nv) reinterpret_cast<v4f *>(lds)[e] = buf[u];
+        }
+    } else {
+        for (int e0 = 0; e0 < in_floats; e0 += 8 * THREADS) {
+            float buf[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int e = e0 + tid + u * THREADS;
+                buf[u] = e < in_floats ? xs[e] : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int e = e0 + tid + u * THREADS;
+                if (e < in_floats) lds[e] = buf[u];
+            }
+        }
+    }
 
     float wreg[NS];
     int toff[NS];

@@ -195,7 +195,8 @@ cnf_status cnf_plan_create(const cnf_desc *desc, cnf_plan **plan)
     // CNF_FORCE_GENERIC environment variable (tests) sends everything to the
     // general family.
     const char *force = std::getenv("CNF_FORCE_GENERIC");
-    // (16-bit inputs: the general family only)
+    // (16-bit inputs: the general family, except the single-write transposed
+    // conv below)
     const bool unit = d.stride == 1 && d.dilation == 1 && d.output_padding == 0 &&
                       d.dtype == CNF_DTYPE_F32 && !(force && force[0] == '1');
     const bool basic = unit && d.padding == 0;
@@ -240,9 +241,19 @@ cnf_status cnf_plan_create(const cnf_desc *desc, cnf_plan **plan)
                                          d.num_groups))
             p.family = FAM_CONVT_FUSED;
     }
+    // 16-bit x and w of the single-write transposed-conv shape: that kernel widens
+    // them to fp32 as it loads them.  The general family stays its fallback (for a
+    // grid that cannot be co-resident), so it must take the descriptor too.
+    const cnf::GenericArgs ga = generic_args(p, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                             nullptr, nullptr, nullptr, norm_groups);
+    if (!p.family && d.dtype != CNF_DTYPE_F32 && !(force && force[0] == '1') &&
+        d.kind == CNF_CONV_TRANSPOSE && d.ndim == 2 && d.reduce == CNF_RED_NONE &&
+        d.stride == 1 && d.dilation == 1 && d.output_padding == 0 && d.padding == 0 &&
+        cnf::convt2d_supported(d.C_in, d.C_out, k, d.groups, H, W, d.act, d.norm, d.num_groups) &&
+        cnf::convt2d_fused_supported(d.C_in, d.C_out, d.groups, H, W, d.act, d.norm, d.num_groups) &&
+        cnf::generic_supported(ga))
+        p.family = FAM_CONVT_FUSED;
     if (!p.family) {
-        const cnf::GenericArgs ga = generic_args(p, nullptr, nullptr, nullptr, nullptr, nullptr,
-                                                 nullptr, nullptr, nullptr, norm_groups);
         if (!cnf::generic_supported(ga)) return CNF_ERR_UNSUPPORTED;
         p.family = FAM_GENERIC;
     }
@@ -256,9 +267,11 @@ cnf_status cnf_plan_create(const cnf_desc *desc, cnf_plan **plan)
                                                           nullptr, nullptr, nullptr, nullptr,
                                                           norm_groups));
     if (p.family == FAM_CONVT_FUSED) {
-        // room for the two-pass fallback too (used if the grid cannot be co-resident)
+        // room for the fallback too (used if the grid cannot be co-resident): the
+        // two-pass kernels for fp32 inputs, the general family for 16-bit ones
         const size_t a = cnf::convt2d_fused_workspace(d.N, d.groups, p.Ho);
-        const size_t b = cnf::convt2d_workspace(d.N, d.C_out, p.Ho, p.Wo);
+        const size_t b = d.dtype == CNF_DTYPE_F32 ? cnf::convt2d_workspace(d.N, d.C_out, p.Ho, p.Wo)
+                                                  : cnf::generic_workspace(ga);
         p.workspace = a > b ? a : b;
     }
 
@@ -363,13 +376,17 @@ cnf_status cnf_forward(const cnf_plan *plan, const void *xv, const void *wv, con
     case FAM_CONVT_FUSED: {
         cnf::ConvT2dArgs a{x, w, b, gamma, beta, out, static_cast<float *>(workspace), d.N,
                            d.C_in, d.C_out, H, W, d.groups, plan->Ho, plan->Wo, d.act,
-                           norm_groups, d.eps, inv_div};
+                           norm_groups, d.eps, inv_div, (int)d.dtype};
         e = hipErrorInvalidValue;
         if (plan->family == FAM_CONVT_FUSED) {
             e = cnf::launch_convt2d_fused(a, st);
             if (e == hipErrorCooperativeLaunchTooLarge) (void)hipGetLastError();
         }
-        if (plan->family == FAM_CONVT || e == hipErrorCooperativeLaunchTooLarge)
+        if (e == hipErrorCooperativeLaunchTooLarge && d.dtype != CNF_DTYPE_F32)
+            e = cnf::launch_generic(generic_args(*plan, xv, wv, b, gamma, beta, out, argmax,
+                                                 workspace, norm_groups),
+                                    st);
+        else if (plan->family == FAM_CONVT || e == hipErrorCooperativeLaunchTooLarge)
             e = cnf::launch_convt2d(a, st);
         break;
     }

@@ -38,6 +38,11 @@
 // two input row pairs from a 4-pair LDS ring refilled from registers loaded
 // three stashes ahead; waves sharing a SIMD alternate the step's MFMAs and
 // the previous step's activation.
+//
+// Input element type DT: 0 fp32; 1 bf16 / 2 fp16 for x and the weights (the
+// second input precision), widened to fp32 as they are loaded, so the
+// products, accumulation and epilogue are the fp32 path's; only the bytes
+// read from x halve.
 #include "device.h"
 #include "kernels.h"
 
@@ -74,7 +79,8 @@ static_assert((EXTWAVE & 3) != (COLWAVE & 3), "extra and column tiles finish on 
 static_assert(SPS == 4, "single tiles are computed in step 2 and finished in step 3");
 
 struct FusedArgs {
-    const float *x, *wt, *bias, *gamma, *beta;
+    const void *x, *wt;  // element type DT
+    const float *bias, *gamma, *beta;
     float *y;
     float *partials;  // [U][S][4]: (count, mean), (M2, count); zero on entry
     int *flag;        // raised if a wait timed out
@@ -85,10 +91,49 @@ struct FusedArgs {
     float eps, inv_div;
 };
 
+// Element size of x and the weights, and loads that widen them to fp32.
+template <int DT>
+constexpr unsigned ESZ = DT == 0 ? 4u : 2u;
+
+template <int DT>
+__device__ __forceinline__ float widen16(unsigned h)
+{
+    if constexpr (DT == 1) return __builtin_bit_cast(float, h << 16);                       // bf16
+    else return (float)__builtin_bit_cast(_Float16, (unsigned short)(h & 0xffffu));       // fp16
+}
+
+// one element at a byte offset (OOB reads 0)
+template <int DT>
+__device__ __forceinline__ float eload1(__amdgpu_buffer_rsrc_t r, unsigned byte_off)
+{
+    if constexpr (DT == 0) {
+        return buf_load1(r, byte_off);
+    } else {
+        const unsigned h = __builtin_amdgcn_raw_buffer_load_b16(r, (int)byte_off, 0, 0);
+        return widen16<DT>(h);
+    }
+}
+
+// four consecutive elements at a byte offset (OOB reads 0)
+template <int DT>
+__device__ __forceinline__ v4f eload4(__amdgpu_buffer_rsrc_t r, unsigned byte_off)
+{
+    if constexpr (DT == 0) {
+        return buf_load4(r, byte_off);
+    } else {
+        const auto raw = __builtin_amdgcn_raw_buffer_load_b64(r, (int)byte_off, 0, 0);
+        const unsigned w0 = (unsigned)raw[0], w1 = (unsigned)raw[1];
+        return v4f{widen16<DT>(w0), widen16<DT>(w0 >> 16), widen16<DT>(w1), widen16<DT>(w1 >> 16)};
+    }
+}
+
+template <int DT>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t x_rsrc(const FusedArgs &a, int unit)
 {
     const int n = unit / a.G, g = unit % a.G;
-    return make_rsrc(a.x + ((size_t)n * a.C + (size_t)g * CG) * a.H * W, (unsigned)(CG * a.H * W * 4));
+    return make_rsrc(static_cast<const char *>(a.x) +
+                         ((size_t)n * a.C + (size_t)g * CG) * a.H * W * ESZ<DT>,
+                     (unsigned)(CG * a.H * W * ESZ<DT>));
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t y_rsrc(const FusedArgs &a, int unit, unsigned plane)
@@ -102,14 +147,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t y_rsrc(const FusedArgs &a, int
 // is issued -- a load under a branch would leave the register a merge of two
 // values, and copying it would wait for the load -- and a row outside [0, H)
 // gets an offset past the buffer, which reads as zeros.
+template <int DT>
 __device__ __forceinline__ void load_pair(v4f (&pf)[2], __amdgpu_buffer_rsrc_t xr, int H, int row0,
                                           unsigned loff)
 {
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr) {
         const int row = row0 + rr;
-        const unsigned ro = row >= 0 && row < H ? (unsigned)(row * W * 4) : OOB;
-        pf[rr] = buf_load4(xr, loff + ro);
+        const unsigned ro = row >= 0 && row < H ? (unsigned)(row * W) * ESZ<DT> : OOB;
+        pf[rr] = eload4<DT>(xr, loff + ro);
     }
 }
 
@@ -125,6 +171,7 @@ __device__ __forceinline__ void stash_pair(float *ring, int slot, const v4f (&pf
 // of the last step; later positions stash nothing.  The loads for position
 // p + 3 are issued right after position p's stash, into register set p % 3
 // (NPOS is a multiple of 3, so every round starts on set 0).
+template <int DT>
 __device__ __forceinline__ void issue_pos(int p, v4f (&dst)[2], int k0, __amdgpu_buffer_rsrc_t xr,
                                           bool nhas, int nk0, __amdgpu_buffer_rsrc_t nxr, int H,
                                           unsigned loff)
@@ -140,7 +187,7 @@ __device__ __forceinline__ void issue_pos(int p, v4f (&dst)[2], int k0, __amdgpu
         pair = p3 - NPOS + 2;
     }
     const bool use_next = next && nhas;
-    load_pair(dst, use_next ? nxr : xr, H, 2 * ((use_next ? nk0 : k0) + pair) - 2, loff);
+    load_pair<DT>(dst, use_next ? nxr : xr, H, 2 * ((use_next ? nk0 : k0) + pair) - 2, loff);
 }
 
 // Chan merge of Welford triples with the weight nb / (n + nb) from the
@@ -310,6 +357,7 @@ __device__ __forceinline__ void epilogue_to_bank(const v4f &acc0, const v4f &acc
 // (the offset is pushed past the buffer, which returns 0).  Row tile:
 // row(c16) = orow, col = 32 rt + 2 c16 + 1.  Column tile: row = 16 c + c16,
 // col = 257.  Lanes of a wave without such a tile read past the buffer.
+template <int DT>
 __device__ __forceinline__ void single_load(float (&b)[SCH], __amdgpu_buffer_rsrc_t xr, int H, int chunk,
                                             bool has, int row, int col)
 {
@@ -317,11 +365,11 @@ __device__ __forceinline__ void single_load(float (&b)[SCH], __amdgpu_buffer_rsr
     for (int j = 0; j < SCH; ++j) {
         const int ci = 2 * chunk + j / KS, rr = row - j % KS;
         const bool ok = has && rr >= 0 && rr < H && col >= 0 && col < W;
-        b[j] = buf_load1(xr, ok ? (unsigned)(((ci * H + rr) * W + col) * 4) : OOB);
+        b[j] = eload1<DT>(xr, ok ? (unsigned)((ci * H + rr) * W + col) * ESZ<DT> : OOB);
     }
 }
 
-template <int ACT>
+template <int ACT, int DT>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void convt2d_gn_fused_kernel(FusedArgs a)
 {
@@ -357,7 +405,7 @@ void convt2d_gn_fused_kernel(FusedArgs a)
         for (int c = 0; c < PADL; ++c) row[c] = 0.f;
     }
 
-    const unsigned loff = (unsigned)((wave * H * W + 4 * lane) * 4);  // pair loads
+    const unsigned loff = (unsigned)(wave * H * W + 4 * lane) * ESZ<DT>;  // pair loads
     const int lb = PADL + 32 * wave + 2 * c16 + 1 - q;                // B operand column
     const unsigned vo0 = ((unsigned)(2 * q) * plane + 32u * wave + 2u * c16) * 4u;
     const unsigned vo1 = vo0 + plane * 4u;
@@ -369,14 +417,14 @@ void convt2d_gn_fused_kernel(FusedArgs a)
     int base = 0;  // ring slot of the current round's pair 0
     {
         const int k0 = s_base * SPS;
-        const __amdgpu_buffer_rsrc_t xr = x_rsrc(a, ulocal);
+        const __amdgpu_buffer_rsrc_t xr = x_rsrc<DT>(a, ulocal);
         v4f p0[2], p1[2];
-        load_pair(p0, xr, H, 2 * k0 - 2, loff);
-        load_pair(p1, xr, H, 2 * k0, loff);
+        load_pair<DT>(p0, xr, H, 2 * k0 - 2, loff);
+        load_pair<DT>(p1, xr, H, 2 * k0, loff);
         stash_pair(ring, 0, p0, wave, lane);
         stash_pair(ring, 1, p1, wave, lane);
 #pragma unroll
-        for (int p = 0; p < 3; ++p) load_pair(pf[p], xr, H, 2 * (k0 + p + 2) - 2, loff);
+        for (int p = 0; p < 3; ++p) load_pair<DT>(pf[p], xr, H, 2 * (k0 + p + 2) - 2, loff);
     }
 
     float wreg[CG * KS];
@@ -404,11 +452,11 @@ void convt2d_gn_fused_kernel(FusedArgs a)
         const int k0 = sg * SPS;
         const int ext = sg < a.NEXT ? sg : -1;           // extra row tile e: tail step e/16, tile e%16
         const int col = S - 1 - sg < a.NCOL ? S - 1 - sg : -1;
-        const __amdgpu_buffer_rsrc_t xr = x_rsrc(a, unit);
+        const __amdgpu_buffer_rsrc_t xr = x_rsrc<DT>(a, unit);
         const int nunit = unit + a.upr;
         const bool nhas = nunit < U;
         const int nk0 = ((sg + 1) % S) * SPS;
-        const __amdgpu_buffer_rsrc_t nxr = x_rsrc(a, nhas ? nunit : unit);
+        const __amdgpu_buffer_rsrc_t nxr = x_rsrc<DT>(a, nhas ? nunit : unit);
         const __amdgpu_buffer_rsrc_t pyr = y_rsrc(a, has_prev ? p_unit : unit, plane);
 
         // ---- weights (A operand), bias, gamma / beta of the unit's group
@@ -416,20 +464,21 @@ void convt2d_gn_fused_kernel(FusedArgs a)
         if (g != wgroup) {
             wgroup = g;
             const __amdgpu_buffer_rsrc_t wr =
-                make_rsrc(a.wt + (size_t)g * CG * CG * KS * KS, CG * CG * KS * KS * 4);
+                make_rsrc(static_cast<const char *>(a.wt) + (size_t)g * CG * CG * KS * KS * ESZ<DT>,
+                          CG * CG * KS * KS * ESZ<DT>);
             const int co = c16 >> 1, t = c16 & 1;
             const int kw = q + t - 1;
             const bool kok = kw >= 0 && kw < KS;
 #pragma unroll
             for (int s = 0; s < CG * KS; ++s) {
                 const int ci = s / KS, kh = s % KS;
-                const float v = buf_load1(wr, (unsigned)((((ci * CG + co) * KS + kh) * KS + (kok ? kw : 0)) * 4));
+                const float v = eload1<DT>(wr, (unsigned)(((ci * CG + co) * KS + kh) * KS + (kok ? kw : 0)) * ESZ<DT>);
                 wreg[s] = kok ? v : 0.0f;
             }
 #pragma unroll
             for (int j = 0; j < SCH; ++j) {
                 const int ci = 2 * (wave & 3) + j / KS, kh = j % KS;
-                const float v = buf_load1(wr, (unsigned)((((ci * CG + co) * KS + kh) * KS + (kok ? kw : 0)) * 4));
+                const float v = eload1<DT>(wr, (unsigned)(((ci * CG + co) * KS + kh) * KS + (kok ? kw : 0)) * ESZ<DT>);
                 wsub[j] = kok ? v : 0.0f;
             }
             const int c0 = g * CG + 2 * q;
@@ -444,7 +493,7 @@ void convt2d_gn_fused_kernel(FusedArgs a)
         const int tsel = wave >> 2, chunk = wave & 3;  // tile (0 extra, 1 column) and K chunk
         const bool has_t = tsel == 0 ? ext >= 0 : col >= 0;
         float sb[SCH];
-        single_load(sb, xr, H, chunk, has_t, tsel == 0 ? ext_row : 16 * col + c16,
+        single_load<DT>(sb, xr, H, chunk, has_t, tsel == 0 ? ext_row : 16 * col + c16,
                     tsel == 0 ? 32 * (ext & 7) + 2 * c16 + 1 - q : 2 * (W / 2) + 1 - q);
 
         // ---- steps.  Iteration k stores the previous unit's step k - 2, runs the
@@ -533,14 +582,14 @@ void convt2d_gn_fused_kernel(FusedArgs a)
             // ---- ring stashes at the end of step k, each followed by its loads
             if (k <= SPS - 2) {
                 stash_pair(ring, (base + k + 2) % NSLOT, pf[k % 3], wave, lane);
-                issue_pos(k, pf[k % 3], k0, xr, nhas, nk0, nxr, H, loff);
+                issue_pos<DT>(k, pf[k % 3], k0, xr, nhas, nk0, nxr, H, loff);
             } else {
                 stash_pair(ring, (base + SPS + 1) % NSLOT, pf[(SPS - 1) % 3], wave, lane);
-                issue_pos(SPS - 1, pf[(SPS - 1) % 3], k0, xr, nhas, nk0, nxr, H, loff);
+                issue_pos<DT>(SPS - 1, pf[(SPS - 1) % 3], k0, xr, nhas, nk0, nxr, H, loff);
                 stash_pair(ring, (base + SPS + 2) % NSLOT, pf[SPS % 3], wave, lane);
-                issue_pos(SPS, pf[SPS % 3], k0, xr, nhas, nk0, nxr, H, loff);
+                issue_pos<DT>(SPS, pf[SPS % 3], k0, xr, nhas, nk0, nxr, H, loff);
 #pragma unroll
-                for (int p = SPS + 1; p < NPOS; ++p) issue_pos(p, pf[p % 3], k0, xr, nhas, nk0, nxr, H, loff);
+                for (int p = SPS + 1; p < NPOS; ++p) issue_pos<DT>(p, pf[p % 3], k0, xr, nhas, nk0, nxr, H, loff);
             }
         }
 
@@ -649,11 +698,11 @@ bool geometry(int Ho, Geometry &g)
 
 struct Occupancy {
     int device = -1;
-    int blocks_per_cu[5] = {0, 0, 0, 0, 0};
+    int blocks_per_cu[5][3] = {};  // [activation][input type]
     int cus = 0;
 };
 
-template <int ACT>
+template <int ACT, int DT>
 hipError_t launch_t(const ConvT2dArgs &p, hipStream_t st)
 {
     Geometry geo;
@@ -663,18 +712,20 @@ hipError_t launch_t(const ConvT2dArgs &p, hipStream_t st)
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     Occupancy &o = occ[dev & 63];
-    if (o.device != dev || o.blocks_per_cu[ACT] == 0) {
+    if (o.device != dev) o = Occupancy{};
+    if (o.blocks_per_cu[ACT][DT] == 0) {
         int nb = 0;
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, convt2d_gn_fused_kernel<ACT>, THREADS, 0);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, convt2d_gn_fused_kernel<ACT, DT>,
+                                                         THREADS, 0);
         if (e != hipSuccess) return e;
         int cus = 0;
         e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess) return e;
         o.device = dev;
-        o.blocks_per_cu[ACT] = nb;
+        o.blocks_per_cu[ACT][DT] = nb;
         o.cus = cus;
     }
-    const int resident = o.blocks_per_cu[ACT] * o.cus;
+    const int resident = o.blocks_per_cu[ACT][DT] * o.cus;
     const int U = p.N * p.groups;
     int upr = resident / geo.S;
     if (upr < 1) return hipErrorCooperativeLaunchTooLarge;
@@ -692,7 +743,7 @@ hipError_t launch_t(const ConvT2dArgs &p, hipStream_t st)
                  reinterpret_cast<int *>(p.partials), p.N, p.C_out, p.H, p.groups, p.Ho,
                  geo.S, geo.NEXT, geo.NCOL, upr, xcd_units, p.eps, p.inv_div};
     void *args[] = {&fa};
-    return hipLaunchCooperativeKernel(reinterpret_cast<const void *>(convt2d_gn_fused_kernel<ACT>),
+    return hipLaunchCooperativeKernel(reinterpret_cast<const void *>(convt2d_gn_fused_kernel<ACT, DT>),
                                       dim3(upr * geo.S), dim3(THREADS), args, 0, st);
 }
 
@@ -719,13 +770,24 @@ size_t convt2d_fused_workspace(int N, int groups, int Ho)
     return (4 + U * (size_t)convt2d_fused_slices(Ho) * 4) * sizeof(float);
 }
 
-hipError_t launch_convt2d_fused(const ConvT2dArgs &a, hipStream_t st)
+template <int DT>
+hipError_t launch_dt(const ConvT2dArgs &a, hipStream_t st)
 {
     switch (a.act) {
-    case ACT_NONE: return launch_t<ACT_NONE>(a, st);
-    case ACT_HARDSWISH: return launch_t<ACT_HARDSWISH>(a, st);
-    case ACT_GELU_ERF: return launch_t<ACT_GELU_ERF>(a, st);
-    case ACT_GELU_TANH: return launch_t<ACT_GELU_TANH>(a, st);
+    case ACT_NONE: return launch_t<ACT_NONE, DT>(a, st);
+    case ACT_HARDSWISH: return launch_t<ACT_HARDSWISH, DT>(a, st);
+    case ACT_GELU_ERF: return launch_t<ACT_GELU_ERF, DT>(a, st);
+    case ACT_GELU_TANH: return launch_t<ACT_GELU_TANH, DT>(a, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_convt2d_fused(const ConvT2dArgs &a, hipStream_t st)
+{
+    switch (a.dtype) {
+    case 0: return launch_dt<0>(a, st);
+    case 1: return launch_dt<1>(a, st);
+    case 2: return launch_dt<2>(a, st);
     default: return hipErrorInvalidValue;
     }
 }

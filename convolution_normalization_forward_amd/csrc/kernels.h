@@ -71,7 +71,7 @@ hipError_t launch_conv2d_igemm(const Conv2dIgemmArgs &a, hipStream_t st);
 // ---- grouped ConvTranspose2d (8 in / 8 out per group, k 3, stride 1) +
 //      act writing y and per-tile Welford partials, then in-place GroupNorm
 struct ConvT2dArgs {
-    const float *x, *w, *b, *gamma, *beta;
+    const float *x, *w, *b, *gamma, *beta;  // x, w: element type dtype
     float *out;
     float *partials;     // workspace
     int N, C_in, C_out, H, W, groups;
@@ -79,6 +79,7 @@ struct ConvT2dArgs {
     int act;
     int norm_groups;     // 0: no norm; else GroupNorm groups (C_out: InstanceNorm)
     float eps, inv_div;
+    int dtype = 0;       // 0 fp32; 1 bf16 / 2 fp16 x and w (single-write kernel only)
 };
 bool convt2d_supported(int C_in, int C_out, int kernel, int groups, int H, int W, int act,
                        int norm, int num_groups);
@@ -86,7 +87,7 @@ size_t convt2d_workspace(int N, int C_out, int Ho, int Wo);  // [N][C_out][row b
 hipError_t launch_convt2d(const ConvT2dArgs &a, hipStream_t st);
 // single-write variant (W == 256, GroupNorm groups == conv groups): cooperative
 // persistent kernel; returns an error (and launches nothing) if the grid cannot
-// be made co-resident
+// be made co-resident.  Takes fp32, bf16 or fp16 x and w (dtype).
 bool convt2d_fused_supported(int C_in, int C_out, int groups, int H, int W, int act, int norm,
                              int num_groups);
 size_t convt2d_fused_workspace(int N, int groups, int Ho);

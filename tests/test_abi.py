@@ -214,13 +214,28 @@ def test_padded_stride1_convs_use_the_implicit_gemm():
 
 
 def test_sixteen_bit_inputs_plan_on_the_general_family():
+    """16-bit x and w run on the general family, except the grouped 3x3
+    ConvTranspose2d + GroupNorm shape of the single-write kernel, which widens
+    them on load; its workspace also holds the general family's (its fallback)."""
     d = _desc("conv2d_in_div_n128")
     d.dtype = 3
     assert cnf.cnf_plan_create_status(d) == cnf.CNF_ERR_INVALID_DESC
     for dt in ("bf16", "f16"):
         for name in cnf_inputs.PAGE_WORKLOADS:
             plan = cnf.Plan(_desc(name, dtype=dt))
-            assert "family=generic" in plan.describe() and f"dtype={dt}" in plan.describe()
+            fam = "family=convt2d_grouped8_gn_fused" if name == "convt2d_gelu_gn_n128" else "family=generic"
+            assert fam in plan.describe() and f"dtype={dt}" in plan.describe(), (name, plan.describe())
+        # the same shape at another width is not the single-write kernel's
+        p = cnf.Plan(_desc("convt2d_gelu_gn_n128", dtype=dt, in_dims=(1, 64, 200)))
+        assert "family=generic" in p.describe()
+        fused = cnf.Plan(_desc("convt2d_gelu_gn_n128", dtype=dt))
+        os.environ["CNF_FORCE_GENERIC"] = "1"
+        try:
+            gen = cnf.Plan(_desc("convt2d_gelu_gn_n128", dtype=dt))
+        finally:
+            del os.environ["CNF_FORCE_GENERIC"]
+        assert "family=generic" in gen.describe()
+        assert fused.workspace_bytes >= gen.workspace_bytes
     # 16-bit packed weights: 16 K entries per step (4 per lane), 2-byte elements
     p = cnf.Plan(_desc("conv2d_in_div_n128", dtype="bf16"))
     S = 126 * 126
@@ -233,8 +248,11 @@ def test_family_routing():
     # the page configurations keep their specialised families ...
     fams = {n: cnf.Plan(_desc(n)).describe().split()[0] for n in cnf_inputs.PAGE_WORKLOADS}
     assert not any("generic" in f for f in fams.values()), fams
+    # the other workloads run on the general family, except the 16-bit form of
+    # the transposed conv, which the single-write kernel takes
     for n in set(cnf_inputs.WORKLOAD_ORDER) - set(cnf_inputs.PAGE_WORKLOADS):
-        assert "family=generic" in cnf.Plan(_desc(n)).describe(), n
+        fam = "family=convt2d_grouped8_gn_fused" if n == "convt2d_gelu_gn_n128_bf16" else "family=generic"
+        assert fam in cnf.Plan(_desc(n)).describe(), n
     # ... and CNF_FORCE_GENERIC=1 sends them to the general one
     os.environ["CNF_FORCE_GENERIC"] = "1"
     try:

@@ -198,6 +198,33 @@ def _fused_slices(Ho):
     return min(32, nst // 4)
 
 
+# 16-bit x and w through the single-write kernel (widened to fp32 on load): the
+# oracle takes the same rounded inputs, so the fp32 tolerance applies.  Shapes:
+# one unit; ragged last step with every slice carrying a single row tile; the
+# tanh GELU and HardSwish forms; several samples and groups per round.
+SIXTEEN_BIT_FUSED = [
+    dict(N=1, in_dims=(1, 21, 256)),
+    dict(N=3, in_dims=(1, 127, 256), act="none"),
+    dict(N=2, in_dims=(1, 30, 256), act="gelu_tanh"),
+    dict(N=2, in_dims=(1, 46, 256), act="hardswish"),
+    dict(N=5, in_dims=(1, 14, 256)),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("over", SIXTEEN_BIT_FUSED)
+def test_sixteen_bit_single_write_every_element(over, dtype):
+    wl = cnf_inputs.workload("convt2d_gelu_gn_n128", dtype=dtype, **over)
+    _say(f"[parity-16] {over} {dtype}")
+    x = cnf_inputs.gen_x(wl)
+    p = cnf_inputs.gen_params(wl)
+    plan, out, _ = run_gpu(wl, x, p)
+    assert "fused" in plan.describe(), plan.describe()
+    ref, _ = oracle.forward(wl, x, **p)
+    err = check_close(out.cpu().numpy(), ref, f"fused {dtype} {over}")
+    _say(f"    max_abs_err={err:.3e}")
+
+
 def test_fused_convt_wait_never_times_out():
     # the single-write kernel raises a flag (workspace word 0) if a
     # cross-workgroup wait hit its bound; it must stay 0.  Every slice's

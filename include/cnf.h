@@ -75,9 +75,11 @@ typedef enum {
 typedef enum { CNF_CONV = 0, CNF_CONV_TRANSPOSE = 1 } cnf_conv_kind;
 
 /* Element type of x and w.  The 16-bit types feed the 16-bit matrix
- * instructions (products exact in fp32, fp32 accumulation); the pages use
- * fp32 throughout, and name tensor-core input precisions only as what a
- * vendor library would pick. */
+ * instructions (products exact in fp32, fp32 accumulation), or, in the
+ * single-write grouped transposed-conv kernel, are widened to fp32 as they are
+ * loaded; either way the epilogue is fp32.  The pages use fp32 throughout, and
+ * name tensor-core input precisions only as what a vendor library would
+ * pick. */
 typedef enum { CNF_DTYPE_F32 = 0, CNF_DTYPE_BF16 = 1, CNF_DTYPE_F16 = 2 } cnf_dtype;
 
 typedef enum {

@@ -778,59 +778,69 @@ hipError_t launch_generic(const GenericArgs &a, hipStream_t st) {
     float *y = a.reduce == 0 ? a.out : stage;  // nullptr: mean of an elementwise activation
     hipError_t e;
 
-    // 1. conv (+ bias + elementwise activation)
-    GenConv g{};
-    g.x = a.x; g.b = a.b;
-    void *wp = ws + L.off_wp;
-    g.wp = wp;
-    g.wp_elems = (unsigned)L.wp_elems;
-    g.P = L.P; g.RPG = 16 / L.P; g.KPG = L.KPG; g.GTn = L.GTn; g.steps = L.steps;
-    g.KP = 4 * L.KL * L.steps;
-    g.y = y;
-    g.part = L.softmax ? nullptr : part;
-    g.C_in = a.C_in; g.C_out = a.C_out; g.G = a.groups;
-    g.Cgi = a.C_in / a.groups; g.Cgo = a.C_out / a.groups;
-    const int NB = L.NB;
-    g.cobN = L.cobN;
-    g.T = L.T;
-    g.Tq = L.Tq;
-    g.CT = L.CT;
-    g.tasks = (int)((long long)a.N * L.nph * L.Tq * L.GTn * g.cobN);
-    g.D = a.D; g.H = a.H; g.W = a.W; g.Do = a.Do; g.Ho = a.Ho; g.Wo = a.Wo; g.S = S;
-    g.kd = a.kd; g.kh = a.kh; g.kw = a.kw;
-    g.sd = a.sd; g.sh = a.sh; g.sw = a.sw; g.pd = a.pd; g.ph = a.ph; g.pw = a.pw;
-    g.dd = a.dd; g.dh = a.dh; g.dw = a.dw;
-    g.in_plane = (unsigned)a.D * a.H * a.W;
-    {
-        // ~256 MFMAs per wave, but at least 16K waves in flight
-        const double taps_issued = (double)a.kd * a.kh * a.kw / L.nph;  // x taps all issued
-        const double mfma = taps_issued * L.steps * 4.0 * NB * (a.dtype ? 0.5 : 1.0);
-        long long tpw = (long long)(256.0 / (mfma > 1.0 ? mfma : 1.0));
-        const long long cap = g.tasks / 16384;
-        if (tpw > cap) tpw = cap;
-        g.tpw = (int)(tpw < 1 ? 1 : tpw > 64 ? 64 : tpw);
+    // 1. conv (+ bias + elementwise activation).  The stride-2 3x3 transposed conv
+    // over 8-channel groups has a direct kernel of its own (k_upsample2.hip); it
+    // writes its own (coarser) statistics tiles, so the finalize reads Tst of them.
+    int Tst = L.T;
+    const float out_scale0 = (!L.softmax && a.norm_groups == 0 && a.reduce == 0) ? a.inv_div : 1.0f;
+    if (!L.softmax && upsample2_supported(a) && upsample2_tiles(a.H, a.W) <= L.T) {
+        Tst = upsample2_tiles(a.H, a.W);
+        e = launch_upsample2(a, y, part, Tst, out_scale0, st);
+        if (e != hipSuccess) return e;
+    } else {
+        GenConv g{};
+        g.x = a.x; g.b = a.b;
+        void *wp = ws + L.off_wp;
+        g.wp = wp;
+        g.wp_elems = (unsigned)L.wp_elems;
+        g.P = L.P; g.RPG = 16 / L.P; g.KPG = L.KPG; g.GTn = L.GTn; g.steps = L.steps;
+        g.KP = 4 * L.KL * L.steps;
+        g.y = y;
+        g.part = L.softmax ? nullptr : part;
+        g.C_in = a.C_in; g.C_out = a.C_out; g.G = a.groups;
+        g.Cgi = a.C_in / a.groups; g.Cgo = a.C_out / a.groups;
+        const int NB = L.NB;
+        g.cobN = L.cobN;
+        g.T = L.T;
+        g.Tq = L.Tq;
+        g.CT = L.CT;
+        g.tasks = (int)((long long)a.N * L.nph * L.Tq * L.GTn * g.cobN);
+        g.D = a.D; g.H = a.H; g.W = a.W; g.Do = a.Do; g.Ho = a.Ho; g.Wo = a.Wo; g.S = S;
+        g.kd = a.kd; g.kh = a.kh; g.kw = a.kw;
+        g.sd = a.sd; g.sh = a.sh; g.sw = a.sw; g.pd = a.pd; g.ph = a.ph; g.pw = a.pw;
+        g.dd = a.dd; g.dh = a.dh; g.dw = a.dw;
+        g.in_plane = (unsigned)a.D * a.H * a.W;
+        {
+            // ~256 MFMAs per wave, but at least 16K waves in flight
+            const double taps_issued = (double)a.kd * a.kh * a.kw / L.nph;  // x taps all issued
+            const double mfma = taps_issued * L.steps * 4.0 * NB * (a.dtype ? 0.5 : 1.0);
+            long long tpw = (long long)(256.0 / (mfma > 1.0 ? mfma : 1.0));
+            const long long cap = g.tasks / 16384;
+            if (tpw > cap) tpw = cap;
+            g.tpw = (int)(tpw < 1 ? 1 : tpw > 64 ? 64 : tpw);
+        }
+        {
+            const unsigned total = (unsigned)L.wp_elems, blocks = (total + GT - 1) / GT;
+            const int taps = a.kd * a.kh * a.kw;
+            if (a.dtype)
+                gen_weight_pack_kernel<unsigned short><<<dim3(blocks), dim3(GT), 0, st>>>(
+                    static_cast<const unsigned short *>(a.w), static_cast<unsigned short *>(wp),
+                    a.groups, g.Cgi, g.Cgo, taps, L.steps, L.P, L.KL, L.cobN, NB, a.transposed,
+                    total);
+            else
+                gen_weight_pack_kernel<float><<<dim3(blocks), dim3(GT), 0, st>>>(
+                    static_cast<const float *>(a.w), static_cast<float *>(wp), a.groups, g.Cgi,
+                    g.Cgo, taps, L.steps, L.P, L.KL, L.cobN, NB, a.transposed, total);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+        // the conv writes the final values when nothing follows but the divide
+        g.out_scale = (!L.softmax && a.norm_groups == 0 && a.reduce == 0) ? a.inv_div : 1.0f;
+        g.act = L.softmax ? ACT_NONE : a.act;
+        if (a.dtype == 1) e = launch_conv<1>(g, a.transposed, NB, L.ROWS, st);
+        else if (a.dtype == 2) e = launch_conv<2>(g, a.transposed, NB, L.ROWS, st);
+        else e = launch_conv<0>(g, a.transposed, NB, L.ROWS, st);
+        if (e != hipSuccess) return e;
     }
-    {
-        const unsigned total = (unsigned)L.wp_elems, blocks = (total + GT - 1) / GT;
-        const int taps = a.kd * a.kh * a.kw;
-        if (a.dtype)
-            gen_weight_pack_kernel<unsigned short><<<dim3(blocks), dim3(GT), 0, st>>>(
-                static_cast<const unsigned short *>(a.w), static_cast<unsigned short *>(wp),
-                a.groups, g.Cgi, g.Cgo, taps, L.steps, L.P, L.KL, L.cobN, NB, a.transposed,
-                total);
-        else
-            gen_weight_pack_kernel<float><<<dim3(blocks), dim3(GT), 0, st>>>(
-                static_cast<const float *>(a.w), static_cast<float *>(wp), a.groups, g.Cgi,
-                g.Cgo, taps, L.steps, L.P, L.KL, L.cobN, NB, a.transposed, total);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-    // the conv writes the final values when nothing follows but the divide
-    g.out_scale = (!L.softmax && a.norm_groups == 0 && a.reduce == 0) ? a.inv_div : 1.0f;
-    g.act = L.softmax ? ACT_NONE : a.act;
-    if (a.dtype == 1) e = launch_conv<1>(g, a.transposed, NB, L.ROWS, st);
-    else if (a.dtype == 2) e = launch_conv<2>(g, a.transposed, NB, L.ROWS, st);
-    else e = launch_conv<0>(g, a.transposed, NB, L.ROWS, st);
-    if (e != hipSuccess) return e;
 
     // 2. channel softmax
     if (L.softmax) {
@@ -847,7 +857,7 @@ hipError_t launch_generic(const GenericArgs &a, hipStream_t st) {
         const int cpg = a.C_out / NG;
         const size_t lds = sizeof(double) * 3 * (GT + cpg);
         gen_finalize_kernel<<<dim3((unsigned)((long long)a.N * NG)), dim3(GT), lds, st>>>(
-            part, a.C_out, L.T, cpg, NG, a.norm_groups > 0, a.gamma, a.beta, a.eps, a.inv_div,
+            part, a.C_out, Tst, cpg, NG, a.norm_groups > 0, a.gamma, a.beta, a.eps, a.inv_div,
             a.reduce == 1 ? a.out : nullptr, ss);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }

@@ -120,6 +120,14 @@ struct GenericArgs {
     int dtype;                   // 0 fp32, 1 bf16, 2 fp16 (x and w)
 };
 bool generic_supported(const GenericArgs &a);
+// The general family's conv stage for a 2-D ConvTranspose2d, k 3, stride 2,
+// padding 1, output_padding 1, conv groups of 8 in / 8 out channels, fp32, no
+// softmax or reduction: direct VALU kernel writing y and (when part is not
+// null) [N][C_out][T] (count, mean, M2, 0) records, T >= upsample2_tiles.
+bool upsample2_supported(const GenericArgs &a);
+int upsample2_tiles(int H, int W);
+hipError_t launch_upsample2(const GenericArgs &a, float *y, void *part, int T, float out_scale,
+                            hipStream_t st);
 size_t generic_workspace(const GenericArgs &a);
 hipError_t launch_generic(const GenericArgs &a, hipStream_t st);
 

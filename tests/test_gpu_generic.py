@@ -124,6 +124,18 @@ GENERAL_CASES = [
     # stride-1 page shapes through non-default padding (the specialised families decline)
     ("convt2d_gelu_gn_n128", dict(N=1, in_dims=(1, 20, 30), padding=1)),
     ("conv2d_in_div_n128", dict(N=1, C_in=16, in_dims=(1, 25, 40), padding=3)),
+    # stride-2 3x3 transposed conv over 8-channel groups: its own direct conv stage
+    # (ragged rows and column blocks, narrow and exact widths, a 1x1 input, no
+    # statistics, a norm group spanning two conv groups, InstanceNorm)
+    ("convt2d_s2_gelu_gn_n128", dict(N=1, in_dims=(1, 7, 70))),
+    ("convt2d_s2_gelu_gn_n128", dict(N=3, C_in=16, C_out=16, groups=2, num_groups=2,
+                                     in_dims=(1, 13, 5), act="hardswish")),
+    ("convt2d_s2_gelu_gn_n128", dict(N=2, in_dims=(1, 6, 64), norm="instance", affine=1)),
+    ("convt2d_s2_gelu_gn_n128", dict(N=2, C_in=8, C_out=8, groups=1, num_groups=1,
+                                     in_dims=(1, 1, 1))),
+    ("convt2d_s2_gelu_gn_n128", dict(N=2, in_dims=(1, 5, 33), norm="none", divide_by=2.0,
+                                     act="gelu_tanh")),
+    ("convt2d_s2_gelu_gn_n128", dict(N=1, in_dims=(1, 10, 20), num_groups=4)),
 ]
 
 

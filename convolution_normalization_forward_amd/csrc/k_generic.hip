@@ -781,11 +781,14 @@ hipError_t launch_generic(const GenericArgs &a, hipStream_t st) {
     // 1. conv (+ bias + elementwise activation).  The stride-2 3x3 transposed conv
     // over 8-channel groups has a direct kernel of its own (k_upsample2.hip); it
     // writes its own (coarser) statistics tiles, so the finalize reads Tst of them.
+    // When a norm follows, that stage only takes statistics here and writes the
+    // normalised output in step 4 (recomputing the conv instead of re-reading it).
     int Tst = L.T;
     const float out_scale0 = (!L.softmax && a.norm_groups == 0 && a.reduce == 0) ? a.inv_div : 1.0f;
-    if (!L.softmax && upsample2_supported(a) && upsample2_tiles(a.H, a.W) <= L.T) {
+    const bool up2 = !L.softmax && upsample2_supported(a) && upsample2_tiles(a.H, a.W) <= L.T;
+    if (up2) {
         Tst = upsample2_tiles(a.H, a.W);
-        e = launch_upsample2(a, y, part, Tst, out_scale0, st);
+        e = launch_upsample2(a, y, part, Tst, out_scale0, nullptr, L.apply ? 1 : 0, st);
         if (e != hipSuccess) return e;
     } else {
         GenConv g{};
@@ -863,7 +866,10 @@ hipError_t launch_generic(const GenericArgs &a, hipStream_t st) {
     }
 
     // 4. in-place normalisation of the output
-    if (L.apply) {
+    if (L.apply && up2) {
+        e = launch_upsample2(a, y, nullptr, Tst, 1.0f, ss, 2, st);
+        if (e != hipSuccess) return e;
+    } else if (L.apply) {
         const unsigned chunks = (unsigned)((S + APPLY_CHUNK - 1) / APPLY_CHUNK);
         gen_apply_kernel<<<dim3((unsigned)((long long)a.N * a.C_out * chunks)), dim3(GT), 0, st>>>(
             a.out, ss, S, (int)chunks);

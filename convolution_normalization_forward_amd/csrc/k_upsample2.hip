@@ -20,6 +20,13 @@
 // Workgroup: 4 input rows x 64 input columns (256 threads) of one (sample,
 // group); its statistics are taken over its 8 channels' 4 x 256 outputs each,
 // two-pass in fp32 (mean, then summed squared deviations).
+//
+// When a norm follows, the conv output is never stored un-normalised: a first
+// launch (MODE_STATS) only takes the statistics, the family's finalize turns
+// them into a scale and shift per (sample, channel), and a second launch
+// (MODE_NORM) recomputes the conv -- bit for bit the same values -- and stores
+// act(conv) * scale + shift once.  The conv is 18 multiply-adds per output;
+// storing, re-reading and rewriting the 4-byte output costs more.
 #include "device.h"
 #include "kernels.h"
 
@@ -40,12 +47,16 @@ __device__ __forceinline__ float wave_sum(float v)
     return v;
 }
 
-template <int ACT>
+enum { MODE_WRITE = 0, MODE_STATS = 1, MODE_NORM = 2 };
+
+// MODE_WRITE: store act(conv) * out_scale, and the statistics if part is set;
+// MODE_STATS: statistics only; MODE_NORM: store act(conv) * ss.x + ss.y.
+template <int ACT, int MODE>
 __global__ __launch_bounds__(UT)
 void upsample2_conv_kernel(const float *__restrict__ x, const float *__restrict__ w,
                            const float *__restrict__ bias, float *__restrict__ y,
-                           v4f *__restrict__ part, int C, int H, int W, int G, int T,
-                           float out_scale)
+                           v4f *__restrict__ part, const v2f *__restrict__ ss, int C, int H,
+                           int W, int G, int T, float out_scale)
 {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -91,15 +102,22 @@ void upsample2_conv_kernel(const float *__restrict__ x, const float *__restrict_
 #pragma unroll
         for (int p = 0; p < 4; ++p) acc[co][p] = activate<ACT>(acc[co][p]);
 
-    if (valid) {
+    if (MODE != MODE_STATS && valid) {
 #pragma unroll
         for (int co = 0; co < G8; ++co) {
-            float *o = y + (((size_t)n * C + (size_t)g * G8 + co) * Ho + 2 * i) * Wo + 2 * j;
-            *reinterpret_cast<v2f *>(o) = v2f{acc[co][0] * out_scale, acc[co][1] * out_scale};
-            *reinterpret_cast<v2f *>(o + Wo) = v2f{acc[co][2] * out_scale, acc[co][3] * out_scale};
+            const size_t c = (size_t)n * C + (size_t)g * G8 + co;
+            float sc = out_scale, sh = 0.0f;
+            if constexpr (MODE == MODE_NORM) {
+                const v2f t = ss[c];
+                sc = t[0];
+                sh = t[1];
+            }
+            float *o = y + (c * Ho + 2 * i) * Wo + 2 * j;
+            *reinterpret_cast<v2f *>(o) = v2f{fmaf(acc[co][0], sc, sh), fmaf(acc[co][1], sc, sh)};
+            *reinterpret_cast<v2f *>(o + Wo) = v2f{fmaf(acc[co][2], sc, sh), fmaf(acc[co][3], sc, sh)};
         }
     }
-    if (!part) return;  // workgroup-uniform
+    if (MODE == MODE_NORM || !part) return;  // workgroup-uniform
 
     // statistics of the block: 4 outputs per valid thread and channel
     __shared__ float red[QR][G8];
@@ -162,16 +180,23 @@ int upsample2_tiles(int H, int W)
 }
 
 hipError_t launch_upsample2(const GenericArgs &a, float *y, void *part, int T, float out_scale,
-                            hipStream_t st)
+                            const void *ss, int mode, hipStream_t st)
 {
     if (!upsample2_supported(a) || (part && T < upsample2_tiles(a.H, a.W))) return hipErrorInvalidValue;
+    if ((mode == MODE_STATS && !part) || (mode == MODE_NORM && !ss) || mode < 0 || mode > 2)
+        return hipErrorInvalidValue;
     const dim3 grid((unsigned)((a.W + QC - 1) / QC), (unsigned)((a.H + QR - 1) / QR),
                     (unsigned)(a.N * a.groups));
     const float *x = static_cast<const float *>(a.x), *w = static_cast<const float *>(a.w);
     v4f *pp = static_cast<v4f *>(part);
-#define CNF_UP2(A)                                                                                 \
-    hipLaunchKernelGGL((upsample2_conv_kernel<A>), grid, dim3(UT), 0, st, x, w, a.b, y, pp, a.C_out, \
-                       a.H, a.W, a.groups, T, out_scale)
+    const v2f *sp = static_cast<const v2f *>(ss);
+#define CNF_UP2M(A, M)                                                                            \
+    hipLaunchKernelGGL((upsample2_conv_kernel<A, M>), grid, dim3(UT), 0, st, x, w, a.b, y, pp, sp, \
+                       a.C_out, a.H, a.W, a.groups, T, out_scale)
+#define CNF_UP2(A)                                                           \
+    if (mode == MODE_WRITE) CNF_UP2M(A, MODE_WRITE);                         \
+    else if (mode == MODE_STATS) CNF_UP2M(A, MODE_STATS);                    \
+    else CNF_UP2M(A, MODE_NORM)
     switch (a.act) {
     case ACT_NONE: CNF_UP2(ACT_NONE); break;
     case ACT_HARDSWISH: CNF_UP2(ACT_HARDSWISH); break;
@@ -180,6 +205,7 @@ hipError_t launch_upsample2(const GenericArgs &a, float *y, void *part, int T, f
     default: return hipErrorInvalidValue;
     }
 #undef CNF_UP2
+#undef CNF_UP2M
     return hipGetLastError();
 }
 

@@ -122,12 +122,14 @@ struct GenericArgs {
 bool generic_supported(const GenericArgs &a);
 // The general family's conv stage for a 2-D ConvTranspose2d, k 3, stride 2,
 // padding 1, output_padding 1, conv groups of 8 in / 8 out channels, fp32, no
-// softmax or reduction: direct VALU kernel writing y and (when part is not
-// null) [N][C_out][T] (count, mean, M2, 0) records, T >= upsample2_tiles.
+// softmax or reduction: direct VALU kernel.  mode 0 writes act(conv) *
+// out_scale to y and, when part is not null, [N][C_out][T] (count, mean, M2, 0)
+// records (T >= upsample2_tiles); mode 1 writes only the records; mode 2
+// writes act(conv) * ss.x + ss.y with ss the [N][C_out] (scale, shift) pairs.
 bool upsample2_supported(const GenericArgs &a);
 int upsample2_tiles(int H, int W);
 hipError_t launch_upsample2(const GenericArgs &a, float *y, void *part, int T, float out_scale,
-                            hipStream_t st);
+                            const void *ss, int mode, hipStream_t st);
 size_t generic_workspace(const GenericArgs &a);
 hipError_t launch_generic(const GenericArgs &a, hipStream_t st);
 

@@ -43,19 +43,19 @@ HEADLINE = "conv3d_softmax_pool_n128"
 #   small:        the full conv -> nominal FLOPs.
 #   igemm:        the full conv -> nominal FLOPs.
 #   convt:        HBM bound: x read once + the output written once (fp32).
-#   upsample2:    the stride-2 transposed conv's direct stage: x read once + the
-#                 conv output written once (its apply pass re-reads and rewrites it).
+#   upsample2:    the stride-2 transposed conv's normalising pass (mode 2): x read
+#                 once + the output written once (a statistics pass precedes it).
 DOMINANT = {
     "conv2d_in_div_n2": ("small_conv_norm_kernel", "mfma"),
     "conv3d_softmax_pool_n128": ("conv3d_softmax_pool_kernel", "mfma"),
     "conv3d_hswish_gn_mean_n1024": ("conv3d_k4_gn_mean_kernel", "mfma"),
     "conv2d_in_div_n128": ("conv2d_igemm_kernel<128", "mfma"),
-    "convt2d_gelu_gn_n128": ("convt2d_gn_fused_kernel", "mfma"),
+    "convt2d_gelu_gn_n128": ("convt2d_gn_fused_kernel<2, 0>", "mfma"),
     "convt2d_dense_gelu_gn_n128": ("conv2d_igemm_kernel<64", "mfma"),
     "conv2d_s2p1_in_div_n128": ("gen_conv_kernel<false, 4, 1, 0>", "mfma"),
-    "convt2d_s2_gelu_gn_n128": ("upsample2_conv_kernel", "hbm"),
+    "convt2d_s2_gelu_gn_n128": ("upsample2_conv_kernel<2, 2>", "hbm"),
     "conv2d_in_div_n128_bf16": ("gen_conv_kernel<false, 4, 1, 1>", "mfma"),
-    "convt2d_gelu_gn_n128_bf16": ("gen_conv_kernel<true, 1, 1, 1>", "mfma"),
+    "convt2d_gelu_gn_n128_bf16": ("convt2d_gn_fused_kernel<2, 1>", "mfma"),
 }
 
 

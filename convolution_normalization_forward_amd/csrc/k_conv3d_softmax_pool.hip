@@ -33,6 +33,7 @@
 //     depth, then across the 16 lanes (positions) of the row.  Ties resolve as
 //     the literal sequence of pools would (first 2x2x2 block in scan order, then
 //     first voxel inside it), or in plain row-major order for a single 4-pool.
+#include <atomic>
 #include <type_traits>
 
 #include "device.h"
@@ -301,15 +302,18 @@ template <int CI, int KS, int ACT, bool TWO>
 hipError_t launch_t2(const Conv3dSoftmaxPoolArgs &a, hipStream_t st)
 {
     const int total = a.N * a.Dp * a.Hp * a.Wp;
-    static int cus[64];
+    // CU count per device, cached; concurrent first calls store the same value
+    static std::atomic<int> cus_cache[64];
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    if (!cus[dev & 63]) {
-        e = hipDeviceGetAttribute(&cus[dev & 63], hipDeviceAttributeMultiprocessorCount, dev);
+    int cus = dev >= 0 && dev < 64 ? cus_cache[dev].load(std::memory_order_relaxed) : 0;
+    if (!cus) {
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess) return e;
+        if (dev >= 0 && dev < 64) cus_cache[dev].store(cus, std::memory_order_relaxed);
     }
-    const int grid = total < cus[dev & 63] * WAVES_PER_CU ? total : cus[dev & 63] * WAVES_PER_CU;
+    const int grid = total < cus * WAVES_PER_CU ? total : cus * WAVES_PER_CU;
     if (a.W % 4 == 0)
         hipLaunchKernelGGL((conv3d_softmax_pool_kernel<CI, KS, ACT, true, TWO>), dim3(grid), dim3(64),
                            0, st, a.x, a.w, a.b, a.out, a.argmax, a.N, a.D, a.H, a.W, a.Ho, a.Wo,

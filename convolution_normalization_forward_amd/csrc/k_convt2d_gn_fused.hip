@@ -43,6 +43,8 @@
 // second input precision), widened to fp32 as they are loaded, so the
 // products, accumulation and epilogue are the fp32 path's; only the bytes
 // read from x halve.
+#include <atomic>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -696,10 +698,11 @@ bool geometry(int Ho, Geometry &g)
     return g.NEXT <= g.S && g.NCOL <= g.S;
 }
 
+// Resident workgroups per CU of each instantiation and the CU count, cached per
+// device; concurrent first calls store the same values.
 struct Occupancy {
-    int device = -1;
-    int blocks_per_cu[5][3] = {};  // [activation][input type]
-    int cus = 0;
+    std::atomic<int> blocks_per_cu[5][3];  // [activation][input type]
+    std::atomic<int> cus;
 };
 
 template <int ACT, int DT>
@@ -707,25 +710,25 @@ hipError_t launch_t(const ConvT2dArgs &p, hipStream_t st)
 {
     Geometry geo;
     if (!geometry(p.Ho, geo)) return hipErrorInvalidValue;
-    static Occupancy occ[64];
+    static Occupancy occ[64];  // zero-initialised (static storage)
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    Occupancy &o = occ[dev & 63];
-    if (o.device != dev) o = Occupancy{};
-    if (o.blocks_per_cu[ACT][DT] == 0) {
-        int nb = 0;
+    Occupancy *o = dev >= 0 && dev < 64 ? &occ[dev] : nullptr;
+    int nb = o ? o->blocks_per_cu[ACT][DT].load(std::memory_order_relaxed) : 0;
+    int cus = o ? o->cus.load(std::memory_order_relaxed) : 0;
+    if (nb == 0 || cus == 0) {
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, convt2d_gn_fused_kernel<ACT, DT>,
                                                          THREADS, 0);
         if (e != hipSuccess) return e;
-        int cus = 0;
         e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess) return e;
-        o.device = dev;
-        o.blocks_per_cu[ACT][DT] = nb;
-        o.cus = cus;
+        if (o) {
+            o->blocks_per_cu[ACT][DT].store(nb, std::memory_order_relaxed);
+            o->cus.store(cus, std::memory_order_relaxed);
+        }
     }
-    const int resident = o.blocks_per_cu[ACT][DT] * o.cus;
+    const int resident = nb * cus;
     const int U = p.N * p.groups;
     int upr = resident / geo.S;
     if (upr < 1) return hipErrorCooperativeLaunchTooLarge;

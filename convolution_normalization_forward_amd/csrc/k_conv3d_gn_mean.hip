@@ -124,7 +124,11 @@ void conv3d_k4_gn_mean_kernel(const float *__restrict__ x, const float *__restri
 #pragma unroll
         for (int kd = 0; kd < KS; ++kd) slot[kd] = ((d + kd) % NSLOT) * PL;
 
-        for (int t0 = wave; t0 < T; t0 += 4 * NB) {
+        // The plane's T tiles go to the four waves by residue mod 4; which wave
+        // takes the residue with the extra tile rotates with the plane and the
+        // sample, so no SIMD carries it every plane (two workgroups share a CU).
+        const int wr = (wave + d + n) & 3;
+        for (int t0 = wr; t0 < T; t0 += 4 * NB) {
             v4f acc[NB];
             int base[NB];
 #pragma unroll

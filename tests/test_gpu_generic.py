@@ -193,6 +193,34 @@ def test_sixteen_bit_inputs_every_element(name, over, dtype):
     _case(name, dtype=dtype, **over)
 
 
+def _stride2_cases(count, seed=4242):
+    """Seeded shapes for the stride-2 3x3 transposed conv over 8-channel groups (the
+    general family's direct stage): sizes, groups, activation, norm, affine, divide."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        g = int(rng.integers(1, 5))
+        norm = ["group", "instance", "none"][int(rng.integers(0, 3))]
+        over = dict(N=int(rng.integers(1, 4)), C_in=8 * g, C_out=8 * g, groups=g,
+                    in_dims=(1, int(rng.integers(1, 40)), int(rng.integers(1, 140))),
+                    act=["gelu", "gelu_tanh", "hardswish", "none"][int(rng.integers(0, 4))],
+                    norm=norm, affine=int(rng.integers(0, 2)) if norm != "none" else 0,
+                    divide_by=[1.0, 2.0][int(rng.integers(0, 2))])
+        if norm == "group":
+            over["num_groups"] = [d for d in (1, 2, 4, 8) if (8 * g) % d == 0][int(rng.integers(0, 4))]
+        out.append(over)
+    return out
+
+
+STRIDE2_CASES = _stride2_cases(12)
+
+
+@pytest.mark.parametrize("over", STRIDE2_CASES)
+def test_stride2_transposed_conv_random_shapes(over):
+    _case("convt2d_s2_gelu_gn_n128", **over)
+
+
 import random_descriptors  # noqa: E402
 
 RANDOM_CASES = random_descriptors.cases(48) + random_descriptors.cases(48, seed=77, first_id=950)

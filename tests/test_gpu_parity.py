@@ -211,6 +211,24 @@ SIXTEEN_BIT_FUSED = [
 ]
 
 
+def _sixteen_bit_fused_random(count, seed=5151):
+    """Seeded shapes the single-write kernel takes: W = 256 and heights whose
+    output half-rows split evenly into four-step slices (H = 8k - 3 or 8k - 2)."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        g = int(rng.integers(1, 5))
+        H = 8 * int(rng.integers(1, 9)) - int(rng.integers(2, 4))
+        out.append(dict(N=int(rng.integers(1, 4)), C_in=8 * g, C_out=8 * g, groups=g, num_groups=g,
+                        in_dims=(1, H, 256),
+                        act=["gelu", "gelu_tanh", "hardswish", "none"][int(rng.integers(0, 4))]))
+    return out
+
+
+SIXTEEN_BIT_FUSED += _sixteen_bit_fused_random(6)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("over", SIXTEEN_BIT_FUSED)
 def test_sixteen_bit_single_write_every_element(over, dtype):

@@ -335,6 +335,36 @@ void conv2d_apply_kernel(float *__restrict__ y, const v2f *__restrict__ ss, floa
         if (i0 + k * 256 < nv) yp[i0 + k * 256] = v[k] * s[0] + s[1];
 }
 
+// Flat form: workgroup b takes float4 vectors [b * 256 * APPLY_V, +256 * APPLY_V)
+// of the whole [N * C][plane] tensor, so every cache line belongs to one
+// workgroup (planes of 126^2 or 258^2 floats do not end on line boundaries).
+// A chunk is no longer than a plane, so it spans at most two planes: the first
+// vector's plane p0 and p0 + 1.
+__global__ __launch_bounds__(256)
+void conv2d_apply_flat_kernel(float *__restrict__ y, const v2f *__restrict__ ss, float uscale,
+                              int plane4, int total4)
+{
+    const int base = blockIdx.x * (256 * APPLY_V);
+    const int p0 = base / plane4, b1 = (p0 + 1) * plane4;
+    const v2f s0 = ss ? ss[p0] : v2f{uscale, 0.0f};
+    const v2f s1 = ss ? ss[min(p0 + 1, total4 / plane4 - 1)] : v2f{uscale, 0.0f};
+    v4f *y4 = reinterpret_cast<v4f *>(y);
+    v4f v[APPLY_V];
+#pragma unroll
+    for (int k = 0; k < APPLY_V; ++k) {
+        const int i = base + threadIdx.x + k * 256;
+        if (i < total4) v[k] = y4[i];
+    }
+#pragma unroll
+    for (int k = 0; k < APPLY_V; ++k) {
+        const int i = base + threadIdx.x + k * 256;
+        if (i < total4) {
+            const v2f s = i < b1 ? s0 : s1;
+            y4[i] = v[k] * s[0] + s[1];
+        }
+    }
+}
+
 }  // namespace
 
 bool conv2d_igemm_supported(int C_in, int C_out, int kernel, int groups, int H, int W, int act)
@@ -402,6 +432,13 @@ hipError_t launch_conv2d_igemm(const Conv2dIgemmArgs &a, hipStream_t st)
         }
         const int plane = a.Ho * a.Wo;
         const int vec = plane % 4 == 0 ? 4 : 1;
+        const long long total4 = (long long)a.N * CO * plane / 4;
+        if (vec == 4 && plane / 4 >= 256 * APPLY_V && total4 < 0x7fffffffLL - 256 * APPLY_V) {
+            const unsigned blocks = (unsigned)((total4 + 256 * APPLY_V - 1) / (256 * APPLY_V));
+            hipLaunchKernelGGL(conv2d_apply_flat_kernel, dim3(blocks), dim3(256), 0, st, a.out, ss,
+                               a.inv_div, plane / 4, (int)total4);
+            return hipGetLastError();
+        }
         const int chunks = (plane / vec + 256 * APPLY_V - 1) / (256 * APPLY_V);
         if ((long long)a.N * CO * chunks > 0x7fffffffLL) return hipErrorInvalidValue;
         const dim3 grid((unsigned)(a.N * CO * chunks));

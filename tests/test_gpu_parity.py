@@ -109,6 +109,10 @@ SMALL_CASES = [
                                 act="gelu")),
     ("conv2d_in_div_n128", dict(N=2, C_in=8, in_dims=(1, 30, 140), norm="group", num_groups=1,
                                 affine=1)),
+    # planes of at least 4096 outputs: the flat apply pass (chunks spanning two planes,
+    # a ragged last chunk; with statistics and divide-only)
+    ("conv2d_in_div_n128", dict(N=3, C_in=8, in_dims=(1, 66, 70))),
+    ("conv2d_in_div_n128", dict(N=1, C_in=8, C_out=64, in_dims=(1, 66, 66), norm="none")),
     # dense transposed conv (groups 1) on the implicit GEMM: padded input, flipped kernel
     ("convt2d_dense_gelu_gn_n128", dict(N=2, C_in=8, C_out=64, in_dims=(1, 9, 20))),
     ("convt2d_dense_gelu_gn_n128", dict(N=2, C_in=16, C_out=128, in_dims=(1, 14, 61),

@@ -573,6 +573,33 @@ __device__ __forceinline__ void apply_chunk(float *p, int lo, int hi, v2f sc) {
         }
     }
 }
+// Flat form for planes of at least one chunk (S % 4 == 0): workgroup b takes
+// vectors [b * APPLY_CHUNK / 4, +APPLY_CHUNK / 4) of the whole [N * C][S] tensor,
+// so no cache line is split between workgroups where planes do not end on line
+// boundaries; a chunk spans at most two planes, p0 and p0 + 1.
+__global__ __launch_bounds__(GT) void gen_apply_flat_kernel(float *y, const v2f *ss, int S4, int total4) {
+    constexpr int CV = APPLY_CHUNK / 4;  // vectors per chunk (= GT * APPLY_PER)
+    const int base = blockIdx.x * CV;
+    const int p0 = base / S4, b1 = (p0 + 1) * S4;
+    const v2f s0 = ss[p0], s1 = ss[min(p0 + 1, total4 / S4 - 1)];
+    v4f *q = reinterpret_cast<v4f *>(y);
+    v4f v[APPLY_PER];
+#pragma unroll
+    for (int k = 0; k < APPLY_PER; ++k) {
+        const int i = base + threadIdx.x + k * GT;
+        if (i < total4) v[k] = q[i];
+    }
+#pragma unroll
+    for (int k = 0; k < APPLY_PER; ++k) {
+        const int i = base + threadIdx.x + k * GT;
+        if (i < total4) {
+            const v2f sc = i < b1 ? s0 : s1;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[k][e] = fmaf(v[k][e], sc[0], sc[1]);
+            q[i] = v[k];
+        }
+    }
+}
 __global__ __launch_bounds__(GT) void gen_apply_kernel(float *y, const v2f *ss, int S, int chunks) {
     const int plane = blockIdx.x / chunks, chunk = blockIdx.x - plane * chunks;
     const v2f sc = ss[plane];
@@ -869,6 +896,12 @@ hipError_t launch_generic(const GenericArgs &a, hipStream_t st) {
     if (L.apply && up2) {
         e = launch_upsample2(a, y, nullptr, Tst, 1.0f, ss, 2, st);
         if (e != hipSuccess) return e;
+    } else if (L.apply && (S & 3) == 0 && S >= APPLY_CHUNK &&
+               (long long)a.N * a.C_out * S / 4 < (1LL << 31) - APPLY_CHUNK) {
+        const int total4 = (int)((long long)a.N * a.C_out * S / 4);
+        const unsigned blocks = (unsigned)((total4 + APPLY_CHUNK / 4 - 1) / (APPLY_CHUNK / 4));
+        gen_apply_flat_kernel<<<dim3(blocks), dim3(GT), 0, st>>>(a.out, ss, S / 4, total4);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
     } else if (L.apply) {
         const unsigned chunks = (unsigned)((S + APPLY_CHUNK - 1) / APPLY_CHUNK);
         gen_apply_kernel<<<dim3((unsigned)((long long)a.N * a.C_out * chunks)), dim3(GT), 0, st>>>(

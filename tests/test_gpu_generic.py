@@ -124,6 +124,9 @@ GENERAL_CASES = [
     # stride-1 page shapes through non-default padding (the specialised families decline)
     ("convt2d_gelu_gn_n128", dict(N=1, in_dims=(1, 20, 30), padding=1)),
     ("conv2d_in_div_n128", dict(N=1, C_in=16, in_dims=(1, 25, 40), padding=3)),
+    # planes of at least 4096 outputs: the flat apply pass (chunks spanning two planes)
+    ("conv2d_in_div_n2", dict(N=2, C_out=24, in_dims=(1, 66, 70), padding=1, norm="group",
+                              num_groups=6, affine=1)),
     # stride-2 3x3 transposed conv over 8-channel groups: its own direct conv stage
     # (ragged rows and column blocks, narrow and exact widths, a 1x1 input, no
     # statistics, a norm group spanning two conv groups, InstanceNorm)
@@ -164,6 +167,7 @@ def test_page_configurations_through_the_general_family(name, over):
 # fp32, so the same tolerance applies.
 SIXTEEN_BIT_CASES = [
     ("conv2d_in_div_n2", {}),
+    ("conv2d_in_div_n128", dict(N=1, C_in=16, in_dims=(1, 66, 66))),  # flat apply pass
     ("conv2d_in_div_n128", dict(N=1, C_in=16, in_dims=(1, 30, 70))),
     ("conv3d_hswish_gn_mean_n1024", dict(N=2)),
     ("conv3d_softmax_pool_n128", dict(N=2)),

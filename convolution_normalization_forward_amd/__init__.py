@@ -20,7 +20,7 @@ import torch  # noqa: F401  (loads the HIP runtime first; see module docstring)
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libcnf.so")
 
-CNF_ABI_VERSION = 3
+CNF_ABI_VERSION = 4
 
 # cnf_status
 CNF_OK = 0
@@ -31,6 +31,8 @@ CNF_ERR_WORKSPACE = 4
 CNF_ERR_ALIGNMENT = 5
 CNF_ERR_HIP = 6
 CNF_ERR_ABI = 7
+CNF_ERR_NOMEM = 8
+CNF_ERR_WAIT_TIMEOUT = 9
 
 CNF_CONV, CNF_CONV_TRANSPOSE = 0, 1
 ACT = {"none": 0, "hardswish": 1, "gelu": 2, "softmax": 3, "gelu_tanh": 4}
@@ -40,7 +42,7 @@ DTYPE = {"f32": 0, "bf16": 1, "f16": 2}
 
 EXPORTED = ("cnf_plan_create", "cnf_plan_output_shape", "cnf_plan_workspace_size",
             "cnf_forward", "cnf_plan_destroy", "cnf_status_string", "cnf_plan_describe",
-            "cnf_abi_version")
+            "cnf_abi_version", "cnf_forward_timed", "cnf_forward_check")
 
 
 class cnf_desc(ctypes.Structure):
@@ -108,6 +110,10 @@ def load_library() -> ctypes.CDLL:
     lib.cnf_plan_describe.restype = ctypes.c_int
     lib.cnf_abi_version.argtypes = []
     lib.cnf_abi_version.restype = ctypes.c_int32
+    lib.cnf_forward_timed.argtypes = [P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P, P, P]
+    lib.cnf_forward_timed.restype = ctypes.c_int
+    lib.cnf_forward_check.argtypes = [P, P, ctypes.c_size_t, P]
+    lib.cnf_forward_check.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -188,6 +194,27 @@ def cnf_forward(plan: int, x, w, b, gamma, beta, out, argmax, workspace, workspa
     return int(load_library().cnf_forward(plan, _ptr(x), _ptr(w), _ptr(b), _ptr(gamma),
                                           _ptr(beta), _ptr(out), _ptr(argmax), _ptr(workspace),
                                           int(workspace_bytes), stream))
+
+
+def cnf_forward_timed(plan: int, x, w, b, gamma, beta, out, argmax, workspace,
+                      workspace_bytes: int, stream, event_before: int, event_after: int) -> int:
+    """cnf_forward that also records the two hipEvent_t handles (ints) right
+    before and after the plan's dominant kernel.  Returns the cnf_status."""
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    return int(load_library().cnf_forward_timed(plan, _ptr(x), _ptr(w), _ptr(b), _ptr(gamma),
+                                                _ptr(beta), _ptr(out), _ptr(argmax),
+                                                _ptr(workspace), int(workspace_bytes), stream,
+                                                event_before, event_after))
+
+
+def cnf_forward_check(plan: int, workspace, workspace_bytes: int, stream=None) -> int:
+    """Waits for the stream; CNF_ERR_WAIT_TIMEOUT if the last call's
+    cross-workgroup wait gave up, else CNF_OK.  Returns the cnf_status."""
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    return int(load_library().cnf_forward_check(plan, _ptr(workspace), int(workspace_bytes),
+                                                stream))
 
 
 # ------------------------------------------------------------ conveniences

@@ -47,10 +47,50 @@ struct cnf_plan {
     int64_t dims[5];
     int32_t rank;
     size_t workspace;
+    size_t flag_offset; // single-write transposed conv: byte offset of its wait flag
     int igemm_pad;      // zero padding the implicit GEMM applies to the input
+    cnf::LaunchHooks knobs;  // test knobs read from the environment at creation
 };
 
+namespace cnf {
+
 namespace {
+thread_local const LaunchHooks *t_hooks = nullptr;
+const LaunchHooks k_default_hooks{};
+}  // namespace
+
+const LaunchHooks &hooks() { return t_hooks ? *t_hooks : k_default_hooks; }
+void set_hooks(const LaunchHooks *h) { t_hooks = h; }
+
+hipError_t dominant_begin(hipStream_t st)
+{
+    const LaunchHooks &h = hooks();
+    return h.before ? hipEventRecord(static_cast<hipEvent_t>(h.before), st) : hipSuccess;
+}
+
+hipError_t dominant_end(hipStream_t st)
+{
+    const LaunchHooks &h = hooks();
+    return h.after ? hipEventRecord(static_cast<hipEvent_t>(h.after), st) : hipSuccess;
+}
+
+}  // namespace cnf
+
+namespace {
+
+// Hooks of one cnf_forward call, in place for its duration on this thread.
+struct HookScope {
+    explicit HookScope(const cnf::LaunchHooks *h) { cnf::set_hooks(h); }
+    ~HookScope() { cnf::set_hooks(nullptr); }
+};
+
+int env_int(const char *name)
+{
+    const char *v = std::getenv(name);
+    return v ? std::atoi(v) : 0;
+}
+
+__global__ void clear_word_kernel(int *p) { *p = 0; }
 
 // The general family's arguments for a plan (pointers may be null when only
 // the workspace size or the limits are wanted).
@@ -99,6 +139,8 @@ const char *cnf_status_string(cnf_status s)
     case CNF_ERR_ALIGNMENT: return "CNF_ERR_ALIGNMENT";
     case CNF_ERR_HIP: return "CNF_ERR_HIP";
     case CNF_ERR_ABI: return "CNF_ERR_ABI";
+    case CNF_ERR_NOMEM: return "CNF_ERR_NOMEM";
+    case CNF_ERR_WAIT_TIMEOUT: return "CNF_ERR_WAIT_TIMEOUT";
     }
     return "CNF_ERR_UNKNOWN";
 }
@@ -275,8 +317,22 @@ cnf_status cnf_plan_create(const cnf_desc *desc, cnf_plan **plan)
         p.workspace = a > b ? a : b;
     }
 
+    p.flag_offset = 0;
+    if (p.family == FAM_CONVT_FUSED) {
+        // the wait flag after everything either path uses, on its own 16 bytes
+        p.flag_offset = (p.workspace + 15) & ~(size_t)15;
+        p.workspace = p.flag_offset + 16;
+    }
+    // Test knobs of the single-write transposed conv (documented in cnf.h):
+    // CNF_TEST_FUSED_SPIN_LIMIT, CNF_TEST_FUSED_NEVER_READY,
+    // CNF_TEST_FORCE_FALLBACK, CNF_TEST_FUSED_MAX_UNITS_PER_ROUND.
+    p.knobs.spin_limit = env_int("CNF_TEST_FUSED_SPIN_LIMIT");
+    p.knobs.never_ready = env_int("CNF_TEST_FUSED_NEVER_READY") ? 1 : 0;
+    p.knobs.force_fallback = env_int("CNF_TEST_FORCE_FALLBACK") ? 1 : 0;
+    p.knobs.max_units_per_round = env_int("CNF_TEST_FUSED_MAX_UNITS_PER_ROUND");
+
     cnf_plan *np = new (std::nothrow) cnf_plan(p);
-    if (!np) return CNF_ERR_INVALID_DESC;
+    if (!np) return CNF_ERR_NOMEM;
     *plan = np;
     return CNF_OK;
 }
@@ -316,9 +372,15 @@ void cnf_plan_destroy(cnf_plan *plan) { delete plan; }
 
 static bool misaligned(const void *p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u); }
 
-cnf_status cnf_forward(const cnf_plan *plan, const void *xv, const void *wv, const float *b,
-                       const float *gamma, const float *beta, float *out, int32_t *argmax,
-                       void *workspace, size_t workspace_bytes, void *stream)
+}  // extern "C"
+
+namespace {
+
+// cnf_forward with optional events around the plan's dominant kernel.
+cnf_status forward_impl(const cnf_plan *plan, const void *xv, const void *wv, const float *b,
+                        const float *gamma, const float *beta, float *out, int32_t *argmax,
+                        void *workspace, size_t workspace_bytes, void *stream, void *ev_before,
+                        void *ev_after)
 {
     if (!plan) return CNF_ERR_NULL;
     const cnf_desc &d = plan->d;
@@ -336,32 +398,44 @@ cnf_status cnf_forward(const cnf_plan *plan, const void *xv, const void *wv, con
         return CNF_ERR_WORKSPACE;
     if (d.N == 0) return CNF_OK;
 
+    cnf::LaunchHooks hk = plan->knobs;
+    hk.before = ev_before;
+    hk.after = ev_after;
+    HookScope scope(&hk);
+
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     const float inv_div = 1.0f / d.divide_by;
     const int D = d.in_dims[0], H = d.in_dims[1], W = d.in_dims[2];
     const int norm_groups = d.norm == CNF_NORM_GROUP ? d.num_groups
                           : d.norm == CNF_NORM_INSTANCE ? d.C_out : 0;
     hipError_t e = hipSuccess;
+    // single-launch families: the events bracket the whole call
+    auto single = [&](auto &&launch) {
+        hipError_t r = cnf::dominant_begin(st);
+        if (r != hipSuccess) return r;
+        if ((r = launch()) != hipSuccess) return r;
+        return cnf::dominant_end(st);
+    };
     switch (plan->family) {
     case FAM_GN_MEAN: {
         cnf::Conv3dGnMeanArgs a{x, w, b, gamma, beta, out, d.N, d.C_in, D, H, W, d.act,
                                 norm_groups ? norm_groups : d.C_out, d.eps, inv_div};
         if (!norm_groups) a.num_groups = -1;  // plain mean of the activation
-        e = cnf::launch_conv3d_gn_mean(a, st);
+        e = single([&] { return cnf::launch_conv3d_gn_mean(a, st); });
         break;
     }
     case FAM_SOFTMAX_POOL: {
         cnf::Conv3dSoftmaxPoolArgs a{x, w, b, out, argmax, d.N, d.C_in, D, H, W, d.kernel,
                                      plan->Do, plan->Ho, plan->Wo, plan->Dp, plan->Hp, plan->Wp,
                                      d.act, d.pool_repeats > 1 ? 1 : 0};
-        e = cnf::launch_conv3d_softmax_pool(a, st);
+        e = single([&] { return cnf::launch_conv3d_softmax_pool(a, st); });
         break;
     }
     case FAM_SMALL: {
         cnf::SmallConvNormArgs a{x, w, b, gamma, beta, out, d.N, d.C_in, D, H, W, d.kernel,
                                  plan->Do, plan->Ho, plan->Wo, d.act, norm_groups, d.eps,
                                  inv_div, d.reduce == CNF_RED_MEAN_SPATIAL ? 1 : 0};
-        e = cnf::launch_small_conv_norm(a, st);
+        e = single([&] { return cnf::launch_small_conv_norm(a, st); });
         break;
     }
     case FAM_IGEMM: {
@@ -379,6 +453,11 @@ cnf_status cnf_forward(const cnf_plan *plan, const void *xv, const void *wv, con
                            norm_groups, d.eps, inv_div, (int)d.dtype};
         e = hipErrorInvalidValue;
         if (plan->family == FAM_CONVT_FUSED) {
+            // the flag reads 0 unless the single-write kernel below raises it
+            int *flag = reinterpret_cast<int *>(static_cast<char *>(workspace) + plan->flag_offset);
+            a.flag = flag;
+            hipLaunchKernelGGL(clear_word_kernel, dim3(1), dim3(1), 0, st, flag);
+            if ((e = hipGetLastError()) != hipSuccess) break;
             e = cnf::launch_convt2d_fused(a, st);
             if (e == hipErrorCooperativeLaunchTooLarge) (void)hipGetLastError();
         }
@@ -398,6 +477,45 @@ cnf_status cnf_forward(const cnf_plan *plan, const void *xv, const void *wv, con
     default: return CNF_ERR_UNSUPPORTED;
     }
     return e == hipSuccess ? CNF_OK : CNF_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+cnf_status cnf_forward(const cnf_plan *plan, const void *xv, const void *wv, const float *b,
+                       const float *gamma, const float *beta, float *out, int32_t *argmax,
+                       void *workspace, size_t workspace_bytes, void *stream)
+{
+    return forward_impl(plan, xv, wv, b, gamma, beta, out, argmax, workspace, workspace_bytes,
+                        stream, nullptr, nullptr);
+}
+
+cnf_status cnf_forward_timed(const cnf_plan *plan, const void *x, const void *w, const float *b,
+                             const float *gamma, const float *beta, float *out, int32_t *argmax,
+                             void *workspace, size_t workspace_bytes, void *stream,
+                             void *event_before, void *event_after)
+{
+    if (!event_before || !event_after) return CNF_ERR_NULL;
+    return forward_impl(plan, x, w, b, gamma, beta, out, argmax, workspace, workspace_bytes,
+                        stream, event_before, event_after);
+}
+
+cnf_status cnf_forward_check(const cnf_plan *plan, const void *workspace, size_t workspace_bytes,
+                             void *stream)
+{
+    if (!plan) return CNF_ERR_NULL;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (plan->family != FAM_CONVT_FUSED || plan->d.N == 0)
+        return hipStreamSynchronize(st) == hipSuccess ? CNF_OK : CNF_ERR_HIP;
+    if (!workspace || workspace_bytes < plan->workspace) return CNF_ERR_WORKSPACE;
+    if (misaligned(workspace)) return CNF_ERR_ALIGNMENT;
+    int flag = 0;
+    const char *src = static_cast<const char *>(workspace) + plan->flag_offset;
+    if (hipMemcpyAsync(&flag, src, sizeof(int), hipMemcpyDeviceToHost, st) != hipSuccess ||
+        hipStreamSynchronize(st) != hipSuccess)
+        return CNF_ERR_HIP;
+    return flag ? CNF_ERR_WAIT_TIMEOUT : CNF_OK;
 }
 
 }  // extern "C"

@@ -146,6 +146,25 @@ __device__ __forceinline__ float gelu_erf(float x) {
     return fmaf(fabsf(x), poly * e, fmaxf(x, 0.0f));
 }
 
+// Exact (erf) GELU in logistic form, x * Phi(x) ~= x * sigma(x P(x^2)): the
+// log-odds of the standard normal CDF is odd, and an odd degree-9 polynomial
+// fitted to it (minimax on |x * (sigma(f(x)) - Phi(x))| over [-12, 12],
+// weighted by the GELU error it causes) keeps the GELU within 3.5e-6 of the
+// erf form for every finite x, fp32 rounding included (the tanh form is the
+// degree-3 member of this family, 4.7e-4 off).  P > 0 on [0, inf), so the
+// log-odds run to +-inf with x: the result tends to x and to -0, never NaN.
+// With -log2(e) folded into P: x / (1 + exp2(x P'(x^2))), 7 VALU ops + exp2 +
+// rcp (the A&S form above takes 11 + rcp + exp2).
+__device__ __forceinline__ float gelu_erf_logistic(float x) {
+    const float u = x * x;
+    float p = fmaf(u, -3.230937637e-06f, 8.828550199e-05f);
+    p = fmaf(u, p, 3.599097254e-04f);
+    p = fmaf(u, p, -1.052256599e-01f);
+    p = fmaf(u, p, -2.302046299e+00f);
+    const float e = __builtin_amdgcn_exp2f(x * p);
+    return x * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
 // Tanh form of GELU, 0.5 x (1 + tanh(u)), u = sqrt(2/pi) (x + 0.044715 x^3).
 // With 1 + tanh(u) = 2 / (1 + exp(-2u)) it is x / (1 + exp2(x (a + b x^2))),
 // a = -2 sqrt(2/pi) log2(e), b = 0.044715 a: 6 VALU ops + exp2 + rcp.  For

@@ -414,6 +414,8 @@ hipError_t launch_conv2d_igemm(const Conv2dIgemmArgs &a, hipStream_t st)
         hipLaunchKernelGGL(conv2d_weight_transpose_kernel, dim3((total + 255) / 256), dim3(256), 0,
                            st, a.w, wt, a.C_in, CO, a.transposed);
     }
+    hipError_t e = dominant_begin(st);
+    if (e != hipSuccess) return e;
 #define CNF_CASE(C, A) \
     if (CO == C && a.act == A) launch_gemm<C, A>(a, wt, tiles_w, tiles_h, tps, st); else
     CNF_CASE(128, ACT_NONE) CNF_CASE(128, ACT_HARDSWISH) CNF_CASE(128, ACT_GELU_ERF)
@@ -421,6 +423,8 @@ hipError_t launch_conv2d_igemm(const Conv2dIgemmArgs &a, hipStream_t st)
     CNF_CASE(64, ACT_GELU_ERF) CNF_CASE(64, ACT_GELU_TANH)
     return hipErrorInvalidValue;
 #undef CNF_CASE
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = dominant_end(st)) != hipSuccess) return e;
     if (a.norm_groups > 0 || a.inv_div != 1.0f) {
         v2f *ss = nullptr;
         if (a.norm_groups > 0) {

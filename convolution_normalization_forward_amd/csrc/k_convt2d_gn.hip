@@ -233,9 +233,13 @@ hipError_t launch_t(const ConvT2dArgs &a, hipStream_t st)
 {
     const int rblocks = (a.Ho + R - 1) / R;
     const size_t lds = (size_t)CG * (R + KS - 1) * row_pitch(a.W) * sizeof(float);
+    hipError_t e = dominant_begin(st);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((convt2d_g8_kernel<ACT>), dim3(rblocks, a.groups, a.N), dim3(THREADS), lds,
                        st, a.x, a.w, a.b, a.out, a.partials, a.C_out, a.H, a.W, a.Ho, a.Wo,
                        rblocks);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = dominant_end(st)) != hipSuccess) return e;
     if (a.norm_groups > 0) {
         hipLaunchKernelGGL(convt2d_gn_pass_kernel, dim3(a.N * a.C_out), dim3(256), 0, st, a.out,
                            a.partials, a.gamma, a.beta, a.C_out, a.norm_groups, a.Ho * a.Wo,

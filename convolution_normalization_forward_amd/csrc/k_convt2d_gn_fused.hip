@@ -25,8 +25,9 @@
 //     slot of step k-1 of round r, which has just been normalised and stored.
 // Each triple travels as two 64-bit relaxed atomics that both carry the
 // count, so a reader that sees both halves non-zero has the whole triple and
-// no fence or counter is needed.  The wait is bounded; on time-out a flag in
-// the workspace is raised and the kernel still terminates.  Triples are
+// no fence or counter is needed.  The wait is bounded: on time-out the
+// caller's flag word is raised, the unit's outputs become NaN and the kernel
+// still terminates.  Triples are
 // merged in slice order, so results do not depend on timing.
 //
 // Tile mapping: rows of a 16x16 MFMA result = (channel, pixel parity),
@@ -86,6 +87,8 @@ struct FusedArgs {
     float *y;
     float *partials;  // [U][S][4]: (count, mean), (M2, count); zero on entry
     int *flag;        // raised if a wait timed out
+    int spin_limit;   // polls before a wait gives up
+    int never_ready;  // test hook: a wait also needs a word nobody writes
     int N, C, H, G, Ho;
     int S, NEXT, NCOL;  // slices, extra row tiles (16 per tail step), column tiles
     int upr;            // units per round
@@ -259,11 +262,15 @@ __device__ __forceinline__ Coef probe_finish(const FusedArgs &a, int unit, int l
                                              unsigned long long p0, unsigned long long p1)
 {
     int it = 0;
+    bool timed_out = false;
     for (;;) {
-        const bool ok = lane >= a.S || (lo_f(p0) > 0.0f && hi_f(p1) > 0.0f);
+        const bool ok = a.never_ready == 0 && (lane >= a.S || (lo_f(p0) > 0.0f && hi_f(p1) > 0.0f));
         if (__all(ok)) break;
-        if (++it > SPIN_LIMIT) {
-            if (lane == 0) __hip_atomic_store(a.flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (++it > a.spin_limit) {
+            // one store per wave at most, and none once the flag is up
+            if (lane == 0 && __hip_atomic_load(a.flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0)
+                __hip_atomic_store(a.flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            timed_out = true;
             break;
         }
         __builtin_amdgcn_s_sleep(1);
@@ -272,7 +279,8 @@ __device__ __forceinline__ Coef probe_finish(const FusedArgs &a, int unit, int l
     const bool mine = lane < a.S;
     float n = mine ? lo_f(p0) : 0.f, m = mine ? hi_f(p0) : 0.f, m2 = mine ? lo_f(p1) : 0.f;
     merge32(n, m, m2);
-    const float rstd = rsqrtf(m2 / n + a.eps);
+    if (timed_out) m = __builtin_nanf("");  // the unit's outputs become NaN
+    const float rstd = timed_out ? m : rsqrtf(m2 / n + a.eps);
     Coef c;
     c.sc0 = rstd * gb[0] * a.inv_div;
     c.sh0 = (gb[1] - m * rstd * gb[0]) * a.inv_div;
@@ -675,9 +683,9 @@ void convt2d_gn_fused_kernel(FusedArgs a)
     }
 }
 
-__global__ void zero_words_kernel(unsigned *p, int n)
+__global__ void zero_words_kernel(unsigned *p, long long n)
 {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) p[i] = 0u;
 }
 
@@ -710,6 +718,7 @@ hipError_t launch_t(const ConvT2dArgs &p, hipStream_t st)
 {
     Geometry geo;
     if (!geometry(p.Ho, geo)) return hipErrorInvalidValue;
+    const LaunchHooks &hk = hooks();
     static Occupancy occ[64];  // zero-initialised (static storage)
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -731,23 +740,28 @@ hipError_t launch_t(const ConvT2dArgs &p, hipStream_t st)
     const int resident = nb * cus;
     const int U = p.N * p.groups;
     int upr = resident / geo.S;
-    if (upr < 1) return hipErrorCooperativeLaunchTooLarge;
+    if (upr < 1 || hk.force_fallback) return hipErrorCooperativeLaunchTooLarge;
     if (upr > U) upr = U;
+    if (hk.max_units_per_round > 0 && upr > hk.max_units_per_round) upr = hk.max_units_per_round;
     const int xcd_units = upr % NXCD == 0 ? upr / NXCD : 0;
 
-    // workspace: flag word, pad to 16 B, then [U][S][4] partials (all zeroed)
-    const int words = 4 + U * geo.S * 4;
-    hipLaunchKernelGGL(zero_words_kernel, dim3((words + 255) / 256), dim3(256), 0, st,
+    // workspace: [U][S][4] partials, zeroed (the flag word sits at p.flag)
+    const long long words = (long long)U * geo.S * 4;
+    hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, st,
                        reinterpret_cast<unsigned *>(p.partials), words);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
 
-    FusedArgs fa{p.x, p.w, p.b, p.gamma, p.beta, p.out, p.partials + 4,
-                 reinterpret_cast<int *>(p.partials), p.N, p.C_out, p.H, p.groups, p.Ho,
+    FusedArgs fa{p.x, p.w, p.b, p.gamma, p.beta, p.out, p.partials, p.flag,
+                 hk.spin_limit > 0 ? hk.spin_limit : SPIN_LIMIT, hk.never_ready,
+                 p.N, p.C_out, p.H, p.groups, p.Ho,
                  geo.S, geo.NEXT, geo.NCOL, upr, xcd_units, p.eps, p.inv_div};
     void *args[] = {&fa};
-    return hipLaunchCooperativeKernel(reinterpret_cast<const void *>(convt2d_gn_fused_kernel<ACT, DT>),
-                                      dim3(upr * geo.S), dim3(THREADS), args, 0, st);
+    if ((e = dominant_begin(st)) != hipSuccess) return e;
+    e = hipLaunchCooperativeKernel(reinterpret_cast<const void *>(convt2d_gn_fused_kernel<ACT, DT>),
+                                   dim3(upr * geo.S), dim3(THREADS), args, 0, st);
+    if (e != hipSuccess) return e;
+    return dominant_end(st);
 }
 
 }  // namespace
@@ -770,7 +784,7 @@ bool convt2d_fused_supported(int C_in, int C_out, int groups, int H, int W_, int
 size_t convt2d_fused_workspace(int N, int groups, int Ho)
 {
     const size_t U = (size_t)N * groups;
-    return (4 + U * (size_t)convt2d_fused_slices(Ho) * 4) * sizeof(float);
+    return U * (size_t)convt2d_fused_slices(Ho) * 4 * sizeof(float);
 }
 
 template <int DT>

@@ -866,10 +866,12 @@ hipError_t launch_generic(const GenericArgs &a, hipStream_t st) {
         // the conv writes the final values when nothing follows but the divide
         g.out_scale = (!L.softmax && a.norm_groups == 0 && a.reduce == 0) ? a.inv_div : 1.0f;
         g.act = L.softmax ? ACT_NONE : a.act;
+        if ((e = dominant_begin(st)) != hipSuccess) return e;
         if (a.dtype == 1) e = launch_conv<1>(g, a.transposed, NB, L.ROWS, st);
         else if (a.dtype == 2) e = launch_conv<2>(g, a.transposed, NB, L.ROWS, st);
         else e = launch_conv<0>(g, a.transposed, NB, L.ROWS, st);
         if (e != hipSuccess) return e;
+        if ((e = dominant_end(st)) != hipSuccess) return e;
     }
 
     // 2. channel softmax

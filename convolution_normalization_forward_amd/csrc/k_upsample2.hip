@@ -197,6 +197,9 @@ hipError_t launch_upsample2(const GenericArgs &a, float *y, void *part, int T, f
     if (mode == MODE_WRITE) CNF_UP2M(A, MODE_WRITE);                         \
     else if (mode == MODE_STATS) CNF_UP2M(A, MODE_STATS);                    \
     else CNF_UP2M(A, MODE_NORM)
+    // a pass that writes the output is the dominant launch
+    hipError_t e = mode != MODE_STATS ? dominant_begin(st) : hipSuccess;
+    if (e != hipSuccess) return e;
     switch (a.act) {
     case ACT_NONE: CNF_UP2(ACT_NONE); break;
     case ACT_HARDSWISH: CNF_UP2(ACT_HARDSWISH); break;
@@ -206,7 +209,8 @@ hipError_t launch_upsample2(const GenericArgs &a, float *y, void *part, int T, f
     }
 #undef CNF_UP2
 #undef CNF_UP2M
-    return hipGetLastError();
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return mode != MODE_STATS ? dominant_end(st) : hipSuccess;
 }
 
 }  // namespace cnf

@@ -8,6 +8,24 @@
 
 namespace cnf {
 
+// ---- Per-call launch hooks, set by the C ABI for the duration of one
+//      cnf_forward call on the calling thread (defaults otherwise):
+//      events recorded on the launch stream right before and right after the
+//      plan's dominant kernel, and test knobs of the single-write transposed
+//      conv read from the environment when the plan was created.
+struct LaunchHooks {
+    void *before = nullptr, *after = nullptr;  // hipEvent_t or null
+    int spin_limit = 0;            // > 0: polls before a cross-workgroup wait gives up
+    int never_ready = 0;           // 1: every such wait also needs a word nobody writes
+    int force_fallback = 0;        // 1: act as if the cooperative grid could not be resident
+    int max_units_per_round = 0;   // > 0: cap on units per round (more rounds)
+};
+const LaunchHooks &hooks();
+void set_hooks(const LaunchHooks *h);  // null: defaults
+// Record hooks().before / .after on st (no-ops when unset).
+hipError_t dominant_begin(hipStream_t st);
+hipError_t dominant_end(hipStream_t st);
+
 // ---- Conv3d (C_out 16, k 4) + act + GroupNorm + mean over D,H,W
 struct Conv3dGnMeanArgs {
     const float *x, *w, *b, *gamma, *beta;
@@ -80,14 +98,16 @@ struct ConvT2dArgs {
     int norm_groups;     // 0: no norm; else GroupNorm groups (C_out: InstanceNorm)
     float eps, inv_div;
     int dtype = 0;       // 0 fp32; 1 bf16 / 2 fp16 x and w (single-write kernel only)
+    int *flag = nullptr; // single-write kernel: raised (1) if a cross-workgroup wait gave up
 };
 bool convt2d_supported(int C_in, int C_out, int kernel, int groups, int H, int W, int act,
                        int norm, int num_groups);
 size_t convt2d_workspace(int N, int C_out, int Ho, int Wo);  // [N][C_out][row blocks][3]
 hipError_t launch_convt2d(const ConvT2dArgs &a, hipStream_t st);
 // single-write variant (W == 256, GroupNorm groups == conv groups): cooperative
-// persistent kernel; returns an error (and launches nothing) if the grid cannot
-// be made co-resident.  Takes fp32, bf16 or fp16 x and w (dtype).
+// persistent kernel; returns hipErrorCooperativeLaunchTooLarge (and launches
+// nothing) if the grid cannot be made co-resident.  Takes fp32, bf16 or fp16 x
+// and w (dtype).  The caller zeroes *flag before the launch.
 bool convt2d_fused_supported(int C_in, int C_out, int groups, int H, int W, int act, int norm,
                              int num_groups);
 size_t convt2d_fused_workspace(int N, int groups, int Ho);

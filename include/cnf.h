@@ -40,8 +40,11 @@
  *     allocates device memory, never frees caller memory and never
  *     synchronises the stream.  The plan owns only host memory.
  *   - Device pointers must be 16-byte aligned (CNF_ERR_ALIGNMENT otherwise).
- *   - No function throws; every failure is a cnf_status.  A failing call
- *     launches nothing.
+ *   - No function throws; every failure is a cnf_status.  Argument errors
+ *     (NULL, ALIGNMENT, WORKSPACE, ...) are found before anything is
+ *     enqueued.  A CNF_ERR_HIP from a family that launches several kernels
+ *     may come after some of them were enqueued; the output is then
+ *     unspecified.
  *   - cnf_forward is asynchronous on `stream` (a hipStream_t; NULL is the
  *     null stream).  Calls on different streams may run concurrently if each
  *     has its own workspace and output.
@@ -59,7 +62,7 @@
 extern "C" {
 #endif
 
-#define CNF_ABI_VERSION 3
+#define CNF_ABI_VERSION 4
 
 typedef enum {
     CNF_OK = 0,
@@ -69,7 +72,9 @@ typedef enum {
     CNF_ERR_WORKSPACE = 4,     /* workspace pointer NULL or smaller than required */
     CNF_ERR_ALIGNMENT = 5,     /* a device pointer is not 16-byte aligned */
     CNF_ERR_HIP = 6,           /* a HIP launch reported an error */
-    CNF_ERR_ABI = 7            /* desc->abi_version != CNF_ABI_VERSION */
+    CNF_ERR_ABI = 7,           /* desc->abi_version != CNF_ABI_VERSION */
+    CNF_ERR_NOMEM = 8,         /* host memory for the plan could not be allocated */
+    CNF_ERR_WAIT_TIMEOUT = 9   /* cnf_forward_check: a bounded cross-workgroup wait gave up */
 } cnf_status;
 
 typedef enum { CNF_CONV = 0, CNF_CONV_TRANSPOSE = 1 } cnf_conv_kind;
@@ -192,6 +197,40 @@ cnf_status cnf_forward(const cnf_plan *plan,
                        float *out, int32_t *argmax,
                        void *workspace, size_t workspace_bytes,
                        void *stream);
+
+/* cnf_forward, and also records event_before (a hipEvent_t) on `stream`
+ * right before the launch of the plan's dominant kernel (the one that does
+ * the contraction) and event_after right after it, so the caller can time
+ * that kernel alone with hipEventElapsedTime.  Both events must be non-NULL
+ * (CNF_ERR_NULL) and are owned by the caller.  Same results as cnf_forward. */
+cnf_status cnf_forward_timed(const cnf_plan *plan,
+                             const void *x, const void *w, const float *b,
+                             const float *gamma, const float *beta,
+                             float *out, int32_t *argmax,
+                             void *workspace, size_t workspace_bytes,
+                             void *stream, void *event_before, void *event_after);
+
+/* Outcome of the last cnf_forward (or cnf_forward_timed) that ran `plan` on
+ * this workspace.  Waits for `stream` (hipStreamSynchronize), then reads the
+ * status word that call left in the workspace.  Only the single-write
+ * grouped ConvTranspose2d + GroupNorm kernel (page "Kimi-K2.6__l2_p19")
+ * waits across workgroups: its workgroups exchange per-slice GroupNorm
+ * statistics and each wait is bounded.  If a wait gave up (for example
+ * because other work on the device kept a sibling workgroup from running),
+ * the affected (sample, group) units of that call's output hold NaN, never
+ * values normalised with partial statistics, and this returns
+ * CNF_ERR_WAIT_TIMEOUT.  Every other plan returns CNF_OK once the stream
+ * is idle.  CNF_ERR_WORKSPACE / CNF_ERR_ALIGNMENT as for cnf_forward.
+ *
+ * Test knobs of that kernel, read from the environment by cnf_plan_create
+ * (unset means off): CNF_TEST_FUSED_SPIN_LIMIT=k (give up after k polls),
+ * CNF_TEST_FUSED_NEVER_READY=1 (each wait also needs a word nothing writes,
+ * so every wait gives up after its polls and the kernel still ends),
+ * CNF_TEST_FORCE_FALLBACK=1 (run the multi-pass fallback the plan keeps for
+ * a grid that cannot be co-resident), CNF_TEST_FUSED_MAX_UNITS_PER_ROUND=k
+ * (at most k units per round, so small batches run many rounds). */
+cnf_status cnf_forward_check(const cnf_plan *plan, const void *workspace,
+                             size_t workspace_bytes, void *stream);
 
 /* Free a plan (NULL is ignored). */
 void cnf_plan_destroy(cnf_plan *plan);

@@ -40,9 +40,17 @@ def check_close(got, ref, what=""):
     return float(err.max())
 
 
-def check_argmax(got_idx, ref_idx, pre_pool, Pk, what=""):
-    """Argmax parity where the window's top two oracle values are separated by
-    more than the parity tolerance; returns the number of windows excluded.
+def check_argmax(got_idx, got_val, ref_idx, pre_pool, Pk, what=""):
+    """Argmax parity of a pooled output.
+
+    Several indices are correct only where a window's maximum is tied, so
+    every window, near-ties included, must name a voxel of its own window
+    whose oracle value is the window maximum within the parity tolerance,
+    and the pooled value the GPU wrote (got_val) must equal the oracle value
+    at the GPU's own index within that tolerance.  Where the window's top two
+    oracle values are further apart than the tolerance the index must also
+    equal the oracle's exactly.  Returns the number of windows whose index
+    was not compared exactly (near-ties).
 
     pre_pool: oracle values the first pool sees, on the conv grid, float64,
     (N, C, Do, Ho, Wo) or (N, C, Ho, Wo) for a 2-D problem (whose pools leave
@@ -54,18 +62,34 @@ def check_argmax(got_idx, ref_idx, pre_pool, Pk, what=""):
     else:
         kd = Pk
     N, C, Dp, Hp, Wp = ref_idx.shape
+    assert got_idx.shape == ref_idx.shape, (what, got_idx.shape, ref_idx.shape)
     win = pre_pool[:, :, :Dp * kd, :Hp * Pk, :Wp * Pk].reshape(N, C, Dp, kd, Hp, Pk, Wp, Pk)
     win = win.transpose(0, 1, 2, 4, 6, 3, 5, 7).reshape(N, C, Dp, Hp, Wp, -1)
     top2 = np.sort(win, axis=-1)[..., -2:]
-    gap = top2[..., 1] - top2[..., 0]
-    clear = gap > ATOL + RTOL * np.abs(top2[..., 1])
+    wmax = top2[..., 1]
+    gap = wmax - top2[..., 0]
+    tol = ATOL + RTOL * np.abs(wmax)
+    clear = gap > tol
     mism = (got_idx != ref_idx) & clear
     assert not mism.any(), f"{what}: {int(mism.sum())} argmax mismatches in clear windows"
-    # every reported index must name a voxel of its own window
+    # every reported index must name a voxel of its own window ...
     Do, Ho, Wo = pre_pool.shape[2:]
+    assert ((got_idx >= 0) & (got_idx < Do * Ho * Wo)).all(), f"{what}: index outside the conv grid"
     d, h, w = got_idx // (Ho * Wo), (got_idx // Wo) % Ho, got_idx % Wo
     od, oh, ow = np.indices((Dp, Hp, Wp))
     assert ((d // kd == od) & (h // Pk == oh) & (w // Pk == ow)).all(), f"{what}: index outside window"
+    # ... that holds the window maximum within the tolerance (near-ties included)
+    n_i, c_i = np.indices((N, C))
+    n_i = n_i[:, :, None, None, None]
+    c_i = c_i[:, :, None, None, None]
+    at_idx = pre_pool[n_i, c_i, d, h, w]
+    short = at_idx < wmax - tol
+    assert not short.any(), f"{what}: {int(short.sum())} indices name a voxel below its window maximum"
+    # and the pooled value must be the oracle value at the GPU's own index
+    gv = np.asarray(got_val, dtype=np.float64)
+    assert gv.shape == at_idx.shape, (what, gv.shape, at_idx.shape)
+    off = np.abs(gv - at_idx) > ATOL + RTOL * np.abs(at_idx)
+    assert not off.any(), f"{what}: {int(off.sum())} pooled values differ from the value at their own index"
     return int((~clear).sum())
 
 

@@ -146,10 +146,11 @@ def test_workspace_sizes_are_what_the_partials_need():
     # partials, the [ci][tap][co] weight copy, one (scale, shift) per (n, c)
     assert p4.workspace_bytes == 128 * tiles * 128 * 3 * 4 + 64 * 9 * 128 * 4 + 128 * 128 * 8
     p5 = cnf.Plan(_desc("convt2d_gelu_gn_n128"))
-    # the larger of the single-write kernel's slice triples (16 B header +
-    # 1024 units x 32 slices x 16 B) and the two-pass fallback's per-channel
-    # row-block triples (128 x 64 channels x 65 row blocks x 12 B)
-    assert p5.workspace_bytes == max(16 + 1024 * 32 * 16, 128 * 64 * 65 * 3 * 4)
+    # the larger of the single-write kernel's slice triples (1024 units x 32
+    # slices x 16 B) and the two-pass fallback's per-channel row-block triples
+    # (128 x 64 channels x 65 row blocks x 12 B), then the 16-byte status word
+    # of the bounded waits
+    assert p5.workspace_bytes == max(1024 * 32 * 16, 128 * 64 * 65 * 3 * 4) + 16
     assert cnf.Plan(_desc()).workspace_bytes == 0
 
 

@@ -42,7 +42,7 @@ def _case(name, force=False, dist="normal", **over):
     err = check_close(out.cpu().numpy(), ref, f"{name} {over}")
     if wl["want_argmax"]:
         Pk = wl["pool_kernel"] ** wl["pool_repeats"]
-        excl = check_argmax(idx.cpu().numpy(), ref_idx, oracle_pre_pool(wl, x, p), Pk, name)
+        excl = check_argmax(idx.cpu().numpy(), out.cpu().numpy(), ref_idx, oracle_pre_pool(wl, x, p), Pk, name)
         _say(f"    argmax ok, {excl} near-tie windows excluded")
     _say(f"    max_abs_err={err:.3e}")
 
@@ -242,7 +242,7 @@ def test_random_descriptor_sweep(wl):
     err = check_close(out.cpu().numpy(), ref, wl["name"])
     if wl["want_argmax"]:
         Pk = wl["pool_kernel"] ** wl["pool_repeats"]
-        excl = check_argmax(idx.cpu().numpy(), ref_idx, oracle_pre_pool(wl, x, p), Pk, wl["name"])
+        excl = check_argmax(idx.cpu().numpy(), out.cpu().numpy(), ref_idx, oracle_pre_pool(wl, x, p), Pk, wl["name"])
         _say(f"    argmax ok, {excl} near-tie windows excluded")
     _say(f"    {plan.describe().split()[0][:20]} max_abs_err={err:.3e}")
 
@@ -262,7 +262,7 @@ def test_random_specialised_family_sweep(wl):
     err = check_close(out.cpu().numpy(), ref, wl["name"])
     if wl["want_argmax"]:
         Pk = wl["pool_kernel"] ** wl["pool_repeats"]
-        excl = check_argmax(idx.cpu().numpy(), ref_idx, oracle_pre_pool(wl, x, p), Pk, wl["name"])
+        excl = check_argmax(idx.cpu().numpy(), out.cpu().numpy(), ref_idx, oracle_pre_pool(wl, x, p), Pk, wl["name"])
         _say(f"    argmax ok, {excl} near-tie windows excluded")
     _say(f"    {plan.describe().split()[0][:40]} max_abs_err={err:.3e}")
 

@@ -37,7 +37,7 @@ def _case(name, dist="normal", **over):
     err = check_close(out.cpu().numpy(), ref, f"{name} {over}")
     if ref_idx is not None:
         Pk = wl["pool_kernel"] ** wl["pool_repeats"]
-        excl = check_argmax(idx.cpu().numpy(), ref_idx, oracle_pre_pool(wl, x, p), Pk, name)
+        excl = check_argmax(idx.cpu().numpy(), out.cpu().numpy(), ref_idx, oracle_pre_pool(wl, x, p), Pk, name)
         _say(f"    argmax ok, {excl} near-tie windows excluded")
     _say(f"    {plan.describe().split()[0]} max_abs_err={err:.3e}")
 
@@ -75,8 +75,8 @@ SMALL_CASES = [
     # single-write cooperative transposed conv (W = 256): odd output height
     # (last step with one row), column tiles with masked rows, units that do
     # not fill a round, tail steps spread as extra row tiles, several rounds
-    # with the XCD-grouped slice mapping; heights it does not take run the
-    # two-pass kernels
+    # with the XCD-grouped slice mapping; heights it does not take (1, 130,
+    # 131, 132, 202) run the two-pass kernels
     ("convt2d_gelu_gn_n128", dict(N=2, C_in=16, C_out=16, groups=2, num_groups=2,
                                   in_dims=(1, 30, 256))),
     ("convt2d_gelu_gn_n128", dict(N=1, in_dims=(1, 21, 256))),
@@ -85,12 +85,19 @@ SMALL_CASES = [
     ("convt2d_gelu_gn_n128", dict(N=3, in_dims=(1, 127, 256), act="none")),  # odd tail step
     ("convt2d_gelu_gn_n128", dict(N=3, in_dims=(1, 126, 256))),
     ("convt2d_gelu_gn_n128", dict(N=3, in_dims=(1, 128, 256), act="hardswish")),
+    ("convt2d_gelu_gn_n128", dict(N=2, C_in=16, C_out=16, groups=2, num_groups=2,
+                                  in_dims=(1, 130, 256))),
+    ("convt2d_gelu_gn_n128", dict(N=1, in_dims=(1, 131, 256), act="none")),
+    ("convt2d_gelu_gn_n128", dict(N=3, C_in=8, C_out=8, groups=1, num_groups=1,
+                                  in_dims=(1, 132, 256), act="hardswish")),
+    ("convt2d_gelu_gn_n128", dict(N=3, in_dims=(1, 202, 256))),
     ("convt2d_gelu_gn_n128", dict(N=2, in_dims=(1, 256, 256))),
     # tanh-form GELU in every family that takes an activation
     ("conv2d_in_div_n2", dict(N=2, act="gelu_tanh")),
     ("conv3d_softmax_pool_n128", dict(N=2, act="gelu_tanh")),
     ("conv3d_hswish_gn_mean_n1024", dict(N=2, act="gelu_tanh")),
     ("convt2d_gelu_gn_n128", dict(N=2, in_dims=(1, 30, 256), act="gelu_tanh")),
+    ("convt2d_gelu_gn_n128", dict(N=2, in_dims=(1, 136, 256), act="gelu_tanh")),
     ("convt2d_gelu_gn_n128", dict(N=2, in_dims=(1, 9, 20), act="gelu_tanh")),
     # norm groups other than the conv groups, InstanceNorm, affine InstanceNorm
     ("convt2d_gelu_gn_n128", dict(N=2, in_dims=(1, 11, 28), num_groups=4)),
@@ -147,17 +154,20 @@ def test_small_uniform_inputs(name, over):
 
 
 # ---------------------------------------------------------------- full size, sampled
+# Samples compared at full size: seeded interior samples (seed 7000 + workload
+# id) plus samples 0 and N - 1 always.  The single-write transposed conv runs
+# its units round by round, so its interior samples exercise middle rounds.
 FULL_SUBSET = {
     "conv2d_in_div_n2": 2,
-    "conv3d_softmax_pool_n128": 16,
-    "conv3d_hswish_gn_mean_n1024": 8,
-    "conv2d_in_div_n128": 2,
-    "convt2d_gelu_gn_n128": 2,
-    "convt2d_dense_gelu_gn_n128": 2,
-    "conv2d_s2p1_in_div_n128": 2,
-    "convt2d_s2_gelu_gn_n128": 2,
-    "conv2d_in_div_n128_bf16": 2,
-    "convt2d_gelu_gn_n128_bf16": 2,
+    "conv3d_softmax_pool_n128": 16 + 2,
+    "conv3d_hswish_gn_mean_n1024": 8 + 2,
+    "conv2d_in_div_n128": 4 + 2,
+    "convt2d_gelu_gn_n128": 8 + 2,
+    "convt2d_dense_gelu_gn_n128": 4 + 2,
+    "conv2d_s2p1_in_div_n128": 4 + 2,
+    "convt2d_s2_gelu_gn_n128": 4 + 2,
+    "conv2d_in_div_n128_bf16": 4 + 2,
+    "convt2d_gelu_gn_n128_bf16": 4 + 2,
 }
 
 
@@ -169,6 +179,8 @@ def test_full_size_sampled(name):
     p = cnf_inputs.gen_params(wl)
     plan, out, idx = run_gpu(wl, x, p)
     sub = cnf_inputs.subset(wl, FULL_SUBSET[name])
+    assert 0 in sub and wl["N"] - 1 in sub and len(sub) == min(FULL_SUBSET[name], wl["N"])
+    _say(f"    samples compared: {sub}")
     del x
     got = out[sub].cpu().numpy()
     del out
@@ -178,7 +190,7 @@ def test_full_size_sampled(name):
     err = check_close(got, ref, name)
     if ref_idx is not None:
         Pk = wl["pool_kernel"] ** wl["pool_repeats"]
-        excl = check_argmax(idx[sub].cpu().numpy(), ref_idx, oracle_pre_pool(wl, xs, p), Pk, name)
+        excl = check_argmax(idx[sub].cpu().numpy(), got, ref_idx, oracle_pre_pool(wl, xs, p), Pk, name)
         _say(f"    argmax ok, {excl} near-tie windows excluded")
     _say(f"    {plan.describe().split()[0]} samples={sub} max_abs_err={err:.3e}")
 
@@ -196,10 +208,17 @@ def test_repeatable_bitwise():
         assert torch.equal(a, b), name
 
 
-def _fused_slices(Ho):
-    # slices per unit of the single-write kernel: at most 32, four steps each
+def _fused_geometry(Ho):
+    """Slices S (four two-row steps each, at most 32), extra row tiles (16 per
+    tail step) and column tiles (the last column pair of 16 rows) of the
+    single-write kernel; None where it does not take the height (at most one
+    extra and one column tile per slice)."""
     nst = (Ho + 1) // 2
-    return min(32, nst // 4)
+    S = min(32, nst // 4)
+    if S < 1:
+        return None
+    next_, ncol = 16 * (nst - 4 * S), (Ho + 15) // 16
+    return (S, next_, ncol) if next_ <= S and ncol <= S else None
 
 
 # 16-bit x and w through the single-write kernel (widened to fp32 on load): the
@@ -217,13 +236,15 @@ SIXTEEN_BIT_FUSED = [
 
 def _sixteen_bit_fused_random(count, seed=5151):
     """Seeded shapes the single-write kernel takes: W = 256 and heights whose
-    output half-rows split evenly into four-step slices (H = 8k - 3 or 8k - 2)."""
+    extra row tiles and column tiles fit one of each per slice."""
     import numpy as np
     rng = np.random.default_rng(seed)
     out = []
-    for _ in range(count):
+    while len(out) < count:
         g = int(rng.integers(1, 5))
-        H = 8 * int(rng.integers(1, 9)) - int(rng.integers(2, 4))
+        H = int(rng.integers(2, 257))
+        if _fused_geometry(H + 2) is None:
+            continue
         out.append(dict(N=int(rng.integers(1, 4)), C_in=8 * g, C_out=8 * g, groups=g, num_groups=g,
                         in_dims=(1, H, 256),
                         act=["gelu", "gelu_tanh", "hardswish", "none"][int(rng.integers(0, 4))]))
@@ -247,36 +268,97 @@ def test_sixteen_bit_single_write_every_element(over, dtype):
     _say(f"    max_abs_err={err:.3e}")
 
 
-def test_fused_convt_wait_never_times_out():
-    # the single-write kernel raises a flag (workspace word 0) if a
-    # cross-workgroup wait hit its bound; it must stay 0.  Every slice's
-    # triple (count, mean, M2, count) sits at float 4 + 4 (unit * S + slice).
+def _fused_run(wl, x, p, reps=1):
     import convolution_normalization_forward_amd as cnf
-    wl = cnf_inputs.workload("convt2d_gelu_gn_n128", N=6, in_dims=(1, 70, 256))
     plan = cnf.Plan(cnf.make_desc(wl))
-    assert "fused" in plan.describe()
-    x = cnf_inputs.gen_x(wl)
-    p = cnf_inputs.gen_params(wl)
     dev = "cuda:0"
-    t = {k: torch.from_numpy(v).to(dev) for k, v in p.items()}
+    t = {k: (torch.from_numpy(v).to(dev) if v is not None else None) for k, v in p.items()}
     out, _, ws = plan.allocate(dev)
     ws.fill_(0xFF)
-    for _ in range(3):
-        st = cnf.cnf_forward(plan.handle, torch.from_numpy(x).to(dev), t["w"], t["b"], t["gamma"],
-                             t["beta"], out, None, ws, plan.workspace_bytes)
-        assert st == cnf.CNF_OK
-    torch.cuda.synchronize()
+    xt = torch.from_numpy(x).to(dev)
+    for _ in range(reps):
+        st = cnf.cnf_forward(plan.handle, xt, t["w"], t["b"], t["gamma"], t["beta"], out, None, ws,
+                             plan.workspace_bytes)
+        assert st == cnf.CNF_OK, cnf.cnf_status_string(st)
+    return plan, out, ws
+
+
+def test_fused_convt_wait_never_times_out():
+    # the single-write kernel's bounded cross-workgroup waits must all succeed;
+    # every slice's published triple (count, mean, M2, count) sits at floats
+    # 4 (unit * S + slice) of the workspace, and the slices of a unit
+    # partition its 8 x Ho x Wo outputs (Ho = 136: 17 slices, no tail step)
+    import convolution_normalization_forward_amd as cnf
+    wl = cnf_inputs.workload("convt2d_gelu_gn_n128", N=6, in_dims=(1, 134, 256))
+    x = cnf_inputs.gen_x(wl)
+    p = cnf_inputs.gen_params(wl)
+    plan, out, ws = _fused_run(wl, x, p, reps=3)
+    assert "fused" in plan.describe()
+    assert cnf.cnf_forward_check(plan.handle, ws, plan.workspace_bytes) == cnf.CNF_OK
     U = wl["N"] * wl["groups"]
     Ho, Wo = plan.out_shape[2], plan.out_shape[3]
-    S = _fused_slices(Ho)
-    words = ws[:16].view(torch.int32).cpu()
-    assert int(words[0]) == 0, "cross-workgroup wait timed out"
-    tri = ws[16: 16 + 16 * U * S].view(torch.float32).cpu().numpy().reshape(U, S, 4)
+    S = _fused_geometry(Ho)[0]
+    tri = ws[: 16 * U * S].view(torch.float32).cpu().numpy().reshape(U, S, 4)
     assert (tri[:, :, 0] > 0).all() and (tri[:, :, 0] == tri[:, :, 3]).all()
-    # the slices of a unit partition its 8 x Ho x Wo outputs
     assert (tri[:, :, 0].sum(axis=1) == 8 * Ho * Wo).all()
     ref, _ = oracle.forward(wl, x, **p)
     check_close(out.cpu().numpy(), ref, "fused convt repeated")
+
+
+def test_fused_convt_wait_timeout_is_reported(monkeypatch):
+    # a wait that cannot succeed (it also needs a word nothing writes) gives up
+    # after a few polls: the kernel still ends, the units' outputs are NaN
+    # (never normalised with partial statistics) and the caller is told
+    import convolution_normalization_forward_amd as cnf
+    wl = cnf_inputs.workload("convt2d_gelu_gn_n128", N=2, in_dims=(1, 126, 256))
+    x = cnf_inputs.gen_x(wl)
+    p = cnf_inputs.gen_params(wl)
+    monkeypatch.setenv("CNF_TEST_FUSED_NEVER_READY", "1")
+    monkeypatch.setenv("CNF_TEST_FUSED_SPIN_LIMIT", "3")
+    plan, out, ws = _fused_run(wl, x, p)
+    assert "fused" in plan.describe()
+    assert cnf.cnf_forward_check(plan.handle, ws, plan.workspace_bytes) == cnf.CNF_ERR_WAIT_TIMEOUT
+    assert torch.isnan(out).all()
+    # a plan made without the knobs runs normally on the same workspace
+    monkeypatch.delenv("CNF_TEST_FUSED_NEVER_READY")
+    monkeypatch.delenv("CNF_TEST_FUSED_SPIN_LIMIT")
+    plan2, out2, ws2 = _fused_run(wl, x, p)
+    assert cnf.cnf_forward_check(plan2.handle, ws2, plan2.workspace_bytes) == cnf.CNF_OK
+    ref, _ = oracle.forward(wl, x, **p)
+    check_close(out2.cpu().numpy(), ref, "fused convt after a timed-out plan")
+
+
+@pytest.mark.parametrize("over,dtype", [
+    (dict(N=2, in_dims=(1, 126, 256)), "f32"),
+    (dict(N=1, in_dims=(1, 127, 256), act="gelu_tanh"), "f32"),
+    (dict(N=2, in_dims=(1, 128, 256)), "bf16"),
+])
+def test_fused_convt_forced_fallback(monkeypatch, over, dtype):
+    # the dispatch a plan keeps for a grid that cannot be co-resident: the
+    # two-pass kernels for fp32, the general family for 16-bit inputs
+    import convolution_normalization_forward_amd as cnf
+    monkeypatch.setenv("CNF_TEST_FORCE_FALLBACK", "1")
+    wl = cnf_inputs.workload("convt2d_gelu_gn_n128", dtype=dtype, **over)
+    _say(f"[fallback] {over} {dtype}")
+    x = cnf_inputs.gen_x(wl)
+    p = cnf_inputs.gen_params(wl)
+    plan, out, _ = run_gpu(wl, x, p)
+    assert "fused" in plan.describe()
+    ref, _ = oracle.forward(wl, x, **p)
+    err = check_close(out.cpu().numpy(), ref, f"fallback {over} {dtype}")
+    _say(f"    max_abs_err={err:.3e}")
+
+
+@pytest.mark.parametrize("over", [
+    dict(N=3, in_dims=(1, 126, 256)),                    # 24 units, 2 per round: 12 rounds
+    dict(N=2, in_dims=(1, 127, 256), act="gelu_tanh"),   # a tail step (extra row tiles) each round
+    dict(N=2, C_in=16, C_out=16, groups=2, num_groups=2, in_dims=(1, 255, 256)),
+])
+def test_fused_convt_many_rounds(monkeypatch, over):
+    # two units per round, so a small batch runs many rounds: the slice
+    # rotation, the extra-tile hand-out and the bank parity over rounds
+    monkeypatch.setenv("CNF_TEST_FUSED_MAX_UNITS_PER_ROUND", "2")
+    _case("convt2d_gelu_gn_n128", **over)
 
 
 def test_empty_batch_is_a_noop():

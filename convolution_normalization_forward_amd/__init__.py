@@ -33,6 +33,8 @@ CNF_ERR_HIP = 6
 CNF_ERR_ABI = 7
 CNF_ERR_NOMEM = 8
 CNF_ERR_WAIT_TIMEOUT = 9
+CNF_ERR_SCRATCH = 10
+CNF_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 CNF_CONV, CNF_CONV_TRANSPOSE = 0, 1
 ACT = {"none": 0, "hardswish": 1, "gelu": 2, "softmax": 3, "gelu_tanh": 4}
@@ -42,7 +44,7 @@ DTYPE = {"f32": 0, "bf16": 1, "f16": 2}
 
 EXPORTED = ("cnf_plan_create", "cnf_plan_output_shape", "cnf_plan_workspace_size",
             "cnf_forward", "cnf_plan_destroy", "cnf_status_string", "cnf_plan_describe",
-            "cnf_abi_version", "cnf_forward_timed", "cnf_forward_check")
+            "cnf_abi_version", "cnf_forward_timed", "cnf_forward_check", "cnf_forward_noalloc")
 
 
 class cnf_desc(ctypes.Structure):
@@ -114,6 +116,8 @@ def load_library() -> ctypes.CDLL:
     lib.cnf_forward_timed.restype = ctypes.c_int
     lib.cnf_forward_check.argtypes = [P, P, ctypes.c_size_t, P]
     lib.cnf_forward_check.restype = ctypes.c_int
+    lib.cnf_forward_noalloc.argtypes = [P, P, P, P, P, P, P, P, P]
+    lib.cnf_forward_noalloc.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -215,6 +219,15 @@ def cnf_forward_check(plan: int, workspace, workspace_bytes: int, stream=None) -
         stream = torch.cuda.current_stream().cuda_stream
     return int(load_library().cnf_forward_check(plan, _ptr(workspace), int(workspace_bytes),
                                                 stream))
+
+
+def cnf_forward_noalloc(plan: int, x, w, b, gamma, beta, out, argmax, stream=None) -> int:
+    """cnf_forward on the library's fixed device scratch (no workspace, no
+    allocation).  Returns the cnf_status; does not synchronise."""
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    return int(load_library().cnf_forward_noalloc(plan, _ptr(x), _ptr(w), _ptr(b), _ptr(gamma),
+                                                  _ptr(beta), _ptr(out), _ptr(argmax), stream))
 
 
 # ------------------------------------------------------------ conveniences

@@ -3,9 +3,11 @@
 // launch of the chosen family on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "cnf.h"
@@ -141,6 +143,7 @@ const char *cnf_status_string(cnf_status s)
     case CNF_ERR_ABI: return "CNF_ERR_ABI";
     case CNF_ERR_NOMEM: return "CNF_ERR_NOMEM";
     case CNF_ERR_WAIT_TIMEOUT: return "CNF_ERR_WAIT_TIMEOUT";
+    case CNF_ERR_SCRATCH: return "CNF_ERR_SCRATCH";
     }
     return "CNF_ERR_UNKNOWN";
 }
@@ -516,6 +519,68 @@ cnf_status cnf_forward_check(const cnf_plan *plan, const void *workspace, size_t
         hipStreamSynchronize(st) != hipSuccess)
         return CNF_ERR_HIP;
     return flag ? CNF_ERR_WAIT_TIMEOUT : CNF_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Workspace of cnf_forward_noalloc: one copy per device, loaded with the
+// library's code object.  In host code `scratch` names a host-side stand-in,
+// never the device memory: only the address hipGetSymbolAddress returns for
+// a device may be handed to kernels.
+static __device__ __align__(256) unsigned char scratch[CNF_NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::atomic<void *> scratch_ptr[MAX_DEVICES];  // device address of scratch, per device
+std::mutex scratch_mu;
+
+// The device address of scratch on device dev, taken once with dev current.
+hipError_t scratch_address(int dev, void **out)
+{
+    if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+    void *ptr = scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!ptr) {
+        std::lock_guard<std::mutex> lock(scratch_mu);
+        ptr = scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!ptr) {
+            int cur = 0;
+            hipError_t e = hipGetDevice(&cur);
+            if (e != hipSuccess) return e;
+            if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+            e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+            if (cur != dev) {
+                const hipError_t r = hipSetDevice(cur);
+                if (e == hipSuccess) e = r;
+            }
+            if (e != hipSuccess) return e;
+            if (!ptr) return hipErrorInvalidSymbol;
+            scratch_ptr[dev].store(ptr, std::memory_order_release);
+        }
+    }
+    *out = ptr;
+    return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+cnf_status cnf_forward_noalloc(const cnf_plan *plan, const void *x, const void *w, const float *b,
+                               const float *gamma, const float *beta, float *out, int32_t *argmax,
+                               void *stream)
+{
+    if (!plan) return CNF_ERR_NULL;
+    if (plan->workspace > CNF_NOALLOC_SCRATCH_BYTES) return CNF_ERR_SCRATCH;
+    void *ws = nullptr;
+    if (plan->workspace > 0 && plan->d.N > 0) {
+        int dev = 0;
+        if (hipStreamGetDevice(reinterpret_cast<hipStream_t>(stream), &dev) != hipSuccess ||
+            scratch_address(dev, &ws) != hipSuccess)
+            return CNF_ERR_HIP;
+    }
+    return forward_impl(plan, x, w, b, gamma, beta, out, argmax, ws, plan->workspace, stream,
+                        nullptr, nullptr);
 }
 
 }  // extern "C"

@@ -37,8 +37,10 @@
  *     step after it (activation, statistics, norm, divide, reduction) is fp32.
  *   - Every tensor pointer passed to cnf_forward is a DEVICE pointer owned by
  *     the caller (for example a torch tensor's data_ptr()); the library never
- *     allocates device memory, never frees caller memory and never
- *     synchronises the stream.  The plan owns only host memory.
+ *     allocates device memory (its only device memory is the fixed scratch
+ *     array of cnf_forward_noalloc, loaded with its code), never frees caller
+ *     memory and never synchronises the stream.  The plan owns only host
+ *     memory.
  *   - Device pointers must be 16-byte aligned (CNF_ERR_ALIGNMENT otherwise).
  *   - No function throws; every failure is a cnf_status.  Argument errors
  *     (NULL, ALIGNMENT, WORKSPACE, ...) are found before anything is
@@ -74,7 +76,8 @@ typedef enum {
     CNF_ERR_HIP = 6,           /* a HIP launch reported an error */
     CNF_ERR_ABI = 7,           /* desc->abi_version != CNF_ABI_VERSION */
     CNF_ERR_NOMEM = 8,         /* host memory for the plan could not be allocated */
-    CNF_ERR_WAIT_TIMEOUT = 9   /* cnf_forward_check: a bounded cross-workgroup wait gave up */
+    CNF_ERR_WAIT_TIMEOUT = 9,  /* cnf_forward_check: a bounded cross-workgroup wait gave up */
+    CNF_ERR_SCRATCH = 10       /* cnf_forward_noalloc: the plan needs more than the fixed scratch */
 } cnf_status;
 
 typedef enum { CNF_CONV = 0, CNF_CONV_TRANSPOSE = 1 } cnf_conv_kind;
@@ -231,6 +234,29 @@ cnf_status cnf_forward_timed(const cnf_plan *plan,
  * (at most k units per round, so small batches run many rounds). */
 cnf_status cnf_forward_check(const cnf_plan *plan, const void *workspace,
                              size_t workspace_bytes, void *stream);
+
+/* Bytes of the fixed device scratch behind cnf_forward_noalloc. */
+#define CNF_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* cnf_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the workspace is the library's own scratch array, a fixed
+ * CNF_NOALLOC_SCRATCH_BYTES (64 MiB) of device memory that each GPU the
+ * library runs on holds from the library's load until the process ends.
+ * Its device address is taken once per device, on the first call that
+ * needs it for the device of `stream`.  Nothing is allocated or freed.
+ * Arguments and results are cnf_forward's without workspace /
+ * workspace_bytes.  Plans whose cnf_plan_workspace_size exceeds
+ * CNF_NOALLOC_SCRATCH_BYTES return CNF_ERR_SCRATCH before anything is
+ * enqueued.  Every call on one GPU shares that GPU's scratch and the kernels
+ * clear what they need cleared, so consecutive calls are fine, but calls that
+ * overlap in time on one GPU (other streams, other threads) race on it and
+ * must not be issued.  A timed-out cross-workgroup wait of the single-write
+ * kernel (see cnf_forward_check) shows here only as NaN outputs. */
+cnf_status cnf_forward_noalloc(const cnf_plan *plan,
+                               const void *x, const void *w, const float *b,
+                               const float *gamma, const float *beta,
+                               float *out, int32_t *argmax, void *stream);
 
 /* Free a plan (NULL is ignored). */
 void cnf_plan_destroy(cnf_plan *plan);

@@ -39,8 +39,9 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
 
 def test_abi_version_and_status_strings():
     assert cnf.cnf_abi_version() == cnf.CNF_ABI_VERSION
-    for s in range(8):
+    for s in range(11):
         assert cnf.cnf_status_string(s).startswith("CNF_")
+        assert cnf.cnf_status_string(s) != "CNF_ERR_UNKNOWN"
     assert cnf.cnf_status_string(99) == "CNF_ERR_UNKNOWN"
 
 

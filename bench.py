@@ -2,19 +2,26 @@
 """Benchmark of the fused conv + norm forward path on one MI355X.
 
 A step is one call of cnf_forward on one batch of seeded synthetic input that
-is already resident in device memory.  The headline workload is the Conv3d
-3->16 k3 -> channel softmax -> MaxPool3d(2) x2 problem at batch 128
-(page "Kimi-K2.6__l2_p6"); every other workload is measured the same way and
-listed under "per_workload" in the same JSON line.
+is already resident in device memory.  The headline workload is the largest
+single-GPU configuration: ConvTranspose2d 64->64 k3 groups 8 on
+128 x 64 x 256 x 256 -> GELU (erf) -> GroupNorm(8) with affine (page
+"Kimi-K2.6__l2_p19"), 2.15 GB in and 2.18 GB out.  Every other workload is
+measured the same way and listed under "per_workload" in the same JSON line.
 
 Metric: effective TFLOP/s = 2 * N * C_out * |conv output grid| * (C_in/groups)
 * k^ndim / time (the nominal conv FLOPs), plus ms per step.  `value` and
-`ms_per_step` time K back-to-back steps (inputs resident; whatever the 256 MB
-MALL keeps between steps); each workload also reports cold single steps
-(ms_cold_*), each after a 512 MB write that evicts L2 and MALL.  "roofline" puts
-the dominant kernel's ALGORITHMIC work per launch against the MI355X peak of
-the unit that bounds it, timed with HIP events on the launch stream.
-"cpu_baseline" is the fp64 oracle timed on the host cores on a bounded sample.
+`ms_per_step` time K back-to-back steps (inputs resident).  Each workload also
+reports cold single steps (ms_cold_*), each after a 512 MB write that evicts
+L2 and MALL; the cold median is the primary per-workload figure.
+
+"roofline" puts the dominant kernel's ALGORITHMIC work per launch against the
+MI355X peak of the unit that bounds it.  The dominant kernel's launch
+duration is measured live: every timed step goes through cnf_forward_timed,
+which records a HIP event pair around that kernel on the launch stream.
+"traffic" (and per workload "counter_hbm_gbs") come from rocprofv3
+FETCH_SIZE / WRITE_SIZE runs summarised in profiles/traffic.json, used only
+while the kernel's sources are the ones measured.  "cpu_baseline" is the fp64
+oracle timed on the host cores on a bounded sample of each workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -33,29 +40,30 @@ sys.path.insert(0, ROOT)
 PEAK_FP32_TFLOPS = 157.3     # MI355X dense fp32 (MFMA and packed vector)
 PEAK_MFMA_TFLOPS = {"f32": 157.3, "bf16": 2500.0, "f16": 2500.0}  # dense MFMA per input type
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
-HEADLINE = "conv3d_softmax_pool_n128"
+HEADLINE = "convt2d_gelu_gn_n128"
+CSRC = os.path.join(ROOT, "convolution_normalization_forward_amd", "csrc")
 
-# Dominant kernel of each workload, as named by rocprofv3 (prefix match), its
-# bounding unit, and the ALGORITHMIC work per launch: the per-unit figure x the
-# units one launch processes (see the per-unit notes below).
-#   softmax-pool: per pooled window 64 voxels x 16 ch x C_in*k^3 MAC x 2.
-#   gn-mean:      per sample, the full conv (nothing skipped) -> nominal FLOPs.
-#   small:        the full conv -> nominal FLOPs.
-#   igemm:        the full conv -> nominal FLOPs.
-#   convt:        HBM bound: x read once + the output written once (fp32).
-#   upsample2:    the stride-2 transposed conv's normalising pass (mode 2): x read
-#                 once + the output written once (a statistics pass precedes it).
+# Dominant kernel of each workload (the launch cnf_forward_timed brackets), as
+# rocprofv3 names it (prefix match), its source file, the unit that bounds it,
+# and the ALGORITHMIC work per launch (the per-unit figure x the units one
+# launch processes):
+#   softmax-pool: per pooled window 64 voxels x 16 ch x C_in*k^3 MAC x 2 FLOP
+#                 (the 25% of conv voxels no window reads are not counted).
+#   gn-mean, small, igemm, generic conv: the full conv, nominal FLOPs.
+#   convt (single write): HBM, x and w read once + the fp32 output written once.
+#   upsample2:    the stride-2 transposed conv's normalising pass (mode 2):
+#                 HBM, x read once + the output written once.
 DOMINANT = {
-    "conv2d_in_div_n2": ("small_conv_norm_kernel", "mfma"),
-    "conv3d_softmax_pool_n128": ("conv3d_softmax_pool_kernel", "mfma"),
-    "conv3d_hswish_gn_mean_n1024": ("conv3d_k4_gn_mean_kernel", "mfma"),
-    "conv2d_in_div_n128": ("conv2d_igemm_kernel<128", "mfma"),
-    "convt2d_gelu_gn_n128": ("convt2d_gn_fused_kernel<2, 0>", "mfma"),
-    "convt2d_dense_gelu_gn_n128": ("conv2d_igemm_kernel<64", "mfma"),
-    "conv2d_s2p1_in_div_n128": ("gen_conv_kernel<false, 4, 1, 0>", "mfma"),
-    "convt2d_s2_gelu_gn_n128": ("upsample2_conv_kernel<2, 2>", "hbm"),
-    "conv2d_in_div_n128_bf16": ("gen_conv_kernel<false, 4, 1, 1>", "mfma"),
-    "convt2d_gelu_gn_n128_bf16": ("convt2d_gn_fused_kernel<2, 1>", "mfma"),
+    "conv2d_in_div_n2": ("small_conv_norm_kernel", "k_small_conv_norm.hip", "mfma"),
+    "conv3d_softmax_pool_n128": ("conv3d_softmax_pool_kernel", "k_conv3d_softmax_pool.hip", "mfma"),
+    "conv3d_hswish_gn_mean_n1024": ("conv3d_k4_gn_mean_kernel", "k_conv3d_gn_mean.hip", "mfma"),
+    "conv2d_in_div_n128": ("conv2d_igemm_kernel<128", "k_conv2d_igemm.hip", "mfma"),
+    "convt2d_gelu_gn_n128": ("convt2d_gn_fused_kernel<2, 0>", "k_convt2d_gn_fused.hip", "hbm"),
+    "convt2d_dense_gelu_gn_n128": ("conv2d_igemm_kernel<64", "k_conv2d_igemm.hip", "mfma"),
+    "conv2d_s2p1_in_div_n128": ("gen_conv_kernel<false, 4, 1, 0>", "k_generic.hip", "mfma"),
+    "convt2d_s2_gelu_gn_n128": ("upsample2_conv_kernel<2, 2>", "k_upsample2.hip", "hbm"),
+    "conv2d_in_div_n128_bf16": ("gen_conv_kernel<false, 4, 1, 1>", "k_generic.hip", "mfma"),
+    "convt2d_gelu_gn_n128_bf16": ("convt2d_gn_fused_kernel<2, 1>", "k_convt2d_gn_fused.hip", "hbm"),
 }
 
 
@@ -113,11 +121,16 @@ def algorithmic_bytes(wl):
     return es * (n + w) + 4.0 * (3 * wl["C_out"] + out)
 
 
-def kernel_source_digest():
+def dominant_work(wl, bound):
+    """Algorithmic work of one launch of the dominant kernel: FLOP or bytes."""
+    return algorithmic_bytes(wl) if bound == "hbm" else algorithmic_flops(wl)
+
+
+def kernel_source_digest(name):
+    """Digest of the sources the workload's dominant kernel is built from."""
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "convolution_normalization_forward_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
+    for f in (DOMINANT[name][1], "device.h", "kernels.h"):
+        with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
 
@@ -132,12 +145,27 @@ def load_traffic(name):
     except (OSError, ValueError):
         return None
     e = t.get(name)
-    if not e or e.get("kernel_source_digest") != kernel_source_digest():
+    if not e or e.get("kernel_source_digest") != kernel_source_digest(name):
         return None
     return e.get("hbm_bytes_per_launch")
 
 
-def time_workload(name, steps, warmup, dev, flush=None, cold_reps=10):
+def _events(n):
+    import torch
+    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+def _pairs(n, stream):
+    """n (before, after) event pairs for cnf_forward_timed, each recorded once
+    so that its HIP handle exists."""
+    ev = list(zip(_events(n), _events(n)))
+    for a, b in ev:
+        a.record(stream)
+        b.record(stream)
+    return ev
+
+
+def time_workload(name, steps, warmup, dev, flush=None, cold_reps=None):
     import numpy as np
     import torch
 
@@ -146,75 +174,91 @@ def time_workload(name, steps, warmup, dev, flush=None, cold_reps=10):
 
     wl = cnf_inputs.workload(name)
     plan = cnf.Plan(cnf.make_desc(wl))
-    p = cnf_inputs.gen_params(wl)
     dt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[wl.get("dtype", "f32")]
-    x = torch.from_numpy(cnf_inputs.gen_x(wl)).to(dev).to(dt)
-    t = {k: (torch.from_numpy(v).to(dev) if v is not None else None) for k, v in p.items()}
+    # x ~ N(0, 1), drawn on the device from a seeded generator; the conv and
+    # norm parameters are the workload's seeded draws
+    g = torch.Generator(device=dev)
+    g.manual_seed(20_000 + wl["id"])
+    x = torch.randn(cnf_inputs.x_shape(wl), generator=g, device=dev).to(dt)
+    t = {k: (torch.from_numpy(v).to(dev) if v is not None else None)
+         for k, v in cnf_inputs.gen_params(wl).items()}
     t["w"] = t["w"].to(dt)
     out, idx, ws = plan.allocate(dev)
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
 
-    def step():
-        st = cnf.cnf_forward(plan.handle, x, t["w"], t["b"], t["gamma"], t["beta"], out, idx, ws,
-                             plan.workspace_bytes, sp)
+    def step(ev=None):
+        if ev is None:
+            st = cnf.cnf_forward(plan.handle, x, t["w"], t["b"], t["gamma"], t["beta"], out, idx,
+                                 ws, plan.workspace_bytes, sp)
+        else:
+            st = cnf.cnf_forward_timed(plan.handle, x, t["w"], t["b"], t["gamma"], t["beta"], out,
+                                       idx, ws, plan.workspace_bytes, sp, ev[0].cuda_event,
+                                       ev[1].cuda_event)
         if st != cnf.CNF_OK:
             raise cnf.CnfError(st, "cnf_forward")
 
+    # one event pair per timed step around the dominant kernel
+    kev = _pairs(steps, stream)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     # timed region: exactly `steps` back-to-back steps between one pair of HIP
     # events recorded on the launch stream, synchronised on both sides
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    e0, e1 = _events(2)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0.record(stream)
-    for _ in range(steps):
-        step()
+    for i in range(steps):
+        step(kev[i])
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1) / steps
-    # per-step event pairs as well (include each launch's own latency)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(min(steps, 20))]
-    for a, b in ev:
-        a.record(stream)
-        step()
-        b.record(stream)
-    torch.cuda.synchronize()
-    per = np.array([a.elapsed_time(b) for a, b in ev])
+    kms = np.array([a.elapsed_time(b) for a, b in kev])
     # cold steps: before each, overwrite a buffer larger than the MALL (256 MB) so
     # no input, weight or output line is left in L2 / MALL; then time one step
-    cold = []
+    if cold_reps is None:
+        cold_reps = 50 if ms < 1.0 else 10
+    cold, cold_k = [], []
     if flush is not None:
-        for i in range(cold_reps):
+        ce = [(a, b, c, d) for (a, b), (c, d) in zip(_pairs(cold_reps, stream),
+                                                      _pairs(cold_reps, stream))]
+        torch.cuda.synchronize()
+        for i, (a, b, c, d) in enumerate(ce):
             flush.fill_(float(i))
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
-            step()
+            step((c, d))
             b.record(stream)
             b.synchronize()
             cold.append(a.elapsed_time(b))
+            cold_k.append(c.elapsed_time(d))
     cold = np.array(cold) if cold else None
+    cold_k = np.array(cold_k) if cold_k else None
     fl = nominal_flops(wl)
-    afl = algorithmic_flops(wl)
     ab = algorithmic_bytes(wl)
-    kern, bound = DOMINANT[name]
+    kern, src, bound = DOMINANT[name]
+    work = dominant_work(wl, bound)
+    k_ms = float(kms.mean())
+    if bound == "hbm":
+        k_ach, k_peak, k_unit = work / (k_ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
+    else:
+        k_peak = PEAK_MFMA_TFLOPS[wl.get("dtype", "f32")]
+        k_ach, k_unit = work / (k_ms * 1e-3) / 1e12, "TFLOP/s"
+    traffic = load_traffic(name)
+    cold_med = float(np.median(cold)) if cold is not None else None
     res = {
         "workload": name,
         "family": plan.describe().split()[0].split("=")[1],
-        "ms": ms,
-        "ms_single_launch_mean": float(per.mean()),
-        "ms_single_launch_min": float(per.min()),
-        "ms_wall_per_step": wall * 1e3 / steps,
-        "ms_cold_median": float(np.median(cold)) if cold is not None else None,
+        "primary": "ms_cold_median",
+        "ms_cold_median": cold_med,
         "ms_cold_min": float(cold.min()) if cold is not None else None,
+        "ms": ms,
+        "ms_wall_per_step": wall * 1e3 / steps,
         "effective_tflops": fl / (ms * 1e-3) / 1e12,
+        "effective_tflops_cold": fl / (cold_med * 1e-3) / 1e12 if cold_med else None,
         "nominal_gflop": fl / 1e9,
-        "algorithmic_gflop": afl / 1e9,
+        "algorithmic_gflop": algorithmic_flops(wl) / 1e9,
         "algorithmic_gb": ab / 1e9,
         "frac_fp32_peak": fl / (ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS,
         "frac_mfma_peak_own_dtype": fl / (ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS[wl.get("dtype", "f32")],
@@ -222,63 +266,84 @@ def time_workload(name, steps, warmup, dev, flush=None, cold_reps=10):
         "dtype": wl.get("dtype", "f32"),
         "dominant_kernel": kern,
         "bound": bound,
+        "dominant_ms_mean": k_ms,
+        "dominant_ms_min": float(kms.min()),
+        "dominant_ms_cold_median": float(np.median(cold_k)) if cold_k is not None else None,
+        "dominant_achieved": k_ach,
+        "dominant_peak": k_peak,
+        "dominant_unit": k_unit,
+        "dominant_frac": k_ach / k_peak,
+        "counter_hbm_bytes_per_launch": traffic,
+        "counter_hbm_gbs": traffic / (k_ms * 1e-3) / 1e9 if traffic else None,
+        "counter_frac_hbm": traffic / (k_ms * 1e-3) / 1e9 / PEAK_HBM_GBS if traffic else None,
     }
-    del x, out, idx, ws, t
-    torch.cuda.empty_cache()
+    del x, out, idx, ws, t, plan
     return wl, res
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            return next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
+    except OSError:
+        return None
+
+
 def cpu_baseline(name, seconds):
-    """The fp64 oracle, as it stands, on the host cores: whole batches of the
-    workload's first samples, repeated until `seconds` of wall time."""
+    """The fp64 oracle, as it stands, on the host cores: passes over the
+    workload's samples 0, 1, 2, ... (doubling the samples per pass while a
+    pass is short) until `seconds` of oracle time; only the oracle is timed."""
     import cnf_inputs
     import oracle
 
     wl = cnf_inputs.workload(name)
     p = cnf_inputs.gen_params(wl)
-    n = min(wl["N"], 16)
-    x = cnf_inputs.gen_x(wl, range(n))
-    wl_n = dict(wl, N=n)
-    done = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.forward(wl_n, x, **p)
-        done += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    fl = nominal_flops(wl_n) * done
-    model = None
-    try:
-        with open("/proc/cpuinfo") as f:
-            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")),
-                         None)
-    except OSError:
-        pass
-    per_sample = el / (done * n)
+    N = wl["N"]
+    fl_sample = nominal_flops(wl) / N
+    el, done, n = 0.0, 0, 1
+    while el < seconds:
+        idx = [(done + j) % N for j in range(n)]
+        x = cnf_inputs.gen_x(wl, idx)
+        t0 = time.perf_counter()
+        oracle.forward(dict(wl, N=n), x, **p)
+        dt = time.perf_counter() - t0
+        el += dt
+        done += n
+        if dt < 0.25 and n < 64:
+            n *= 2
+    per_sample = el / done
     return {
-        "value": fl / el / 1e12,
+        "value": fl_sample * done / el / 1e12,
         "unit": "TFLOP/s",
         "cores": oracle.num_threads(),
         "kind": "oracle",
-        "sample": f"fp64 oracle on samples 0..{n - 1} of {name} (full conv grid), "
-                  f"{done} passes in {el:.1f} s",
-        "subset_seconds": el,
+        "sample": f"fp64 oracle over {done} samples of {name} (samples 0..{min(done, N) - 1}, "
+                  f"full conv grid each), {el:.1f} s of oracle time",
+        "samples": done,
+        "oracle_seconds": el,
         "ms_per_sample": per_sample * 1e3,
-        "full_batch_seconds_extrapolated": per_sample * wl["N"],
-        "cpu_model": model,
+        "full_batch_seconds_extrapolated": per_sample * N,
+        "cpu_model": cpu_model(),
     }
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--only", action="store_true", help="measure the named workload only")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cold-reps", type=int, default=None,
+                    help="cold single steps per workload (default 50 below 1 ms, else 10)")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
+                    help="oracle seconds for the headline workload's CPU baseline")
+    ap.add_argument("--cpu-seconds-other", type=float, default=4.0,
+                    help="oracle seconds for every other workload's CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--print-maps", action="store_true",
+                    help="at the end, print the executable mappings of the loaded shared "
+                         "objects to stderr (to attribute frames of a crash at process exit)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="first run 5 plain device copies of this many MiB (a known-size "
                          "kernel for scaling HBM byte counters)")
@@ -316,29 +381,27 @@ def main():
     for nm in names:
         print(f"[bench] {nm}: timing {args.steps} steps after {args.warmup} warm-up",
               file=sys.stderr, flush=True)
-        wl, r = time_workload(nm, args.steps, args.warmup, dev, flush)
+        wl, r = time_workload(nm, args.steps, args.warmup, dev, flush, args.cold_reps)
         per[nm] = r
         if nm == args.workload:
             head_wl = wl
+        torch.cuda.empty_cache()
+    del flush
+    torch.cuda.synchronize()
     h = per[args.workload]
 
-    kern, bound = DOMINANT[args.workload]
-    if bound == "mfma":
-        achieved = algorithmic_flops(head_wl) / (h["ms"] * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP32_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_TFLOPS}
-    else:
-        achieved = algorithmic_bytes(head_wl) / (h["ms"] * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS}
-    roof["kernel"] = kern
-    roof["traffic"] = load_traffic(args.workload)
+    roof = {"bound": h["bound"], "achieved": h["dominant_achieved"], "peak": h["dominant_peak"],
+            "unit": h["dominant_unit"], "frac": h["dominant_frac"],
+            "traffic": h["counter_hbm_bytes_per_launch"], "kernel": h["dominant_kernel"],
+            "kernel_ms_mean": h["dominant_ms_mean"],
+            "work_per_launch": dominant_work(head_wl, h["bound"])}
 
-    cpu = None
     if not args.no_cpu_baseline:
-        print(f"[bench] cpu baseline: oracle for ~{args.cpu_seconds:.0f} s", file=sys.stderr,
-              flush=True)
-        cpu = cpu_baseline(args.workload, args.cpu_seconds)
+        for nm in names:
+            s = args.cpu_seconds if nm == args.workload else args.cpu_seconds_other
+            print(f"[bench] cpu baseline {nm}: oracle for ~{s:.0f} s", file=sys.stderr, flush=True)
+            per[nm]["cpu_baseline"] = cpu_baseline(nm, s)
+    cpu = per[args.workload].get("cpu_baseline")
 
     line = {
         "metric": "fused conv+norm fwd effective TFLOP/s",
@@ -348,19 +411,27 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": h["ms"],
+        "ms_cold_median": h["ms_cold_median"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": h["dtype"],
         "data": "synthetic",
         "config": {"workload": args.workload, "N": head_wl["N"], "C_in": head_wl["C_in"],
                    "C_out": head_wl["C_out"], "in_dims": list(head_wl["in_dims"]),
-                   "kernel": head_wl["kernel"], "parallelism": "single-gpu"},
+                   "kernel": head_wl["kernel"], "groups": head_wl["groups"],
+                   "parallelism": "single-gpu"},
         "roofline": roof,
         "cpu_baseline": cpu,
         "per_workload": list(per.values()),
     }
     print(json.dumps(line), flush=True)
+    if args.print_maps:
+        with open("/proc/self/maps") as f:
+            for l in f:
+                if " r-xp " in l and ".so" in l:
+                    sys.stderr.write("[maps] " + l)
+        sys.stderr.flush()
 
 
 if __name__ == "__main__":

@@ -125,37 +125,18 @@ __device__ __forceinline__ float hardswish(float x) {
     return x * fminf(fmaxf(x + 3.0f, 0.0f), 6.0f) * (1.0f / 6.0f);
 }
 
-// Exact (erf) GELU, gelu(x) = x * Phi(x) = 0.5 x (1 + erf(x / sqrt 2)),
-// written as relu(x) - 0.5 |x| erfc(z), z = |x| / sqrt 2, which holds for
-// both signs and keeps the negative tail's relative accuracy.  erfc uses the
-// rational-exponential approximation of Abramowitz & Stegun, Handbook of
-// Mathematical Functions (1964), formula 7.1.26 (|error| <= 1.5e-7):
-// erfc(z) = t (a1 + a2 t + ... + a5 t^4) exp(-z^2), t = 1 / (1 + p z).
-// Constants are folded so the whole activation is 11 VALU ops + rcp + exp2:
-// u = |x| sqrt(log2(e) / 2) gives exp(-z^2) = exp2(-u^2) and p z = (p / (sqrt 2
-// sqrt(log2(e) / 2))) u; the a_i carry the factor -0.5 (exact in binary).
-__device__ __forceinline__ float gelu_erf(float x) {
-    const float u = fabsf(x) * 0.849321800f;
-    const float t = __builtin_amdgcn_rcpf(fmaf(0.272737481f, u, 1.0f));
-    float poly = fmaf(t, -0.5307027145f, 0.7265760135f);  // -a5/2, -a4/2
-    poly = fmaf(t, poly, -0.7107068705f);                 // -a3/2
-    poly = fmaf(t, poly, 0.1422483680f);                  // -a2/2
-    poly = fmaf(t, poly, -0.1274147960f);                 // -a1/2
-    poly = poly * t;
-    const float e = __builtin_amdgcn_exp2f(-(u * u));
-    return fmaf(fabsf(x), poly * e, fmaxf(x, 0.0f));
-}
-
-// Exact (erf) GELU in logistic form, x * Phi(x) ~= x * sigma(x P(x^2)): the
-// log-odds of the standard normal CDF is odd, and an odd degree-9 polynomial
+// Exact (erf) GELU, gelu(x) = x * Phi(x) = 0.5 x (1 + erf(x / sqrt 2)), in
+// logistic form x * Phi(x) ~= x * sigma(x P(x^2)): the log-odds of the
+// standard normal CDF is an odd function, and an odd degree-9 polynomial
 // fitted to it (minimax on |x * (sigma(f(x)) - Phi(x))| over [-12, 12],
-// weighted by the GELU error it causes) keeps the GELU within 3.5e-6 of the
-// erf form for every finite x, fp32 rounding included (the tanh form is the
-// degree-3 member of this family, 4.7e-4 off).  P > 0 on [0, inf), so the
-// log-odds run to +-inf with x: the result tends to x and to -0, never NaN.
-// With -log2(e) folded into P: x / (1 + exp2(x P'(x^2))), 7 VALU ops + exp2 +
-// rcp (the A&S form above takes 11 + rcp + exp2).
-__device__ __forceinline__ float gelu_erf_logistic(float x) {
+// weighted by the GELU error it causes) keeps the result within 3.5e-6 of
+// x * Phi(x) for every finite x, fp32 rounding included (the tanh form below
+// is the degree-3 member of this family, 4.7e-4 off; Abramowitz & Stegun's
+// erfc formula 7.1.26 reaches 1.5e-7 but costs 11 VALU ops + rcp + exp2).
+// P > 0 on [0, inf), so the log-odds run to +-inf with x: the result tends to
+// x and to -0, never NaN.  With -log2(e) folded into P:
+// x / (1 + exp2(x P'(x^2))), 7 VALU ops + exp2 + rcp.
+__device__ __forceinline__ float gelu_erf(float x) {
     const float u = x * x;
     float p = fmaf(u, -3.230937637e-06f, 8.828550199e-05f);
     p = fmaf(u, p, 3.599097254e-04f);

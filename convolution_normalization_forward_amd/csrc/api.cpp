@@ -51,6 +51,7 @@ struct cnf_plan {
     size_t workspace;
     size_t flag_offset; // single-write transposed conv: byte offset of its wait flag
     int igemm_pad;      // zero padding the implicit GEMM applies to the input
+    int igemm_stride;   // its stride (1 or 2)
     cnf::LaunchHooks knobs;  // test knobs read from the environment at creation
 };
 
@@ -246,6 +247,7 @@ cnf_status cnf_plan_create(const cnf_desc *desc, cnf_plan **plan)
                       d.dtype == CNF_DTYPE_F32 && !(force && force[0] == '1');
     const bool basic = unit && d.padding == 0;
     p.igemm_pad = d.kind == CNF_CONV_TRANSPOSE ? k - 1 : 0;
+    p.igemm_stride = 1;
     if (!basic) {
         // Stride-1, dilation-1 2-D convs with padding up to k - 1 are the implicit
         // GEMM with that padding; a dense transposed conv with padding p is the
@@ -257,6 +259,16 @@ cnf_status cnf_plan_create(const cnf_desc *desc, cnf_plan **plan)
                                         d.act)) {
             p.family = FAM_IGEMM;
             p.igemm_pad = gp;
+        }
+        // stride-2 2-D convs with padding up to k - 1: the same GEMM at stride 2
+        if (d.kind == CNF_CONV && d.stride == 2 && d.dilation == 1 && d.dtype == CNF_DTYPE_F32 &&
+            !(force && force[0] == '1') && d.ndim == 2 && d.groups == 1 &&
+            d.reduce == CNF_RED_NONE && d.padding <= k - 1 &&
+            cnf::conv2d_igemm_supported(d.C_in, d.C_out, k, d.groups, H + 2 * d.padding,
+                                        W + 2 * d.padding, d.act, 2)) {
+            p.family = FAM_IGEMM;
+            p.igemm_pad = d.padding;
+            p.igemm_stride = 2;
         }
     } else if (d.kind == CNF_CONV && d.groups == 1) {
         if (d.ndim == 3 && d.reduce == CNF_RED_MEAN_SPATIAL && d.act != CNF_ACT_SOFTMAX_CHANNEL &&
@@ -446,6 +458,7 @@ cnf_status forward_impl(const cnf_plan *plan, const void *xv, const void *wv, co
         cnf::Conv2dIgemmArgs a{x, w, b, gamma, beta, out, static_cast<float *>(workspace), d.N,
                                d.C_in, d.C_out, H, W, plan->Ho, plan->Wo, plan->igemm_pad, tr,
                                d.act, norm_groups, d.eps, inv_div};
+        a.stride = plan->igemm_stride;
         e = cnf::launch_conv2d_igemm(a, st);
         break;
     }

@@ -26,8 +26,12 @@
 //     32-column tiles keep the padding of the last column tile small for
 //     widths just past a multiple of 64 (258 = 4 * 64 + 2 wasted a quarter of
 //     the MFMA work with 64-column tiles).
-//   * K is walked in chunks of CC input channels: the chunk's input halo
-//     (CC x (TR + 2) x 34) and its weights (9*CC x CO, from a [ci][tap][co] copy the
+//   * Stride s = 1 or 2: output position (r, c) reads input rows s r + kh and
+//     columns s c + kw of the (padded) input, so a tile's halo is
+//     (TR - 1) s + 3 rows of 31 s + 3 columns.
+//   * K is walked in chunks of CC input channels (4 at stride 1, 2 at stride 2,
+//     so two workgroups still fit a CU's LDS): the chunk's input halo
+//     (CC x halo rows x halo columns) and its weights (9*CC x CO, from a [ci][tap][co] copy the
 //     first kernel makes) are double-buffered in LDS; the next chunk is
 //     fetched into registers while the current one is multiplied.
 //   * Epilogue: bias, coalesced fp32 stores of y (32 consecutive positions per
@@ -42,30 +46,39 @@ namespace cnf {
 
 namespace {
 
-constexpr int CC = 4;                    // input channels per K chunk
-constexpr int KC = 9 * CC;               // K per chunk
 constexpr int TC = 32;                   // output tile columns
-constexpr int PITCH = 36;                // LDS row pitch of the input halo
 constexpr int THREADS = 512;
 constexpr int NWAVES = THREADS / 64;
+constexpr int MAX_CC = 4;                // input channels per K chunk at stride 1
 
-// Tile geometry for CO output channels (128 or 64): 64 channels x 64 columns
-// (two rows of 32) per wave, so NR = 8 waves / (CO / 64) waves along the rows
-// and TR = 2 * NR output rows per tile.
-template <int CO>
+// Tile geometry for CO output channels (128 or 64) and stride SD: 64 channels x
+// 64 columns (two rows of 32) per wave, so NR = 8 waves / (CO / 64) waves along
+// the rows and TR = 2 * NR output rows per tile.  At stride 1 the halo row
+// pitch is 36 and a channel's block starts 32 floats past a multiple of 64, so
+// the two K rows of an operand (lane halves) read disjoint banks; at stride 2 a
+// lane half reads every other float of a row, so the channel block starts an
+// odd number of floats in and the two halves take the even and the odd banks.
+template <int CO, int SD>
 struct Geo {
+    static constexpr int CC = SD == 1 ? MAX_CC : 2;
+    static constexpr int KC = 9 * CC;
     static constexpr int WM = CO / 64, NR = NWAVES / WM, TR = 2 * NR;
-    static constexpr int CS_BASE = (TR + 2) * PITCH;
-    static constexpr int CS = CS_BASE + ((32 - CS_BASE % 64) + 64) % 64;  // == 32 mod 64
+    static constexpr int HR = (TR - 1) * SD + 3, HC = (TC - 1) * SD + 3;  // halo rows, columns
+    static constexpr int PITCH = SD == 1 ? 36 : 68;
+    static constexpr int CS_BASE = HR * PITCH;
+    static constexpr int CS = SD == 1 ? CS_BASE + ((32 - CS_BASE % 64) + 64) % 64  // == 32 mod 64
+                                      : CS_BASE + ((33 - CS_BASE % 64) + 64) % 64; // == 33 mod 64
     static constexpr int WPITCH = CO + 32;                                // == 32 mod 64
-    static constexpr int XS_FLOATS = CC * CS;
+    static constexpr int XS_FLOATS = (CC * CS + 3) / 4 * 4;             // float4-aligned weights after it
     static constexpr int WS_FLOATS = KC * WPITCH;
     static constexpr int BUF_FLOATS = XS_FLOATS + WS_FLOATS;
-    static constexpr int XIN = CC * (TR + 2) * (TC + 2);           // halo floats per chunk
+    static constexpr int XIN = CC * HR * HC;                       // halo floats per chunk
     static constexpr int XPF = (XIN + THREADS - 1) / THREADS;      // per-thread prefetch (scalar)
     static constexpr int WPF = (KC * CO / 4 + THREADS - 1) / THREADS;  // (float4)
-    static_assert(CS % 64 == 32 && WPITCH % 64 == 32, "bank spread");
+    static_assert(WPITCH % 64 == 32, "bank spread");
+    static_assert(HC <= PITCH, "halo row fits its pitch");
     static_assert(NR * WM == NWAVES, "one 64-channel x 64-position block per wave");
+    static_assert(2 * BUF_FLOATS * 4 <= 80 * 1024, "two workgroups per CU");
 };
 
 // Conv: w[co][ci][kh][kw] -> wt[ci][tap][co].  Transposed conv (weights
@@ -81,12 +94,13 @@ __global__ void conv2d_weight_transpose_kernel(const float *__restrict__ w, floa
     wt[i] = transposed ? w[((size_t)ci * CO + co) * 9 + (8 - tap)] : w[(size_t)co * C_in * 9 + rest];
 }
 
-template <int CO, int XPF = Geo<CO>::XPF, int WPF = Geo<CO>::WPF>
+template <int CO, int SD, int XPF = Geo<CO, SD>::XPF, int WPF = Geo<CO, SD>::WPF>
 __device__ __forceinline__ void igemm_fetch(const float *__restrict__ xn, const float *__restrict__ wt,
                                             int chunk, int H, int W, int tid,
                                             const int (&xoff)[XPF], const bool (&xok)[XPF],
                                             float (&xpf)[XPF], v4f (&wpf)[WPF])
 {
+    constexpr int CC = Geo<CO, SD>::CC, KC = Geo<CO, SD>::KC;
     const float *xc = xn + (size_t)chunk * CC * H * W;
 #pragma unroll
     for (int u = 0; u < XPF; ++u) {
@@ -101,13 +115,13 @@ __device__ __forceinline__ void igemm_fetch(const float *__restrict__ xn, const 
     }
 }
 
-template <int CO, int XPF = Geo<CO>::XPF, int WPF = Geo<CO>::WPF>
+template <int CO, int SD, int XPF = Geo<CO, SD>::XPF, int WPF = Geo<CO, SD>::WPF>
 __device__ __forceinline__ void igemm_stash(float *lds, int buf, const int (&xdst)[XPF],
                                             const int (&wdst)[WPF], const float (&xpf)[XPF],
                                             const v4f (&wpf)[WPF])
 {
-    float *xs = lds + buf * Geo<CO>::BUF_FLOATS;
-    float *ws = xs + Geo<CO>::XS_FLOATS;
+    float *xs = lds + buf * Geo<CO, SD>::BUF_FLOATS;
+    float *ws = xs + Geo<CO, SD>::XS_FLOATS;
 #pragma unroll
     for (int u = 0; u < XPF; ++u)
         if (xdst[u] >= 0) xs[xdst[u]] = xpf[u];
@@ -116,16 +130,17 @@ __device__ __forceinline__ void igemm_stash(float *lds, int buf, const int (&xds
         if (wdst[u] >= 0) *reinterpret_cast<v4f *>(ws + wdst[u]) = wpf[u];
 }
 
-template <int CO, int ACT>
+template <int CO, int ACT, int SD>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4, 4)))
 void conv2d_igemm_kernel(const float *__restrict__ x, const float *__restrict__ wt,
                          const float *__restrict__ bias, float *__restrict__ y,
                          float *__restrict__ partials, int C_in, int H, int W, int Ho, int Wo,
                          int pad, int tiles_w, int tiles_per_sample)
 {
-    using G = Geo<CO>;
+    using G = Geo<CO, SD>;
     constexpr int TR = G::TR, NR = G::NR, CS = G::CS, WPITCH = G::WPITCH, XPF = G::XPF, WPF = G::WPF;
     constexpr int XIN = G::XIN, BUF_FLOATS = G::BUF_FLOATS, XS_FLOATS = G::XS_FLOATS;
+    constexpr int CC = G::CC, KC = G::KC, PITCH = G::PITCH, HR = G::HR, HC = G::HC;
     __shared__ float lds[2 * BUF_FLOATS];
 
     const int tid = threadIdx.x;
@@ -150,10 +165,10 @@ void conv2d_igemm_kernel(const float *__restrict__ x, const float *__restrict__ 
     for (int u = 0; u < XPF; ++u) {
         const int e = tid + u * THREADS;
         const int ec = e < XIN ? e : XIN - 1;
-        const int cc = ec % (TC + 2), rest = ec / (TC + 2);
-        const int rr = rest % (TR + 2), c = rest / (TR + 2);
+        const int cc = ec % HC, rest = ec / HC;
+        const int rr = rest % HR, c = rest / HR;
         // input row / column of the (zero-padded by pad) halo element
-        const int gr = row0 + rr - pad, gc = col0 + cc - pad;
+        const int gr = SD * row0 + rr - pad, gc = SD * col0 + cc - pad;
         xok[u] = e < XIN && gr >= 0 && gr < H && gc >= 0 && gc < W;
         xoff[u] = xok[u] ? (c * H + gr) * W + gc : 0;
         xdst[u] = e < XIN ? c * CS + rr * PITCH + cc : -1;
@@ -177,16 +192,16 @@ void conv2d_igemm_kernel(const float *__restrict__ x, const float *__restrict__ 
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
     const int nchunks = C_in / CC;
-    igemm_fetch<CO>(xn, wt, 0, H, W, tid, xoff, xok, xpf, wpf);
-    igemm_stash<CO>(lds, 0, xdst, wdst, xpf, wpf);
+    igemm_fetch<CO, SD>(xn, wt, 0, H, W, tid, xoff, xok, xpf, wpf);
+    igemm_stash<CO, SD>(lds, 0, xdst, wdst, xpf, wpf);
     __syncthreads();
     for (int ch = 0; ch < nchunks; ++ch) {
         const int buf = ch & 1;
-        if (ch + 1 < nchunks) igemm_fetch<CO>(xn, wt, ch + 1, H, W, tid, xoff, xok, xpf, wpf);
+        if (ch + 1 < nchunks) igemm_fetch<CO, SD>(xn, wt, ch + 1, H, W, tid, xoff, xok, xpf, wpf);
         const float *xs = lds + buf * BUF_FLOATS;
         const float *ws = xs + XS_FLOATS;
         const float *wa = ws + h * WPITCH + 64 * wm + i32;
-        const float *xb = xs + h * CS + 2 * wn * PITCH + i32;
+        const float *xb = xs + h * CS + 2 * SD * wn * PITCH + SD * i32;
 #pragma unroll
         for (int tap = 0; tap < 9; ++tap) {
             const int kh = tap / 3, kw = tap % 3;
@@ -196,7 +211,7 @@ void conv2d_igemm_kernel(const float *__restrict__ x, const float *__restrict__ 
                 const float a0 = wa[2 * s * WPITCH];
                 const float a1 = wa[2 * s * WPITCH + 32];
                 const float b0 = xb[2 * p * CS + kh * PITCH + kw];
-                const float b1 = xb[2 * p * CS + (kh + 1) * PITCH + kw];
+                const float b1 = xb[2 * p * CS + (kh + SD) * PITCH + kw];
                 acc[0][0] = mfma_32x32x2(a0, b0, acc[0][0]);
                 acc[0][1] = mfma_32x32x2(a0, b1, acc[0][1]);
                 acc[1][0] = mfma_32x32x2(a1, b0, acc[1][0]);
@@ -204,7 +219,7 @@ void conv2d_igemm_kernel(const float *__restrict__ x, const float *__restrict__ 
             }
         }
         if (ch + 1 < nchunks)  // buf^1 was last read in iteration ch-1
-            igemm_stash<CO>(lds, buf ^ 1, xdst, wdst, xpf, wpf);
+            igemm_stash<CO, SD>(lds, buf ^ 1, xdst, wdst, xpf, wpf);
         __syncthreads();
     }
 
@@ -367,18 +382,21 @@ void conv2d_apply_flat_kernel(float *__restrict__ y, const v2f *__restrict__ ss,
 
 }  // namespace
 
-bool conv2d_igemm_supported(int C_in, int C_out, int kernel, int groups, int H, int W, int act)
+bool conv2d_igemm_supported(int C_in, int C_out, int kernel, int groups, int H, int W, int act,
+                            int stride)
 {
     // (H, W: the padded input; one sample's output planes are addressed with
     // 32-bit byte offsets and its input planes with 32-bit element offsets)
-    return (C_out == 128 || C_out == 64) && kernel == 3 && groups == 1 && C_in % CC == 0 &&
-           C_in >= CC && H >= 3 && W >= 3 &&
-           (long long)C_out * (H - 2) * (W - 2) * 4 < (long long)RES_MAX &&
+    const int cc = stride == 1 ? Geo<128, 1>::CC : Geo<128, 2>::CC;
+    const long long ho = H >= 3 ? (H - 3) / stride + 1 : 0, wo = W >= 3 ? (W - 3) / stride + 1 : 0;
+    return (C_out == 128 || C_out == 64) && kernel == 3 && groups == 1 && (stride == 1 || stride == 2) &&
+           C_in % cc == 0 && C_in >= cc && H >= 3 && W >= 3 &&
+           (long long)C_out * ho * wo * 4 < (long long)RES_MAX &&
            (long long)C_in * H * W < (1LL << 31) &&
            (act == ACT_NONE || act == ACT_HARDSWISH || act == ACT_GELU_ERF || act == ACT_GELU_TANH);
 }
 
-static int tile_rows(int C_out) { return C_out == 128 ? Geo<128>::TR : Geo<64>::TR; }
+static int tile_rows(int C_out) { return C_out == 128 ? Geo<128, 1>::TR : Geo<64, 1>::TR; }
 
 static size_t tiles_of(int C_out, int Ho, int Wo)
 {
@@ -398,13 +416,20 @@ template <int CO, int ACT>
 static void launch_gemm(const Conv2dIgemmArgs &a, const float *wt, int tiles_w, int tiles_h, int tps,
                         hipStream_t st)
 {
-    hipLaunchKernelGGL((conv2d_igemm_kernel<CO, ACT>), dim3(tiles_w, tiles_h, a.N), dim3(THREADS), 0, st,
-                       a.x, wt, a.b, a.out, a.partials, a.C_in, a.H, a.W, a.Ho, a.Wo, a.pad, tiles_w,
-                       tps);
+    static_assert(Geo<CO, 1>::TR == Geo<CO, 2>::TR, "one tile height per channel count");
+    if (a.stride == 2)
+        hipLaunchKernelGGL((conv2d_igemm_kernel<CO, ACT, 2>), dim3(tiles_w, tiles_h, a.N), dim3(THREADS),
+                           0, st, a.x, wt, a.b, a.out, a.partials, a.C_in, a.H, a.W, a.Ho, a.Wo, a.pad,
+                           tiles_w, tps);
+    else
+        hipLaunchKernelGGL((conv2d_igemm_kernel<CO, ACT, 1>), dim3(tiles_w, tiles_h, a.N), dim3(THREADS),
+                           0, st, a.x, wt, a.b, a.out, a.partials, a.C_in, a.H, a.W, a.Ho, a.Wo, a.pad,
+                           tiles_w, tps);
 }
 
 hipError_t launch_conv2d_igemm(const Conv2dIgemmArgs &a, hipStream_t st)
 {
+    if (a.stride != 1 && (a.stride != 2 || a.transposed)) return hipErrorInvalidValue;
     const int CO = a.C_out, tr = tile_rows(CO);
     const int tiles_w = (a.Wo + TC - 1) / TC, tiles_h = (a.Ho + tr - 1) / tr;
     const int tps = tiles_w * tiles_h;

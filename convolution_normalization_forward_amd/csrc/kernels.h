@@ -69,7 +69,8 @@ hipError_t launch_small_conv_norm(const SmallConvNormArgs &a, hipStream_t st);
 
 // ---- Conv2d implicit GEMM on fp32 MFMA (C_out 128 or 64, k 3) writing y and
 //      per-tile Welford partials, then in-place InstanceNorm/GroupNorm + divide;
-//      also a dense stride-1 ConvTranspose2d (input padded by 2, kernel flipped)
+//      stride 1 or 2; also a dense stride-1 ConvTranspose2d (input padded by 2,
+//      kernel flipped)
 struct Conv2dIgemmArgs {
     const float *x, *w, *b, *gamma, *beta;
     float *out;
@@ -81,8 +82,11 @@ struct Conv2dIgemmArgs {
     int act;
     int norm_groups;     // 0: no norm; C_out: instance norm
     float eps, inv_div;
+    int stride = 1;      // 1 or 2 (a transposed conv: 1)
 };
-bool conv2d_igemm_supported(int C_in, int C_out, int kernel, int groups, int H, int W, int act);
+// H, W: the input extents after the zero padding the kernel applies
+bool conv2d_igemm_supported(int C_in, int C_out, int kernel, int groups, int H, int W, int act,
+                            int stride = 1);
 size_t conv2d_igemm_workspace(int N, int C_in, int C_out, int Ho, int Wo);
 hipError_t launch_conv2d_igemm(const Conv2dIgemmArgs &a, hipStream_t st);
 

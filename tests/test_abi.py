@@ -185,7 +185,7 @@ def test_transposed_conv_output_padding_rule():
 
 @pytest.mark.parametrize("name,over,shape", [
     # conv: floor((L + 2p - d(k-1) - 1) / s) + 1
-    ("conv2d_in_div_n128", dict(stride=2, padding=1), (128, 128, 64, 64)),
+    ("conv2d_in_div_n128", dict(stride=2, padding=1, dilation=2), (128, 128, 63, 63)),
     ("conv2d_in_div_n128", dict(dilation=2, padding=2), (128, 128, 128, 128)),
     ("conv3d_hswish_gn_mean_n1024", dict(stride=2, reduce="none"), (1024, 16, 7, 15, 15)),
     # transposed: (L - 1)s - 2p + d(k-1) + op + 1
@@ -210,9 +210,26 @@ def test_padded_stride1_convs_use_the_implicit_gemm():
         plan = cnf.Plan(_desc(name, **over))
         assert "conv2d_igemm" in plan.describe(), (name, over)
         assert plan.out_shape == shape
-    # beyond k - 1, or strided / dilated: the general family
-    for over in (dict(padding=3), dict(padding=1, dilation=2), dict(padding=1, stride=2)):
+    # beyond k - 1, or dilated, or strided past 2: the general family
+    for over in (dict(padding=3), dict(padding=1, dilation=2), dict(padding=1, stride=3),
+                 dict(padding=3, stride=2)):
         assert "family=generic" in cnf.Plan(_desc("conv2d_in_div_n128", **over)).describe(), over
+
+
+def test_stride2_convs_use_the_implicit_gemm():
+    # floor((L + 2p - 3) / 2) + 1, padding 0..2, both channel counts; a
+    # transposed conv at stride 2 stays on the general family
+    for name, over, shape in [("conv2d_in_div_n128", dict(stride=2, padding=1), (128, 128, 64, 64)),
+                              ("conv2d_in_div_n128", dict(stride=2), (128, 128, 63, 63)),
+                              ("conv2d_in_div_n128", dict(stride=2, padding=2), (128, 128, 65, 65)),
+                              ("conv2d_in_div_n128", dict(stride=2, C_out=64, num_groups=64),
+                               (128, 64, 63, 63))]:
+        plan = cnf.Plan(_desc(name, **over))
+        assert "conv2d_igemm" in plan.describe(), (name, over)
+        assert plan.out_shape == shape
+    # stride 2 takes input channels in pairs
+    assert "family=generic" in cnf.Plan(_desc("conv2d_in_div_n128", stride=2, C_in=3)).describe()
+    assert "family=generic" in cnf.Plan(_desc("convt2d_dense_gelu_gn_n128", stride=2)).describe()
 
 
 def test_sixteen_bit_inputs_plan_on_the_general_family():
@@ -250,11 +267,13 @@ def test_family_routing():
     # the page configurations keep their specialised families ...
     fams = {n: cnf.Plan(_desc(n)).describe().split()[0] for n in cnf_inputs.PAGE_WORKLOADS}
     assert not any("generic" in f for f in fams.values()), fams
-    # the other workloads run on the general family, except the 16-bit form of
-    # the transposed conv, which the single-write kernel takes
+    # the other workloads: the 16-bit form of the transposed conv runs on the
+    # single-write kernel, the strided conv on the implicit GEMM, the rest on
+    # the general family
+    special = {"convt2d_gelu_gn_n128_bf16": "family=convt2d_grouped8_gn_fused",
+               "conv2d_s2p1_in_div_n128": "family=conv2d_igemm"}
     for n in set(cnf_inputs.WORKLOAD_ORDER) - set(cnf_inputs.PAGE_WORKLOADS):
-        fam = "family=convt2d_grouped8_gn_fused" if n == "convt2d_gelu_gn_n128_bf16" else "family=generic"
-        assert fam in cnf.Plan(_desc(n)).describe(), n
+        assert special.get(n, "family=generic") in cnf.Plan(_desc(n)).describe(), n
     # ... and CNF_FORCE_GENERIC=1 sends them to the general one
     os.environ["CNF_FORCE_GENERIC"] = "1"
     try:
@@ -283,10 +302,12 @@ def _packed_weights(G, taps, Cgi, Cgo):
     return _align(-(-G // P) * taps * 4 * steps * cobN * 16 * NB * 4)
 
 
-def test_general_workspace_layout_sizes():
+def test_general_workspace_layout_sizes(monkeypatch):
     # InstanceNorm, no reduction: packed weights, per-tile triples (16 B),
     # per-channel scale/shift (8 B)
+    monkeypatch.setenv("CNF_FORCE_GENERIC", "1")
     p = cnf.Plan(_desc("conv2d_in_div_n128", stride=2, padding=1))
+    monkeypatch.delenv("CNF_FORCE_GENERIC")
     S = 64 * 64
     T = (S + 63) // 64
     assert p.workspace_bytes == (_packed_weights(1, 9, 64, 128) + _align(128 * 128 * T * 16)

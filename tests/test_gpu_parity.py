@@ -66,6 +66,14 @@ SMALL_CASES = [
     ("conv2d_in_div_n128", dict(N=1, C_in=64, in_dims=(1, 19, 131))),
     ("conv2d_in_div_n128", dict(N=2, C_in=12, in_dims=(1, 9, 9), norm="group", num_groups=32,
                                 affine=1)),
+    # the implicit GEMM at stride 2 (input channels in pairs): padding 0, 1, 2;
+    # ragged row and column tiles; 64 and 128 output channels; activations
+    ("conv2d_in_div_n128", dict(N=2, C_in=6, in_dims=(1, 37, 70), stride=2, padding=1)),
+    ("conv2d_in_div_n128", dict(N=1, C_in=4, in_dims=(1, 20, 20), stride=2, act="hardswish")),
+    ("conv2d_in_div_n128", dict(N=2, C_in=2, C_out=64, in_dims=(1, 41, 67), stride=2, padding=2,
+                                norm="group", num_groups=8, affine=1, act="gelu")),
+    ("conv2d_in_div_n128", dict(N=1, C_in=8, C_out=64, in_dims=(1, 66, 9), stride=2, padding=1,
+                                num_groups=64, act="gelu_tanh")),
     # grouped ConvTranspose2d + GELU + GroupNorm
     ("convt2d_gelu_gn_n128", dict(N=2, C_in=16, C_out=16, groups=2, num_groups=2,
                                   in_dims=(1, 13, 20))),

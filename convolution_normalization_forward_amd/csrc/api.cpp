@@ -22,7 +22,8 @@ enum Family : int {
     FAM_IGEMM = 4,         // Conv2d C_out 128/64 k3 implicit GEMM (also dense stride-1 ConvTranspose2d) + norm pass
     FAM_CONVT = 5,         // grouped ConvTranspose2d 8x8 per group + act + GroupNorm pass
     FAM_CONVT_FUSED = 6,   // same, single write: cooperative kernel, cross-workgroup merge
-    FAM_GENERIC = 7        // any validated descriptor: gathered implicit GEMM + passes
+    FAM_GENERIC = 7,       // any validated descriptor: gathered implicit GEMM + passes
+    FAM_IGEMM16 = 8        // Conv2d C_out 128/64 k3, 16-bit x and w: implicit GEMM on 32x32x16 MFMA + norm pass
 };
 
 const char *family_name(int f)
@@ -35,6 +36,7 @@ const char *family_name(int f)
     case FAM_CONVT: return "convt2d_grouped8(mfma16x16x4,column-pair)+groupnorm_pass";
     case FAM_CONVT_FUSED: return "convt2d_grouped8_gn_fused(cooperative,single-write)";
     case FAM_GENERIC: return "generic(gathered-igemm mfma16x16x4 + softmax/finalize/apply/pool passes)";
+    case FAM_IGEMM16: return "conv2d_igemm16(mfma32x32x16,channel-innermost halo)+norm_finalize+apply";
     default: return "none";
     }
 }
@@ -298,6 +300,13 @@ cnf_status cnf_plan_create(const cnf_desc *desc, cnf_plan **plan)
                                          d.num_groups))
             p.family = FAM_CONVT_FUSED;
     }
+    // 16-bit x and w of an unpadded stride-1 Conv2d with 64 or 128 output
+    // channels: the implicit GEMM on the 16-bit MFMA
+    if (!p.family && d.dtype != CNF_DTYPE_F32 && !(force && force[0] == '1') &&
+        d.kind == CNF_CONV && d.ndim == 2 && d.groups == 1 && d.reduce == CNF_RED_NONE &&
+        d.stride == 1 && d.dilation == 1 && d.padding == 0 &&
+        cnf::conv2d_igemm16_supported(d.C_in, d.C_out, k, d.groups, H, W, d.act))
+        p.family = FAM_IGEMM16;
     // 16-bit x and w of the single-write transposed-conv shape: that kernel widens
     // them to fp32 as it loads them.  The general family stays its fallback (for a
     // grid that cannot be co-resident), so it must take the descriptor too.
@@ -318,6 +327,8 @@ cnf_status cnf_plan_create(const cnf_desc *desc, cnf_plan **plan)
     p.workspace = 0;
     if (p.family == FAM_IGEMM)
         p.workspace = cnf::conv2d_igemm_workspace(d.N, d.C_in, d.C_out, p.Ho, p.Wo);
+    if (p.family == FAM_IGEMM16)
+        p.workspace = cnf::conv2d_igemm_workspace(d.N, d.C_in, d.C_out, p.Ho, p.Wo, (int)d.dtype);
     if (p.family == FAM_CONVT) p.workspace = cnf::convt2d_workspace(d.N, d.C_out, p.Ho, p.Wo);
     if (p.family == FAM_GENERIC)
         p.workspace = cnf::generic_workspace(generic_args(p, nullptr, nullptr, nullptr, nullptr,
@@ -453,12 +464,14 @@ cnf_status forward_impl(const cnf_plan *plan, const void *xv, const void *wv, co
         e = single([&] { return cnf::launch_small_conv_norm(a, st); });
         break;
     }
-    case FAM_IGEMM: {
+    case FAM_IGEMM:
+    case FAM_IGEMM16: {
         const int tr = d.kind == CNF_CONV_TRANSPOSE;
-        cnf::Conv2dIgemmArgs a{x, w, b, gamma, beta, out, static_cast<float *>(workspace), d.N,
+        cnf::Conv2dIgemmArgs a{xv, wv, b, gamma, beta, out, static_cast<float *>(workspace), d.N,
                                d.C_in, d.C_out, H, W, plan->Ho, plan->Wo, plan->igemm_pad, tr,
                                d.act, norm_groups, d.eps, inv_div};
         a.stride = plan->igemm_stride;
+        a.dtype = plan->family == FAM_IGEMM16 ? (int)d.dtype : 0;
         e = cnf::launch_conv2d_igemm(a, st);
         break;
     }

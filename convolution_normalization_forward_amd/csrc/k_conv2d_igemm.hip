@@ -285,6 +285,269 @@ void conv2d_igemm_kernel(const float *__restrict__ x, const float *__restrict__ 
     }
 }
 
+// ---- 16-bit inputs (bf16 or fp16 x and w, fp32 accumulation): the same GEMM
+// on v_mfma_f32_32x32x16_{bf16,f16}.  Lane l of that MFMA supplies A[l % 32][8
+// (l / 32) .. + 7] and B[8 (l / 32) .. + 7][l % 32] (eight 16-bit values, one
+// 16-byte register quad), so a K step is one tap x 16 input channels and a
+// lane's eight K values are eight channels of one input pixel.  The chunk's
+// input halo is therefore kept channel-innermost in LDS: pixel (row, col)
+// holds its 16 channels in 32 contiguous bytes, and every B operand is one
+// 16-byte LDS read (the 64 lanes of a wave read 1 KB of consecutive bytes).
+// x arrives row-major per channel, so the staging threads load 8 columns of 8
+// channels (eight 16-byte loads) and transpose the 8 x 8 block in registers
+// with byte permutes before the 16-byte LDS writes.  Weights are copied once
+// per launch into [chunk][tap][co][16 ci] order, which is exactly the LDS
+// layout of the A operand.
+//   * A wave owns 64 channels x 4 rows x 32 columns (2 x 4 blocks of 32 x 32);
+//     the workgroup (8 waves) all CO channels x 4 NR rows x 32 columns.
+//   * Zero padding is not applied here (the planner sends only unpadded
+//     stride-1 convs with W % 8 == 0, so a row's 8-column groups are whole and
+//     16-byte aligned); halo pixels past the input read as zeros.
+//   * Epilogue and statistics as in the fp32 kernel (4 rows per wave).
+typedef unsigned u4v __attribute__((ext_vector_type(4)));
+typedef __bf16 bf8v __attribute__((ext_vector_type(8)));
+typedef _Float16 h8v __attribute__((ext_vector_type(8)));
+
+constexpr int CC16 = 16;                 // input channels per K chunk (one K step per tap)
+constexpr int HCOL16 = TC + 2;           // halo columns
+
+template <int CO>
+struct Geo16 {
+    static constexpr int WM = CO / 64, NR = NWAVES / WM, TR = 4 * NR;  // 4 rows per wave
+    static constexpr int HR = TR + 2;
+    static constexpr int XBYTES = HR * HCOL16 * CC16 * 2;     // halo, channel-innermost
+    static constexpr int WBYTES = 9 * CO * CC16 * 2;          // [tap][co][16 ci]
+    static constexpr int BUF = XBYTES + WBYTES;
+    static constexpr int NFULL = HR * 2 * (TC / 8);           // 8 ch x 8 col units
+    static constexpr int NLEFT = HR * 2;                      // 8 ch x the last 2 columns
+    static constexpr int WV = WBYTES / 16;                    // 16-byte weight vectors
+    static constexpr int WPF = (WV + THREADS - 1) / THREADS;
+    static_assert(NFULL + NLEFT <= THREADS, "one staging unit per thread");
+    static_assert(2 * BUF <= 160 * 1024, "double buffer fits the LDS");
+    static_assert(NR * 2 * CO * 3 * 4 <= 2 * BUF, "row partials fit the staging buffers");
+};
+
+// w[co][ci][3][3] (16-bit) -> [ci / 16][tap][co][ci % 16]
+__global__ void conv2d_weight_pack16_kernel(const unsigned short *__restrict__ w,
+                                            unsigned short *__restrict__ wt, int C_in, int CO)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= CO * C_in * 9) return;
+    const int cl = i % CC16, co = (i / CC16) % CO, tap = (i / (CC16 * CO)) % 9,
+              chunk = i / (CC16 * CO * 9);
+    wt[i] = w[((size_t)co * C_in + chunk * CC16 + cl) * 9 + tap];
+}
+
+__device__ __forceinline__ unsigned lo_pair(unsigned a, unsigned b)  // (a.lo16, b.lo16)
+{
+    return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ unsigned hi_pair(unsigned a, unsigned b)  // (a.hi16, b.hi16)
+{
+    return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+template <int DT>
+__device__ __forceinline__ v16f mfma16(const u4v &a, const u4v &b, const v16f &c)
+{
+    if constexpr (DT == 1)
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf8v, a),
+                                                       __builtin_bit_cast(bf8v, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8v, a),
+                                                      __builtin_bit_cast(h8v, b), c, 0, 0, 0);
+}
+
+template <int CO, int ACT, int DT>
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void conv2d_igemm16_kernel(const unsigned short *__restrict__ x, const unsigned short *__restrict__ wt,
+                           const float *__restrict__ bias, float *__restrict__ y,
+                           float *__restrict__ partials, int C_in, int H, int W, int Ho, int Wo,
+                           int tiles_w, int tiles_per_sample)
+{
+    using G = Geo16<CO>;
+    constexpr int TR = G::TR, NR = G::NR, XBYTES = G::XBYTES, BUF = G::BUF, WPF = G::WPF;
+    __shared__ u4v lds4[2 * BUF / 16];
+    unsigned char *const lds = reinterpret_cast<unsigned char *>(lds4);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / NR, wn = wave % NR;
+    const int h = lane >> 5, j = lane & 31;
+    const int tiles_h = gridDim.y;
+    const int L = blockIdx.x + gridDim.x * (blockIdx.y + tiles_h * blockIdx.z);
+    const int T = xcd_remap(L, gridDim.x * tiles_h * gridDim.z);
+    const int tw = T % tiles_w, th = (T / tiles_w) % tiles_h, n = T / (tiles_w * tiles_h);
+    const int row0 = th * TR, col0 = tw * TC;
+    const auto xr = make_rsrc(x + (size_t)n * C_in * H * W, (unsigned)((size_t)C_in * H * W * 2));
+
+    // staging unit of this thread: full (8 channels x 8 columns of one halo row)
+    // or left-over (8 channels x the halo's last 2 columns), or none
+    const bool full = tid < G::NFULL, left = !full && tid < G::NFULL + G::NLEFT;
+    const bool stager = wave * 64 < G::NFULL + G::NLEFT;  // wave-uniform
+    const int u = full ? tid : tid - G::NFULL;
+    const int cg = full ? u % 4 : 0, cb = full ? (u / 4) % 2 : u % 2, rr = full ? u / 8 : u / 2;
+    const int gr = row0 + rr, gc = col0 + (full ? 8 * cg : TC);
+    const bool uok = (full || left) && gr < H && gc < W;
+    // byte offset of channel c8 of the unit in chunk 0; chunk k adds k * 16 H W * 2
+    const unsigned ubase = uok ? (unsigned)(((cb * 8) * H + gr) * W + gc) * 2u : GOOB;
+    const unsigned cstride = (unsigned)(H * W) * 2u;               // next channel
+    const int lbase = (rr * HCOL16 + (full ? 8 * cg : TC)) * 32 + cb * 16;  // LDS byte offset
+
+    u4v xf[8];        // full unit: channel c8's 8 columns; left-over: .x = its 2 columns
+    u4v wf[WPF];
+    auto fetch = [&](int chunk) {
+        const unsigned cbase = (unsigned)chunk * CC16 * cstride;
+#pragma unroll
+        for (int c8 = 0; c8 < 8 && stager; ++c8) {
+            const unsigned off = uok ? ubase + cbase + (unsigned)c8 * cstride : GOOB;
+            if (full)
+                xf[c8] = __builtin_bit_cast(u4v, __builtin_amdgcn_raw_buffer_load_b128(xr, (int)off, 0, 0));
+            else
+                xf[c8] = u4v{__builtin_amdgcn_raw_buffer_load_b32(xr, (int)off, 0, 0), 0u, 0u, 0u};
+        }
+        const u4v *src = reinterpret_cast<const u4v *>(wt) + (size_t)chunk * G::WV;
+#pragma unroll
+        for (int q = 0; q < WPF; ++q) {
+            const int e = tid + q * THREADS;
+            wf[q] = src[e < G::WV ? e : 0];
+        }
+    };
+    auto stash = [&](int buf) {
+        unsigned char *b = lds + buf * BUF;
+        if (full) {
+            // column c gets dwords (ch 0,1), (2,3), (4,5), (6,7) of that column
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                u4v o0, o1;
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    o0[p] = lo_pair(xf[2 * p][m], xf[2 * p + 1][m]);
+                    o1[p] = hi_pair(xf[2 * p][m], xf[2 * p + 1][m]);
+                }
+                *reinterpret_cast<u4v *>(b + lbase + (2 * m) * 32) = o0;
+                *reinterpret_cast<u4v *>(b + lbase + (2 * m + 1) * 32) = o1;
+            }
+        } else if (left) {
+            u4v o0, o1;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                o0[p] = lo_pair(xf[2 * p][0], xf[2 * p + 1][0]);
+                o1[p] = hi_pair(xf[2 * p][0], xf[2 * p + 1][0]);
+            }
+            *reinterpret_cast<u4v *>(b + lbase) = o0;
+            *reinterpret_cast<u4v *>(b + lbase + 32) = o1;
+        }
+        u4v *wl = reinterpret_cast<u4v *>(b + XBYTES);
+#pragma unroll
+        for (int q = 0; q < WPF; ++q) {
+            const int e = tid + q * THREADS;
+            if (e < G::WV) wl[e] = wf[q];
+        }
+    };
+
+    v16f acc[2][4];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+
+    const int nchunks = C_in / CC16;
+    fetch(0);
+    stash(0);
+    __syncthreads();
+    for (int ch = 0; ch < nchunks; ++ch) {
+        const int buf = ch & 1;
+        if (ch + 1 < nchunks) fetch(ch + 1);
+        const unsigned char *xs = lds + buf * BUF;
+        const unsigned char *as = xs + XBYTES + ((64 * wm + j) * CC16 + 8 * h) * 2;
+        const unsigned char *bs = xs + ((4 * wn) * HCOL16 + j) * 32 + 16 * h;
+#pragma unroll
+        for (int tap = 0; tap < 9; ++tap) {
+            const int kh = tap / 3, kw = tap % 3;
+            u4v a[2], b[4];
+#pragma unroll
+            for (int bi = 0; bi < 2; ++bi)
+                a[bi] = *reinterpret_cast<const u4v *>(as + ((tap * CO + 32 * bi) * CC16) * 2);
+#pragma unroll
+            for (int bj = 0; bj < 4; ++bj)
+                b[bj] = *reinterpret_cast<const u4v *>(bs + ((bj + kh) * HCOL16 + kw) * 32);
+#pragma unroll
+            for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+                for (int bj = 0; bj < 4; ++bj) acc[bi][bj] = mfma16<DT>(a[bi], b[bj], acc[bi][bj]);
+        }
+        if (ch + 1 < nchunks) stash(buf ^ 1);  // buf^1 was last read in iteration ch-1
+        __syncthreads();
+    }
+
+    // ---- epilogue: register r of acc[bi][bj] is channel 64 wm + 32 bi +
+    // 8 (r / 4) + 4 h + r % 4 at row row0 + 4 wn + bj, column col0 + j.
+    // Statistics per 16-lane row s16 (columns 16 s16 .. + 15 of the wave's 4
+    // rows), then one Chan merge per channel over the 2 NR row partials.
+    const int s16 = (lane >> 4) & 1;
+    int rem[4];
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) rem[bj] = row0 + 4 * wn + bj < Ho ? Wo - col0 : 0;
+    int cnt = 0;
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) cnt += min(max(rem[bj] - 16 * s16, 0), 16);
+    const float rcnt = cnt ? 1.0f / (float)cnt : 0.0f;
+    const unsigned plane = (unsigned)Ho * Wo;
+    const auto yr = make_rsrc(y + (size_t)n * CO * plane, CO * plane * 4u);
+    bool ok[4];
+    unsigned off[4];
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj) {
+        ok[bj] = j < rem[bj];
+        off[bj] = ((unsigned)(64 * wm + 4 * h) * plane + (unsigned)(row0 + 4 * wn + bj) * Wo + col0 + j) * 4u;
+    }
+    float (*red)[2][CO][3] = reinterpret_cast<float (*)[2][CO][3]>(lds);
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int dc = 32 * bi + 8 * (r >> 2) + (r & 3);  // co - 64 * wm - 4 * h
+            const int co = 64 * wm + 4 * h + dc;
+            const float bc = bias ? bias[co] : 0.0f;
+            float v[4], sum = 0.0f;
+#pragma unroll
+            for (int bj = 0; bj < 4; ++bj) {
+                v[bj] = activate<ACT>(acc[bi][bj][r] + bc);
+                buf_store1(v[bj], yr, ok[bj] ? off[bj] + (unsigned)dc * plane * 4u : GOOB);
+                sum += ok[bj] ? v[bj] : 0.0f;
+            }
+            const float mean = row_sum16(sum) * rcnt;
+            float sq = 0.0f;
+#pragma unroll
+            for (int bj = 0; bj < 4; ++bj) {
+                const float d = v[bj] - mean;
+                sq += ok[bj] ? d * d : 0.0f;
+            }
+            const float m2 = row_sum16(sq);
+            if ((lane & 15) == 0) {
+                red[wn][s16][co][0] = (float)cnt;
+                red[wn][s16][co][1] = mean;
+                red[wn][s16][co][2] = m2;
+            }
+        }
+    }
+    __syncthreads();
+    if (tid < CO) {
+        float tc = 0.f, tm = 0.f, tq = 0.f;
+#pragma unroll
+        for (int k = 0; k < NR; ++k)
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                chan_merge(tc, tm, tq, red[k][q][tid][0], red[k][q][tid][1], red[k][q][tid][2]);
+        const size_t tile = (size_t)th * tiles_w + tw;
+        float *pp = partials + (((size_t)n * tiles_per_sample + tile) * CO + tid) * 3;
+        pp[0] = tc; pp[1] = tm; pp[2] = tq;
+    }
+}
+
 // Statistics -> per-channel scale and shift.  One wave per (sample, norm
 // group): lane l folds the group's (channel, tile) partials l, l + 64, ... in
 // order, the 64 lane results are merged by a fixed tree (DPP rows, then the two
@@ -396,20 +659,38 @@ bool conv2d_igemm_supported(int C_in, int C_out, int kernel, int groups, int H, 
            (act == ACT_NONE || act == ACT_HARDSWISH || act == ACT_GELU_ERF || act == ACT_GELU_TANH);
 }
 
-static int tile_rows(int C_out) { return C_out == 128 ? Geo<128, 1>::TR : Geo<64, 1>::TR; }
-
-static size_t tiles_of(int C_out, int Ho, int Wo)
+bool conv2d_igemm16_supported(int C_in, int C_out, int kernel, int groups, int H, int W, int act)
 {
-    const int tr = tile_rows(C_out);
+    return (C_out == 128 || C_out == 64) && kernel == 3 && groups == 1 && C_in % CC16 == 0 &&
+           C_in >= CC16 && H >= 3 && W >= 8 && W % 8 == 0 &&
+           (long long)C_out * (H - 2) * (W - 2) * 4 < (long long)RES_MAX &&
+           (long long)C_in * H * W * 2 < (1LL << 31) &&
+           (act == ACT_NONE || act == ACT_HARDSWISH || act == ACT_GELU_ERF || act == ACT_GELU_TANH);
+}
+
+static int tile_rows(int C_out, int dtype)
+{
+    if (dtype) return C_out == 128 ? Geo16<128>::TR : Geo16<64>::TR;
+    return C_out == 128 ? Geo<128, 1>::TR : Geo<64, 1>::TR;
+}
+
+static size_t tiles_of(int C_out, int Ho, int Wo, int dtype)
+{
+    const int tr = tile_rows(C_out, dtype);
     return (size_t)((Wo + TC - 1) / TC) * ((Ho + tr - 1) / tr);
 }
 
-size_t conv2d_igemm_workspace(int N, int C_in, int C_out, int Ho, int Wo)
+// [N][tiles][C_out][3] Welford partials, the weight copy ([ci][tap][co] fp32,
+// or [ci / 16][tap][co][16] 16-bit), then [N][C_out] (scale, shift) pairs
+static size_t weight_copy_bytes(int C_in, int C_out, int dtype)
 {
-    // [N][tiles][C_out][3] Welford partials, the [ci][tap][co] weight copy, then
-    // [N][C_out] (scale, shift) pairs
-    return (size_t)N * tiles_of(C_out, Ho, Wo) * C_out * 3 * sizeof(float) +
-           (size_t)C_in * 9 * C_out * sizeof(float) + (size_t)N * C_out * 2 * sizeof(float);
+    return (size_t)C_in * 9 * C_out * (dtype ? 2 : 4);
+}
+
+size_t conv2d_igemm_workspace(int N, int C_in, int C_out, int Ho, int Wo, int dtype)
+{
+    return (size_t)N * tiles_of(C_out, Ho, Wo, dtype) * C_out * 3 * sizeof(float) +
+           weight_copy_bytes(C_in, C_out, dtype) + (size_t)N * C_out * 2 * sizeof(float);
 }
 
 template <int CO, int ACT>
@@ -419,30 +700,58 @@ static void launch_gemm(const Conv2dIgemmArgs &a, const float *wt, int tiles_w, 
     static_assert(Geo<CO, 1>::TR == Geo<CO, 2>::TR, "one tile height per channel count");
     if (a.stride == 2)
         hipLaunchKernelGGL((conv2d_igemm_kernel<CO, ACT, 2>), dim3(tiles_w, tiles_h, a.N), dim3(THREADS),
-                           0, st, a.x, wt, a.b, a.out, a.partials, a.C_in, a.H, a.W, a.Ho, a.Wo, a.pad,
+                           0, st, static_cast<const float *>(a.x), wt, a.b, a.out, a.partials, a.C_in, a.H, a.W, a.Ho, a.Wo, a.pad,
                            tiles_w, tps);
     else
         hipLaunchKernelGGL((conv2d_igemm_kernel<CO, ACT, 1>), dim3(tiles_w, tiles_h, a.N), dim3(THREADS),
-                           0, st, a.x, wt, a.b, a.out, a.partials, a.C_in, a.H, a.W, a.Ho, a.Wo, a.pad,
+                           0, st, static_cast<const float *>(a.x), wt, a.b, a.out, a.partials, a.C_in, a.H, a.W, a.Ho, a.Wo, a.pad,
                            tiles_w, tps);
+}
+
+template <int CO, int ACT>
+static void launch_gemm16(const Conv2dIgemmArgs &a, const unsigned short *wt, int tiles_w, int tiles_h,
+                          int tps, hipStream_t st)
+{
+    const unsigned short *x = static_cast<const unsigned short *>(a.x);
+    if (a.dtype == 1)
+        hipLaunchKernelGGL((conv2d_igemm16_kernel<CO, ACT, 1>), dim3(tiles_w, tiles_h, a.N), dim3(THREADS),
+                           0, st, x, wt, a.b, a.out, a.partials, a.C_in, a.H, a.W, a.Ho, a.Wo, tiles_w,
+                           tps);
+    else
+        hipLaunchKernelGGL((conv2d_igemm16_kernel<CO, ACT, 2>), dim3(tiles_w, tiles_h, a.N), dim3(THREADS),
+                           0, st, x, wt, a.b, a.out, a.partials, a.C_in, a.H, a.W, a.Ho, a.Wo, tiles_w,
+                           tps);
 }
 
 hipError_t launch_conv2d_igemm(const Conv2dIgemmArgs &a, hipStream_t st)
 {
     if (a.stride != 1 && (a.stride != 2 || a.transposed)) return hipErrorInvalidValue;
-    const int CO = a.C_out, tr = tile_rows(CO);
+    const int dt = a.dtype;
+    if (dt != 0 && (dt > 2 || a.stride != 1 || a.transposed || a.pad != 0 || a.W % 8 != 0 ||
+                    a.C_in % CC16 != 0))
+        return hipErrorInvalidValue;
+    const int CO = a.C_out, tr = tile_rows(CO, dt);
     const int tiles_w = (a.Wo + TC - 1) / TC, tiles_h = (a.Ho + tr - 1) / tr;
     const int tps = tiles_w * tiles_h;
     float *wt = a.partials + (size_t)a.N * tps * CO * 3;
     {
         const int total = CO * a.C_in * 9;
-        hipLaunchKernelGGL(conv2d_weight_transpose_kernel, dim3((total + 255) / 256), dim3(256), 0,
-                           st, a.w, wt, a.C_in, CO, a.transposed);
+        if (dt)
+            hipLaunchKernelGGL(conv2d_weight_pack16_kernel, dim3((total + 255) / 256), dim3(256), 0, st,
+                               static_cast<const unsigned short *>(a.w),
+                               reinterpret_cast<unsigned short *>(wt), a.C_in, CO);
+        else
+            hipLaunchKernelGGL(conv2d_weight_transpose_kernel, dim3((total + 255) / 256), dim3(256), 0,
+                               st, static_cast<const float *>(a.w), wt, a.C_in, CO, a.transposed);
     }
     hipError_t e = dominant_begin(st);
     if (e != hipSuccess) return e;
-#define CNF_CASE(C, A) \
-    if (CO == C && a.act == A) launch_gemm<C, A>(a, wt, tiles_w, tiles_h, tps, st); else
+    const unsigned short *wt16 = reinterpret_cast<const unsigned short *>(wt);
+#define CNF_CASE(C, A)                                                                    \
+    if (CO == C && a.act == A) {                                                          \
+        if (dt) launch_gemm16<C, A>(a, wt16, tiles_w, tiles_h, tps, st);                  \
+        else launch_gemm<C, A>(a, wt, tiles_w, tiles_h, tps, st);                         \
+    } else
     CNF_CASE(128, ACT_NONE) CNF_CASE(128, ACT_HARDSWISH) CNF_CASE(128, ACT_GELU_ERF)
     CNF_CASE(128, ACT_GELU_TANH) CNF_CASE(64, ACT_NONE) CNF_CASE(64, ACT_HARDSWISH)
     CNF_CASE(64, ACT_GELU_ERF) CNF_CASE(64, ACT_GELU_TANH)
@@ -453,7 +762,7 @@ hipError_t launch_conv2d_igemm(const Conv2dIgemmArgs &a, hipStream_t st)
     if (a.norm_groups > 0 || a.inv_div != 1.0f) {
         v2f *ss = nullptr;
         if (a.norm_groups > 0) {
-            ss = reinterpret_cast<v2f *>(wt + (size_t)a.C_in * 9 * CO);
+            ss = reinterpret_cast<v2f *>(reinterpret_cast<char *>(wt) + weight_copy_bytes(a.C_in, CO, dt));
             const int waves = a.N * a.norm_groups;
             hipLaunchKernelGGL(conv2d_norm_finalize_kernel, dim3((waves + 3) / 4), dim3(256), 0, st,
                                a.partials, a.gamma, a.beta, ss, a.N, CO, tps, a.norm_groups, a.eps,

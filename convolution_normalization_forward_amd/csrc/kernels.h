@@ -72,7 +72,8 @@ hipError_t launch_small_conv_norm(const SmallConvNormArgs &a, hipStream_t st);
 //      stride 1 or 2; also a dense stride-1 ConvTranspose2d (input padded by 2,
 //      kernel flipped)
 struct Conv2dIgemmArgs {
-    const float *x, *w, *b, *gamma, *beta;
+    const void *x, *w;   // element type dtype
+    const float *b, *gamma, *beta;
     float *out;
     float *partials;     // workspace: [N][tiles][C_out][3], then the weight copy
     int N, C_in, C_out, H, W;
@@ -83,11 +84,14 @@ struct Conv2dIgemmArgs {
     int norm_groups;     // 0: no norm; C_out: instance norm
     float eps, inv_div;
     int stride = 1;      // 1 or 2 (a transposed conv: 1)
+    int dtype = 0;       // 0 fp32; 1 bf16 / 2 fp16 x and w (stride 1, no padding, W % 8 == 0,
+                         // C_in % 16 == 0: v_mfma_f32_32x32x16 on a channel-innermost halo)
 };
 // H, W: the input extents after the zero padding the kernel applies
 bool conv2d_igemm_supported(int C_in, int C_out, int kernel, int groups, int H, int W, int act,
                             int stride = 1);
-size_t conv2d_igemm_workspace(int N, int C_in, int C_out, int Ho, int Wo);
+bool conv2d_igemm16_supported(int C_in, int C_out, int kernel, int groups, int H, int W, int act);
+size_t conv2d_igemm_workspace(int N, int C_in, int C_out, int Ho, int Wo, int dtype = 0);
 hipError_t launch_conv2d_igemm(const Conv2dIgemmArgs &a, hipStream_t st);
 
 // ---- grouped ConvTranspose2d (8 in / 8 out per group, k 3, stride 1) +

@@ -276,6 +276,33 @@ def test_sixteen_bit_single_write_every_element(over, dtype):
     _say(f"    max_abs_err={err:.3e}")
 
 
+# 16-bit x and w through the implicit GEMM on the 32x32x16 MFMA (unpadded
+# stride-1 Conv2d, W % 8 == 0, C_in % 16 == 0): ragged row and column tiles,
+# the last halo columns past the input, 64 and 128 output channels, several K
+# chunks, activations and norms; the oracle takes the same rounded inputs.
+IGEMM16_CASES = [
+    dict(N=2, C_in=16, in_dims=(1, 20, 40)),
+    dict(N=1, C_in=32, in_dims=(1, 37, 72), act="gelu", norm="group", num_groups=32, affine=1),
+    dict(N=2, C_in=16, C_out=64, in_dims=(1, 35, 16), act="hardswish", num_groups=64),
+    dict(N=1, C_in=48, in_dims=(1, 9, 8), act="gelu_tanh"),
+    dict(N=1, C_in=64, C_out=64, in_dims=(1, 70, 24), norm="none", divide_by=3.0),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("over", IGEMM16_CASES)
+def test_sixteen_bit_implicit_gemm_every_element(over, dtype):
+    wl = cnf_inputs.workload("conv2d_in_div_n128", dtype=dtype, **over)
+    _say(f"[igemm16] {over} {dtype}")
+    x = cnf_inputs.gen_x(wl)
+    p = cnf_inputs.gen_params(wl)
+    plan, out, _ = run_gpu(wl, x, p)
+    assert "igemm16" in plan.describe(), plan.describe()
+    ref, _ = oracle.forward(wl, x, **p)
+    err = check_close(out.cpu().numpy(), ref, f"igemm16 {dtype} {over}")
+    _say(f"    max_abs_err={err:.3e}")
+
+
 def _fused_run(wl, x, p, reps=1):
     import convolution_normalization_forward_amd as cnf
     plan = cnf.Plan(cnf.make_desc(wl))

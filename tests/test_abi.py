@@ -232,17 +232,20 @@ def test_stride2_convs_use_the_implicit_gemm():
     assert "family=generic" in cnf.Plan(_desc("convt2d_dense_gelu_gn_n128", stride=2)).describe()
 
 
-def test_sixteen_bit_inputs_plan_on_the_general_family():
+def test_sixteen_bit_inputs_plan_on_the_general_family(monkeypatch):
     """16-bit x and w run on the general family, except the grouped 3x3
     ConvTranspose2d + GroupNorm shape of the single-write kernel, which widens
-    them on load; its workspace also holds the general family's (its fallback)."""
+    them on load (its workspace also holds the general family's: its
+    fallback), and unpadded stride-1 Conv2d with 64 / 128 output channels,
+    W % 8 == 0 and C_in % 16 == 0, which the 16-bit implicit GEMM takes."""
     d = _desc("conv2d_in_div_n128")
     d.dtype = 3
     assert cnf.cnf_plan_create_status(d) == cnf.CNF_ERR_INVALID_DESC
     for dt in ("bf16", "f16"):
         for name in cnf_inputs.PAGE_WORKLOADS:
             plan = cnf.Plan(_desc(name, dtype=dt))
-            fam = "family=convt2d_grouped8_gn_fused" if name == "convt2d_gelu_gn_n128" else "family=generic"
+            fam = {"convt2d_gelu_gn_n128": "family=convt2d_grouped8_gn_fused",
+                   "conv2d_in_div_n128": "family=conv2d_igemm16"}.get(name, "family=generic")
             assert fam in plan.describe() and f"dtype={dt}" in plan.describe(), (name, plan.describe())
         # the same shape at another width is not the single-write kernel's
         p = cnf.Plan(_desc("convt2d_gelu_gn_n128", dtype=dt, in_dims=(1, 64, 200)))
@@ -255,8 +258,21 @@ def test_sixteen_bit_inputs_plan_on_the_general_family():
             del os.environ["CNF_FORCE_GENERIC"]
         assert "family=generic" in gen.describe()
         assert fused.workspace_bytes >= gen.workspace_bytes
-    # 16-bit packed weights: 16 K entries per step (4 per lane), 2-byte elements
+    # the 16-bit implicit GEMM's conditions
+    for over in (dict(in_dims=(1, 128, 124)), dict(C_in=24), dict(padding=1), dict(stride=2),
+                 dict(C_out=96, num_groups=96)):
+        assert "family=generic" in cnf.Plan(_desc("conv2d_in_div_n128", dtype="bf16", **over)).describe(), over
+    for over in (dict(in_dims=(1, 9, 8)), dict(C_in=16, C_out=64, num_groups=64)):
+        assert "family=conv2d_igemm16" in cnf.Plan(_desc("conv2d_in_div_n128", dtype="f16", **over)).describe(), over
+    # its workspace: [N][tiles of 16 rows x 32 columns][C_out][3] partials, the
+    # [C_in / 16][tap][co][16] 16-bit weight copy, [N][C_out] (scale, shift)
     p = cnf.Plan(_desc("conv2d_in_div_n128", dtype="bf16"))
+    assert p.workspace_bytes == 128 * (8 * 4) * 128 * 3 * 4 + 64 * 9 * 128 * 2 + 128 * 128 * 8
+    # 16-bit packed weights of the general family: 16 K entries per step (4 per
+    # lane), 2-byte elements
+    monkeypatch.setenv("CNF_FORCE_GENERIC", "1")
+    p = cnf.Plan(_desc("conv2d_in_div_n128", dtype="bf16"))
+    monkeypatch.delenv("CNF_FORCE_GENERIC")
     S = 126 * 126
     T = -(-126 // 1) * -(-126 // 64)   # one-row tiles of 64 columns
     wp = 1 * 9 * 16 * (64 // 16) * 2 * 16 * 4 * 2   # taps x 16 x steps x cobN x 16 x NB x 2 B
@@ -268,10 +284,11 @@ def test_family_routing():
     fams = {n: cnf.Plan(_desc(n)).describe().split()[0] for n in cnf_inputs.PAGE_WORKLOADS}
     assert not any("generic" in f for f in fams.values()), fams
     # the other workloads: the 16-bit form of the transposed conv runs on the
-    # single-write kernel, the strided conv on the implicit GEMM, the rest on
-    # the general family
+    # single-write kernel, the strided conv on the implicit GEMM, the 16-bit
+    # conv on the 16-bit implicit GEMM, the rest on the general family
     special = {"convt2d_gelu_gn_n128_bf16": "family=convt2d_grouped8_gn_fused",
-               "conv2d_s2p1_in_div_n128": "family=conv2d_igemm"}
+               "conv2d_s2p1_in_div_n128": "family=conv2d_igemm",
+               "conv2d_in_div_n128_bf16": "family=conv2d_igemm16"}
     for n in set(cnf_inputs.WORKLOAD_ORDER) - set(cnf_inputs.PAGE_WORKLOADS):
         assert special.get(n, "family=generic") in cnf.Plan(_desc(n)).describe(), n
     # ... and CNF_FORCE_GENERIC=1 sends them to the general one

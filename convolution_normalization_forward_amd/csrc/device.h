@@ -47,9 +47,12 @@ __device__ __forceinline__ float buf_load1(__amdgpu_buffer_rsrc_t r, unsigned by
 __device__ __forceinline__ v2f buf_load2(__amdgpu_buffer_rsrc_t r, unsigned byte_off) {
     return __builtin_bit_cast(v2f, __builtin_amdgcn_raw_buffer_load_b64(r, (int)byte_off, 0, 0));
 }
-// 4-byte store (dropped when the offset is past the end).
-__device__ __forceinline__ void buf_store1(float v, __amdgpu_buffer_rsrc_t r, unsigned byte_off) {
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, (int)byte_off, 0, 0);
+// 4-byte store (dropped when the per-lane offset is past the end; a uniform
+// offset rides in the scalar operand).
+__device__ __forceinline__ void buf_store1(float v, __amdgpu_buffer_rsrc_t r, unsigned byte_off,
+                                           unsigned uniform_off = 0) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, (int)byte_off,
+                                          (int)uniform_off, 0);
 }
 // 8-byte store, and its non-temporal (streaming) form.
 __device__ __forceinline__ void buf_store2(v2f v, __amdgpu_buffer_rsrc_t r, unsigned byte_off,

@@ -39,6 +39,8 @@
 //     two passes over the registers (DPP row sums, no division per lane); one
 //     Chan merge per channel over the rows (LDS) leaves one partial per
 //     (sample, tile, channel).
+#include <type_traits>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -368,6 +370,7 @@ void conv2d_igemm16_kernel(const unsigned short *__restrict__ x, const unsigned 
     using G = Geo16<CO>;
     constexpr int TR = G::TR, NR = G::NR, XBYTES = G::XBYTES, BUF = G::BUF, WPF = G::WPF;
     __shared__ u4v lds4[2 * BUF / 16];
+    __shared__ float sbias[CO];
     unsigned char *const lds = reinterpret_cast<unsigned char *>(lds4);
 
     const int tid = threadIdx.x;
@@ -394,17 +397,19 @@ void conv2d_igemm16_kernel(const unsigned short *__restrict__ x, const unsigned 
     const unsigned cstride = (unsigned)(H * W) * 2u;               // next channel
     const int lbase = (rr * HCOL16 + (full ? 8 * cg : TC)) * 32 + cb * 16;  // LDS byte offset
 
-    u4v xf[8];        // full unit: channel c8's 8 columns; left-over: .x = its 2 columns
+    // channel c8's 8 columns from the unit's first column (a left-over unit uses
+    // the first 2; its 8-column group is whole and aligned too, since W % 8 ==
+    // 0): one kind of load for every staging lane, issued without a branch
+    u4v xf[8];
     u4v wf[WPF];
     auto fetch = [&](int chunk) {
         const unsigned cbase = (unsigned)chunk * CC16 * cstride;
+        if (stager) {
 #pragma unroll
-        for (int c8 = 0; c8 < 8 && stager; ++c8) {
-            const unsigned off = uok ? ubase + cbase + (unsigned)c8 * cstride : GOOB;
-            if (full)
+            for (int c8 = 0; c8 < 8; ++c8) {
+                const unsigned off = uok ? ubase + cbase + (unsigned)c8 * cstride : GOOB;
                 xf[c8] = __builtin_bit_cast(u4v, __builtin_amdgcn_raw_buffer_load_b128(xr, (int)off, 0, 0));
-            else
-                xf[c8] = u4v{__builtin_amdgcn_raw_buffer_load_b32(xr, (int)off, 0, 0), 0u, 0u, 0u};
+            }
         }
         const u4v *src = reinterpret_cast<const u4v *>(wt) + (size_t)chunk * G::WV;
 #pragma unroll
@@ -455,6 +460,7 @@ void conv2d_igemm16_kernel(const unsigned short *__restrict__ x, const unsigned 
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
     const int nchunks = C_in / CC16;
+    if (tid < CO) sbias[tid] = bias ? bias[tid] : 0.0f;
     fetch(0);
     stash(0);
     __syncthreads();
@@ -486,54 +492,66 @@ void conv2d_igemm16_kernel(const unsigned short *__restrict__ x, const unsigned 
     // ---- epilogue: register r of acc[bi][bj] is channel 64 wm + 32 bi +
     // 8 (r / 4) + 4 h + r % 4 at row row0 + 4 wn + bj, column col0 + j.
     // Statistics per 16-lane row s16 (columns 16 s16 .. + 15 of the wave's 4
-    // rows), then one Chan merge per channel over the 2 NR row partials.
+    // rows), then one Chan merge per channel over the 2 NR row partials.  A
+    // tile wholly inside the output (every tile but the last row and column
+    // ones) takes the unmasked path.
     const int s16 = (lane >> 4) & 1;
-    int rem[4];
-#pragma unroll
-    for (int bj = 0; bj < 4; ++bj) rem[bj] = row0 + 4 * wn + bj < Ho ? Wo - col0 : 0;
-    int cnt = 0;
-#pragma unroll
-    for (int bj = 0; bj < 4; ++bj) cnt += min(max(rem[bj] - 16 * s16, 0), 16);
-    const float rcnt = cnt ? 1.0f / (float)cnt : 0.0f;
     const unsigned plane = (unsigned)Ho * Wo;
     const auto yr = make_rsrc(y + (size_t)n * CO * plane, CO * plane * 4u);
-    bool ok[4];
-    unsigned off[4];
-#pragma unroll
-    for (int bj = 0; bj < 4; ++bj) {
-        ok[bj] = j < rem[bj];
-        off[bj] = ((unsigned)(64 * wm + 4 * h) * plane + (unsigned)(row0 + 4 * wn + bj) * Wo + col0 + j) * 4u;
-    }
     float (*red)[2][CO][3] = reinterpret_cast<float (*)[2][CO][3]>(lds);
+    auto epilogue = [&](auto whole) {
+        constexpr bool WHOLE = decltype(whole)::value;
+        int rem[4];
 #pragma unroll
-    for (int bi = 0; bi < 2; ++bi) {
+        for (int bj = 0; bj < 4; ++bj) rem[bj] = WHOLE ? TC : row0 + 4 * wn + bj < Ho ? Wo - col0 : 0;
+        int cnt = 0;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int dc = 32 * bi + 8 * (r >> 2) + (r & 3);  // co - 64 * wm - 4 * h
-            const int co = 64 * wm + 4 * h + dc;
-            const float bc = bias ? bias[co] : 0.0f;
-            float v[4], sum = 0.0f;
+        for (int bj = 0; bj < 4; ++bj) cnt += min(max(rem[bj] - 16 * s16, 0), 16);
+        const float rcnt = WHOLE ? 1.0f / 64.0f : cnt ? 1.0f / (float)cnt : 0.0f;
+        bool ok[4];
+        unsigned voff[4];
 #pragma unroll
-            for (int bj = 0; bj < 4; ++bj) {
-                v[bj] = activate<ACT>(acc[bi][bj][r] + bc);
-                buf_store1(v[bj], yr, ok[bj] ? off[bj] + (unsigned)dc * plane * 4u : GOOB);
-                sum += ok[bj] ? v[bj] : 0.0f;
-            }
-            const float mean = row_sum16(sum) * rcnt;
-            float sq = 0.0f;
+        for (int bj = 0; bj < 4; ++bj) {
+            ok[bj] = WHOLE || j < rem[bj];
+            voff[bj] = ok[bj] ? ((unsigned)(64 * wm + 4 * h) * plane +
+                                 (unsigned)(row0 + 4 * wn + bj) * Wo + col0 + j) * 4u
+                              : GOOB;
+        }
 #pragma unroll
-            for (int bj = 0; bj < 4; ++bj) {
-                const float d = v[bj] - mean;
-                sq += ok[bj] ? d * d : 0.0f;
-            }
-            const float m2 = row_sum16(sq);
-            if ((lane & 15) == 0) {
-                red[wn][s16][co][0] = (float)cnt;
-                red[wn][s16][co][1] = mean;
-                red[wn][s16][co][2] = m2;
+        for (int bi = 0; bi < 2; ++bi) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int dc = 32 * bi + 8 * (r >> 2) + (r & 3);  // co - 64 * wm - 4 * h
+                const int co = 64 * wm + 4 * h + dc;
+                const float bc = sbias[co];
+                const unsigned so = (unsigned)dc * plane * 4u;     // uniform
+                float v[4], sum = 0.0f;
+#pragma unroll
+                for (int bj = 0; bj < 4; ++bj) {
+                    v[bj] = activate<ACT>(acc[bi][bj][r] + bc);
+                    buf_store1(v[bj], yr, voff[bj], so);
+                    sum += ok[bj] ? v[bj] : 0.0f;
+                }
+                const float mean = row_sum16(sum) * rcnt;
+                float sq = 0.0f;
+#pragma unroll
+                for (int bj = 0; bj < 4; ++bj) {
+                    const float d = v[bj] - mean;
+                    sq = ok[bj] ? fmaf(d, d, sq) : sq;
+                }
+                const float m2 = row_sum16(sq);
+                if ((lane & 15) == 0) {
+                    red[wn][s16][co][0] = (float)cnt;
+                    red[wn][s16][co][1] = mean;
+                    red[wn][s16][co][2] = m2;
+                }
             }
         }
-    }
+    };
+    if (row0 + TR <= Ho && col0 + TC <= Wo)
+        epilogue(std::integral_constant<bool, true>{});
+    else
+        epilogue(std::integral_constant<bool, false>{});
     __syncthreads();
     if (tid < CO) {
         float tc = 0.f, tm = 0.f, tq = 0.f;

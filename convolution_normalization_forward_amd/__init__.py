@@ -18,7 +18,8 @@ import os
 import torch  # noqa: F401  (loads the HIP runtime first; see module docstring)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libcnf.so")
+# CNF_LIB_PATH selects another build of the library (the host-ASan one, say)
+LIB_PATH = os.environ.get("CNF_LIB_PATH") or os.path.join(_HERE, "libcnf.so")
 
 CNF_ABI_VERSION = 4
 

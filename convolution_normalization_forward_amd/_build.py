@@ -3,6 +3,12 @@
 Each source is compiled with hipcc in parallel into _build/, then linked into
 convolution_normalization_forward_amd/libcnf.so.  Packed-fp32 instruction
 selection is switched off for all device code.
+
+build(asan=True) (or `python -m convolution_normalization_forward_amd._build
+--asan`) builds libcnf_asan.so into _build_asan/ with AddressSanitizer on the
+host code only (device code is built as usual).  Loading it needs clang's ASan
+runtime preloaded (asan_runtime() names it) and CNF_LIB_PATH pointing at it;
+the binding honours CNF_LIB_PATH.
 """
 from __future__ import annotations
 
@@ -18,6 +24,11 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcnf.so")
+BUILD_ASAN = os.path.join(ROOT, "_build_asan")
+LIB_ASAN = os.path.join(PKG, "libcnf_asan.so")
+# host-side AddressSanitizer (each -fsanitize= behind -Xarch_host: the device
+# code is not instrumented)
+ASAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
 ARCH = os.environ.get("CNF_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -43,9 +54,19 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + FLAGS + FILE_FLAGS.get(os.path.basename(src), []) + ["-x", "hip", "-c", src, "-o", obj]
+def asan_runtime() -> str:
+    """Path of the ASan runtime shared library of the ROCm clang that hipcc drives."""
+    import glob as _glob
+    hits = sorted(_glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not hits:
+        raise RuntimeError("no libclang_rt.asan-x86_64.so under /opt/rocm/llvm")
+    return hits[-1]
+
+
+def _compile(src: str, asan: bool = False) -> str:
+    obj = os.path.join(BUILD_ASAN if asan else BUILD, os.path.basename(src) + ".o")
+    cmd = [HIPCC] + FLAGS + (ASAN_FLAGS if asan else []) + FILE_FLAGS.get(os.path.basename(src), []) + \
+        ["-x", "hip", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
@@ -56,21 +77,23 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = True, asan: bool = False) -> str:
+    out = LIB_ASAN if asan else LIB
+    os.makedirs(BUILD_ASAN if asan else BUILD, exist_ok=True)
     srcs = sources()
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+        objs = list(ex.map(lambda s: _compile(s, asan), srcs))
+    tmp = out + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + \
+        (["-Xarch_host", "-fsanitize=address", "-shared-libasan"] if asan else []) + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources")
-    return LIB
+        print(f"built {out} from {len(srcs)} sources")
+    return out
 
 
 if __name__ == "__main__":
-    build()
+    build(asan="--asan" in sys.argv[1:])

@@ -20,18 +20,27 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "cnf_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# CNF_ORACLE_LIB selects another build of the oracle (the ASan one, say)
+_LIB_PATH = os.environ.get("CNF_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
+_ASAN_LIB_PATH = os.path.join(_HERE, "liboracle_asan.so")
 _lib = None
 
 
-def build(force: bool = True) -> str:
-    """Compile the oracle with gcc (-O2, strict IEEE, OpenMP)."""
-    if force or not os.path.exists(_LIB_PATH):
-        tmp = _LIB_PATH + ".tmp"
-        subprocess.check_call(["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp",
-                               "-std=c11", "-Wall", "-shared", "-fPIC", _SRC, "-o", tmp, "-lm"])
-        os.replace(tmp, _LIB_PATH)
-    return _LIB_PATH
+def build(force: bool = True, asan: bool = False) -> str:
+    """Compile the oracle with gcc (-O2, strict IEEE, OpenMP).  asan=True:
+    with ROCm's clang and AddressSanitizer instead (the HIP library's
+    host-ASan build uses that compiler's runtime, so both share one), into
+    liboracle_asan.so."""
+    path = _ASAN_LIB_PATH if asan else _LIB_PATH
+    if force or not os.path.exists(path):
+        tmp = path + ".tmp"
+        cc = ["/opt/rocm/llvm/bin/clang", "-fsanitize=address", "-fno-omit-frame-pointer",
+              "-shared-libasan"] if asan else ["gcc"]
+        omp = ["-fopenmp=libgomp"] if asan else ["-fopenmp"]
+        subprocess.check_call(cc + ["-O2", "-fno-fast-math", "-ffp-contract=off"] + omp +
+                              ["-std=c11", "-Wall", "-shared", "-fPIC", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, path)
+    return path
 
 
 def _load():

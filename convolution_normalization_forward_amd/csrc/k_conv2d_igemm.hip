@@ -716,14 +716,14 @@ static void launch_gemm(const Conv2dIgemmArgs &a, const float *wt, int tiles_w, 
                         hipStream_t st)
 {
     static_assert(Geo<CO, 1>::TR == Geo<CO, 2>::TR, "one tile height per channel count");
+    const float *x = static_cast<const float *>(a.x);
+    const dim3 grid(tiles_w, tiles_h, a.N);
     if (a.stride == 2)
-        hipLaunchKernelGGL((conv2d_igemm_kernel<CO, ACT, 2>), dim3(tiles_w, tiles_h, a.N), dim3(THREADS),
-                           0, st, static_cast<const float *>(a.x), wt, a.b, a.out, a.partials, a.C_in, a.H, a.W, a.Ho, a.Wo, a.pad,
-                           tiles_w, tps);
+        hipLaunchKernelGGL((conv2d_igemm_kernel<CO, ACT, 2>), grid, dim3(THREADS), 0, st, x, wt, a.b,
+                           a.out, a.partials, a.C_in, a.H, a.W, a.Ho, a.Wo, a.pad, tiles_w, tps);
     else
-        hipLaunchKernelGGL((conv2d_igemm_kernel<CO, ACT, 1>), dim3(tiles_w, tiles_h, a.N), dim3(THREADS),
-                           0, st, static_cast<const float *>(a.x), wt, a.b, a.out, a.partials, a.C_in, a.H, a.W, a.Ho, a.Wo, a.pad,
-                           tiles_w, tps);
+        hipLaunchKernelGGL((conv2d_igemm_kernel<CO, ACT, 1>), grid, dim3(THREADS), 0, st, x, wt, a.b,
+                           a.out, a.partials, a.C_in, a.H, a.W, a.Ho, a.Wo, a.pad, tiles_w, tps);
 }
 
 template <int CO, int ACT>

@@ -132,19 +132,18 @@ __device__ __forceinline__ v4f eload4(__amdgpu_buffer_rsrc_t r, unsigned byte_of
     }
 }
 
+// Unit (n, g) = n G + g owns channels n C + g CG .. + CG - 1, and C = G CG, so
+// its first channel is unit * CG: no division by G.
 template <int DT>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t x_rsrc(const FusedArgs &a, int unit)
 {
-    const int n = unit / a.G, g = unit % a.G;
-    return make_rsrc(static_cast<const char *>(a.x) +
-                         ((size_t)n * a.C + (size_t)g * CG) * a.H * W * ESZ<DT>,
+    return make_rsrc(static_cast<const char *>(a.x) + (size_t)unit * CG * a.H * W * ESZ<DT>,
                      (unsigned)(CG * a.H * W * ESZ<DT>));
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t y_rsrc(const FusedArgs &a, int unit, unsigned plane)
 {
-    const int n = unit / a.G, g = unit % a.G;
-    return make_rsrc(a.y + ((size_t)n * a.C + (size_t)g * CG) * plane, CG * plane * 4u);
+    return make_rsrc(a.y + (size_t)unit * CG * plane, CG * plane * 4u);
 }
 
 // One input row pair (rows row0, row0 + 1 of the group's 8 channels): this

@@ -41,9 +41,13 @@
 // the previous step's activation.
 //
 // Input element type DT: 0 fp32; 1 bf16 / 2 fp16 for x and the weights (the
-// second input precision), widened to fp32 as they are loaded, so the
-// products, accumulation and epilogue are the fp32 path's; only the bytes
-// read from x halve.
+// second input precision).  16-bit inputs stay 16-bit in the ring and in the
+// A operands, and a step's contraction runs on v_mfma_f32_16x16x32_{bf16,f16}
+// with fp32 accumulation: K = 32 entries (ci, v') per kh, lane (q, c16)
+// supplying ci = 2q, 2q+1 and v' = 0..3, i.e. four consecutive input columns
+// 2 c16 - 2 .. 2 c16 + 1 of each channel (v' = 3 - v).  A row tile then takes
+// 3 MFMAs instead of 24.  The single tiles widen to fp32 as they are loaded
+// (products of 16-bit values are exact in fp32 either way).
 #include <atomic>
 
 #include "device.h"
@@ -63,6 +67,10 @@ constexpr int THREADS = 512;
 constexpr int NWAVE = THREADS / 64;          // one 32-pixel row tile per wave
 constexpr int NSLOT = 4;                     // input row pairs in the LDS ring
 constexpr int PAIR_FLOATS = 2 * CG * RP;
+// 16-bit ring rows: 4 zero elements left of x, pitch 272 elements (136 words:
+// the four lane groups of a B read, channels 2q, start 16 q banks apart)
+constexpr int RP16 = 272;
+constexpr int PAIR16_WORDS = 2 * CG * RP16 / 2;
 constexpr int SPS = 4;                       // steps per slice
 constexpr int NBANK = SPS + 1;               // LDS bank slots
 constexpr int NPOS = 6;                      // ring stash positions per round (SPS + 1, padded to 3 k)
@@ -132,6 +140,34 @@ __device__ __forceinline__ v4f eload4(__amdgpu_buffer_rsrc_t r, unsigned byte_of
     }
 }
 
+// Ring staging registers: fp32 widened float4, or four raw 16-bit elements.
+template <int DT>
+struct Stage {
+    using T = v2u;
+};
+template <>
+struct Stage<0> {
+    using T = v4f;
+};
+
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// D(16x16) += A(16x32) B(32x16) on 16-bit operands: lane l supplies
+// A[l%16][8(l/16) + e] and B[8(l/16) + e][l%16], e = 0..7, two per word (low
+// half first); D element [4(l/16) + r][l%16] lives in register r of lane l.
+template <int DT>
+__device__ __forceinline__ v4f mfma16x32(v4u a, v4u b, v4f c)
+{
+    if constexpr (DT == 1)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
 // Unit (n, g) = n G + g owns channels n C + g CG .. + CG - 1, and C = G CG, so
 // its first channel is unit * CG: no division by G.
 template <int DT>
@@ -152,22 +188,32 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t y_rsrc(const FusedArgs &a, int
 // values, and copying it would wait for the load -- and a row outside [0, H)
 // gets an offset past the buffer, which reads as zeros.
 template <int DT>
-__device__ __forceinline__ void load_pair(v4f (&pf)[2], __amdgpu_buffer_rsrc_t xr, int H, int row0,
-                                          unsigned loff)
+__device__ __forceinline__ void load_pair(typename Stage<DT>::T (&pf)[2], __amdgpu_buffer_rsrc_t xr, int H,
+                                          int row0, unsigned loff)
 {
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr) {
         const int row = row0 + rr;
         const unsigned ro = row >= 0 && row < H ? (unsigned)(row * W) * ESZ<DT> : OOB;
-        pf[rr] = eload4<DT>(xr, loff + ro);
+        if constexpr (DT == 0)
+            pf[rr] = eload4<DT>(xr, loff + ro);
+        else
+            pf[rr] = __builtin_bit_cast(v2u, __builtin_amdgcn_raw_buffer_load_b64(xr, (int)(loff + ro), 0, 0));
     }
 }
 
-__device__ __forceinline__ void stash_pair(float *ring, int slot, const v4f (&pf)[2], int wave, int lane)
+template <int DT>
+__device__ __forceinline__ void stash_pair(float *ring, int slot, const typename Stage<DT>::T (&pf)[2], int wave,
+                                           int lane)
 {
 #pragma unroll
-    for (int rr = 0; rr < 2; ++rr)
-        *reinterpret_cast<v4f *>(ring + slot * PAIR_FLOATS + (rr * CG + wave) * RP + PADL + 4 * lane) = pf[rr];
+    for (int rr = 0; rr < 2; ++rr) {
+        if constexpr (DT == 0)
+            *reinterpret_cast<v4f *>(ring + slot * PAIR_FLOATS + (rr * CG + wave) * RP + PADL + 4 * lane) = pf[rr];
+        else  // 8-byte aligned: RP16 and PADL are multiples of 4 elements
+            *reinterpret_cast<v2u *>(reinterpret_cast<unsigned *>(ring) + slot * PAIR16_WORDS +
+                                     (rr * CG + wave) * (RP16 / 2) + PADL / 2 + 2 * lane) = pf[rr];
+    }
 }
 
 // Ring stash positions of a round: p <= SPS-2 stashes pair p+2 at the end of
@@ -176,7 +222,7 @@ __device__ __forceinline__ void stash_pair(float *ring, int slot, const v4f (&pf
 // p + 3 are issued right after position p's stash, into register set p % 3
 // (NPOS is a multiple of 3, so every round starts on set 0).
 template <int DT>
-__device__ __forceinline__ void issue_pos(int p, v4f (&dst)[2], int k0, __amdgpu_buffer_rsrc_t xr,
+__device__ __forceinline__ void issue_pos(int p, typename Stage<DT>::T (&dst)[2], int k0, __amdgpu_buffer_rsrc_t xr,
                                           bool nhas, int nk0, __amdgpu_buffer_rsrc_t nxr, int H,
                                           unsigned loff)
 {
@@ -382,7 +428,8 @@ template <int ACT, int DT>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void convt2d_gn_fused_kernel(FusedArgs a)
 {
-    __shared__ float ring[NSLOT * PAIR_FLOATS];
+    using PF = typename Stage<DT>::T;
+    __shared__ __align__(16) float ring[DT == 0 ? NSLOT * PAIR_FLOATS : NSLOT * PAIR16_WORDS];
     __shared__ float red[NWAVE * 4 * 3];  // [wave][row of 16 lanes] slice triples
     __shared__ v4f spart[2 * 4 * 64];     // [tile][chunk][lane] single-tile partial sums
     __shared__ float coefs[CG * 2];       // the previous unit's (scale, shift) per channel
@@ -409,34 +456,43 @@ void convt2d_gn_fused_kernel(FusedArgs a)
     }
 
     for (int e = tid; e < NSLOT * 2 * CG; e += THREADS) {  // pad columns, never overwritten
-        float *row = ring + e * RP;
+        if constexpr (DT == 0) {
+            float *row = ring + e * RP;
 #pragma unroll
-        for (int c = 0; c < PADL; ++c) row[c] = 0.f;
+            for (int c = 0; c < PADL; ++c) row[c] = 0.f;
+        } else {
+            unsigned *row = reinterpret_cast<unsigned *>(ring) + e * (RP16 / 2);
+#pragma unroll
+            for (int c = 0; c < PADL / 2; ++c) row[c] = 0u;
+        }
     }
 
     const unsigned loff = (unsigned)(wave * H * W + 4 * lane) * ESZ<DT>;  // pair loads
     const int lb = PADL + 32 * wave + 2 * c16 + 1 - q;                // B operand column
+    // 16-bit B operand: word of columns 2 c16 - 2, -1 of channel 2q in a ring row
+    const int lb16 = 2 * q * (RP16 / 2) + (PADL - 2) / 2 + 16 * wave + c16;
     const unsigned vo0 = ((unsigned)(2 * q) * plane + 32u * wave + 2u * c16) * 4u;
     const unsigned vo1 = vo0 + plane * 4u;
     v4f *const mybank = bank + tid;
     auto slot_of = [](int k, int rho) { return (k + NBANK - rho % NBANK) % NBANK; };
 
     // ---- prologue: round 0's pairs 0, 1 in the ring, positions 0..2 in flight
-    v4f pf[3][2];
+    PF pf[3][2];
     int base = 0;  // ring slot of the current round's pair 0
     {
         const int k0 = s_base * SPS;
         const __amdgpu_buffer_rsrc_t xr = x_rsrc<DT>(a, ulocal);
-        v4f p0[2], p1[2];
+        PF p0[2], p1[2];
         load_pair<DT>(p0, xr, H, 2 * k0 - 2, loff);
         load_pair<DT>(p1, xr, H, 2 * k0, loff);
-        stash_pair(ring, 0, p0, wave, lane);
-        stash_pair(ring, 1, p1, wave, lane);
+        stash_pair<DT>(ring, 0, p0, wave, lane);
+        stash_pair<DT>(ring, 1, p1, wave, lane);
 #pragma unroll
         for (int p = 0; p < 3; ++p) load_pair<DT>(pf[p], xr, H, 2 * (k0 + p + 2) - 2, loff);
     }
 
     float wreg[CG * KS];
+    v4u a16[KS];  // 16-bit A operands, one per kh
     float wsub[SCH];  // this wave's single-tile chunk of the weights
     v4f bias4 = v4f{0.f, 0.f, 0.f, 0.f};  // accumulator start: bias of channels 2q, 2q, 2q+1, 2q+1
     v4f gb = v4f{1.f, 0.f, 1.f, 0.f}, p_gb = gb;
@@ -478,11 +534,32 @@ void convt2d_gn_fused_kernel(FusedArgs a)
             const int co = c16 >> 1, t = c16 & 1;
             const int kw = q + t - 1;
             const bool kok = kw >= 0 && kw < KS;
+            if constexpr (DT == 0) {
 #pragma unroll
-            for (int s = 0; s < CG * KS; ++s) {
-                const int ci = s / KS, kh = s % KS;
-                const float v = eload1<DT>(wr, (unsigned)(((ci * CG + co) * KS + kh) * KS + (kok ? kw : 0)) * ESZ<DT>);
-                wreg[s] = kok ? v : 0.0f;
+                for (int s = 0; s < CG * KS; ++s) {
+                    const int ci = s / KS, kh = s % KS;
+                    const float v = eload1<DT>(wr, (unsigned)(((ci * CG + co) * KS + kh) * KS + (kok ? kw : 0)) * ESZ<DT>);
+                    wreg[s] = kok ? v : 0.0f;
+                }
+            } else {
+                // A[(co, t)][(ci, v')] = w[ci][co][kh][2 - v' + t], ci = 2q + e / 4, v' = e % 4;
+                // taps outside the kernel read past the buffer (zero)
+#pragma unroll
+                for (int kh = 0; kh < KS; ++kh) {
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        unsigned word = 0u;
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+                            const int e = 2 * d + h, ci = 2 * q + e / 4, kw16 = 2 - e % 4 + t;
+                            const bool ok = kw16 >= 0 && kw16 < KS;
+                            const unsigned v = __builtin_amdgcn_raw_buffer_load_b16(
+                                wr, ok ? (int)((((ci * CG + co) * KS + kh) * KS + kw16) * 2) : (int)OOB, 0, 0);
+                            word |= (v & 0xffffu) << (16 * h);
+                        }
+                        a16[kh][d] = word;
+                    }
+                }
             }
 #pragma unroll
             for (int j = 0; j < SCH; ++j) {
@@ -515,16 +592,27 @@ void convt2d_gn_fused_kernel(FusedArgs a)
 #pragma unroll
         for (int k = 0; k < SPS; ++k) {
             if (k > 0) __syncthreads();  // pair k + 1 in the ring
-            const float *rA = ring + ((base + k) % NSLOT) * PAIR_FLOATS + lb;
-            const float *rB = ring + ((base + k + 1) % NSLOT) * PAIR_FLOATS + lb;
             // B operands of the whole step first: input rows 2(k0+k) - 2 + m
             float xb[CG][4];
+            v4u xb16[4];
+            if constexpr (DT == 0) {
+                const float *rA = ring + ((base + k) % NSLOT) * PAIR_FLOATS + lb;
+                const float *rB = ring + ((base + k + 1) % NSLOT) * PAIR_FLOATS + lb;
 #pragma unroll
-            for (int ci = 0; ci < CG; ++ci) {
-                xb[ci][0] = rA[ci * RP];
-                xb[ci][1] = rA[(CG + ci) * RP];
-                xb[ci][2] = rB[ci * RP];
-                xb[ci][3] = rB[(CG + ci) * RP];
+                for (int ci = 0; ci < CG; ++ci) {
+                    xb[ci][0] = rA[ci * RP];
+                    xb[ci][1] = rA[(CG + ci) * RP];
+                    xb[ci][2] = rB[ci * RP];
+                    xb[ci][3] = rB[(CG + ci) * RP];
+                }
+            } else {
+                const unsigned *r16 = reinterpret_cast<const unsigned *>(ring);
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const unsigned *rp = r16 + ((base + k + m / 2) % NSLOT) * PAIR16_WORDS +
+                                         (m % 2) * CG * (RP16 / 2) + lb16;
+                    xb16[m] = v4u{rp[0], rp[1], rp[RP16 / 2], rp[RP16 / 2 + 1]};
+                }
             }
             if (k == 1 && has_prev && wave == COEFWAVE) probe_issue(a, p_unit, lane, pr0, pr1);
             if (k == 2 && has_prev) {
@@ -557,15 +645,24 @@ void convt2d_gn_fused_kernel(FusedArgs a)
                 epilogue_to_bank<ACT>(acc0, acc1, 2 * (k0 + k - 1) + 1 < Ho, s1, s2, cnt,
                                       mybank + slot_of(k - 1, r) * 2 * THREADS);
             v4f n0 = bias4, n1 = bias4;
+            // output row 2(k0+k) + j reads input row 2(k0+k) + j - kh, i.e. m = 2 + j - kh
+            if constexpr (DT == 0) {
 #pragma unroll
-            for (int ci = 0; ci < CG; ++ci) {
-                // output row 2(k0+k) + j reads input row 2(k0+k) + j - kh, i.e. m = 2 + j - kh
-                n0 = mfma_16x16x4(wreg[ci * KS + 0], xb[ci][2], n0);
-                n1 = mfma_16x16x4(wreg[ci * KS + 0], xb[ci][3], n1);
-                n0 = mfma_16x16x4(wreg[ci * KS + 1], xb[ci][1], n0);
-                n1 = mfma_16x16x4(wreg[ci * KS + 1], xb[ci][2], n1);
-                n0 = mfma_16x16x4(wreg[ci * KS + 2], xb[ci][0], n0);
-                n1 = mfma_16x16x4(wreg[ci * KS + 2], xb[ci][1], n1);
+                for (int ci = 0; ci < CG; ++ci) {
+                    n0 = mfma_16x16x4(wreg[ci * KS + 0], xb[ci][2], n0);
+                    n1 = mfma_16x16x4(wreg[ci * KS + 0], xb[ci][3], n1);
+                    n0 = mfma_16x16x4(wreg[ci * KS + 1], xb[ci][1], n0);
+                    n1 = mfma_16x16x4(wreg[ci * KS + 1], xb[ci][2], n1);
+                    n0 = mfma_16x16x4(wreg[ci * KS + 2], xb[ci][0], n0);
+                    n1 = mfma_16x16x4(wreg[ci * KS + 2], xb[ci][1], n1);
+                }
+            } else {
+                n0 = mfma16x32<DT>(a16[0], xb16[2], n0);
+                n1 = mfma16x32<DT>(a16[0], xb16[3], n1);
+                n0 = mfma16x32<DT>(a16[1], xb16[1], n0);
+                n1 = mfma16x32<DT>(a16[1], xb16[2], n1);
+                n0 = mfma16x32<DT>(a16[2], xb16[0], n0);
+                n1 = mfma16x32<DT>(a16[2], xb16[1], n1);
             }
             if (k >= 1 && !late)
                 epilogue_to_bank<ACT>(acc0, acc1, 2 * (k0 + k - 1) + 1 < Ho, s1, s2, cnt,
@@ -590,12 +687,12 @@ void convt2d_gn_fused_kernel(FusedArgs a)
 
             // ---- ring stashes at the end of step k, each followed by its loads
             if (k <= SPS - 2) {
-                stash_pair(ring, (base + k + 2) % NSLOT, pf[k % 3], wave, lane);
+                stash_pair<DT>(ring, (base + k + 2) % NSLOT, pf[k % 3], wave, lane);
                 issue_pos<DT>(k, pf[k % 3], k0, xr, nhas, nk0, nxr, H, loff);
             } else {
-                stash_pair(ring, (base + SPS + 1) % NSLOT, pf[(SPS - 1) % 3], wave, lane);
+                stash_pair<DT>(ring, (base + SPS + 1) % NSLOT, pf[(SPS - 1) % 3], wave, lane);
                 issue_pos<DT>(SPS - 1, pf[(SPS - 1) % 3], k0, xr, nhas, nk0, nxr, H, loff);
-                stash_pair(ring, (base + SPS + 2) % NSLOT, pf[SPS % 3], wave, lane);
+                stash_pair<DT>(ring, (base + SPS + 2) % NSLOT, pf[SPS % 3], wave, lane);
                 issue_pos<DT>(SPS, pf[SPS % 3], k0, xr, nhas, nk0, nxr, H, loff);
 #pragma unroll
                 for (int p = SPS + 1; p < NPOS; ++p) issue_pos<DT>(p, pf[p % 3], k0, xr, nhas, nk0, nxr, H, loff);

@@ -229,8 +229,9 @@ def _fused_geometry(Ho):
     return (S, next_, ncol) if next_ <= S and ncol <= S else None
 
 
-# 16-bit x and w through the single-write kernel (widened to fp32 on load): the
-# oracle takes the same rounded inputs, so the fp32 tolerance applies.  Shapes:
+# 16-bit x and w through the single-write kernel (16-bit MFMA contraction,
+# fp32 accumulation; single tiles widened on load): the oracle takes the same
+# rounded inputs, so the fp32 tolerance applies.  Shapes:
 # one unit; ragged last step with every slice carrying a single row tile; the
 # tanh GELU and HardSwish forms; several samples and groups per round.
 SIXTEEN_BIT_FUSED = [
@@ -388,6 +389,9 @@ def test_fused_convt_forced_fallback(monkeypatch, over, dtype):
     dict(N=3, in_dims=(1, 126, 256)),                    # 24 units, 2 per round: 12 rounds
     dict(N=2, in_dims=(1, 127, 256), act="gelu_tanh"),   # a tail step (extra row tiles) each round
     dict(N=2, C_in=16, C_out=16, groups=2, num_groups=2, in_dims=(1, 255, 256)),
+    # 16-bit ring and A operands over many rounds, with and without a tail step
+    dict(N=3, in_dims=(1, 126, 256), dtype="bf16"),
+    dict(N=2, in_dims=(1, 127, 256), act="gelu_tanh", dtype="f16"),
 ])
 def test_fused_convt_many_rounds(monkeypatch, over):
     # two units per round, so a small batch runs many rounds: the slice

@@ -14,15 +14,22 @@
 //     per round (units handed out round by round; the launch is cooperative,
 //     so all workgroups are resident at once);
 //   * round r: a workgroup computes its slice of unit u_r (conv + bias +
-//     activation) into an LDS bank (each lane's own values, so no barrier),
-//     keeps running sums, and early in round r+1 publishes the slice's
-//     (count, mean, M2) triple;
+//     activation) into an LDS bank laid out in output order, keeps running
+//     sums, and early in round r+1 publishes the slice's (count, mean, M2)
+//     triple;
 //   * during round r+1 the same workgroup normalises the bank of u_r and
-//     stores it, two steps behind its new MFMA work: the coefficients of u_r
-//     are read one step into round r+1 and needed two steps in, by which time
-//     the sibling slices have normally published.  Step k of round rho lives in bank slot
-//     (k - rho) mod (SPS + 1), so step k of round r+1 goes into exactly the
-//     slot of step k-1 of round r, which has just been normalised and stored.
+//     stores it: the coefficients of u_r are merged at the end of step 1 of
+//     round r+1 (by which time the sibling slices have normally published),
+//     and steps 2 and 3 store two of u_r's steps each.  Step k of round rho
+//     lives in bank slot (rho SPS + k) mod (SPS + 1); a slot is read for its
+//     store before the barrier after which a later step's epilogue rewrites
+//     it (slots at risk are read into registers at the end of the step before).
+//   * stores: the output row is 258 floats (1032 bytes), so a 32-pixel tile's
+//     run of a row straddles two 128-byte lines in every row; such stores
+//     measured ~2.7x slower than line-aligned ones.  Wave c instead writes
+//     channel c's rows of a finished step, which are contiguous in memory, as
+//     whole aligned lines: the line shared by two steps of a slice is written
+//     by the later one, with the earlier step's floats carried in registers.
 // Each triple travels as two 64-bit relaxed atomics that both carry the
 // count, so a reader that sees both halves non-zero has the whole triple and
 // no fence or counter is needed.  The wait is bounded: on time-out the
@@ -35,7 +42,8 @@
 // read the same input columns shifted by one, so 72 of every 96 K entries are
 // useful (zero-padded weights fill the rest).  An output row of 258 pixels is
 // 8 row tiles (pixels 0..255, one per wave) plus the last column pair; the
-// last pairs of 16 consecutive rows form one column tile.  Each step reads
+// last pairs of a slice's 8 rows form its column tile (slice 0's also takes
+// the rows past the slices, at most 4).  Each step reads
 // two input row pairs from a 4-pair LDS ring refilled from registers loaded
 // three stashes ahead; waves sharing a SIMD alternate the step's MFMAs and
 // the previous step's activation.
@@ -72,7 +80,17 @@ constexpr int PAIR_FLOATS = 2 * CG * RP;
 constexpr int RP16 = 272;
 constexpr int PAIR16_WORDS = 2 * CG * RP16 / 2;
 constexpr int SPS = 4;                       // steps per slice
-constexpr int NBANK = SPS + 1;               // LDS bank slots
+// Bank: finished steps in output order, [slot][channel][row j * 258 + pixel]
+// (CP = 528 = 16 mod 32: the four lane groups of an epilogue write land 32
+// banks apart), SPS + 1 slots: step k of round rho in slot (rho SPS + k) mod
+// (SPS + 1).  A slot is read (gathered for its store) at least one barrier
+// before the epilogue of step k + SPS + 1 rewrites it.
+constexpr int CP = 528;
+constexpr int SLOT_FLOATS = CG * CP;
+constexpr int BPAD = 32;                     // floats before slot 0 (line offsets start at -30)
+constexpr int BTAIL = 128;                   // floats past the last slot (line slots past a range)
+constexpr int NBANK = SPS + 1;
+constexpr int LINE_SLOTS = 5;                // store instructions per wave per step: 20 lines >= 18
 constexpr int NPOS = 6;                      // ring stash positions per round (SPS + 1, padded to 3 k)
 constexpr int MAX_S = 32;                    // slices per unit
 constexpr int SCH = CG * KS / 4;             // K entries of a single tile per wave (4 waves per tile)
@@ -98,7 +116,7 @@ struct FusedArgs {
     int spin_limit;   // polls before a wait gives up
     int never_ready;  // test hook: a wait also needs a word nobody writes
     int N, C, H, G, Ho;
-    int S, NEXT, NCOL;  // slices, extra row tiles (16 per tail step), column tiles
+    int S, NEXT;        // slices, extra row tiles (16 per tail step)
     int upr;            // units per round
     int xcd_units;      // units per XCD per round (0: plain workgroup order)
     float eps, inv_div;
@@ -177,9 +195,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t x_rsrc(const FusedArgs &a, int
                      (unsigned)(CG * a.H * W * ESZ<DT>));
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t y_rsrc(const FusedArgs &a, int unit, unsigned plane)
+// The unit's output resource, built from a base address held in scalar
+// registers (readfirstlane), so that its stores take the descriptor as is.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t y_rsrc_u(const FusedArgs &a, int unit, unsigned plane)
 {
-    return make_rsrc(a.y + (size_t)unit * CG * plane, CG * plane * 4u);
+    const unsigned long long p = reinterpret_cast<unsigned long long>(a.y + (size_t)unit * CG * plane);
+    const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)p),
+                   hi = __builtin_amdgcn_readfirstlane((unsigned)(p >> 32));
+    const unsigned long long pu = (unsigned long long)lo | ((unsigned long long)hi << 32);
+    return make_rsrc(reinterpret_cast<float *>(pu), __builtin_amdgcn_readfirstlane(CG * plane * 4u));
 }
 
 // One input row pair (rows row0, row0 + 1 of the group's 8 channels): this
@@ -389,19 +413,79 @@ __device__ __forceinline__ void sums4(const v4f &c, float &s1, float &s2)
 // Activation of a finished step's two row tiles (bias already in the
 // accumulators; the second row may lie past Ho: then it is skipped) ->
 // running sums and the bank slot wp.
+// Bank position p = slot + 2q CP + j 258 + pixel of the lane's pair: the
+// lane's channels 2q (p) and 2q + 1 (p + CP).
+__device__ __forceinline__ void bank_put(float *p, const v4f &e)
+{
+    *reinterpret_cast<v2f *>(p) = v2f{e[0], e[1]};
+    *reinterpret_cast<v2f *>(p + CP) = v2f{e[2], e[3]};
+}
+
 template <int ACT>
 __device__ __forceinline__ void epilogue_to_bank(const v4f &acc0, const v4f &acc1, bool v1, float &s1,
-                                                 float &s2, int &cnt, v4f *wp)
+                                                 float &s2, int &cnt, float *p)
 {
     const v4f e0 = activate4<ACT>(acc0);
     sums4(e0, s1, s2);
-    wp[0] = e0;
+    bank_put(p, e0);
     cnt += 4;
     if (v1) {
         const v4f e1 = activate4<ACT>(acc1);
         sums4(e1, s1, s2);
-        wp[THREADS] = e1;
+        bank_put(p + WO, e1);
         cnt += 4;
+    }
+}
+
+// One finished step of the previous unit, normalised and stored by the wave
+// of channel c (= wave).  Its rows are the contiguous float range [F, F + R)
+// of the channel plane (R = 258 per row); t = F mod 32, so the step's lines of
+// 32 floats start at offsets -t + 32 m, and lane (q, c16) of store i writes
+// offsets u = 128 i + 32 q + 2 c16 - t: whole 128-byte lines.  The line that
+// straddles two steps of a slice is written once, by the later step, its
+// earlier floats (u < 0) taken from `carry`, which the earlier step read from
+// its own slot; floats at or past `hi` are left to the next step.  Only the
+// first and last lines of a slice are partial (masked lanes): their other
+// floats belong to the neighbouring slices.
+//
+// gather_lines reads a step's values from its bank row `chan` (and the next
+// step's carry), emit_lines normalises and stores them, so a slot can be read
+// before the barrier after which another step's epilogue rewrites it.
+struct Lines {
+    v2f v[LINE_SLOTS];
+};
+
+__device__ __forceinline__ void gather_lines(Lines &L, const float *chan, int t, bool has_next, int next_t,
+                                             v2f &carry, int q, int c16)
+{
+    const int base = 32 * q + 2 * c16 - t;
+#pragma unroll
+    for (int i = 0; i < LINE_SLOTS; ++i) {
+        const int u = base + 128 * i;
+        const v2f v = *reinterpret_cast<const v2f *>(chan + u);
+        L.v[i] = i == 0 && u < 0 ? carry : v;
+    }
+    if (has_next) carry = *reinterpret_cast<const v2f *>(chan + 2 * WO - next_t + 2 * c16);
+}
+
+// soff = byte offset of the step's first float; with active false every store
+// goes past the buffer.  The buffer range check sees only the per-lane offset,
+// so after the first step (whose lanes never go below 0) the uniform offset
+// moves back one line and the lanes' offsets forward by the same amount.
+__device__ __forceinline__ void emit_lines(__amdgpu_buffer_rsrc_t yr, const Lines &L, float sc, float sh, int t,
+                                           int hi, bool first, unsigned soff, int q, int c16, bool active)
+{
+    soff = __builtin_amdgcn_readfirstlane(soff);
+    const int base = 32 * q + 2 * c16 - t;
+    const int lift = first ? 0 : 32;
+#pragma unroll
+    for (int i = 0; i < LINE_SLOTS; ++i) {
+        const int u = base + 128 * i;
+        bool ok = active && u < hi;
+        if (i == 0) ok = ok && (!first || u >= 0);
+        const v2f v = L.v[i];
+        buf_store2(v2f{fmaf(v[0], sc, sh), fmaf(v[1], sc, sh)}, yr, ok ? (unsigned)(4 * (u + lift)) : OOB,
+                   soff - 4u * (unsigned)lift);
     }
 }
 
@@ -429,11 +513,12 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void convt2d_gn_fused_kernel(FusedArgs a)
 {
     using PF = typename Stage<DT>::T;
+    constexpr int NB = NBANK;
     __shared__ __align__(16) float ring[DT == 0 ? NSLOT * PAIR_FLOATS : NSLOT * PAIR16_WORDS];
     __shared__ float red[NWAVE * 4 * 3];  // [wave][row of 16 lanes] slice triples
     __shared__ v4f spart[2 * 4 * 64];     // [tile][chunk][lane] single-tile partial sums
     __shared__ float coefs[CG * 2];       // the previous unit's (scale, shift) per channel
-    __shared__ v4f bank[NBANK * 2 * THREADS];  // [slot][tile][thread], private to each thread
+    __shared__ __align__(16) float bank[BPAD + NB * SLOT_FLOATS + BTAIL];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -441,6 +526,7 @@ void convt2d_gn_fused_kernel(FusedArgs a)
     const int H = a.H, Ho = a.Ho, S = a.S;
     const int U = a.N * a.G;
     const unsigned plane = (unsigned)Ho * WO;
+    const int rows_main = 2 * S * SPS;  // rows of the slices; the rest are extra row tiles
     // Waves w and w + 4 share a SIMD: one runs a step's MFMAs while the other
     // runs the previous step's activation, then they swap.
     const bool late = (wave & 4) != 0;
@@ -471,10 +557,10 @@ void convt2d_gn_fused_kernel(FusedArgs a)
     const int lb = PADL + 32 * wave + 2 * c16 + 1 - q;                // B operand column
     // 16-bit B operand: word of columns 2 c16 - 2, -1 of channel 2q in a ring row
     const int lb16 = 2 * q * (RP16 / 2) + (PADL - 2) / 2 + 16 * wave + c16;
-    const unsigned vo0 = ((unsigned)(2 * q) * plane + 32u * wave + 2u * c16) * 4u;
-    const unsigned vo1 = vo0 + plane * 4u;
-    v4f *const mybank = bank + tid;
-    auto slot_of = [](int k, int rho) { return (k + NBANK - rho % NBANK) % NBANK; };
+    const int bo = 2 * q * CP + 32 * wave + 2 * c16;                   // bank position of the lane's pair
+    // bank slot of step k of round rho (steps numbered over rounds; rho = -1,
+    // the round before the first, when a store is issued with nothing to store)
+    auto slot = [&](int rho, int k) { return bank + BPAD + (((rho * SPS + k) % NB + NB) % NB) * SLOT_FLOATS; };
 
     // ---- prologue: round 0's pairs 0, 1 in the ring, positions 0..2 in flight
     PF pf[3][2];
@@ -499,8 +585,59 @@ void convt2d_gn_fused_kernel(FusedArgs a)
     int wgroup = -1;
     v4f cur_ext = v4f{0.f, 0.f, 0.f, 0.f}, prv_ext = cur_ext;  // extra row tile (wave EXTWAVE)
     v4f cur_col = cur_ext, prv_col = cur_ext;                  // column tile (wave COLWAVE)
-    int p_unit = -1, p_sg = 0, p_k0 = 0, p_ext = -1, p_col = -1;
+    int p_unit = -1, p_sg = 0, p_k0 = 0, p_ext = -1;
     Coef pc{0.f, 0.f, 0.f, 0.f};
+    float psc = 0.f, psh = 0.f;  // the previous unit's scale / shift of channel `wave`
+
+    // Column tile of a slice: its own rows 2 k0 + c16 (c16 < 8); slice 0 also
+    // takes the rows past the slices (c16 - 8 of them, at most 4).
+    auto col_row = [&](int k0, int sg) { return c16 < 8 ? 2 * k0 + c16 : (sg == 0 ? rows_main + c16 - 8 : Ho); };
+
+    // The previous unit's step s, by the wave of its channel `wave`: gathered
+    // from its slot, then normalised and stored (active false: the same
+    // instructions, every store past the buffer -- the memory waits the
+    // compiler places then count the same stores on every path).
+    v2f carry = v2f{0.f, 0.f};
+    Lines held;
+    auto gather_step = [&](int rho, int s, unsigned cu) {
+        const int prow = 2 * (p_k0 + s);
+        const bool last = s == SPS - 1 || prow + 2 >= Ho;
+        gather_lines(held, slot(rho, s) + wave * CP, (int)((cu + 4u * s) & 31u), !last,
+                     (int)((cu + 4u * s + 4u) & 31u), carry, q, c16);
+    };
+    auto emit_step = [&](int s, __amdgpu_buffer_rsrc_t pyr, unsigned cu, bool active) {
+        const int prow = 2 * (p_k0 + s);
+        const int nr = prow + 1 < Ho ? 2 : 1;
+        const bool last = s == SPS - 1 || prow + 2 >= Ho;
+        const int t = (int)((cu + 4u * s) & 31u), nt = (int)((cu + 4u * s + 4u) & 31u);
+        emit_lines(pyr, held, psc, psh, t, last ? WO * nr : 2 * WO - nt, s == 0,
+                   ((unsigned)wave * plane + (unsigned)prow * WO) * 4u, q, c16, active);
+    };
+    // (float offset of the unit's channel-`wave` slice start) mod 32, even
+    auto line_phase = [&](int unit, int k0) {
+        const unsigned long long f = (reinterpret_cast<unsigned long long>(a.y) >> 2) +
+                                     (unsigned long long)unit * CG * plane + (unsigned long long)wave * plane +
+                                     (unsigned long long)(2 * k0) * WO;
+        return (unsigned)f & 30u;
+    };
+    // the previous unit's tiles outside the slices' rows: its extra row tile
+    // and the column pixels of those rows (slice 0's column tile, lanes c16 >= 8)
+    // (issued by every wave, masked ones past the buffer, as in store_step)
+    auto store_outside = [&](__amdgpu_buffer_rsrc_t pyr, bool active) {
+        const int prow_e = rows_main + 2 * (p_ext >> 4) + ((p_ext >> 3) & 1);
+        const bool e_ok = active && wave == EXTWAVE && p_ext >= 0 && prow_e < Ho;
+        const unsigned oe = ((unsigned)(2 * q) * plane + (unsigned)prow_e * WO + 32u * (p_ext & 7) + 2u * c16) * 4u;
+        store_tile(pyr, prv_ext, pc, e_ok ? oe : OOB, e_ok ? oe + plane * 4u : OOB, 0u);
+        const int prow_c = rows_main + c16 - 8;
+        const bool c_ok = active && wave == COLWAVE && p_sg == 0 && c16 >= 8 && prow_c < Ho;
+        const unsigned oc = ((unsigned)(2 * q) * plane + (unsigned)prow_c * WO + W) * 4u;
+        store_tile(pyr, prv_col, pc, c_ok ? oc : OOB, c_ok ? oc + plane * 4u : OOB, 0u);
+    };
+    // the column pixels (256, 257) of the previous unit's rows into its bank slots
+    auto put_col = [&](int rho) {
+        if (wave == COLWAVE && c16 < 8 && 2 * p_k0 + c16 < Ho)
+            bank_put(slot(rho, c16 >> 1) + 2 * q * CP + (c16 & 1) * WO + W, prv_col);
+    };
 
     int r = 0;
     for (;; ++r) {
@@ -512,17 +649,18 @@ void convt2d_gn_fused_kernel(FusedArgs a)
         }
         const bool has_prev = p_unit >= 0;
         if (has_prev && wave == PUBWAVE) publish(a, red, p_unit, p_sg, lane);
+        if (has_prev) put_col(r - 1);
 
         const int sg = (s_base + r) % S;
         const int k0 = sg * SPS;
         const int ext = sg < a.NEXT ? sg : -1;           // extra row tile e: tail step e/16, tile e%16
-        const int col = S - 1 - sg < a.NCOL ? S - 1 - sg : -1;
         const __amdgpu_buffer_rsrc_t xr = x_rsrc<DT>(a, unit);
         const int nunit = unit + a.upr;
         const bool nhas = nunit < U;
         const int nk0 = ((sg + 1) % S) * SPS;
         const __amdgpu_buffer_rsrc_t nxr = x_rsrc<DT>(a, nhas ? nunit : unit);
-        const __amdgpu_buffer_rsrc_t pyr = y_rsrc(a, has_prev ? p_unit : unit, plane);
+        const __amdgpu_buffer_rsrc_t pyr = y_rsrc_u(a, has_prev ? p_unit : unit, plane);
+        const unsigned pcu = has_prev ? line_phase(p_unit, p_k0) : 0u;
 
         // ---- weights (A operand), bias, gamma / beta of the unit's group
         const int g = unit % a.G;
@@ -575,16 +713,18 @@ void convt2d_gn_fused_kernel(FusedArgs a)
         }
 
         // ---- this slice's single tiles: B operands straight from x (L2)
-        const int ext_row = 2 * (S * SPS + (ext >> 4)) + ((ext >> 3) & 1);
+        const int ext_row = rows_main + 2 * (ext >> 4) + ((ext >> 3) & 1);
         const int tsel = wave >> 2, chunk = wave & 3;  // tile (0 extra, 1 column) and K chunk
-        const bool has_t = tsel == 0 ? ext >= 0 : col >= 0;
+        const int crow = col_row(k0, sg);
+        const bool has_t = tsel == 0 ? ext >= 0 : crow < Ho;
         float sb[SCH];
-        single_load<DT>(sb, xr, H, chunk, has_t, tsel == 0 ? ext_row : 16 * col + c16,
-                    tsel == 0 ? 32 * (ext & 7) + 2 * c16 + 1 - q : 2 * (W / 2) + 1 - q);
+        single_load<DT>(sb, xr, H, chunk, has_t, tsel == 0 ? ext_row : crow,
+                        tsel == 0 ? 32 * (ext & 7) + 2 * c16 + 1 - q : 2 * (W / 2) + 1 - q);
 
-        // ---- steps.  Iteration k stores the previous unit's step k - 2, runs the
-        // MFMAs of step k and the activation, sums and bank write of step k - 1
-        // (before or after the MFMAs, by wave), then stashes / loads ring pairs.
+        // ---- steps.  Iteration k runs the MFMAs of step k and the activation, sums
+        // and bank write of step k - 1 (before or after the MFMAs, by wave), then
+        // stashes / loads ring pairs; iterations 2 and 3 also store the previous
+        // unit's steps 0, 1 and 2, 3 (its coefficients are merged in iteration 1).
         float s1 = 0.f, s2 = 0.f;
         int cnt = 0;
         unsigned long long pr0 = 0ull, pr1 = 0ull;
@@ -618,15 +758,17 @@ void convt2d_gn_fused_kernel(FusedArgs a)
             if (k == 2 && has_prev) {
                 const float *cq = coefs + 4 * q;  // channels 2q, 2q+1, merged last step
                 pc = Coef{cq[0], cq[1], cq[2], cq[3]};
+                psc = coefs[2 * wave];
+                psh = coefs[2 * wave + 1];
             }
             if (k == 3) {
                 // single tiles: the four chunk partials, summed in chunk order
-                const bool fin_e = wave == EXTWAVE && ext >= 0, fin_c = wave == COLWAVE && col >= 0;
+                const bool fin_e = wave == EXTWAVE && ext >= 0, fin_c = wave == COLWAVE;
                 if (fin_e || fin_c) {
                     const v4f *pp = spart + (fin_e ? 0 : 4) * 64 + lane;
                     const v4f e = activate4<ACT>(((pp[0] + pp[64]) + pp[128]) + pp[192]);
                     // the tile's row (column tile: the lane's row) may lie past Ho
-                    if (fin_e ? ext_row < Ho : 16 * col + c16 < Ho) {
+                    if (fin_e ? ext_row < Ho : crow < Ho) {
                         sums4(e, s1, s2);
                         cnt += 4;
                     }
@@ -634,16 +776,19 @@ void convt2d_gn_fused_kernel(FusedArgs a)
                     else cur_col = e;
                 }
             }
-            if (k >= 2 && has_prev) {
-                // the previous unit's step k - 2: its bank slot takes this round's step k - 1
-                const v4f *sp = mybank + slot_of(k - 1, r) * 2 * THREADS;
-                const int prow = 2 * (p_k0 + k - 2);
-                store_tile(pyr, sp[0], pc, vo0, vo1, (unsigned)(prow * WO * 4));
-                if (prow + 1 < Ho) store_tile(pyr, sp[THREADS], pc, vo0, vo1, (unsigned)((prow + 1) * WO * 4));
+            if (k == 2 || k == 3) {
+                // the previous unit's steps 2(k - 2) (gathered at the end of the last
+                // iteration: this iteration's epilogue rewrites its slot) and
+                // 2(k - 2) + 1; no store is issued late in a round, so a memory wait
+                // early in the next round (vmcnt counts loads and stores in issue
+                // order) finds them done
+                emit_step(2 * (k - 2), pyr, pcu, has_prev);
+                gather_step(r - 1, 2 * (k - 2) + 1, pcu);
+                emit_step(2 * (k - 2) + 1, pyr, pcu, has_prev);
+                if (k == 3) store_outside(pyr, has_prev);
             }
             if (k >= 1 && late)
-                epilogue_to_bank<ACT>(acc0, acc1, 2 * (k0 + k - 1) + 1 < Ho, s1, s2, cnt,
-                                      mybank + slot_of(k - 1, r) * 2 * THREADS);
+                epilogue_to_bank<ACT>(acc0, acc1, 2 * (k0 + k - 1) + 1 < Ho, s1, s2, cnt, slot(r, k - 1) + bo);
             v4f n0 = bias4, n1 = bias4;
             // output row 2(k0+k) + j reads input row 2(k0+k) + j - kh, i.e. m = 2 + j - kh
             if constexpr (DT == 0) {
@@ -665,8 +810,7 @@ void convt2d_gn_fused_kernel(FusedArgs a)
                 n1 = mfma16x32<DT>(a16[2], xb16[1], n1);
             }
             if (k >= 1 && !late)
-                epilogue_to_bank<ACT>(acc0, acc1, 2 * (k0 + k - 1) + 1 < Ho, s1, s2, cnt,
-                                      mybank + slot_of(k - 1, r) * 2 * THREADS);
+                epilogue_to_bank<ACT>(acc0, acc1, 2 * (k0 + k - 1) + 1 < Ho, s1, s2, cnt, slot(r, k - 1) + bo);
             acc0 = n0;
             acc1 = n1;
             if (k == 1 && has_prev && wave == COEFWAVE) {
@@ -697,17 +841,14 @@ void convt2d_gn_fused_kernel(FusedArgs a)
 #pragma unroll
                 for (int p = SPS + 1; p < NPOS; ++p) issue_pos<DT>(p, pf[p % 3], k0, xr, nhas, nk0, nxr, H, loff);
             }
+            // the previous unit's step 2(k - 1), before the barrier after which the
+            // next iteration's epilogue rewrites its slot
+            if (k == 1 || k == 2) gather_step(r - 1, 2 * (k - 1), pcu);
         }
 
-        // ---- previous unit's step SPS - 2, then the last step's activation -> bank
-        if (has_prev) {
-            const v4f *sp = mybank + slot_of(SPS - 1, r) * 2 * THREADS;
-            const int prow = 2 * (p_k0 + SPS - 2);
-            store_tile(pyr, sp[0], pc, vo0, vo1, (unsigned)(prow * WO * 4));
-            if (prow + 1 < Ho) store_tile(pyr, sp[THREADS], pc, vo0, vo1, (unsigned)((prow + 1) * WO * 4));
-        }
-        epilogue_to_bank<ACT>(acc0, acc1, 2 * (k0 + SPS - 1) + 1 < Ho, s1, s2, cnt,
-                              mybank + slot_of(SPS - 1, r) * 2 * THREADS);
+        // ---- the last step's activation -> bank (the slot of the previous unit's
+        // step SPS - 2, gathered at the end of iteration 2)
+        epilogue_to_bank<ACT>(acc0, acc1, 2 * (k0 + SPS - 1) + 1 < Ho, s1, s2, cnt, slot(r, SPS - 1) + bo);
 
         // ---- slice statistics -> red[wave][row]; published after the next barrier
         {
@@ -721,26 +862,6 @@ void convt2d_gn_fused_kernel(FusedArgs a)
             }
         }
 
-        // ---- the previous unit's last step and single tiles
-        if (has_prev) {
-            const v4f *sp = mybank + slot_of(SPS, r) * 2 * THREADS;
-            const int prow = 2 * (p_k0 + SPS - 1);
-            store_tile(pyr, sp[0], pc, vo0, vo1, (unsigned)(prow * WO * 4));
-            if (prow + 1 < Ho) store_tile(pyr, sp[THREADS], pc, vo0, vo1, (unsigned)((prow + 1) * WO * 4));
-            if (wave == EXTWAVE && p_ext >= 0) {
-                const int prow_e = 2 * (S * SPS + (p_ext >> 4)) + ((p_ext >> 3) & 1);
-                const unsigned o = ((unsigned)(2 * q) * plane + 32u * (p_ext & 7) + 2u * c16) * 4u;
-                if (prow_e < Ho) store_tile(pyr, prv_ext, pc, o, o + plane * 4u, (unsigned)(prow_e * WO * 4));
-            }
-            if (wave == COLWAVE && p_col >= 0) {
-                const int prow_c = 16 * p_col + c16;
-                if (prow_c < Ho) {
-                    const unsigned o = ((unsigned)(2 * q) * plane + (unsigned)prow_c * WO + W) * 4u;
-                    store_tile(pyr, prv_col, pc, o, o + plane * 4u, 0u);
-                }
-            }
-        }
-
         prv_ext = cur_ext;
         prv_col = cur_col;
         p_gb = gb;
@@ -748,34 +869,29 @@ void convt2d_gn_fused_kernel(FusedArgs a)
         p_sg = sg;
         p_k0 = k0;
         p_ext = ext;
-        p_col = col;
         base = (base + SPS + 1) % NSLOT;
     }
 
     // ---- the last unit: its triple was published above; wait, normalise, store
     if (p_unit >= 0) {
-        const __amdgpu_buffer_rsrc_t pyr = y_rsrc(a, p_unit, plane);
+        put_col(r - 1);
+        const __amdgpu_buffer_rsrc_t pyr = y_rsrc_u(a, p_unit, plane);
         unsigned long long pr0, pr1;
         probe_issue(a, p_unit, lane, pr0, pr1);
         pc = probe_finish(a, p_unit, lane, p_gb, pr0, pr1);
+        // channel `wave`'s coefficients from the lane that holds them
+        const int src = 16 * (wave >> 1);
+        psc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                  __builtin_bit_cast(int, (wave & 1) ? pc.sc1 : pc.sc0), src));
+        psh = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                  __builtin_bit_cast(int, (wave & 1) ? pc.sh1 : pc.sh0), src));
+        __syncthreads();  // the column pixels in the bank
+        const unsigned pcu = line_phase(p_unit, p_k0);
         for (int j = 0; j < SPS; ++j) {
-            const v4f *sp = mybank + slot_of(j, r - 1) * 2 * THREADS;
-            const int prow = 2 * (p_k0 + j);
-            store_tile(pyr, sp[0], pc, vo0, vo1, (unsigned)(prow * WO * 4));
-            if (prow + 1 < Ho) store_tile(pyr, sp[THREADS], pc, vo0, vo1, (unsigned)((prow + 1) * WO * 4));
+            gather_step(r - 1, j, pcu);
+            emit_step(j, pyr, pcu, true);
         }
-        if (wave == EXTWAVE && p_ext >= 0) {
-            const int prow_e = 2 * (S * SPS + (p_ext >> 4)) + ((p_ext >> 3) & 1);
-            const unsigned o = ((unsigned)(2 * q) * plane + 32u * (p_ext & 7) + 2u * c16) * 4u;
-            if (prow_e < Ho) store_tile(pyr, prv_ext, pc, o, o + plane * 4u, (unsigned)(prow_e * WO * 4));
-        }
-        if (wave == COLWAVE && p_col >= 0) {
-            const int prow_c = 16 * p_col + c16;
-            if (prow_c < Ho) {
-                const unsigned o = ((unsigned)(2 * q) * plane + (unsigned)prow_c * WO + W) * 4u;
-                store_tile(pyr, prv_col, pc, o, o + plane * 4u, 0u);
-            }
-        }
+        store_outside(pyr, true);
     }
 }
 
@@ -786,11 +902,12 @@ __global__ void zero_words_kernel(unsigned *p, long long n)
 }
 
 struct Geometry {
-    int S, NEXT, NCOL;
+    int S, NEXT;
 };
 
 // S slices of SPS steps; the NST - S * SPS tail steps become 16 extra row
-// tiles each, at most one per slice; at most one column tile per slice.
+// tiles each, at most one per slice (so at most 4 rows lie past the slices,
+// whose column pixels slice 0's column tile takes).
 bool geometry(int Ho, Geometry &g)
 {
     const int NST = (Ho + 1) / 2;
@@ -798,8 +915,7 @@ bool geometry(int Ho, Geometry &g)
     if (g.S < 1) return false;
     const int tail = NST - g.S * SPS;
     g.NEXT = 16 * tail;
-    g.NCOL = (Ho + 15) / 16;
-    return g.NEXT <= g.S && g.NCOL <= g.S;
+    return g.NEXT <= g.S;
 }
 
 // Resident workgroups per CU of each instantiation and the CU count, cached per
@@ -851,7 +967,7 @@ hipError_t launch_t(const ConvT2dArgs &p, hipStream_t st)
     FusedArgs fa{p.x, p.w, p.b, p.gamma, p.beta, p.out, p.partials, p.flag,
                  hk.spin_limit > 0 ? hk.spin_limit : SPIN_LIMIT, hk.never_ready,
                  p.N, p.C_out, p.H, p.groups, p.Ho,
-                 geo.S, geo.NEXT, geo.NCOL, upr, xcd_units, p.eps, p.inv_div};
+                 geo.S, geo.NEXT, upr, xcd_units, p.eps, p.inv_div};
     void *args[] = {&fa};
     if ((e = dominant_begin(st)) != hipSuccess) return e;
     e = hipLaunchCooperativeKernel(reinterpret_cast<const void *>(convt2d_gn_fused_kernel<ACT, DT>),

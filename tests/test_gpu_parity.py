@@ -217,16 +217,16 @@ def test_repeatable_bitwise():
 
 
 def _fused_geometry(Ho):
-    """Slices S (four two-row steps each, at most 32), extra row tiles (16 per
-    tail step) and column tiles (the last column pair of 16 rows) of the
-    single-write kernel; None where it does not take the height (at most one
-    extra and one column tile per slice)."""
+    """Slices S (four two-row steps each, at most 32) and extra row tiles (16
+    per tail step) of the single-write kernel; None where it does not take the
+    height (at most one extra row tile per slice).  Each slice also computes
+    the last column pair of its own rows."""
     nst = (Ho + 1) // 2
     S = min(32, nst // 4)
     if S < 1:
         return None
-    next_, ncol = 16 * (nst - 4 * S), (Ho + 15) // 16
-    return (S, next_, ncol) if next_ <= S and ncol <= S else None
+    next_ = 16 * (nst - 4 * S)
+    return (S, next_) if next_ <= S else None
 
 
 # 16-bit x and w through the single-write kernel (16-bit MFMA contraction,

@@ -19,8 +19,9 @@
 //     triple;
 //   * during round r+1 the same workgroup normalises the bank of u_r and
 //     stores it: the coefficients of u_r are merged at the end of step 1 of
-//     round r+1 (by which time the sibling slices have normally published),
-//     and steps 2 and 3 store two of u_r's steps each.  Step k of round rho
+//     round r+1 (step 2 with 16-bit inputs), by which time the sibling slices
+//     have normally published, and the steps after that store u_r's four
+//     steps (2 and 3 two each; 3 all four).  Step k of round rho
 //     lives in bank slot (rho SPS + k) mod (SPS + 1); a slot is read for its
 //     store before the barrier after which a later step's epilogue rewrites
 //     it (slots at risk are read into registers at the end of the step before).
@@ -514,6 +515,11 @@ void convt2d_gn_fused_kernel(FusedArgs a)
 {
     using PF = typename Stage<DT>::T;
     constexpr int NB = NBANK;
+    // iteration at whose end the previous unit's coefficients are merged: one
+    // step later with 16-bit inputs, whose steps are short, so that the sibling
+    // slices have published (measured: 0.90 -> 0.85 ms; fp32, whose SIMDs are
+    // MFMA-bound, loses 3% to the extra registers and the single store burst)
+    constexpr int MERGE = DT == 0 ? 1 : 2;
     __shared__ __align__(16) float ring[DT == 0 ? NSLOT * PAIR_FLOATS : NSLOT * PAIR16_WORDS];
     __shared__ float red[NWAVE * 4 * 3];  // [wave][row of 16 lanes] slice triples
     __shared__ v4f spart[2 * 4 * 64];     // [tile][chunk][lane] single-tile partial sums
@@ -598,14 +604,14 @@ void convt2d_gn_fused_kernel(FusedArgs a)
     // instructions, every store past the buffer -- the memory waits the
     // compiler places then count the same stores on every path).
     v2f carry = v2f{0.f, 0.f};
-    Lines held;
-    auto gather_step = [&](int rho, int s, unsigned cu) {
+    Lines held0, held1, held2;
+    auto gather_step = [&](int rho, int s, unsigned cu, Lines &held) {
         const int prow = 2 * (p_k0 + s);
         const bool last = s == SPS - 1 || prow + 2 >= Ho;
         gather_lines(held, slot(rho, s) + wave * CP, (int)((cu + 4u * s) & 31u), !last,
                      (int)((cu + 4u * s + 4u) & 31u), carry, q, c16);
     };
-    auto emit_step = [&](int s, __amdgpu_buffer_rsrc_t pyr, unsigned cu, bool active) {
+    auto emit_step = [&](int s, __amdgpu_buffer_rsrc_t pyr, unsigned cu, bool active, const Lines &held) {
         const int prow = 2 * (p_k0 + s);
         const int nr = prow + 1 < Ho ? 2 : 1;
         const bool last = s == SPS - 1 || prow + 2 >= Ho;
@@ -723,8 +729,8 @@ void convt2d_gn_fused_kernel(FusedArgs a)
 
         // ---- steps.  Iteration k runs the MFMAs of step k and the activation, sums
         // and bank write of step k - 1 (before or after the MFMAs, by wave), then
-        // stashes / loads ring pairs; iterations 2 and 3 also store the previous
-        // unit's steps 0, 1 and 2, 3 (its coefficients are merged in iteration 1).
+        // stashes / loads ring pairs; the iterations after MERGE also store the
+        // previous unit.
         float s1 = 0.f, s2 = 0.f;
         int cnt = 0;
         unsigned long long pr0 = 0ull, pr1 = 0ull;
@@ -754,8 +760,8 @@ void convt2d_gn_fused_kernel(FusedArgs a)
                     xb16[m] = v4u{rp[0], rp[1], rp[RP16 / 2], rp[RP16 / 2 + 1]};
                 }
             }
-            if (k == 1 && has_prev && wave == COEFWAVE) probe_issue(a, p_unit, lane, pr0, pr1);
-            if (k == 2 && has_prev) {
+            if (k == MERGE && has_prev && wave == COEFWAVE) probe_issue(a, p_unit, lane, pr0, pr1);
+            if (k == MERGE + 1 && has_prev) {
                 const float *cq = coefs + 4 * q;  // channels 2q, 2q+1, merged last step
                 pc = Coef{cq[0], cq[1], cq[2], cq[3]};
                 psc = coefs[2 * wave];
@@ -776,16 +782,25 @@ void convt2d_gn_fused_kernel(FusedArgs a)
                     else cur_col = e;
                 }
             }
-            if (k == 2 || k == 3) {
-                // the previous unit's steps 2(k - 2) (gathered at the end of the last
-                // iteration: this iteration's epilogue rewrites its slot) and
-                // 2(k - 2) + 1; no store is issued late in a round, so a memory wait
-                // early in the next round (vmcnt counts loads and stores in issue
-                // order) finds them done
-                emit_step(2 * (k - 2), pyr, pcu, has_prev);
-                gather_step(r - 1, 2 * (k - 2) + 1, pcu);
-                emit_step(2 * (k - 2) + 1, pyr, pcu, has_prev);
-                if (k == 3) store_outside(pyr, has_prev);
+            // The previous unit's steps, in the iterations after the merge (steps
+            // whose slots an epilogue rewrites are gathered before the barrier that
+            // precedes the rewrite); no store is issued late in a round, so a memory
+            // wait early in the next round (vmcnt counts loads and stores in issue
+            // order) finds them done.
+            if constexpr (MERGE == 1) {
+                if (k == 2 || k == 3) {
+                    emit_step(2 * (k - 2), pyr, pcu, has_prev, held0);
+                    gather_step(r - 1, 2 * (k - 2) + 1, pcu, held0);
+                    emit_step(2 * (k - 2) + 1, pyr, pcu, has_prev, held0);
+                    if (k == 3) store_outside(pyr, has_prev);
+                }
+            } else if (k == 3) {
+                emit_step(0, pyr, pcu, has_prev, held0);
+                emit_step(1, pyr, pcu, has_prev, held1);
+                emit_step(2, pyr, pcu, has_prev, held2);
+                gather_step(r - 1, 3, pcu, held0);
+                emit_step(3, pyr, pcu, has_prev, held0);
+                store_outside(pyr, has_prev);
             }
             if (k >= 1 && late)
                 epilogue_to_bank<ACT>(acc0, acc1, 2 * (k0 + k - 1) + 1 < Ho, s1, s2, cnt, slot(r, k - 1) + bo);
@@ -813,7 +828,7 @@ void convt2d_gn_fused_kernel(FusedArgs a)
                 epilogue_to_bank<ACT>(acc0, acc1, 2 * (k0 + k - 1) + 1 < Ho, s1, s2, cnt, slot(r, k - 1) + bo);
             acc0 = n0;
             acc1 = n1;
-            if (k == 1 && has_prev && wave == COEFWAVE) {
+            if (k == MERGE && has_prev && wave == COEFWAVE) {
                 // the previous unit's coefficients for the next step (one merge per workgroup)
                 const Coef cw = probe_finish(a, p_unit, lane, p_gb, pr0, pr1);
                 if (c16 == 0) {
@@ -841,9 +856,15 @@ void convt2d_gn_fused_kernel(FusedArgs a)
 #pragma unroll
                 for (int p = SPS + 1; p < NPOS; ++p) issue_pos<DT>(p, pf[p % 3], k0, xr, nhas, nk0, nxr, H, loff);
             }
-            // the previous unit's step 2(k - 1), before the barrier after which the
-            // next iteration's epilogue rewrites its slot
-            if (k == 1 || k == 2) gather_step(r - 1, 2 * (k - 1), pcu);
+            // the previous unit's steps whose slots the next iterations' epilogues
+            // rewrite (0 in iteration 2, 1 in iteration 3, 2 after the loop) and
+            // that are not stored before then, ahead of the barrier that precedes
+            // the rewrite
+            if (k == 1) gather_step(r - 1, 0, pcu, held0);
+            if (k == 2) {
+                if constexpr (MERGE == 2) gather_step(r - 1, 1, pcu, held1);
+                gather_step(r - 1, 2, pcu, MERGE == 2 ? held2 : held0);
+            }
         }
 
         // ---- the last step's activation -> bank (the slot of the previous unit's
@@ -888,8 +909,8 @@ void convt2d_gn_fused_kernel(FusedArgs a)
         __syncthreads();  // the column pixels in the bank
         const unsigned pcu = line_phase(p_unit, p_k0);
         for (int j = 0; j < SPS; ++j) {
-            gather_step(r - 1, j, pcu);
-            emit_step(j, pyr, pcu, true);
+            gather_step(r - 1, j, pcu, held0);
+            emit_step(j, pyr, pcu, true, held0);
         }
         store_outside(pyr, true);
     }

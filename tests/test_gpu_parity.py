@@ -400,6 +400,41 @@ def test_fused_convt_many_rounds(monkeypatch, over):
     _case("convt2d_gelu_gn_n128", **over)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("offset_floats", [4, 8, 20])
+def test_fused_output_off_line_boundary(offset_floats, dtype):
+    # The single-write kernel stores whole 128-byte lines of the output as it
+    # lies in memory.  An output that starts 16, 32 or 80 bytes past a line
+    # boundary (still 16-byte aligned, as the ABI requires) moves every line
+    # boundary inside the rows; the floats just before and after the output
+    # must stay untouched.  Odd output height: the last step holds one row.
+    import convolution_normalization_forward_amd as cnf
+    wl = cnf_inputs.workload("convt2d_gelu_gn_n128", dtype=dtype, N=2, in_dims=(1, 127, 256))
+    _say(f"[off-line] offset {offset_floats} floats {dtype}")
+    x = cnf_inputs.gen_x(wl)
+    p = cnf_inputs.gen_params(wl)
+    dev = "cuda:0"
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16}[dtype]
+    t = {k: (torch.from_numpy(v).to(dev) if v is not None else None) for k, v in p.items()}
+    plan = cnf.Plan(cnf.make_desc(wl, N=x.shape[0]))
+    assert "fused" in plan.describe(), plan.describe()
+    _, argmax, ws = plan.allocate(dev)
+    n = 1
+    for e in plan.out_shape:
+        n *= e
+    guard = 64
+    buf = torch.full((offset_floats + n + guard,), float("nan"), dtype=torch.float32, device=dev)
+    out = buf[offset_floats:offset_floats + n].view(plan.out_shape)
+    assert out.data_ptr() % 128 == 4 * offset_floats % 128
+    plan.forward(torch.from_numpy(x).to(dev).to(dt), t["w"].to(dt), t["b"], t["gamma"], t["beta"],
+                 out=out, argmax=argmax, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.isnan(buf[:offset_floats]).all() and torch.isnan(buf[offset_floats + n:]).all()
+    ref, _ = oracle.forward(wl, x, **p)
+    err = check_close(out.cpu().numpy(), ref, f"fused, output {offset_floats} floats past a line, {dtype}")
+    _say(f"    max_abs_err={err:.3e}")
+
+
 def test_empty_batch_is_a_noop():
     import convolution_normalization_forward_amd as cnf
     wl = cnf_inputs.workload("conv3d_hswish_gn_mean_n1024")

@@ -52,8 +52,8 @@ CSRC = os.path.join(ROOT, "convolution_normalization_forward_amd", "csrc")
 #   gn-mean, small, implicit GEMMs (fp32 at stride 1 or 2, 16-bit): the full
 #                 conv, nominal FLOPs (the 16-bit one against the bf16 peak).
 #   convt (single write): HBM, x and w read once + the fp32 output written once.
-#   upsample2:    the stride-2 transposed conv's normalising pass (mode 2):
-#                 HBM, x read once + the output written once.
+#   upsample2:    the stride-2 transposed conv's single-write kernel: HBM,
+#                 x read once + the output written once.
 DOMINANT = {
     "conv2d_in_div_n2": ("small_conv_norm_kernel", "k_small_conv_norm.hip", "mfma"),
     "conv3d_softmax_pool_n128": ("conv3d_softmax_pool_kernel", "k_conv3d_softmax_pool.hip", "mfma"),
@@ -62,7 +62,7 @@ DOMINANT = {
     "convt2d_gelu_gn_n128": ("convt2d_gn_fused_kernel<2, 0>", "k_convt2d_gn_fused.hip", "hbm"),
     "convt2d_dense_gelu_gn_n128": ("conv2d_igemm_kernel<64, 2, 1>", "k_conv2d_igemm.hip", "mfma"),
     "conv2d_s2p1_in_div_n128": ("conv2d_igemm_kernel<128, 0, 2>", "k_conv2d_igemm.hip", "mfma"),
-    "convt2d_s2_gelu_gn_n128": ("upsample2_conv_kernel<2, 2>", "k_upsample2.hip", "hbm"),
+    "convt2d_s2_gelu_gn_n128": ("upsample2_gn_fused_kernel<2>", "k_convt2d_gn_fused.hip", "hbm"),
     "conv2d_in_div_n128_bf16": ("conv2d_igemm16_kernel<128, 0, 1>", "k_conv2d_igemm.hip", "mfma"),
     "convt2d_gelu_gn_n128_bf16": ("convt2d_gn_fused_kernel<2, 1>", "k_convt2d_gn_fused.hip", "hbm"),
 }

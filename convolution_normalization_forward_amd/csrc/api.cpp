@@ -23,7 +23,8 @@ enum Family : int {
     FAM_CONVT = 5,         // grouped ConvTranspose2d 8x8 per group + act + GroupNorm pass
     FAM_CONVT_FUSED = 6,   // same, single write: cooperative kernel, cross-workgroup merge
     FAM_GENERIC = 7,       // any validated descriptor: gathered implicit GEMM + passes
-    FAM_IGEMM16 = 8        // Conv2d C_out 128/64 k3, 16-bit x and w: implicit GEMM on 32x32x16 MFMA + norm pass
+    FAM_IGEMM16 = 8,       // Conv2d C_out 128/64 k3, 16-bit x and w: implicit GEMM on 32x32x16 MFMA + norm pass
+    FAM_UPS2_FUSED = 9     // stride-2 upsampling grouped ConvTranspose2d + act + GroupNorm, single write
 };
 
 const char *family_name(int f)
@@ -37,6 +38,7 @@ const char *family_name(int f)
     case FAM_CONVT_FUSED: return "convt2d_grouped8_gn_fused(cooperative,single-write)";
     case FAM_GENERIC: return "generic(gathered-igemm mfma16x16x4 + softmax/finalize/apply/pool passes)";
     case FAM_IGEMM16: return "conv2d_igemm16(mfma32x32x16,channel-innermost halo)+norm_finalize+apply";
+    case FAM_UPS2_FUSED: return "convt2d_s2_grouped8_gn_fused(cooperative,single-write,valu)";
     default: return "none";
     }
 }
@@ -319,6 +321,14 @@ cnf_status cnf_plan_create(const cnf_desc *desc, cnf_plan **plan)
         cnf::convt2d_fused_supported(d.C_in, d.C_out, d.groups, H, W, d.act, d.norm, d.num_groups) &&
         cnf::generic_supported(ga))
         p.family = FAM_CONVT_FUSED;
+    // the stride-2 upsampling transposed conv over 8-channel groups + GroupNorm:
+    // the single-write kernel, with the general family as its fallback
+    if (!p.family && d.dtype == CNF_DTYPE_F32 && !(force && force[0] == '1') &&
+        d.kind == CNF_CONV_TRANSPOSE && d.ndim == 2 && d.reduce == CNF_RED_NONE && k == 3 &&
+        d.stride == 2 && d.padding == 1 && d.output_padding == 1 && d.dilation == 1 &&
+        cnf::upsample2_fused_supported(d.C_in, d.C_out, d.groups, H, W, d.act, d.norm, d.num_groups) &&
+        cnf::generic_supported(ga))
+        p.family = FAM_UPS2_FUSED;
     if (!p.family) {
         if (!cnf::generic_supported(ga)) return CNF_ERR_UNSUPPORTED;
         p.family = FAM_GENERIC;
@@ -343,8 +353,13 @@ cnf_status cnf_plan_create(const cnf_desc *desc, cnf_plan **plan)
         p.workspace = a > b ? a : b;
     }
 
+    if (p.family == FAM_UPS2_FUSED) {
+        const size_t a = cnf::upsample2_fused_workspace(d.N, d.groups, H), b = cnf::generic_workspace(ga);
+        p.workspace = a > b ? a : b;
+    }
+
     p.flag_offset = 0;
-    if (p.family == FAM_CONVT_FUSED) {
+    if (p.family == FAM_CONVT_FUSED || p.family == FAM_UPS2_FUSED) {
         // the wait flag after everything either path uses, on its own 16 bytes
         p.flag_offset = (p.workspace + 15) & ~(size_t)15;
         p.workspace = p.flag_offset + 16;
@@ -498,6 +513,23 @@ cnf_status forward_impl(const cnf_plan *plan, const void *xv, const void *wv, co
             e = cnf::launch_convt2d(a, st);
         break;
     }
+    case FAM_UPS2_FUSED: {
+        cnf::ConvT2dArgs a{x, w, b, gamma, beta, out, static_cast<float *>(workspace), d.N,
+                           d.C_in, d.C_out, H, W, d.groups, plan->Ho, plan->Wo, d.act,
+                           norm_groups, d.eps, inv_div, 0};
+        int *flag = reinterpret_cast<int *>(static_cast<char *>(workspace) + plan->flag_offset);
+        a.flag = flag;
+        hipLaunchKernelGGL(clear_word_kernel, dim3(1), dim3(1), 0, st, flag);
+        if ((e = hipGetLastError()) != hipSuccess) break;
+        e = cnf::launch_upsample2_fused(a, st);
+        if (e == hipErrorCooperativeLaunchTooLarge) {
+            (void)hipGetLastError();
+            e = cnf::launch_generic(generic_args(*plan, xv, wv, b, gamma, beta, out, argmax,
+                                                 workspace, norm_groups),
+                                    st);
+        }
+        break;
+    }
     case FAM_GENERIC:
         e = cnf::launch_generic(generic_args(*plan, xv, wv, b, gamma, beta, out, argmax,
                                              workspace, norm_groups),
@@ -535,7 +567,7 @@ cnf_status cnf_forward_check(const cnf_plan *plan, const void *workspace, size_t
 {
     if (!plan) return CNF_ERR_NULL;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    if (plan->family != FAM_CONVT_FUSED || plan->d.N == 0)
+    if ((plan->family != FAM_CONVT_FUSED && plan->family != FAM_UPS2_FUSED) || plan->d.N == 0)
         return hipStreamSynchronize(st) == hipSuccess ? CNF_OK : CNF_ERR_HIP;
     if (!workspace || workspace_bytes < plan->workspace) return CNF_ERR_WORKSPACE;
     if (misaligned(workspace)) return CNF_ERR_ALIGNMENT;

@@ -456,6 +456,8 @@ struct Lines {
     v2f v[LINE_SLOTS];
 };
 
+// R2 = floats in a step's two rows (2 x 258 here, 2 x 256 for the upsampling kernel)
+template <int R2>
 __device__ __forceinline__ void gather_lines(Lines &L, const float *chan, int t, bool has_next, int next_t,
                                              v2f &carry, int q, int c16)
 {
@@ -466,7 +468,7 @@ __device__ __forceinline__ void gather_lines(Lines &L, const float *chan, int t,
         const v2f v = *reinterpret_cast<const v2f *>(chan + u);
         L.v[i] = i == 0 && u < 0 ? carry : v;
     }
-    if (has_next) carry = *reinterpret_cast<const v2f *>(chan + 2 * WO - next_t + 2 * c16);
+    if (has_next) carry = *reinterpret_cast<const v2f *>(chan + R2 - next_t + 2 * c16);
 }
 
 // soff = byte offset of the step's first float; with active false every store
@@ -608,7 +610,7 @@ void convt2d_gn_fused_kernel(FusedArgs a)
     auto gather_step = [&](int rho, int s, unsigned cu, Lines &held) {
         const int prow = 2 * (p_k0 + s);
         const bool last = s == SPS - 1 || prow + 2 >= Ho;
-        gather_lines(held, slot(rho, s) + wave * CP, (int)((cu + 4u * s) & 31u), !last,
+        gather_lines<2 * WO>(held, slot(rho, s) + wave * CP, (int)((cu + 4u * s) & 31u), !last,
                      (int)((cu + 4u * s + 4u) & 31u), carry, q, c16);
     };
     auto emit_step = [&](int s, __amdgpu_buffer_rsrc_t pyr, unsigned cu, bool active, const Lines &held) {
@@ -916,6 +918,294 @@ void convt2d_gn_fused_kernel(FusedArgs a)
     }
 }
 
+// ===========================================================================
+// The upsampling form of the grouped transposed conv: ConvTranspose2d k 3,
+// stride 2, padding 1, output_padding 1, 8 in / 8 out channels per group,
+// input width 128 (output 2H x 256), + activation + GroupNorm, in the same
+// single-write scheme (page "Kimi-K2.6__l2_p19", its layer at stride 2).
+// Output (2i + a, 2j + b) takes inputs (i, j), (i, j + 1), (i + 1, j) and
+// (i + 1, j + 1) only: kh = 1 for a = 0, kh = 2 from row i and kh = 0 from row
+// i + 1 for a = 1 (columns alike).  So a step is one input row i -> output
+// rows 2i, 2i + 1: wave c computes output channel c, lane l the 2 x 2 blocks
+// of input columns 2l and 2l + 1 (output columns 4l .. 4l + 3), on the VALU
+// (9 taps per input / output channel pair, 18 multiply-adds per output: too
+// thin for MFMA tiles), with the channel's 72 weights in registers.
+// A slice is SPS input rows, every unit has H / SPS slices, and the output
+// rows are 256 floats, so no single tiles are needed and a step's rows start
+// on a 128-byte line.  The input rows of a round (i0 .. i0 + SPS) sit in LDS
+// slots 0 .. SPS, refilled from registers loaded three stashes ahead; the
+// statistics exchange, the bank and the line stores are the ones above, with
+// the merge at the end of step 2 and the previous unit stored in step 3.
+constexpr int UW = 128;                      // input width
+constexpr int UWO = 2 * UW;                  // output row
+constexpr int URP = UW + 4;                  // ring row pitch: x at 0..127, zeros at 128..131
+constexpr int UROW_FLOATS = CG * URP;        // one input row of the group's 8 channels
+constexpr int UMAX_S = 32;
+static_assert(2 * UWO + 16 == CP, "the bank's channel rows hold a step");
+static_assert(CG * 64 == THREADS && UW == 2 * 64, "one row load: channel = wave, 2 columns per lane");
+
+// One input row (row of this unit; rows past H read as zeros): this thread's
+// two columns of channel `wave`.
+__device__ __forceinline__ v2u load_urow(__amdgpu_buffer_rsrc_t xr, int H, int row, unsigned loff)
+{
+    const unsigned ro = row < H ? (unsigned)(row * UW) * 4u : OOB;
+    return __builtin_bit_cast(v2u, __builtin_amdgcn_raw_buffer_load_b64(xr, (int)(loff + ro), 0, 0));
+}
+
+__device__ __forceinline__ void stash_urow(float *ring, int slot, v2u v, int wave, int lane)
+{
+    *reinterpret_cast<v2u *>(ring + slot * UROW_FLOATS + wave * URP + 2 * lane) = v;
+}
+
+// Stash positions of a round: p <= SPS - 2 stashes row p + 2 at the end of
+// step p; p = SPS - 1 and SPS stash the next round's rows 0 and 1 at the end
+// of the last step; position SPS + 1 stashes nothing.  Position p + 3 is
+// loaded right after position p's stash, into register set p % 3.
+__device__ __forceinline__ v2u issue_upos(int p, int i0, __amdgpu_buffer_rsrc_t xr, bool nhas, int ni0,
+                                          __amdgpu_buffer_rsrc_t nxr, int H, unsigned loff)
+{
+    const int p3 = p + 3;
+    int row;
+    bool next;
+    if (p3 < NPOS) {
+        next = p3 >= SPS - 1;
+        row = p3 <= SPS - 2 ? p3 + 2 : p3 - (SPS - 1);
+    } else {
+        next = true;
+        row = p3 - NPOS + 2;
+    }
+    const bool use_next = next && nhas;
+    return load_urow(use_next ? nxr : xr, H, (use_next ? ni0 : i0) + row, loff);
+}
+
+template <int ACT>
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void upsample2_gn_fused_kernel(FusedArgs a)
+{
+    __shared__ __align__(16) float ring[(SPS + 1) * UROW_FLOATS];
+    __shared__ float red[NWAVE * 4 * 3];
+    __shared__ float coefs[CG * 2];
+    __shared__ __align__(16) float bank[BPAD + NBANK * SLOT_FLOATS + BTAIL];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int q = lane >> 4, c16 = lane & 15;
+    const int H = a.H, Ho = a.Ho, S = a.S;
+    const int U = a.N * a.G;
+    const unsigned plane = (unsigned)Ho * UWO;
+
+    int ulocal, s_base;
+    if (a.xcd_units > 0) {
+        const int xcd = blockIdx.x % NXCD, l = blockIdx.x / NXCD;
+        ulocal = xcd * a.xcd_units + l / S;
+        s_base = l % S;
+    } else {
+        ulocal = blockIdx.x / S;
+        s_base = blockIdx.x % S;
+    }
+    for (int e = tid; e < (SPS + 1) * CG; e += THREADS) {  // zero columns right of x, never overwritten
+        float *row = ring + e * URP + UW;
+#pragma unroll
+        for (int c = 0; c < URP - UW; ++c) row[c] = 0.f;
+    }
+    const unsigned loff = (unsigned)(wave * H * UW + 2 * lane) * 4u;
+    auto slot = [&](int rho, int k) { return bank + BPAD + (((rho * SPS + k) % NBANK + NBANK) % NBANK) * SLOT_FLOATS; };
+    auto xres = [&](int unit) {
+        return make_rsrc(static_cast<const char *>(a.x) + (size_t)unit * CG * H * UW * 4, (unsigned)(CG * H * UW * 4));
+    };
+
+    // ---- prologue: round 0's rows 0, 1 in the ring, positions 0..2 in flight
+    v2u pf[3];
+    {
+        const int i0 = s_base * SPS;
+        const __amdgpu_buffer_rsrc_t xr = xres(ulocal);
+        stash_urow(ring, 0, load_urow(xr, H, i0, loff), wave, lane);
+        stash_urow(ring, 1, load_urow(xr, H, i0 + 1, loff), wave, lane);
+#pragma unroll
+        for (int p = 0; p < 3; ++p) pf[p] = load_urow(xr, H, i0 + p + 2, loff);
+    }
+
+    float bias1 = 0.f;
+    v4f gb = v4f{1.f, 0.f, 1.f, 0.f}, p_gb = gb;
+    int wgroup = -1;
+    float wk[CG][KS * KS];  // w[ci][c][kh][kw] of this wave's output channel c
+    int p_unit = -1, p_sg = 0, p_i0 = 0;
+    float psc = 0.f, psh = 0.f;
+    v2f carry = v2f{0.f, 0.f};
+    Lines held0, held1, held2;
+    // (float offset of the previous unit's channel-`wave` slice start) mod 32, even
+    auto line_phase = [&](int unit, int i0) {
+        const unsigned long long f = (reinterpret_cast<unsigned long long>(a.y) >> 2) +
+                                     (unsigned long long)unit * CG * plane + (unsigned long long)wave * plane +
+                                     (unsigned long long)(2 * i0) * UWO;
+        return (unsigned)f & 30u;
+    };
+    // a step's rows are 512 floats (0 mod 32), so its line phase is the slice's
+    auto gather_step = [&](int rho, int s, unsigned cu, Lines &held) {
+        gather_lines<2 * UWO>(held, slot(rho, s) + wave * CP, (int)cu, s < SPS - 1, (int)cu, carry, q, c16);
+    };
+    auto emit_step = [&](int s, __amdgpu_buffer_rsrc_t pyr, unsigned cu, bool active, const Lines &held) {
+        const int prow = 2 * (p_i0 + s);
+        emit_lines(pyr, held, psc, psh, (int)cu, s == SPS - 1 ? 2 * UWO : 2 * UWO - (int)cu, s == 0,
+                   ((unsigned)wave * plane + (unsigned)prow * UWO) * 4u, q, c16, active);
+    };
+
+    int r = 0;
+    for (;; ++r) {
+        const int unit = r * a.upr + ulocal;
+        __syncthreads();  // rows 0, 1 in the ring; last round's ring readers done; red[] complete
+        if (unit >= U) {
+            if (p_unit >= 0 && wave == PUBWAVE) publish(a, red, p_unit, p_sg, lane);
+            break;
+        }
+        const bool has_prev = p_unit >= 0;
+        if (has_prev && wave == PUBWAVE) publish(a, red, p_unit, p_sg, lane);
+
+        const int sg = (s_base + r) % S;
+        const int i0 = sg * SPS;
+        const __amdgpu_buffer_rsrc_t xr = xres(unit);
+        const int nunit = unit + a.upr;
+        const bool nhas = nunit < U;
+        const int ni0 = ((sg + 1) % S) * SPS;
+        const __amdgpu_buffer_rsrc_t nxr = xres(nhas ? nunit : unit);
+        const __amdgpu_buffer_rsrc_t pyr = y_rsrc_u(a, has_prev ? p_unit : unit, plane);
+        const unsigned pcu = has_prev ? line_phase(p_unit, p_i0) : 0u;
+
+        const int g = unit % a.G;
+        if (g != wgroup) {
+            wgroup = g;
+            const float *wg = static_cast<const float *>(a.wt) + ((size_t)g * CG * CG + wave) * KS * KS;
+#pragma unroll
+            for (int ci = 0; ci < CG; ++ci)
+#pragma unroll
+                for (int t = 0; t < KS * KS; ++t) wk[ci][t] = wg[ci * CG * KS * KS + t];
+            bias1 = a.bias ? a.bias[g * CG + wave] : 0.0f;
+            const int cg = g * CG + 2 * q;  // the (gamma, beta) pairs probe_finish uses
+            gb = v4f{a.gamma ? a.gamma[cg] : 1.0f, a.beta ? a.beta[cg] : 0.0f,
+                     a.gamma ? a.gamma[cg + 1] : 1.0f, a.beta ? a.beta[cg + 1] : 0.0f};
+        }
+
+        float s1 = 0.f, s2 = 0.f;
+        unsigned long long pr0 = 0ull, pr1 = 0ull;
+#pragma unroll
+        for (int k = 0; k < SPS; ++k) {
+            if (k > 0) __syncthreads();  // row k + 1 in the ring
+            if (k == 2 && has_prev && wave == COEFWAVE) probe_issue(a, p_unit, lane, pr0, pr1);
+            if (k == 3 && has_prev) {
+                psc = coefs[2 * wave];
+                psh = coefs[2 * wave + 1];
+            }
+            // ---- conv of input row i0 + k (ring slots k, k + 1): acc[h][p] is the
+            // block of input column 2 lane + h, p = 2a + b (output row 2i + a,
+            // column 2(2 lane + h) + b)
+            const float *r0 = ring + k * UROW_FLOATS + 2 * lane, *r1 = ring + (k + 1) * UROW_FLOATS + 2 * lane;
+            float acc[2][4];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int pp = 0; pp < 4; ++pp) acc[h][pp] = bias1;
+#pragma unroll
+            for (int ci = 0; ci < CG; ++ci) {
+                // input columns 2 lane .. 2 lane + 2 of rows i and i + 1
+                const v2f a01 = *reinterpret_cast<const v2f *>(r0 + ci * URP);
+                const v2f b01 = *reinterpret_cast<const v2f *>(r1 + ci * URP);
+                const float a2 = r0[ci * URP + 2], b2 = r1[ci * URP + 2];
+                const float *kk = wk[ci];  // kk[kh * 3 + kw]
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const float x00 = h ? a01[1] : a01[0], x01 = h ? a2 : a01[1];
+                    const float x10 = h ? b01[1] : b01[0], x11 = h ? b2 : b01[1];
+                    acc[h][0] = fmaf(x00, kk[4], acc[h][0]);
+                    acc[h][1] = fmaf(x01, kk[3], fmaf(x00, kk[5], acc[h][1]));
+                    acc[h][2] = fmaf(x10, kk[1], fmaf(x00, kk[7], acc[h][2]));
+                    acc[h][3] = fmaf(x11, kk[0], fmaf(x10, kk[2], fmaf(x01, kk[6], fmaf(x00, kk[8], acc[h][3]))));
+                }
+            }
+            // ---- activation, sums, bank (channel `wave`, output columns 4 lane .. + 3)
+            {
+                const v4f e0 = activate4<ACT>(v4f{acc[0][0], acc[0][1], acc[1][0], acc[1][1]});
+                const v4f e1 = activate4<ACT>(v4f{acc[0][2], acc[0][3], acc[1][2], acc[1][3]});
+                sums4(e0, s1, s2);
+                sums4(e1, s1, s2);
+                float *bp = slot(r, k) + wave * CP + 4 * lane;
+                *reinterpret_cast<v4f *>(bp) = e0;
+                *reinterpret_cast<v4f *>(bp + UWO) = e1;
+            }
+            // ---- the previous unit, in the step after the merge: steps 0..2 were
+            // gathered at the ends of steps 0..2 (each iteration's epilogue
+            // rewrites the slot of the previous unit's step k - 1); stores are
+            // issued on every path (masked past the buffer) so that the memory
+            // waits the compiler places count the same stores everywhere
+            if (k == SPS - 1) {
+                emit_step(0, pyr, pcu, has_prev, held0);
+                emit_step(1, pyr, pcu, has_prev, held1);
+                emit_step(2, pyr, pcu, has_prev, held2);
+                gather_step(r - 1, 3, pcu, held0);
+                emit_step(3, pyr, pcu, has_prev, held0);
+            }
+            if (k == 2 && has_prev && wave == COEFWAVE) {
+                const Coef cw = probe_finish(a, p_unit, lane, p_gb, pr0, pr1);
+                if (c16 == 0) {
+                    coefs[4 * q] = cw.sc0; coefs[4 * q + 1] = cw.sh0;
+                    coefs[4 * q + 2] = cw.sc1; coefs[4 * q + 3] = cw.sh1;
+                }
+            }
+            // ---- ring stashes at the end of step k, each followed by its loads
+            if (k <= SPS - 2) {
+                stash_urow(ring, k + 2, pf[k % 3], wave, lane);
+                pf[k % 3] = issue_upos(k, i0, xr, nhas, ni0, nxr, H, loff);
+            } else {
+                stash_urow(ring, 0, pf[(SPS - 1) % 3], wave, lane);
+                pf[(SPS - 1) % 3] = issue_upos(SPS - 1, i0, xr, nhas, ni0, nxr, H, loff);
+                stash_urow(ring, 1, pf[SPS % 3], wave, lane);
+                pf[SPS % 3] = issue_upos(SPS, i0, xr, nhas, ni0, nxr, H, loff);
+#pragma unroll
+                for (int p = SPS + 1; p < NPOS; ++p) pf[p % 3] = issue_upos(p, i0, xr, nhas, ni0, nxr, H, loff);
+            }
+            // the previous unit's step k, before the barrier after which the next
+            // iteration's epilogue rewrites its slot
+            if (k == 0) gather_step(r - 1, 0, pcu, held0);
+            if (k == 1) gather_step(r - 1, 1, pcu, held1);
+            if (k == 2) gather_step(r - 1, 2, pcu, held2);
+        }
+
+        // ---- slice statistics -> red[wave][row]; published after the next barrier
+        {
+            const int cnt = 8 * SPS;  // every lane: 8 outputs per step
+            float fn = (float)cnt;
+            float mean = s1 / fn;
+            float m2 = fmaxf(s2 - s1 * mean, 0.0f);
+            row_merge16(fn, mean, m2);
+            if (c16 == 0) {
+                float *e = red + (wave * 4 + q) * 3;
+                e[0] = fn; e[1] = mean; e[2] = m2;
+            }
+        }
+        p_gb = gb;
+        p_unit = unit;
+        p_sg = sg;
+        p_i0 = i0;
+    }
+
+    // ---- the last unit: its triple was published above; wait, normalise, store
+    if (p_unit >= 0) {
+        const __amdgpu_buffer_rsrc_t pyr = y_rsrc_u(a, p_unit, plane);
+        unsigned long long pr0, pr1;
+        probe_issue(a, p_unit, lane, pr0, pr1);
+        const Coef pc = probe_finish(a, p_unit, lane, p_gb, pr0, pr1);
+        const int src = 16 * (wave >> 1);
+        psc = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                  __builtin_bit_cast(int, (wave & 1) ? pc.sc1 : pc.sc0), src));
+        psh = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                  __builtin_bit_cast(int, (wave & 1) ? pc.sh1 : pc.sh0), src));
+        const unsigned pcu = line_phase(p_unit, p_i0);
+        for (int s = 0; s < SPS; ++s) {
+            gather_step(r - 1, s, pcu, held0);
+            emit_step(s, pyr, pcu, true, held0);
+        }
+    }
+}
+
 __global__ void zero_words_kernel(unsigned *p, long long n)
 {
     const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -997,6 +1287,60 @@ hipError_t launch_t(const ConvT2dArgs &p, hipStream_t st)
     return dominant_end(st);
 }
 
+// Slices of the upsampling kernel: SPS input rows each, at most UMAX_S (0 if H
+// does not split so).
+int ups_slices(int H)
+{
+    return H >= SPS && H % SPS == 0 && H / SPS <= UMAX_S ? H / SPS : 0;
+}
+
+template <int ACT>
+hipError_t launch_ups_t(const ConvT2dArgs &p, hipStream_t st)
+{
+    const int S = ups_slices(p.H);
+    if (!S || p.W != UW || p.Ho != 2 * p.H) return hipErrorInvalidValue;
+    const LaunchHooks &hk = hooks();
+    static std::atomic<int> blocks_per_cu[64][5], cus_cache[64];  // zero-initialised
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const bool cache = dev >= 0 && dev < 64;
+    int nb = cache ? blocks_per_cu[dev][ACT].load(std::memory_order_relaxed) : 0;
+    int cus = cache ? cus_cache[dev].load(std::memory_order_relaxed) : 0;
+    if (nb == 0 || cus == 0) {
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, upsample2_gn_fused_kernel<ACT>, THREADS, 0);
+        if (e != hipSuccess) return e;
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        if (cache) {
+            blocks_per_cu[dev][ACT].store(nb, std::memory_order_relaxed);
+            cus_cache[dev].store(cus, std::memory_order_relaxed);
+        }
+    }
+    const int U = p.N * p.groups;
+    int upr = nb * cus / S;
+    if (upr < 1 || hk.force_fallback) return hipErrorCooperativeLaunchTooLarge;
+    if (upr > U) upr = U;
+    if (hk.max_units_per_round > 0 && upr > hk.max_units_per_round) upr = hk.max_units_per_round;
+    const int xcd_units = upr % NXCD == 0 ? upr / NXCD : 0;
+
+    const long long words = (long long)U * S * 4;
+    hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, st,
+                       reinterpret_cast<unsigned *>(p.partials), words);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+
+    FusedArgs fa{p.x, p.w, p.b, p.gamma, p.beta, p.out, p.partials, p.flag,
+                 hk.spin_limit > 0 ? hk.spin_limit : SPIN_LIMIT, hk.never_ready,
+                 p.N, p.C_out, p.H, p.groups, p.Ho, S, 0, upr, xcd_units, p.eps, p.inv_div};
+    void *args[] = {&fa};
+    if ((e = dominant_begin(st)) != hipSuccess) return e;
+    e = hipLaunchCooperativeKernel(reinterpret_cast<const void *>(upsample2_gn_fused_kernel<ACT>),
+                                   dim3(upr * S), dim3(THREADS), args, 0, st);
+    if (e != hipSuccess) return e;
+    return dominant_end(st);
+}
+
 }  // namespace
 
 int convt2d_fused_slices(int Ho)
@@ -1038,6 +1382,31 @@ hipError_t launch_convt2d_fused(const ConvT2dArgs &a, hipStream_t st)
     case 0: return launch_dt<0>(a, st);
     case 1: return launch_dt<1>(a, st);
     case 2: return launch_dt<2>(a, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+bool upsample2_fused_supported(int C_in, int C_out, int groups, int H, int W_, int act, int norm,
+                               int num_groups)
+{
+    return W_ == UW && C_in == CG * groups && C_out == CG * groups && ups_slices(H) > 0 &&
+           norm == 1 /* group */ && num_groups == groups &&
+           (act == ACT_NONE || act == ACT_HARDSWISH || act == ACT_GELU_ERF || act == ACT_GELU_TANH);
+}
+
+size_t upsample2_fused_workspace(int N, int groups, int H)
+{
+    return (size_t)N * groups * (size_t)ups_slices(H) * 4 * sizeof(float);
+}
+
+hipError_t launch_upsample2_fused(const ConvT2dArgs &a, hipStream_t st)
+{
+    if (a.dtype != 0) return hipErrorInvalidValue;
+    switch (a.act) {
+    case ACT_NONE: return launch_ups_t<ACT_NONE>(a, st);
+    case ACT_HARDSWISH: return launch_ups_t<ACT_HARDSWISH>(a, st);
+    case ACT_GELU_ERF: return launch_ups_t<ACT_GELU_ERF>(a, st);
+    case ACT_GELU_TANH: return launch_ups_t<ACT_GELU_TANH>(a, st);
     default: return hipErrorInvalidValue;
     }
 }

@@ -120,6 +120,14 @@ bool convt2d_fused_supported(int C_in, int C_out, int groups, int H, int W, int 
                              int num_groups);
 size_t convt2d_fused_workspace(int N, int groups, int Ho);
 hipError_t launch_convt2d_fused(const ConvT2dArgs &a, hipStream_t st);
+// The same single-write scheme for the stride-2 upsampling form (k 3, padding
+// 1, output_padding 1, 8 -> 8 channels per group, input width 128, H a
+// multiple of 4 up to 128), fp32; hipErrorCooperativeLaunchTooLarge when the
+// grid cannot be co-resident (the caller falls back to the general family).
+bool upsample2_fused_supported(int C_in, int C_out, int groups, int H, int W, int act, int norm,
+                               int num_groups);
+size_t upsample2_fused_workspace(int N, int groups, int H);
+hipError_t launch_upsample2_fused(const ConvT2dArgs &a, hipStream_t st);
 
 // ---- general family: any validated descriptor (2-D or 3-D, conv or
 //      transposed conv, groups, stride, padding, dilation, output_padding,

@@ -283,10 +283,12 @@ def test_family_routing():
     # the page configurations keep their specialised families ...
     fams = {n: cnf.Plan(_desc(n)).describe().split()[0] for n in cnf_inputs.PAGE_WORKLOADS}
     assert not any("generic" in f for f in fams.values()), fams
-    # the other workloads: the 16-bit form of the transposed conv runs on the
-    # single-write kernel, the strided conv on the implicit GEMM, the 16-bit
-    # conv on the 16-bit implicit GEMM, the rest on the general family
+    # the other workloads: the 16-bit form of the transposed conv and its
+    # stride-2 upsampling form run on single-write kernels, the strided conv on
+    # the implicit GEMM, the 16-bit conv on the 16-bit implicit GEMM, the rest
+    # on the general family
     special = {"convt2d_gelu_gn_n128_bf16": "family=convt2d_grouped8_gn_fused",
+               "convt2d_s2_gelu_gn_n128": "family=convt2d_s2_grouped8_gn_fused",
                "conv2d_s2p1_in_div_n128": "family=conv2d_igemm",
                "conv2d_in_div_n128_bf16": "family=conv2d_igemm16"}
     for n in set(cnf_inputs.WORKLOAD_ORDER) - set(cnf_inputs.PAGE_WORKLOADS):
@@ -339,11 +341,13 @@ def test_general_workspace_layout_sizes(monkeypatch):
     pool1 = 128 * 16 * 8 * 16 * 16
     assert p.workspace_bytes == (_packed_weights(1, 27, 3, 16) + _align(128 * 16 * S * 4)
                                  + 4 * _align(pool1 * 4))
-    # strided transposed conv: stride^2 phases of ceil(256/2)^2 positions each
+    # strided (upsampling) transposed conv: the single-write plan keeps room for
+    # its general-family fallback (stride^2 phases of ceil(256/2)^2 positions
+    # each), then its 16-byte wait flag
     p = cnf.Plan(_desc("convt2d_s2_gelu_gn_n128"))
     T = 4 * (128 * 128 // 64)
     assert p.workspace_bytes == (_packed_weights(8, 9, 8, 8) + _align(128 * 64 * T * 16)
-                                 + _align(128 * 64 * 8))
+                                 + _align(128 * 64 * 8)) + 16
 
 
 def test_descriptor_layout_matches_the_c_header(tmp_path):

@@ -400,6 +400,89 @@ def test_fused_convt_many_rounds(monkeypatch, over):
     _case("convt2d_gelu_gn_n128", **over)
 
 
+# The stride-2 upsampling transposed conv (k 3, padding 1, output_padding 1)
+# over 8-channel groups + GroupNorm through its single-write kernel (input
+# width 128, H a multiple of 4 up to 128): one slice per unit, several slices,
+# several groups and rounds per launch, every activation.
+UPS2_FUSED = [
+    dict(N=1, in_dims=(1, 4, 128)),
+    dict(N=2, in_dims=(1, 12, 128), act="none"),
+    dict(N=3, C_in=16, C_out=16, groups=2, num_groups=2, in_dims=(1, 20, 128), act="gelu_tanh"),
+    dict(N=2, C_in=24, C_out=24, groups=3, num_groups=3, in_dims=(1, 36, 128), act="hardswish"),
+    dict(N=1, in_dims=(1, 128, 128)),
+    dict(N=2, C_in=16, C_out=16, groups=2, num_groups=2, in_dims=(1, 64, 128), affine=0, divide_by=2.0),
+]
+
+
+@pytest.mark.parametrize("over", UPS2_FUSED)
+def test_upsample_single_write_every_element(over):
+    wl = cnf_inputs.workload("convt2d_s2_gelu_gn_n128", **over)
+    _say(f"[ups2-fused] {over}")
+    x = cnf_inputs.gen_x(wl)
+    p = cnf_inputs.gen_params(wl)
+    plan, out, _ = run_gpu(wl, x, p)
+    assert "convt2d_s2_grouped8_gn_fused" in plan.describe(), plan.describe()
+    ref, _ = oracle.forward(wl, x, **p)
+    err = check_close(out.cpu().numpy(), ref, f"upsample fused {over}")
+    _say(f"    max_abs_err={err:.3e}")
+
+
+def test_upsample_single_write_many_rounds(monkeypatch):
+    # two units per round: 12 rounds, the bank rotation and ring hand-over across them
+    monkeypatch.setenv("CNF_TEST_FUSED_MAX_UNITS_PER_ROUND", "2")
+    _case("convt2d_s2_gelu_gn_n128", N=3, in_dims=(1, 32, 128))
+
+
+def test_upsample_single_write_waits(monkeypatch):
+    # every wait succeeds on a normal run; a wait that cannot succeed gives up
+    # after a few polls, the outputs are NaN and the caller is told
+    import convolution_normalization_forward_amd as cnf
+    wl = cnf_inputs.workload("convt2d_s2_gelu_gn_n128", N=2, in_dims=(1, 40, 128))
+    x = cnf_inputs.gen_x(wl)
+    p = cnf_inputs.gen_params(wl)
+    plan, out, ws = _fused_run(wl, x, p, reps=2)
+    assert "convt2d_s2_grouped8_gn_fused" in plan.describe()
+    assert cnf.cnf_forward_check(plan.handle, ws, plan.workspace_bytes) == cnf.CNF_OK
+    ref, _ = oracle.forward(wl, x, **p)
+    check_close(out.cpu().numpy(), ref, "upsample fused repeated")
+    monkeypatch.setenv("CNF_TEST_FUSED_NEVER_READY", "1")
+    monkeypatch.setenv("CNF_TEST_FUSED_SPIN_LIMIT", "3")
+    plan2, out2, ws2 = _fused_run(wl, x, p)
+    assert cnf.cnf_forward_check(plan2.handle, ws2, plan2.workspace_bytes) == cnf.CNF_ERR_WAIT_TIMEOUT
+    assert torch.isnan(out2).all()
+
+
+def test_upsample_single_write_forced_fallback(monkeypatch):
+    # a grid that cannot be co-resident runs on the general family
+    monkeypatch.setenv("CNF_TEST_FORCE_FALLBACK", "1")
+    _case("convt2d_s2_gelu_gn_n128", N=2, in_dims=(1, 16, 128))
+
+
+@pytest.mark.parametrize("offset_floats", [4, 20])
+def test_upsample_output_off_line_boundary(offset_floats):
+    import convolution_normalization_forward_amd as cnf
+    wl = cnf_inputs.workload("convt2d_s2_gelu_gn_n128", N=2, in_dims=(1, 24, 128))
+    _say(f"[ups2 off-line] offset {offset_floats} floats")
+    x = cnf_inputs.gen_x(wl)
+    p = cnf_inputs.gen_params(wl)
+    dev = "cuda:0"
+    t = {k: (torch.from_numpy(v).to(dev) if v is not None else None) for k, v in p.items()}
+    plan = cnf.Plan(cnf.make_desc(wl, N=x.shape[0]))
+    assert "convt2d_s2_grouped8_gn_fused" in plan.describe(), plan.describe()
+    _, argmax, ws = plan.allocate(dev)
+    n = 1
+    for e in plan.out_shape:
+        n *= e
+    buf = torch.full((offset_floats + n + 64,), float("nan"), dtype=torch.float32, device=dev)
+    out = buf[offset_floats:offset_floats + n].view(plan.out_shape)
+    plan.forward(torch.from_numpy(x).to(dev), t["w"], t["b"], t["gamma"], t["beta"],
+                 out=out, argmax=argmax, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.isnan(buf[:offset_floats]).all() and torch.isnan(buf[offset_floats + n:]).all()
+    ref, _ = oracle.forward(wl, x, **p)
+    check_close(out.cpu().numpy(), ref, f"upsample fused, output {offset_floats} floats past a line")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("offset_floats", [4, 8, 20])
 def test_fused_output_off_line_boundary(offset_floats, dtype):

@@ -935,7 +935,9 @@ void convt2d_gn_fused_kernel(FusedArgs a)
 // on a 128-byte line.  The input rows of a round (i0 .. i0 + SPS) sit in LDS
 // slots 0 .. SPS, refilled from registers loaded three stashes ahead; the
 // statistics exchange, the bank and the line stores are the ones above, with
-// the merge at the end of step 2 and the previous unit stored in step 3.
+// the merge at the end of step 1 and two of the previous unit's steps stored
+// in each of steps 2 and 3 (measured: all four in step 3 0.85 ms, this 0.79;
+// a merge at the end of step 0 spins on the siblings, 0.97).
 constexpr int UW = 128;                      // input width
 constexpr int UWO = 2 * UW;                  // output row
 constexpr int URP = UW + 4;                  // ring row pitch: x at 0..127, zeros at 128..131
@@ -1090,8 +1092,8 @@ void upsample2_gn_fused_kernel(FusedArgs a)
 #pragma unroll
         for (int k = 0; k < SPS; ++k) {
             if (k > 0) __syncthreads();  // row k + 1 in the ring
-            if (k == 2 && has_prev && wave == COEFWAVE) probe_issue(a, p_unit, lane, pr0, pr1);
-            if (k == 3 && has_prev) {
+            if (k == 1 && has_prev && wave == COEFWAVE) probe_issue(a, p_unit, lane, pr0, pr1);
+            if (k == 2 && has_prev) {
                 psc = coefs[2 * wave];
                 psh = coefs[2 * wave + 1];
             }
@@ -1131,19 +1133,21 @@ void upsample2_gn_fused_kernel(FusedArgs a)
                 *reinterpret_cast<v4f *>(bp) = e0;
                 *reinterpret_cast<v4f *>(bp + UWO) = e1;
             }
-            // ---- the previous unit, in the step after the merge: steps 0..2 were
-            // gathered at the ends of steps 0..2 (each iteration's epilogue
+            // ---- the previous unit, in the two steps after the merge: steps 0..2
+            // were gathered at the ends of steps 0..2 (each iteration's epilogue
             // rewrites the slot of the previous unit's step k - 1); stores are
             // issued on every path (masked past the buffer) so that the memory
             // waits the compiler places count the same stores everywhere
-            if (k == SPS - 1) {
+            if (k == 2) {
                 emit_step(0, pyr, pcu, has_prev, held0);
                 emit_step(1, pyr, pcu, has_prev, held1);
+            }
+            if (k == 3) {
                 emit_step(2, pyr, pcu, has_prev, held2);
                 gather_step(r - 1, 3, pcu, held0);
                 emit_step(3, pyr, pcu, has_prev, held0);
             }
-            if (k == 2 && has_prev && wave == COEFWAVE) {
+            if (k == 1 && has_prev && wave == COEFWAVE) {
                 const Coef cw = probe_finish(a, p_unit, lane, p_gb, pr0, pr1);
                 if (c16 == 0) {
                     coefs[4 * q] = cw.sc0; coefs[4 * q + 1] = cw.sh0;

@@ -216,16 +216,17 @@ cnf_status cnf_forward_timed(const cnf_plan *plan,
 /* Outcome of the last cnf_forward (or cnf_forward_timed) that ran `plan` on
  * this workspace.  Waits for `stream` (hipStreamSynchronize), then reads the
  * status word that call left in the workspace.  Only the single-write
- * grouped ConvTranspose2d + GroupNorm kernel (page "Kimi-K2.6__l2_p19")
- * waits across workgroups: its workgroups exchange per-slice GroupNorm
- * statistics and each wait is bounded.  If a wait gave up (for example
+ * grouped ConvTranspose2d + GroupNorm kernels (page "Kimi-K2.6__l2_p19": the
+ * stride-1 layer and its stride-2 upsampling form) wait across workgroups:
+ * their workgroups exchange per-slice GroupNorm statistics and each wait is
+ * bounded.  If a wait gave up (for example
  * because other work on the device kept a sibling workgroup from running),
  * the affected (sample, group) units of that call's output hold NaN, never
  * values normalised with partial statistics, and this returns
  * CNF_ERR_WAIT_TIMEOUT.  Every other plan returns CNF_OK once the stream
  * is idle.  CNF_ERR_WORKSPACE / CNF_ERR_ALIGNMENT as for cnf_forward.
  *
- * Test knobs of that kernel, read from the environment by cnf_plan_create
+ * Test knobs of those kernels, read from the environment by cnf_plan_create
  * (unset means off): CNF_TEST_FUSED_SPIN_LIMIT=k (give up after k polls),
  * CNF_TEST_FUSED_NEVER_READY=1 (each wait also needs a word nothing writes,
  * so every wait gives up after its polls and the kernel still ends),

@@ -29,6 +29,9 @@ Workloads (shapes and options as the four source pages state their problems):
   * conv2d_in_div_n128_bf16, convt2d_gelu_gn_n128_bf16
                           the l2_p17 and l2_p19 problems with x and w in bf16
                           (fp32 accumulation and epilogue).
+  * convt2d_gelu_gn_n128_bf16x3
+                          the l2_p19 problem in fp32, its contraction on
+                          three bf16 pieces of each fp32 operand (f32_math).
   * convt2d_s2_gelu_gn_n128
                           l2_p19's chain as an upsampling layer:
                           ConvTranspose2d 64->64 k3 stride 2 padding 1
@@ -60,7 +63,7 @@ _TID_X, _TID_W, _TID_B, _TID_GAMMA, _TID_BETA = 1, 2, 3, 4, 5
 _BASE = dict(ndim=2, kind="conv", groups=1, has_bias=1, act="none", norm="none",
              num_groups=1, eps=1e-5, affine=0, divide_by=1.0, reduce="none",
              pool_kernel=0, pool_repeats=0, want_argmax=0, stride=1, padding=0, dilation=1,
-             output_padding=0, dtype="f32")
+             output_padding=0, dtype="f32", f32_math="native")
 
 
 def _wl(**kw):
@@ -105,6 +108,10 @@ WORKLOADS = {
 WORKLOADS["conv2d_in_div_n128_bf16"] = dict(WORKLOADS["conv2d_in_div_n128"], id=9, dtype="bf16")
 WORKLOADS["convt2d_gelu_gn_n128_bf16"] = dict(WORKLOADS["convt2d_gelu_gn_n128"], id=10,
                                               dtype="bf16")
+# The l2_p19 problem in fp32 with the contraction on three bf16 pieces of each
+# operand (fp32 accuracy; the library's f32_math option).
+WORKLOADS["convt2d_gelu_gn_n128_bf16x3"] = dict(WORKLOADS["convt2d_gelu_gn_n128"], id=11,
+                                                f32_math="bf16x3")
 
 # The workloads the pages state (the others vary their geometry or precision).
 PAGE_WORKLOADS = [n for n in WORKLOADS if WORKLOADS[n]["id"] <= 6]

@@ -21,7 +21,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 # CNF_LIB_PATH selects another build of the library (the host-ASan one, say)
 LIB_PATH = os.environ.get("CNF_LIB_PATH") or os.path.join(_HERE, "libcnf.so")
 
-CNF_ABI_VERSION = 4
+CNF_ABI_VERSION = 5
 
 # cnf_status
 CNF_OK = 0
@@ -42,6 +42,7 @@ ACT = {"none": 0, "hardswish": 1, "gelu": 2, "softmax": 3, "gelu_tanh": 4}
 NORM = {"none": 0, "group": 1, "instance": 2}
 REDUCE = {"none": 0, "mean": 1, "maxpool": 2}
 DTYPE = {"f32": 0, "bf16": 1, "f16": 2}
+F32_MATH = {"native": 0, "bf16x3": 1}
 
 EXPORTED = ("cnf_plan_create", "cnf_plan_output_shape", "cnf_plan_workspace_size",
             "cnf_forward", "cnf_plan_destroy", "cnf_status_string", "cnf_plan_describe",
@@ -75,6 +76,7 @@ class cnf_desc(ctypes.Structure):
         ("dilation", ctypes.c_int32),
         ("output_padding", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
+        ("f32_math", ctypes.c_int32),
     ]
 
 
@@ -252,6 +254,7 @@ def make_desc(wl: dict, N: int | None = None) -> cnf_desc:
     d.stride, d.padding = wl.get("stride", 1), wl.get("padding", 0)
     d.dilation, d.output_padding = wl.get("dilation", 1), wl.get("output_padding", 0)
     d.dtype = DTYPE[wl.get("dtype", "f32")]
+    d.f32_math = F32_MATH[wl.get("f32_math", "native")]
     return d
 
 

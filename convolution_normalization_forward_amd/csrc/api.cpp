@@ -59,6 +59,14 @@ struct cnf_plan {
     cnf::LaunchHooks knobs;  // test knobs read from the environment at creation
 };
 
+namespace {
+// fp32 x and w contracted as bf16 pieces: asked for, and the plan's kernel has that form
+bool split_f32(const cnf_plan &p)
+{
+    return p.family == FAM_CONVT_FUSED && p.d.dtype == CNF_DTYPE_F32 && p.d.f32_math == CNF_F32_BF16X3;
+}
+}  // namespace
+
 namespace cnf {
 
 namespace {
@@ -185,6 +193,7 @@ cnf_status cnf_plan_create(const cnf_desc *desc, cnf_plan **plan)
     if (d.kind == CNF_CONV && d.output_padding != 0) return CNF_ERR_INVALID_DESC;
     if (d.dtype != CNF_DTYPE_F32 && d.dtype != CNF_DTYPE_BF16 && d.dtype != CNF_DTYPE_F16)
         return CNF_ERR_INVALID_DESC;
+    if (d.f32_math != CNF_F32_NATIVE && d.f32_math != CNF_F32_BF16X3) return CNF_ERR_INVALID_DESC;
     if (d.kind == CNF_CONV_TRANSPOSE &&
         d.output_padding >= (d.stride > d.dilation ? d.stride : d.dilation))
         return CNF_ERR_INVALID_DESC;
@@ -399,13 +408,13 @@ cnf_status cnf_plan_describe(const cnf_plan *plan, char *buf, size_t len)
     if (len == 0) return CNF_OK;
     const cnf_desc &d = plan->d;
     std::snprintf(buf, len, "family=%s N=%d C_in=%d C_out=%d in=%dx%dx%d k=%d groups=%d "
-                  "stride=%d padding=%d dilation=%d output_padding=%d dtype=%s out_rank=%d "
+                  "stride=%d padding=%d dilation=%d output_padding=%d dtype=%s%s out_rank=%d "
                   "workspace=%zu",
                   family_name(plan->family), d.N, d.C_in, d.C_out, d.in_dims[0], d.in_dims[1],
                   d.in_dims[2], d.kernel, d.groups, d.stride, d.padding, d.dilation,
                   d.output_padding,
                   d.dtype == CNF_DTYPE_BF16 ? "bf16" : d.dtype == CNF_DTYPE_F16 ? "f16" : "f32",
-                  plan->rank, plan->workspace);
+                  split_f32(*plan) ? " contraction=bf16x3" : "", plan->rank, plan->workspace);
     return CNF_OK;
 }
 
@@ -502,7 +511,9 @@ cnf_status forward_impl(const cnf_plan *plan, const void *xv, const void *wv, co
             a.flag = flag;
             hipLaunchKernelGGL(clear_word_kernel, dim3(1), dim3(1), 0, st, flag);
             if ((e = hipGetLastError()) != hipSuccess) break;
+            if (split_f32(*plan)) a.dtype = 3;  // the kernel's fp32-on-bf16-pieces form
             e = cnf::launch_convt2d_fused(a, st);
+            a.dtype = (int)d.dtype;
             if (e == hipErrorCooperativeLaunchTooLarge) (void)hipGetLastError();
         }
         if (e == hipErrorCooperativeLaunchTooLarge && d.dtype != CNF_DTYPE_F32)

@@ -187,6 +187,55 @@ __device__ __forceinline__ v4f mfma16x32(v4u a, v4u b, v4f c)
                                                       __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 values -> one word of two bf16 (round to nearest even, low half first).
+__device__ __forceinline__ unsigned pack_bf16(float lo, float hi)
+{
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(v2f{lo, hi}, bf16x2));
+}
+
+// Three bf16 pieces of each of two fp32 values, v = p1 + p2 + p3 exactly:
+// p1 = bf16(v) leaves a remainder r = v - p1 that is exact (Sterbenz) and
+// at most 2^-9 |v| with at most 16 significant bits; p2 = bf16(r) leaves at
+// most 8 bits, which p3 holds exactly.  Words w1, w2, w3 hold the pieces of
+// (lo, hi).  (Exponents below 2^-103 would make p3 subnormal.)
+struct Pieces {
+    unsigned w1, w2, w3;
+};
+__device__ __forceinline__ Pieces split3(float lo, float hi)
+{
+    Pieces p;
+    p.w1 = pack_bf16(lo, hi);
+    const float rl = lo - __builtin_bit_cast(float, p.w1 << 16),
+                rh = hi - __builtin_bit_cast(float, p.w1 & 0xffff0000u);
+    p.w2 = pack_bf16(rl, rh);
+    const float sl = rl - __builtin_bit_cast(float, p.w2 << 16),
+                sh = rh - __builtin_bit_cast(float, p.w2 & 0xffff0000u);
+    p.w3 = pack_bf16(sl, sh);
+    return p;
+}
+
+__device__ __forceinline__ void put_pieces(v4u (&dst)[3], int d, const Pieces &p)
+{
+    dst[0][d] = p.w1;
+    dst[1][d] = p.w2;
+    dst[2][d] = p.w3;
+}
+
+// The 16-bit B operand of input row m from the fp32 ring, as three pieces:
+// p points at channel 2q, column 2 c16 - 2 of the lane's tile; words 0, 1
+// take that channel's four columns, words 2, 3 channel 2q + 1's.
+__device__ __forceinline__ void split_row(v4u (&xp)[4][3], int m, const float *p)
+{
+    const v2f f0 = *reinterpret_cast<const v2f *>(p), f1 = *reinterpret_cast<const v2f *>(p + 2);
+    const v2f g0 = *reinterpret_cast<const v2f *>(p + RP), g1 = *reinterpret_cast<const v2f *>(p + RP + 2);
+    put_pieces(xp[m], 0, split3(f0[0], f0[1]));
+    put_pieces(xp[m], 1, split3(f1[0], f1[1]));
+    put_pieces(xp[m], 2, split3(g0[0], g0[1]));
+    put_pieces(xp[m], 3, split3(g1[0], g1[1]));
+}
+
 // Unit (n, g) = n G + g owns channels n C + g CG .. + CG - 1, and C = G CG, so
 // its first channel is unit * CG: no division by G.
 template <int DT>
@@ -515,14 +564,17 @@ template <int ACT, int DT>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void convt2d_gn_fused_kernel(FusedArgs a)
 {
-    using PF = typename Stage<DT>::T;
+    // DT 3: x and w are fp32 in memory (load type LT = 0) and the contraction
+    // runs on bf16 pieces of them (split3) in the 16-bit tile mapping
+    constexpr int LT = DT == 3 ? 0 : DT;
+    using PF = typename Stage<LT>::T;
     constexpr int NB = NBANK;
     // iteration at whose end the previous unit's coefficients are merged: one
     // step later with 16-bit inputs, whose steps are short, so that the sibling
     // slices have published (measured: 0.90 -> 0.85 ms; fp32, whose SIMDs are
     // MFMA-bound, loses 3% to the extra registers and the single store burst)
-    constexpr int MERGE = DT == 0 ? 1 : 2;
-    __shared__ __align__(16) float ring[DT == 0 ? NSLOT * PAIR_FLOATS : NSLOT * PAIR16_WORDS];
+    constexpr int MERGE = DT == 1 || DT == 2 ? 2 : 1;
+    __shared__ __align__(16) float ring[LT == 0 ? NSLOT * PAIR_FLOATS : NSLOT * PAIR16_WORDS];
     __shared__ float red[NWAVE * 4 * 3];  // [wave][row of 16 lanes] slice triples
     __shared__ v4f spart[2 * 4 * 64];     // [tile][chunk][lane] single-tile partial sums
     __shared__ float coefs[CG * 2];       // the previous unit's (scale, shift) per channel
@@ -550,7 +602,7 @@ void convt2d_gn_fused_kernel(FusedArgs a)
     }
 
     for (int e = tid; e < NSLOT * 2 * CG; e += THREADS) {  // pad columns, never overwritten
-        if constexpr (DT == 0) {
+        if constexpr (LT == 0) {
             float *row = ring + e * RP;
 #pragma unroll
             for (int c = 0; c < PADL; ++c) row[c] = 0.f;
@@ -561,11 +613,13 @@ void convt2d_gn_fused_kernel(FusedArgs a)
         }
     }
 
-    const unsigned loff = (unsigned)(wave * H * W + 4 * lane) * ESZ<DT>;  // pair loads
+    const unsigned loff = (unsigned)(wave * H * W + 4 * lane) * ESZ<LT>;  // pair loads
     const int lb = PADL + 32 * wave + 2 * c16 + 1 - q;                // B operand column
     // 16-bit B operand: word of columns 2 c16 - 2, -1 of channel 2q in a ring row
     const int lb16 = 2 * q * (RP16 / 2) + (PADL - 2) / 2 + 16 * wave + c16;
     const int bo = 2 * q * CP + 32 * wave + 2 * c16;                   // bank position of the lane's pair
+    // fp32 ring float of channel 2q, column 32 wave + 2 c16 - 2 (DT 3's B operand)
+    const int lbe = 2 * q * RP + PADL - 2 + 32 * wave + 2 * c16;
     // bank slot of step k of round rho (steps numbered over rounds; rho = -1,
     // the round before the first, when a store is issued with nothing to store)
     auto slot = [&](int rho, int k) { return bank + BPAD + (((rho * SPS + k) % NB + NB) % NB) * SLOT_FLOATS; };
@@ -575,18 +629,19 @@ void convt2d_gn_fused_kernel(FusedArgs a)
     int base = 0;  // ring slot of the current round's pair 0
     {
         const int k0 = s_base * SPS;
-        const __amdgpu_buffer_rsrc_t xr = x_rsrc<DT>(a, ulocal);
+        const __amdgpu_buffer_rsrc_t xr = x_rsrc<LT>(a, ulocal);
         PF p0[2], p1[2];
-        load_pair<DT>(p0, xr, H, 2 * k0 - 2, loff);
-        load_pair<DT>(p1, xr, H, 2 * k0, loff);
-        stash_pair<DT>(ring, 0, p0, wave, lane);
-        stash_pair<DT>(ring, 1, p1, wave, lane);
+        load_pair<LT>(p0, xr, H, 2 * k0 - 2, loff);
+        load_pair<LT>(p1, xr, H, 2 * k0, loff);
+        stash_pair<LT>(ring, 0, p0, wave, lane);
+        stash_pair<LT>(ring, 1, p1, wave, lane);
 #pragma unroll
-        for (int p = 0; p < 3; ++p) load_pair<DT>(pf[p], xr, H, 2 * (k0 + p + 2) - 2, loff);
+        for (int p = 0; p < 3; ++p) load_pair<LT>(pf[p], xr, H, 2 * (k0 + p + 2) - 2, loff);
     }
 
     float wreg[CG * KS];
     v4u a16[KS];  // 16-bit A operands, one per kh
+    v4u ap[KS][3];  // DT 3: bf16 pieces of the A operands, [kh][piece]
     float wsub[SCH];  // this wave's single-tile chunk of the weights
     v4f bias4 = v4f{0.f, 0.f, 0.f, 0.f};  // accumulator start: bias of channels 2q, 2q, 2q+1, 2q+1
     v4f gb = v4f{1.f, 0.f, 1.f, 0.f}, p_gb = gb;
@@ -662,11 +717,11 @@ void convt2d_gn_fused_kernel(FusedArgs a)
         const int sg = (s_base + r) % S;
         const int k0 = sg * SPS;
         const int ext = sg < a.NEXT ? sg : -1;           // extra row tile e: tail step e/16, tile e%16
-        const __amdgpu_buffer_rsrc_t xr = x_rsrc<DT>(a, unit);
+        const __amdgpu_buffer_rsrc_t xr = x_rsrc<LT>(a, unit);
         const int nunit = unit + a.upr;
         const bool nhas = nunit < U;
         const int nk0 = ((sg + 1) % S) * SPS;
-        const __amdgpu_buffer_rsrc_t nxr = x_rsrc<DT>(a, nhas ? nunit : unit);
+        const __amdgpu_buffer_rsrc_t nxr = x_rsrc<LT>(a, nhas ? nunit : unit);
         const __amdgpu_buffer_rsrc_t pyr = y_rsrc_u(a, has_prev ? p_unit : unit, plane);
         const unsigned pcu = has_prev ? line_phase(p_unit, p_k0) : 0u;
 
@@ -675,8 +730,8 @@ void convt2d_gn_fused_kernel(FusedArgs a)
         if (g != wgroup) {
             wgroup = g;
             const __amdgpu_buffer_rsrc_t wr =
-                make_rsrc(static_cast<const char *>(a.wt) + (size_t)g * CG * CG * KS * KS * ESZ<DT>,
-                          CG * CG * KS * KS * ESZ<DT>);
+                make_rsrc(static_cast<const char *>(a.wt) + (size_t)g * CG * CG * KS * KS * ESZ<LT>,
+                          CG * CG * KS * KS * ESZ<LT>);
             const int co = c16 >> 1, t = c16 & 1;
             const int kw = q + t - 1;
             const bool kok = kw >= 0 && kw < KS;
@@ -684,8 +739,24 @@ void convt2d_gn_fused_kernel(FusedArgs a)
 #pragma unroll
                 for (int s = 0; s < CG * KS; ++s) {
                     const int ci = s / KS, kh = s % KS;
-                    const float v = eload1<DT>(wr, (unsigned)(((ci * CG + co) * KS + kh) * KS + (kok ? kw : 0)) * ESZ<DT>);
+                    const float v = eload1<LT>(wr, (unsigned)(((ci * CG + co) * KS + kh) * KS + (kok ? kw : 0)) * ESZ<LT>);
                     wreg[s] = kok ? v : 0.0f;
+                }
+            } else if constexpr (DT == 3) {
+                // the 16-bit mapping below, on three bf16 pieces of each fp32 weight
+#pragma unroll
+                for (int kh = 0; kh < KS; ++kh) {
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        float v[2];
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+                            const int e = 2 * d + h, ci = 2 * q + e / 4, kw16 = 2 - e % 4 + t;
+                            const bool ok = kw16 >= 0 && kw16 < KS;
+                            v[h] = buf_load1(wr, ok ? (unsigned)((((ci * CG + co) * KS + kh) * KS + kw16) * 4) : OOB);
+                        }
+                        put_pieces(ap[kh], d, split3(v[0], v[1]));
+                    }
                 }
             } else {
                 // A[(co, t)][(ci, v')] = w[ci][co][kh][2 - v' + t], ci = 2q + e / 4, v' = e % 4;
@@ -710,7 +781,7 @@ void convt2d_gn_fused_kernel(FusedArgs a)
 #pragma unroll
             for (int j = 0; j < SCH; ++j) {
                 const int ci = 2 * (wave & 3) + j / KS, kh = j % KS;
-                const float v = eload1<DT>(wr, (unsigned)(((ci * CG + co) * KS + kh) * KS + (kok ? kw : 0)) * ESZ<DT>);
+                const float v = eload1<LT>(wr, (unsigned)(((ci * CG + co) * KS + kh) * KS + (kok ? kw : 0)) * ESZ<LT>);
                 wsub[j] = kok ? v : 0.0f;
             }
             const int c0 = g * CG + 2 * q;
@@ -726,7 +797,7 @@ void convt2d_gn_fused_kernel(FusedArgs a)
         const int crow = col_row(k0, sg);
         const bool has_t = tsel == 0 ? ext >= 0 : crow < Ho;
         float sb[SCH];
-        single_load<DT>(sb, xr, H, chunk, has_t, tsel == 0 ? ext_row : crow,
+        single_load<LT>(sb, xr, H, chunk, has_t, tsel == 0 ? ext_row : crow,
                         tsel == 0 ? 32 * (ext & 7) + 2 * c16 + 1 - q : 2 * (W / 2) + 1 - q);
 
         // ---- steps.  Iteration k runs the MFMAs of step k and the activation, sums
@@ -736,6 +807,7 @@ void convt2d_gn_fused_kernel(FusedArgs a)
         float s1 = 0.f, s2 = 0.f;
         int cnt = 0;
         unsigned long long pr0 = 0ull, pr1 = 0ull;
+        v4u xp[4][3];  // DT 3: bf16 pieces of the B operands, [input row m][piece]
         v4f acc0 = v4f{0.f, 0.f, 0.f, 0.f}, acc1 = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int k = 0; k < SPS; ++k) {
@@ -753,6 +825,23 @@ void convt2d_gn_fused_kernel(FusedArgs a)
                     xb[ci][2] = rB[ci * RP];
                     xb[ci][3] = rB[(CG + ci) * RP];
                 }
+            } else if constexpr (DT == 3) {
+                // rows m = 0, 1 are the last step's rows 2, 3 (split then), except at a
+                // round's first step
+                const float *rA = ring + ((base + k) % NSLOT) * PAIR_FLOATS + lbe;
+                const float *rB = ring + ((base + k + 1) % NSLOT) * PAIR_FLOATS + lbe;
+                if (k == 0) {
+                    split_row(xp, 0, rA);
+                    split_row(xp, 1, rA + CG * RP);
+                } else {
+#pragma unroll
+                    for (int pc3 = 0; pc3 < 3; ++pc3) {
+                        xp[0][pc3] = xp[2][pc3];
+                        xp[1][pc3] = xp[3][pc3];
+                    }
+                }
+                split_row(xp, 2, rB);
+                split_row(xp, 3, rB + CG * RP);
             } else {
                 const unsigned *r16 = reinterpret_cast<const unsigned *>(ring);
 #pragma unroll
@@ -818,6 +907,18 @@ void convt2d_gn_fused_kernel(FusedArgs a)
                     n0 = mfma_16x16x4(wreg[ci * KS + 2], xb[ci][0], n0);
                     n1 = mfma_16x16x4(wreg[ci * KS + 2], xb[ci][1], n1);
                 }
+            } else if constexpr (DT == 3) {
+                // six of the nine piece products, smallest first: the three dropped
+                // ones are below 2^-26 of |w x| together
+                constexpr int PA[6] = {2, 1, 0, 1, 0, 0}, PB[6] = {0, 1, 2, 0, 1, 0};
+#pragma unroll
+                for (int s = 0; s < 6; ++s) {
+#pragma unroll
+                    for (int kh = 0; kh < KS; ++kh) {
+                        n0 = mfma16x32<1>(ap[kh][PA[s]], xp[2 - kh][PB[s]], n0);
+                        n1 = mfma16x32<1>(ap[kh][PA[s]], xp[3 - kh][PB[s]], n1);
+                    }
+                }
             } else {
                 n0 = mfma16x32<DT>(a16[0], xb16[2], n0);
                 n1 = mfma16x32<DT>(a16[0], xb16[3], n1);
@@ -848,15 +949,15 @@ void convt2d_gn_fused_kernel(FusedArgs a)
 
             // ---- ring stashes at the end of step k, each followed by its loads
             if (k <= SPS - 2) {
-                stash_pair<DT>(ring, (base + k + 2) % NSLOT, pf[k % 3], wave, lane);
-                issue_pos<DT>(k, pf[k % 3], k0, xr, nhas, nk0, nxr, H, loff);
+                stash_pair<LT>(ring, (base + k + 2) % NSLOT, pf[k % 3], wave, lane);
+                issue_pos<LT>(k, pf[k % 3], k0, xr, nhas, nk0, nxr, H, loff);
             } else {
-                stash_pair<DT>(ring, (base + SPS + 1) % NSLOT, pf[(SPS - 1) % 3], wave, lane);
-                issue_pos<DT>(SPS - 1, pf[(SPS - 1) % 3], k0, xr, nhas, nk0, nxr, H, loff);
-                stash_pair<DT>(ring, (base + SPS + 2) % NSLOT, pf[SPS % 3], wave, lane);
-                issue_pos<DT>(SPS, pf[SPS % 3], k0, xr, nhas, nk0, nxr, H, loff);
+                stash_pair<LT>(ring, (base + SPS + 1) % NSLOT, pf[(SPS - 1) % 3], wave, lane);
+                issue_pos<LT>(SPS - 1, pf[(SPS - 1) % 3], k0, xr, nhas, nk0, nxr, H, loff);
+                stash_pair<LT>(ring, (base + SPS + 2) % NSLOT, pf[SPS % 3], wave, lane);
+                issue_pos<LT>(SPS, pf[SPS % 3], k0, xr, nhas, nk0, nxr, H, loff);
 #pragma unroll
-                for (int p = SPS + 1; p < NPOS; ++p) issue_pos<DT>(p, pf[p % 3], k0, xr, nhas, nk0, nxr, H, loff);
+                for (int p = SPS + 1; p < NPOS; ++p) issue_pos<LT>(p, pf[p % 3], k0, xr, nhas, nk0, nxr, H, loff);
             }
             // the previous unit's steps whose slots the next iterations' epilogues
             // rewrite (0 in iteration 2, 1 in iteration 3, 2 after the loop) and
@@ -1236,7 +1337,7 @@ bool geometry(int Ho, Geometry &g)
 // Resident workgroups per CU of each instantiation and the CU count, cached per
 // device; concurrent first calls store the same values.
 struct Occupancy {
-    std::atomic<int> blocks_per_cu[5][3];  // [activation][input type]
+    std::atomic<int> blocks_per_cu[5][4];  // [activation][input type / contraction]
     std::atomic<int> cus;
 };
 
@@ -1386,6 +1487,7 @@ hipError_t launch_convt2d_fused(const ConvT2dArgs &a, hipStream_t st)
     case 0: return launch_dt<0>(a, st);
     case 1: return launch_dt<1>(a, st);
     case 2: return launch_dt<2>(a, st);
+    case 3: return launch_dt<3>(a, st);
     default: return hipErrorInvalidValue;
     }
 }

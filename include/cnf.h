@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define CNF_ABI_VERSION 4
+#define CNF_ABI_VERSION 5
 
 typedef enum {
     CNF_OK = 0,
@@ -89,6 +89,22 @@ typedef enum { CNF_CONV = 0, CNF_CONV_TRANSPOSE = 1 } cnf_conv_kind;
  * name tensor-core input precisions only as what a vendor library would
  * pick. */
 typedef enum { CNF_DTYPE_F32 = 0, CNF_DTYPE_BF16 = 1, CNF_DTYPE_F16 = 2 } cnf_dtype;
+
+/* How fp32 x and w are contracted (ignored for 16-bit inputs).
+ *   NATIVE  products of fp32 values on the fp32 matrix (or vector) units.
+ *   BF16X3  each fp32 operand split into three bf16 pieces, v = v1 + v2 + v3
+ *           exactly (v1 = bf16(v), v2 = bf16(v - v1), v3 = v - v1 - v2), and
+ *           the six leading piece products (w1x1, w1x2, w2x1, w1x3, w2x2,
+ *           w3x1) summed on the bf16 matrix instruction with fp32
+ *           accumulation.  Each piece product is exact in fp32; the three
+ *           dropped ones are below 2^-26 |w x| together, under the 2^-24
+ *           relative rounding of one fp32 product, so the result has fp32
+ *           accuracy (values below 2^-103 in magnitude lose their last
+ *           piece to bf16 subnormals).  The 16-bit matrix instruction runs
+ *           beside the vector unit's epilogue work, where fp32 products do
+ *           not.  Only the single-write grouped transposed-conv kernel has
+ *           this form; every other kernel contracts fp32 natively. */
+typedef enum { CNF_F32_NATIVE = 0, CNF_F32_BF16X3 = 1 } cnf_f32_math;
 
 typedef enum {
     CNF_ACT_NONE = 0,
@@ -142,6 +158,7 @@ typedef struct {
     int32_t output_padding;/* transposed conv: 0 <= output_padding < max(stride,
                               dilation), extra extent at the high end; conv: 0 */
     int32_t dtype;         /* cnf_dtype of x and w (added in ABI version 3) */
+    int32_t f32_math;      /* cnf_f32_math (added in ABI version 5) */
 } cnf_desc;
 
 typedef struct cnf_plan cnf_plan;
@@ -151,7 +168,7 @@ typedef struct cnf_plan cnf_plan;
  * Checks: abi_version; ndim in {2,3}; N >= 0; C_in, C_out, kernel >= 1;
  * groups divides C_in and C_out; num_groups divides C_out (GroupNorm);
  * stride, dilation >= 1; padding >= 0; output_padding as stated above;
- * dtype in range;
+ * dtype and f32_math in range;
  * every conv output extent >= 1; pooled extents >= 1; eps > 0 when a norm is
  * requested; divide_by != 0; enum fields in range.  Shapes the specialised
  * kernel families cover take them; every other valid descriptor takes the

@@ -60,6 +60,7 @@ def test_every_workload_plans_with_expected_shape(name):
         "convt2d_s2_gelu_gn_n128": (128, 64, 256, 256),
         "conv2d_in_div_n128_bf16": (128, 128, 126, 126),
         "convt2d_gelu_gn_n128_bf16": (128, 64, 258, 258),
+        "convt2d_gelu_gn_n128_bf16x3": (128, 64, 258, 258),
     }[name]
     assert plan.out_shape == exp
     assert "family=" in plan.describe()
@@ -279,6 +280,30 @@ def test_sixteen_bit_inputs_plan_on_the_general_family(monkeypatch):
     assert p.workspace_bytes == _align(wp) + _align(128 * 128 * T * 16) + _align(128 * 128 * 8)
 
 
+def test_f32_math_option():
+    """f32_math: NATIVE or BF16X3, anything else is an invalid descriptor; the
+    split form is named only where the plan's kernel has it (the single-write
+    grouped transposed conv with fp32 inputs), every other plan contracts fp32
+    natively and says nothing."""
+    d = _desc("convt2d_gelu_gn_n128")
+    d.f32_math = 2
+    assert cnf.cnf_plan_create_status(d) == cnf.CNF_ERR_INVALID_DESC
+    d.f32_math = -1
+    assert cnf.cnf_plan_create_status(d) == cnf.CNF_ERR_INVALID_DESC
+    split = cnf.Plan(_desc("convt2d_gelu_gn_n128", f32_math="bf16x3"))
+    native = cnf.Plan(_desc("convt2d_gelu_gn_n128"))
+    assert "family=convt2d_grouped8_gn_fused" in split.describe()
+    assert "contraction=bf16x3" in split.describe()
+    assert "contraction=" not in native.describe()
+    # the same kernel and workspace either way
+    assert split.workspace_bytes == native.workspace_bytes
+    for name, over in (("conv2d_in_div_n128", {}), ("convt2d_s2_gelu_gn_n128", {}),
+                       ("convt2d_gelu_gn_n128", dict(dtype="bf16")),
+                       ("convt2d_gelu_gn_n128", dict(in_dims=(1, 64, 200)))):
+        p = cnf.Plan(_desc(name, f32_math="bf16x3", **over))
+        assert "contraction=" not in p.describe(), (name, over)
+
+
 def test_family_routing():
     # the page configurations keep their specialised families ...
     fams = {n: cnf.Plan(_desc(n)).describe().split()[0] for n in cnf_inputs.PAGE_WORKLOADS}
@@ -288,6 +313,7 @@ def test_family_routing():
     # the implicit GEMM, the 16-bit conv on the 16-bit implicit GEMM, the rest
     # on the general family
     special = {"convt2d_gelu_gn_n128_bf16": "family=convt2d_grouped8_gn_fused",
+               "convt2d_gelu_gn_n128_bf16x3": "family=convt2d_grouped8_gn_fused",
                "convt2d_s2_gelu_gn_n128": "family=convt2d_s2_grouped8_gn_fused",
                "conv2d_s2p1_in_div_n128": "family=conv2d_igemm",
                "conv2d_in_div_n128_bf16": "family=conv2d_igemm16"}

@@ -176,6 +176,7 @@ FULL_SUBSET = {
     "convt2d_s2_gelu_gn_n128": 4 + 2,
     "conv2d_in_div_n128_bf16": 4 + 2,
     "convt2d_gelu_gn_n128_bf16": 4 + 2,
+    "convt2d_gelu_gn_n128_bf16x3": 8 + 2,
 }
 
 
@@ -277,6 +278,49 @@ def test_sixteen_bit_single_write_every_element(over, dtype):
     _say(f"    max_abs_err={err:.3e}")
 
 
+# fp32 x and w through the same kernel with the contraction on three bf16
+# pieces of each operand (f32_math bf16x3): the fp32 tolerance, every shape
+# above.
+@pytest.mark.parametrize("over", SIXTEEN_BIT_FUSED)
+def test_split_f32_single_write_every_element(over):
+    wl = cnf_inputs.workload("convt2d_gelu_gn_n128", f32_math="bf16x3", **over)
+    _say(f"[parity-bf16x3] {over}")
+    x = cnf_inputs.gen_x(wl)
+    p = cnf_inputs.gen_params(wl)
+    plan, out, _ = run_gpu(wl, x, p)
+    assert "fused" in plan.describe() and "contraction=bf16x3" in plan.describe(), plan.describe()
+    ref, _ = oracle.forward(wl, x, **p)
+    err = check_close(out.cpu().numpy(), ref, f"fused bf16x3 {over}")
+    _say(f"    max_abs_err={err:.3e}")
+
+
+@pytest.mark.parametrize("spread", [0.0, 3.0])
+def test_split_f32_as_accurate_as_native(spread):
+    # The bf16x3 contraction carries every bit of each fp32 operand and drops
+    # only products below 2^-26 |w x|, so against the fp64 oracle it must be as
+    # accurate as the fp32 contraction: no activation (the conv and the
+    # statistics alone set the error), inputs N(0, 1) and, with spread 3,
+    # scaled by 10^U(-3, 3) element by element (every piece of the split in use
+    # at once).  Same inputs through both contractions.
+    import numpy as np
+    base = dict(N=2, in_dims=(1, 62, 256), act="none")
+    errs = {}
+    for fm in ("native", "bf16x3"):
+        wl = cnf_inputs.workload("convt2d_gelu_gn_n128", f32_math=fm, **base)
+        x = cnf_inputs.gen_x(wl)
+        if spread:
+            rng = np.random.default_rng(4242)
+            x = x * np.power(10.0, rng.uniform(-spread, spread, size=x.shape))
+            x = x.astype(np.float32).astype(np.float64)
+        p = cnf_inputs.gen_params(wl)
+        plan, out, _ = run_gpu(wl, x, p)
+        assert "fused" in plan.describe()
+        ref, _ = oracle.forward(wl, x, **p)
+        errs[fm] = check_close(out.cpu().numpy(), ref, f"{fm} spread {spread}")
+    _say(f"    max_abs_err native {errs['native']:.3e} bf16x3 {errs['bf16x3']:.3e}")
+    assert errs["bf16x3"] <= 2.0 * errs["native"] + 2e-7, errs
+
+
 # 16-bit x and w through the implicit GEMM on the 32x32x16 MFMA (unpadded
 # stride-1 Conv2d, W % 8 == 0, C_in % 16 == 0): ragged row and column tiles,
 # the last halo columns past the input, 64 and 128 output channels, several K
@@ -341,12 +385,13 @@ def test_fused_convt_wait_never_times_out():
     check_close(out.cpu().numpy(), ref, "fused convt repeated")
 
 
-def test_fused_convt_wait_timeout_is_reported(monkeypatch):
+@pytest.mark.parametrize("f32_math", ["native", "bf16x3"])
+def test_fused_convt_wait_timeout_is_reported(monkeypatch, f32_math):
     # a wait that cannot succeed (it also needs a word nothing writes) gives up
     # after a few polls: the kernel still ends, the units' outputs are NaN
     # (never normalised with partial statistics) and the caller is told
     import convolution_normalization_forward_amd as cnf
-    wl = cnf_inputs.workload("convt2d_gelu_gn_n128", N=2, in_dims=(1, 126, 256))
+    wl = cnf_inputs.workload("convt2d_gelu_gn_n128", N=2, in_dims=(1, 126, 256), f32_math=f32_math)
     x = cnf_inputs.gen_x(wl)
     p = cnf_inputs.gen_params(wl)
     monkeypatch.setenv("CNF_TEST_FUSED_NEVER_READY", "1")
@@ -368,6 +413,7 @@ def test_fused_convt_wait_timeout_is_reported(monkeypatch):
     (dict(N=2, in_dims=(1, 126, 256)), "f32"),
     (dict(N=1, in_dims=(1, 127, 256), act="gelu_tanh"), "f32"),
     (dict(N=2, in_dims=(1, 128, 256)), "bf16"),
+    (dict(N=2, in_dims=(1, 126, 256), f32_math="bf16x3"), "f32"),
 ])
 def test_fused_convt_forced_fallback(monkeypatch, over, dtype):
     # the dispatch a plan keeps for a grid that cannot be co-resident: the
@@ -392,6 +438,9 @@ def test_fused_convt_forced_fallback(monkeypatch, over, dtype):
     # 16-bit ring and A operands over many rounds, with and without a tail step
     dict(N=3, in_dims=(1, 126, 256), dtype="bf16"),
     dict(N=2, in_dims=(1, 127, 256), act="gelu_tanh", dtype="f16"),
+    # fp32 on bf16 pieces over many rounds
+    dict(N=3, in_dims=(1, 126, 256), f32_math="bf16x3"),
+    dict(N=2, in_dims=(1, 127, 256), act="hardswish", f32_math="bf16x3"),
 ])
 def test_fused_convt_many_rounds(monkeypatch, over):
     # two units per round, so a small batch runs many rounds: the slice
@@ -483,7 +532,7 @@ def test_upsample_output_off_line_boundary(offset_floats):
     check_close(out.cpu().numpy(), ref, f"upsample fused, output {offset_floats} floats past a line")
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f32:bf16x3"])
 @pytest.mark.parametrize("offset_floats", [4, 8, 20])
 def test_fused_output_off_line_boundary(offset_floats, dtype):
     # The single-write kernel stores whole 128-byte lines of the output as it
@@ -492,8 +541,10 @@ def test_fused_output_off_line_boundary(offset_floats, dtype):
     # boundary inside the rows; the floats just before and after the output
     # must stay untouched.  Odd output height: the last step holds one row.
     import convolution_normalization_forward_amd as cnf
-    wl = cnf_inputs.workload("convt2d_gelu_gn_n128", dtype=dtype, N=2, in_dims=(1, 127, 256))
-    _say(f"[off-line] offset {offset_floats} floats {dtype}")
+    dtype, _, fm = dtype.partition(":")
+    wl = cnf_inputs.workload("convt2d_gelu_gn_n128", dtype=dtype, N=2, in_dims=(1, 127, 256),
+                             f32_math=fm or "native")
+    _say(f"[off-line] offset {offset_floats} floats {dtype} {fm}")
     x = cnf_inputs.gen_x(wl)
     p = cnf_inputs.gen_params(wl)
     dev = "cuda:0"

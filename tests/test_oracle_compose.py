@@ -104,6 +104,8 @@ SMALL = {
     "conv2d_in_div_n128_bf16": dict(N=1, C_in=8, C_out=16, in_dims=(1, 12, 11)),
     "convt2d_gelu_gn_n128_bf16": dict(N=2, C_in=16, C_out=16, in_dims=(1, 9, 10), groups=8,
                                       num_groups=8),
+    "convt2d_gelu_gn_n128_bf16x3": dict(N=2, C_in=16, C_out=16, in_dims=(1, 9, 10), groups=8,
+                                        num_groups=8),
 }
 
 

@@ -266,6 +266,7 @@ def time_workload(name, steps, warmup, dev, flush=None, cold_reps=None):
         "frac_mfma_peak_own_dtype": fl / (ms * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS[wl.get("dtype", "f32")],
         "frac_hbm_peak_algorithmic": ab / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "dtype": wl.get("dtype", "f32"),
+        "f32_math": wl.get("f32_math", "native"),
         "dominant_kernel": kern,
         "bound": bound,
         "dominant_ms_mean": k_ms,

@@ -57,6 +57,15 @@
 // 2 c16 - 2 .. 2 c16 + 1 of each channel (v' = 3 - v).  A row tile then takes
 // 3 MFMAs instead of 24.  The single tiles widen to fp32 as they are loaded
 // (products of 16-bit values are exact in fp32 either way).
+//
+// DT 3: fp32 x and w contracted on bf16 pieces.  fp32 MFMAs and the
+// epilogue's vector work issue one after the other on a SIMD, bf16 MFMAs run
+// beside it, so this form keeps x and w fp32 (ring and loads as DT 0) and
+// splits each operand into three bf16 pieces, v = v1 + v2 + v3 exactly: the
+// weights once per group, a step's two new input rows as it reads them.  The
+// 16-bit tile mapping above then sums the six leading piece products per
+// kernel row (18 MFMAs per tile), smallest first; the three dropped ones are
+// below 2^-26 |w x|, under fp32's own product rounding.
 #include <atomic>
 
 #include "device.h"
@@ -796,9 +805,17 @@ void convt2d_gn_fused_kernel(FusedArgs a)
         const int tsel = wave >> 2, chunk = wave & 3;  // tile (0 extra, 1 column) and K chunk
         const int crow = col_row(k0, sg);
         const bool has_t = tsel == 0 ? ext >= 0 : crow < Ho;
+        // their loads: at the round top with 16-bit inputs, in iteration 1 with
+        // fp32 ones (off the round boundary, where all eight waves would issue
+        // these scattered loads at once; measured 1.20 -> 1.18 ms with bf16
+        // pieces, 0.85 -> 0.89 ms the other way with 16-bit inputs)
+        constexpr int SINGLE_AT = DT == 1 || DT == 2 ? -1 : 1;
         float sb[SCH];
-        single_load<LT>(sb, xr, H, chunk, has_t, tsel == 0 ? ext_row : crow,
-                        tsel == 0 ? 32 * (ext & 7) + 2 * c16 + 1 - q : 2 * (W / 2) + 1 - q);
+        auto load_single = [&]() {
+            single_load<LT>(sb, xr, H, chunk, has_t, tsel == 0 ? ext_row : crow,
+                            tsel == 0 ? 32 * (ext & 7) + 2 * c16 + 1 - q : 2 * (W / 2) + 1 - q);
+        };
+        if constexpr (SINGLE_AT < 0) load_single();
 
         // ---- steps.  Iteration k runs the MFMAs of step k and the activation, sums
         // and bank write of step k - 1 (before or after the MFMAs, by wave), then
@@ -851,6 +868,7 @@ void convt2d_gn_fused_kernel(FusedArgs a)
                     xb16[m] = v4u{rp[0], rp[1], rp[RP16 / 2], rp[RP16 / 2 + 1]};
                 }
             }
+            if (k == SINGLE_AT) load_single();
             if (k == MERGE && has_prev && wave == COEFWAVE) probe_issue(a, p_unit, lane, pr0, pr1);
             if (k == MERGE + 1 && has_prev) {
                 const float *cq = coefs + 4 * q;  // channels 2q, 2q+1, merged last step

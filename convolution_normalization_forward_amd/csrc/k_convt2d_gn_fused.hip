@@ -711,6 +711,10 @@ void convt2d_gn_fused_kernel(FusedArgs a)
             bank_put(slot(rho, c16 >> 1) + 2 * q * CP + (c16 & 1) * WO + W, prv_col);
     };
 
+    // the round's slice and group, stepped once per round (no division in the loop):
+    // slice (s_base + r) mod S, group (r upr + ulocal) mod G
+    int sg = s_base, g = ulocal % a.G;
+    const int g_step = a.upr % a.G;
     int r = 0;
     for (;; ++r) {
         const int unit = r * a.upr + ulocal;
@@ -723,19 +727,17 @@ void convt2d_gn_fused_kernel(FusedArgs a)
         if (has_prev && wave == PUBWAVE) publish(a, red, p_unit, p_sg, lane);
         if (has_prev) put_col(r - 1);
 
-        const int sg = (s_base + r) % S;
         const int k0 = sg * SPS;
         const int ext = sg < a.NEXT ? sg : -1;           // extra row tile e: tail step e/16, tile e%16
         const __amdgpu_buffer_rsrc_t xr = x_rsrc<LT>(a, unit);
         const int nunit = unit + a.upr;
         const bool nhas = nunit < U;
-        const int nk0 = ((sg + 1) % S) * SPS;
+        const int nk0 = (sg + 1 == S ? 0 : sg + 1) * SPS;
         const __amdgpu_buffer_rsrc_t nxr = x_rsrc<LT>(a, nhas ? nunit : unit);
         const __amdgpu_buffer_rsrc_t pyr = y_rsrc_u(a, has_prev ? p_unit : unit, plane);
         const unsigned pcu = has_prev ? line_phase(p_unit, p_k0) : 0u;
 
         // ---- weights (A operand), bias, gamma / beta of the unit's group
-        const int g = unit % a.G;
         if (g != wgroup) {
             wgroup = g;
             const __amdgpu_buffer_rsrc_t wr =
@@ -1012,6 +1014,9 @@ void convt2d_gn_fused_kernel(FusedArgs a)
         p_k0 = k0;
         p_ext = ext;
         base = (base + SPS + 1) % NSLOT;
+        sg = sg + 1 == S ? 0 : sg + 1;
+        g += g_step;
+        if (g >= a.G) g -= a.G;
     }
 
     // ---- the last unit: its triple was published above; wait, normalise, store
@@ -1172,6 +1177,8 @@ void upsample2_gn_fused_kernel(FusedArgs a)
     };
 
     int r = 0;
+    int sg = s_base, g = ulocal % a.G;  // stepped once per round, as above
+    const int g_step = a.upr % a.G;
     for (;; ++r) {
         const int unit = r * a.upr + ulocal;
         __syncthreads();  // rows 0, 1 in the ring; last round's ring readers done; red[] complete
@@ -1182,17 +1189,15 @@ void upsample2_gn_fused_kernel(FusedArgs a)
         const bool has_prev = p_unit >= 0;
         if (has_prev && wave == PUBWAVE) publish(a, red, p_unit, p_sg, lane);
 
-        const int sg = (s_base + r) % S;
         const int i0 = sg * SPS;
         const __amdgpu_buffer_rsrc_t xr = xres(unit);
         const int nunit = unit + a.upr;
         const bool nhas = nunit < U;
-        const int ni0 = ((sg + 1) % S) * SPS;
+        const int ni0 = (sg + 1 == S ? 0 : sg + 1) * SPS;
         const __amdgpu_buffer_rsrc_t nxr = xres(nhas ? nunit : unit);
         const __amdgpu_buffer_rsrc_t pyr = y_rsrc_u(a, has_prev ? p_unit : unit, plane);
         const unsigned pcu = has_prev ? line_phase(p_unit, p_i0) : 0u;
 
-        const int g = unit % a.G;
         if (g != wgroup) {
             wgroup = g;
             const float *wg = static_cast<const float *>(a.wt) + ((size_t)g * CG * CG + wave) * KS * KS;
@@ -1308,6 +1313,9 @@ void upsample2_gn_fused_kernel(FusedArgs a)
         p_unit = unit;
         p_sg = sg;
         p_i0 = i0;
+        sg = sg + 1 == S ? 0 : sg + 1;
+        g += g_step;
+        if (g >= a.G) g -= a.G;
     }
 
     // ---- the last unit: its triple was published above; wait, normalise, store

@@ -64,8 +64,8 @@
 // splits each operand into three bf16 pieces, v = v1 + v2 + v3 exactly: the
 // weights once per group, a step's two new input rows as it reads them.  The
 // 16-bit tile mapping above then sums the six leading piece products per
-// kernel row (18 MFMAs per tile), smallest first; the three dropped ones are
-// below 2^-26 |w x|, under fp32's own product rounding.
+// kernel row (18 MFMAs per tile), smallest first; the three dropped ones total
+// at most about 2^-23 |w x|, two units in the last place of an fp32 product.
 #include <atomic>
 
 #include "device.h"
@@ -929,7 +929,7 @@ void convt2d_gn_fused_kernel(FusedArgs a)
                 }
             } else if constexpr (DT == 3) {
                 // six of the nine piece products, smallest first: the three dropped
-                // ones are below 2^-26 of |w x| together
+                // ones total at most about 2^-23 |w x|
                 constexpr int PA[6] = {2, 1, 0, 1, 0, 0}, PB[6] = {0, 1, 2, 0, 1, 0};
 #pragma unroll
                 for (int s = 0; s < 6; ++s) {

@@ -97,10 +97,11 @@ typedef enum { CNF_DTYPE_F32 = 0, CNF_DTYPE_BF16 = 1, CNF_DTYPE_F16 = 2 } cnf_dt
  *           the six leading piece products (w1x1, w1x2, w2x1, w1x3, w2x2,
  *           w3x1) summed on the bf16 matrix instruction with fp32
  *           accumulation.  Each piece product is exact in fp32; the three
- *           dropped ones are below 2^-26 |w x| together, under the 2^-24
- *           relative rounding of one fp32 product, so the result has fp32
- *           accuracy (values below 2^-103 in magnitude lose their last
- *           piece to bf16 subnormals).  The 16-bit matrix instruction runs
+ *           dropped ones total at most about 2^-23 |w x| (two units in the
+ *           last place of one fp32 product, which rounds by up to 2^-24
+ *           itself), so the result keeps fp32 accuracy (values below
+ *           2^-100 in magnitude can lose their last piece to bf16
+ *           subnormals).  The 16-bit matrix instruction runs
  *           beside the vector unit's epilogue work, where fp32 products do
  *           not.  Only the single-write grouped transposed-conv kernel has
  *           this form; every other kernel contracts fp32 natively. */

@@ -297,7 +297,7 @@ def test_split_f32_single_write_every_element(over):
 @pytest.mark.parametrize("spread", [0.0, 3.0])
 def test_split_f32_as_accurate_as_native(spread):
     # The bf16x3 contraction carries every bit of each fp32 operand and drops
-    # only products below 2^-26 |w x|, so against the fp64 oracle it must be as
+    # only products of at most ~2^-23 |w x|, so against the fp64 oracle it must be as
     # accurate as the fp32 contraction: no activation (the conv and the
     # statistics alone set the error), inputs N(0, 1) and, with spread 3,
     # scaled by 10^U(-3, 3) element by element (every piece of the split in use

@@ -25,6 +25,59 @@ __device__ __forceinline__ v16f mfma_32x32x2(float a, float b, v16f c) {
 
 typedef float v2f __attribute__((ext_vector_type(2)));
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// D(16x16) += A(16x32) B(32x16) on bf16 operands: lane l supplies
+// A[l%16][8(l/16) + e] and B[8(l/16) + e][l%16], e = 0..7, two per word (low
+// half first); D element [4(l/16) + r][l%16] lives in register r of lane l
+// (the layout of mfma_16x16x4 above).
+__device__ __forceinline__ v4f mfma_bf16_16x16x32(v4u a, v4u b, v4f c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// ---- fp32 operands as three bf16 pieces (f32_math = BF16X3)
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 values -> one word of two bf16 (round to nearest even, low half first).
+__device__ __forceinline__ unsigned pack_bf16(float lo, float hi)
+{
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(v2f{lo, hi}, bf16x2));
+}
+
+// Three bf16 pieces of each of two fp32 values, v = p1 + p2 + p3 exactly:
+// p1 = bf16(v) leaves a remainder r = v - p1 that is exact (Sterbenz) and
+// at most 2^-8 |v| with at most 16 significant bits; p2 = bf16(r) leaves at
+// most 8 bits, which p3 holds exactly.  Words w1, w2, w3 hold the pieces of
+// (lo, hi).  (Below 2^-100 in magnitude p3 can be a bf16 subnormal.)
+struct Pieces {
+    unsigned w1, w2, w3;
+};
+__device__ __forceinline__ Pieces split3(float lo, float hi)
+{
+    Pieces p;
+    p.w1 = pack_bf16(lo, hi);
+    const float rl = lo - __builtin_bit_cast(float, p.w1 << 16),
+                rh = hi - __builtin_bit_cast(float, p.w1 & 0xffff0000u);
+    p.w2 = pack_bf16(rl, rh);
+    const float sl = rl - __builtin_bit_cast(float, p.w2 << 16),
+                sh = rh - __builtin_bit_cast(float, p.w2 & 0xffff0000u);
+    p.w3 = pack_bf16(sl, sh);
+    return p;
+}
+
+__device__ __forceinline__ void put_pieces(v4u (&dst)[3], int d, const Pieces &p)
+{
+    dst[0][d] = p.w1;
+    dst[1][d] = p.w2;
+    dst[2][d] = p.w3;
+}
+
+// The six leading piece products, smallest first: (A piece, B piece) of
+// w3x1, w2x2, w1x3, w2x1, w1x2, w1x1; the three dropped ones total at most
+// about 2^-23 |w x|.
+constexpr int PIECE_A[6] = {2, 1, 0, 1, 0, 0}, PIECE_B[6] = {0, 1, 2, 0, 1, 0};
 
 // Raw buffer resource over [base, base + bytes): loads past the end return 0
 // and stores past it are dropped; offsets are 32-bit byte offsets.

@@ -178,8 +178,6 @@ struct Stage<0> {
     using T = v4f;
 };
 
-typedef unsigned v4u __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 // D(16x16) += A(16x32) B(32x16) on 16-bit operands: lane l supplies
@@ -194,42 +192,6 @@ __device__ __forceinline__ v4f mfma16x32(v4u a, v4u b, v4f c)
     else
         return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                       __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-}
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-// Two fp32 values -> one word of two bf16 (round to nearest even, low half first).
-__device__ __forceinline__ unsigned pack_bf16(float lo, float hi)
-{
-    return __builtin_bit_cast(unsigned, __builtin_convertvector(v2f{lo, hi}, bf16x2));
-}
-
-// Three bf16 pieces of each of two fp32 values, v = p1 + p2 + p3 exactly:
-// p1 = bf16(v) leaves a remainder r = v - p1 that is exact (Sterbenz) and
-// at most 2^-9 |v| with at most 16 significant bits; p2 = bf16(r) leaves at
-// most 8 bits, which p3 holds exactly.  Words w1, w2, w3 hold the pieces of
-// (lo, hi).  (Exponents below 2^-103 would make p3 subnormal.)
-struct Pieces {
-    unsigned w1, w2, w3;
-};
-__device__ __forceinline__ Pieces split3(float lo, float hi)
-{
-    Pieces p;
-    p.w1 = pack_bf16(lo, hi);
-    const float rl = lo - __builtin_bit_cast(float, p.w1 << 16),
-                rh = hi - __builtin_bit_cast(float, p.w1 & 0xffff0000u);
-    p.w2 = pack_bf16(rl, rh);
-    const float sl = rl - __builtin_bit_cast(float, p.w2 << 16),
-                sh = rh - __builtin_bit_cast(float, p.w2 & 0xffff0000u);
-    p.w3 = pack_bf16(sl, sh);
-    return p;
-}
-
-__device__ __forceinline__ void put_pieces(v4u (&dst)[3], int d, const Pieces &p)
-{
-    dst[0][d] = p.w1;
-    dst[1][d] = p.w2;
-    dst[2][d] = p.w3;
 }
 
 // The 16-bit B operand of input row m from the fp32 ring, as three pieces:
@@ -930,7 +892,7 @@ void convt2d_gn_fused_kernel(FusedArgs a)
             } else if constexpr (DT == 3) {
                 // six of the nine piece products, smallest first: the three dropped
                 // ones total at most about 2^-23 |w x|
-                constexpr int PA[6] = {2, 1, 0, 1, 0, 0}, PB[6] = {0, 1, 2, 0, 1, 0};
+                constexpr const int *PA = PIECE_A, *PB = PIECE_B;
 #pragma unroll
                 for (int s = 0; s < 6; ++s) {
 #pragma unroll

@@ -62,10 +62,11 @@ DOMINANT = {
     "convt2d_gelu_gn_n128": ("convt2d_gn_fused_kernel<2, 0>", "k_convt2d_gn_fused.hip", "hbm"),
     "convt2d_dense_gelu_gn_n128": ("conv2d_igemm_kernel<64, 2, 1>", "k_conv2d_igemm.hip", "mfma"),
     "conv2d_s2p1_in_div_n128": ("conv2d_igemm_kernel<128, 0, 2>", "k_conv2d_igemm.hip", "mfma"),
-    "convt2d_s2_gelu_gn_n128": ("upsample2_gn_fused_kernel<2>", "k_convt2d_gn_fused.hip", "hbm"),
+    "convt2d_s2_gelu_gn_n128": ("upsample2_gn_fused_kernel<2, false>", "k_convt2d_gn_fused.hip", "hbm"),
     "conv2d_in_div_n128_bf16": ("conv2d_igemm16_kernel<128, 0, 1>", "k_conv2d_igemm.hip", "mfma"),
     "convt2d_gelu_gn_n128_bf16": ("convt2d_gn_fused_kernel<2, 1>", "k_convt2d_gn_fused.hip", "hbm"),
     "convt2d_gelu_gn_n128_bf16x3": ("convt2d_gn_fused_kernel<2, 3>", "k_convt2d_gn_fused.hip", "hbm"),
+    "convt2d_s2_gelu_gn_n128_bf16x3": ("upsample2_gn_fused_kernel<2, true>", "k_convt2d_gn_fused.hip", "hbm"),
 }
 
 

@@ -29,9 +29,10 @@ Workloads (shapes and options as the four source pages state their problems):
   * conv2d_in_div_n128_bf16, convt2d_gelu_gn_n128_bf16
                           the l2_p17 and l2_p19 problems with x and w in bf16
                           (fp32 accumulation and epilogue).
-  * convt2d_gelu_gn_n128_bf16x3
-                          the l2_p19 problem in fp32, its contraction on
-                          three bf16 pieces of each fp32 operand (f32_math).
+  * convt2d_gelu_gn_n128_bf16x3, convt2d_s2_gelu_gn_n128_bf16x3
+                          the l2_p19 problem and its upsampling form in fp32,
+                          the contraction on three bf16 pieces of each fp32
+                          operand (f32_math).
   * convt2d_s2_gelu_gn_n128
                           l2_p19's chain as an upsampling layer:
                           ConvTranspose2d 64->64 k3 stride 2 padding 1
@@ -112,6 +113,8 @@ WORKLOADS["convt2d_gelu_gn_n128_bf16"] = dict(WORKLOADS["convt2d_gelu_gn_n128"],
 # operand (fp32 accuracy; the library's f32_math option).
 WORKLOADS["convt2d_gelu_gn_n128_bf16x3"] = dict(WORKLOADS["convt2d_gelu_gn_n128"], id=11,
                                                 f32_math="bf16x3")
+WORKLOADS["convt2d_s2_gelu_gn_n128_bf16x3"] = dict(WORKLOADS["convt2d_s2_gelu_gn_n128"], id=12,
+                                                   f32_math="bf16x3")
 
 # The workloads the pages state (the others vary their geometry or precision).
 PAGE_WORKLOADS = [n for n in WORKLOADS if WORKLOADS[n]["id"] <= 6]

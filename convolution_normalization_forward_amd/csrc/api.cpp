@@ -60,10 +60,12 @@ struct cnf_plan {
 };
 
 namespace {
-// fp32 x and w contracted as bf16 pieces: asked for, and the plan's kernel has that form
+// fp32 x and w contracted as bf16 pieces: asked for, and the plan's kernel has
+// that form (the two single-write transposed-conv kernels)
 bool split_f32(const cnf_plan &p)
 {
-    return p.family == FAM_CONVT_FUSED && p.d.dtype == CNF_DTYPE_F32 && p.d.f32_math == CNF_F32_BF16X3;
+    return (p.family == FAM_CONVT_FUSED || p.family == FAM_UPS2_FUSED) && p.d.dtype == CNF_DTYPE_F32 &&
+           p.d.f32_math == CNF_F32_BF16X3;
 }
 }  // namespace
 
@@ -527,7 +529,7 @@ cnf_status forward_impl(const cnf_plan *plan, const void *xv, const void *wv, co
     case FAM_UPS2_FUSED: {
         cnf::ConvT2dArgs a{x, w, b, gamma, beta, out, static_cast<float *>(workspace), d.N,
                            d.C_in, d.C_out, H, W, d.groups, plan->Ho, plan->Wo, d.act,
-                           norm_groups, d.eps, inv_div, 0};
+                           norm_groups, d.eps, inv_div, split_f32(*plan) ? 3 : 0};
         int *flag = reinterpret_cast<int *>(static_cast<char *>(workspace) + plan->flag_offset);
         a.flag = flag;
         hipLaunchKernelGGL(clear_word_kernel, dim3(1), dim3(1), 0, st, flag);

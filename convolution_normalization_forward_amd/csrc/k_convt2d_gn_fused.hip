@@ -1066,7 +1066,16 @@ __device__ __forceinline__ v2u issue_upos(int p, int i0, __amdgpu_buffer_rsrc_t 
     return load_urow(use_next ? nxr : xr, H, (use_next ? ni0 : i0) + row, loff);
 }
 
-template <int ACT>
+// SPLIT (f32_math = BF16X3): the conv as 16x16x32 bf16 tiles on three pieces
+// of every fp32 operand.  Wave w takes input columns j = 16 w + c16; tile b
+// (output column parity) has rows (co, a) = (c16 / 2, c16 % 2) and K = (ci =
+// 2q + e / 4, di = e / 2 % 2, dj = e % 2), the 2 x 2 input neighbourhood of
+// 8 channels, so A[(co, a)][(ci, di, dj)] is the tap of (a, di), (b, dj) or
+// zero (9 of 16 useful) and B[(ci, di, dj)][j] = x[ci][i + di][j + dj].  A step
+// splits one new input row (two words per lane), issues 12 MFMAs, and the D
+// rows 4q + r of tile b are channel 2q + r / 2, output row 2i + r % 2,
+// column 2j + b.
+template <int ACT, bool SPLIT>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void upsample2_gn_fused_kernel(FusedArgs a)
 {
@@ -1117,6 +1126,10 @@ void upsample2_gn_fused_kernel(FusedArgs a)
     v4f gb = v4f{1.f, 0.f, 1.f, 0.f}, p_gb = gb;
     int wgroup = -1;
     float wk[CG][KS * KS];  // w[ci][c][kh][kw] of this wave's output channel c
+    v4u uwa[2][3];          // SPLIT: A pieces of tiles b = 0, 1
+    v4f ubias4 = v4f{0.f, 0.f, 0.f, 0.f};  // SPLIT: bias of channels 2q, 2q, 2q+1, 2q+1
+    v4u bq[3];              // SPLIT: B pieces, words d: channel 2q + d / 2, input row i + d % 2
+    const int uj = 16 * wave + c16;  // SPLIT: this lane's input column
     int p_unit = -1, p_sg = 0, p_i0 = 0;
     float psc = 0.f, psh = 0.f;
     v2f carry = v2f{0.f, 0.f};
@@ -1162,12 +1175,36 @@ void upsample2_gn_fused_kernel(FusedArgs a)
 
         if (g != wgroup) {
             wgroup = g;
-            const float *wg = static_cast<const float *>(a.wt) + ((size_t)g * CG * CG + wave) * KS * KS;
+            if constexpr (SPLIT) {
+                // A[(co, aa)][(ci, di, dj)] = w[ci][co][kh][kw]: kh 1 for (aa, di) = (0, 0),
+                // 2 for (1, 0), 0 for (1, 1), none for (0, 1); kw alike from (b, dj)
+                const float *wg = static_cast<const float *>(a.wt) + (size_t)g * CG * CG * KS * KS;
+                const int co = c16 >> 1, aa = c16 & 1;
 #pragma unroll
-            for (int ci = 0; ci < CG; ++ci)
+                for (int b = 0; b < 2; ++b)
 #pragma unroll
-                for (int t = 0; t < KS * KS; ++t) wk[ci][t] = wg[ci * CG * KS * KS + t];
-            bias1 = a.bias ? a.bias[g * CG + wave] : 0.0f;
+                    for (int d = 0; d < 4; ++d) {
+                        float v2[2];
+#pragma unroll
+                        for (int hh = 0; hh < 2; ++hh) {
+                            const int e = 2 * d + hh, ci = 2 * q + e / 4, di = (e >> 1) & 1, dj = e & 1;
+                            const int kh = aa == 0 ? (di == 0 ? 1 : -1) : (di == 0 ? 2 : 0);
+                            const int kw = b == 0 ? (dj == 0 ? 1 : -1) : (dj == 0 ? 2 : 0);
+                            v2[hh] = kh >= 0 && kw >= 0 ? wg[(ci * CG + co) * KS * KS + kh * KS + kw] : 0.0f;
+                        }
+                        put_pieces(uwa[b], d, split3(v2[0], v2[1]));
+                    }
+                const int c0 = g * CG + 2 * q;
+                const float b0 = a.bias ? a.bias[c0] : 0.0f, b1 = a.bias ? a.bias[c0 + 1] : 0.0f;
+                ubias4 = v4f{b0, b0, b1, b1};
+            } else {
+                const float *wg = static_cast<const float *>(a.wt) + ((size_t)g * CG * CG + wave) * KS * KS;
+#pragma unroll
+                for (int ci = 0; ci < CG; ++ci)
+#pragma unroll
+                    for (int t = 0; t < KS * KS; ++t) wk[ci][t] = wg[ci * CG * KS * KS + t];
+                bias1 = a.bias ? a.bias[g * CG + wave] : 0.0f;
+            }
             const int cg = g * CG + 2 * q;  // the (gamma, beta) pairs probe_finish uses
             gb = v4f{a.gamma ? a.gamma[cg] : 1.0f, a.beta ? a.beta[cg] : 0.0f,
                      a.gamma ? a.gamma[cg + 1] : 1.0f, a.beta ? a.beta[cg + 1] : 0.0f};
@@ -1183,6 +1220,34 @@ void upsample2_gn_fused_kernel(FusedArgs a)
                 psc = coefs[2 * wave];
                 psh = coefs[2 * wave + 1];
             }
+            if constexpr (SPLIT) {
+                // ---- B pieces: rows i (words 0, 2) are the last step's rows i + 1,
+                // except at a round's first step; then 12 MFMAs, the activation,
+                // sums and the bank (v2f per (channel, output row): columns 2j, 2j + 1)
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    if (k > 0 && (d & 1) == 0) {
+#pragma unroll
+                        for (int pc = 0; pc < 3; ++pc) bq[pc][d] = bq[pc][d + 1];
+                    } else {
+                        const float *src = ring + (k + (d & 1)) * UROW_FLOATS + (2 * q + (d >> 1)) * URP + uj;
+                        put_pieces(bq, d, split3(src[0], src[1]));
+                    }
+                }
+                v4f t0 = ubias4, t1 = ubias4;
+#pragma unroll
+                for (int s = 0; s < 6; ++s) {
+                    t0 = mfma_bf16_16x16x32(uwa[0][PIECE_A[s]], bq[PIECE_B[s]], t0);
+                    t1 = mfma_bf16_16x16x32(uwa[1][PIECE_A[s]], bq[PIECE_B[s]], t1);
+                }
+                const v4f e0 = activate4<ACT>(t0), e1 = activate4<ACT>(t1);
+                sums4(e0, s1, s2);
+                sums4(e1, s1, s2);
+                float *bp = slot(r, k) + 2 * q * CP + 2 * uj;
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr)
+                    *reinterpret_cast<v2f *>(bp + (rr >> 1) * CP + (rr & 1) * UWO) = v2f{e0[rr], e1[rr]};
+            } else {
             // ---- conv of input row i0 + k (ring slots k, k + 1): acc[h][p] is the
             // block of input column 2 lane + h, p = 2a + b (output row 2i + a,
             // column 2(2 lane + h) + b)
@@ -1218,6 +1283,7 @@ void upsample2_gn_fused_kernel(FusedArgs a)
                 float *bp = slot(r, k) + wave * CP + 4 * lane;
                 *reinterpret_cast<v4f *>(bp) = e0;
                 *reinterpret_cast<v4f *>(bp + UWO) = e1;
+            }
             }
             // ---- the previous unit, in the two steps after the merge: steps 0..2
             // were gathered at the ends of steps 0..2 (each iteration's epilogue
@@ -1387,26 +1453,26 @@ int ups_slices(int H)
     return H >= SPS && H % SPS == 0 && H / SPS <= UMAX_S ? H / SPS : 0;
 }
 
-template <int ACT>
+template <int ACT, bool SPLIT>
 hipError_t launch_ups_t(const ConvT2dArgs &p, hipStream_t st)
 {
     const int S = ups_slices(p.H);
     if (!S || p.W != UW || p.Ho != 2 * p.H) return hipErrorInvalidValue;
     const LaunchHooks &hk = hooks();
-    static std::atomic<int> blocks_per_cu[64][5], cus_cache[64];  // zero-initialised
+    static std::atomic<int> blocks_per_cu[64][5][2], cus_cache[64];  // zero-initialised
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     const bool cache = dev >= 0 && dev < 64;
-    int nb = cache ? blocks_per_cu[dev][ACT].load(std::memory_order_relaxed) : 0;
+    int nb = cache ? blocks_per_cu[dev][ACT][SPLIT].load(std::memory_order_relaxed) : 0;
     int cus = cache ? cus_cache[dev].load(std::memory_order_relaxed) : 0;
     if (nb == 0 || cus == 0) {
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, upsample2_gn_fused_kernel<ACT>, THREADS, 0);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, upsample2_gn_fused_kernel<ACT, SPLIT>, THREADS, 0);
         if (e != hipSuccess) return e;
         e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess) return e;
         if (cache) {
-            blocks_per_cu[dev][ACT].store(nb, std::memory_order_relaxed);
+            blocks_per_cu[dev][ACT][SPLIT].store(nb, std::memory_order_relaxed);
             cus_cache[dev].store(cus, std::memory_order_relaxed);
         }
     }
@@ -1428,7 +1494,7 @@ hipError_t launch_ups_t(const ConvT2dArgs &p, hipStream_t st)
                  p.N, p.C_out, p.H, p.groups, p.Ho, S, 0, upr, xcd_units, p.eps, p.inv_div};
     void *args[] = {&fa};
     if ((e = dominant_begin(st)) != hipSuccess) return e;
-    e = hipLaunchCooperativeKernel(reinterpret_cast<const void *>(upsample2_gn_fused_kernel<ACT>),
+    e = hipLaunchCooperativeKernel(reinterpret_cast<const void *>(upsample2_gn_fused_kernel<ACT, SPLIT>),
                                    dim3(upr * S), dim3(THREADS), args, 0, st);
     if (e != hipSuccess) return e;
     return dominant_end(st);
@@ -1493,16 +1559,24 @@ size_t upsample2_fused_workspace(int N, int groups, int H)
     return (size_t)N * groups * (size_t)ups_slices(H) * 4 * sizeof(float);
 }
 
-hipError_t launch_upsample2_fused(const ConvT2dArgs &a, hipStream_t st)
+template <bool SPLIT>
+hipError_t launch_ups_act(const ConvT2dArgs &a, hipStream_t st)
 {
-    if (a.dtype != 0) return hipErrorInvalidValue;
     switch (a.act) {
-    case ACT_NONE: return launch_ups_t<ACT_NONE>(a, st);
-    case ACT_HARDSWISH: return launch_ups_t<ACT_HARDSWISH>(a, st);
-    case ACT_GELU_ERF: return launch_ups_t<ACT_GELU_ERF>(a, st);
-    case ACT_GELU_TANH: return launch_ups_t<ACT_GELU_TANH>(a, st);
+    case ACT_NONE: return launch_ups_t<ACT_NONE, SPLIT>(a, st);
+    case ACT_HARDSWISH: return launch_ups_t<ACT_HARDSWISH, SPLIT>(a, st);
+    case ACT_GELU_ERF: return launch_ups_t<ACT_GELU_ERF, SPLIT>(a, st);
+    case ACT_GELU_TANH: return launch_ups_t<ACT_GELU_TANH, SPLIT>(a, st);
     default: return hipErrorInvalidValue;
     }
+}
+
+// dtype 0: fp32 on the vector unit; 3: fp32 operands as bf16 pieces on the MFMA
+hipError_t launch_upsample2_fused(const ConvT2dArgs &a, hipStream_t st)
+{
+    if (a.dtype == 0) return launch_ups_act<false>(a, st);
+    if (a.dtype == 3) return launch_ups_act<true>(a, st);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace cnf

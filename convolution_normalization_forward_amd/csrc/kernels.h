@@ -105,7 +105,7 @@ struct ConvT2dArgs {
     int act;
     int norm_groups;     // 0: no norm; else GroupNorm groups (C_out: InstanceNorm)
     float eps, inv_div;
-    int dtype = 0;       // 0 fp32; 1 bf16 / 2 fp16 x and w; 3 fp32 on bf16 pieces (single-write kernel only)
+    int dtype = 0;       // 0 fp32; 1 bf16 / 2 fp16 x and w; 3 fp32 on bf16 pieces (single-write kernels only)
     int *flag = nullptr; // single-write kernel: raised (1) if a cross-workgroup wait gave up
 };
 bool convt2d_supported(int C_in, int C_out, int kernel, int groups, int H, int W, int act,

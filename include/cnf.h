@@ -103,8 +103,9 @@ typedef enum { CNF_DTYPE_F32 = 0, CNF_DTYPE_BF16 = 1, CNF_DTYPE_F16 = 2 } cnf_dt
  *           2^-100 in magnitude can lose their last piece to bf16
  *           subnormals).  The 16-bit matrix instruction runs
  *           beside the vector unit's epilogue work, where fp32 products do
- *           not.  Only the single-write grouped transposed-conv kernel has
- *           this form; every other kernel contracts fp32 natively. */
+ *           not.  The two single-write grouped transposed-conv kernels
+ *           (stride 1, and the stride-2 upsampling one) have this form;
+ *           every other kernel contracts fp32 natively. */
 typedef enum { CNF_F32_NATIVE = 0, CNF_F32_BF16X3 = 1 } cnf_f32_math;
 
 typedef enum {

@@ -61,6 +61,7 @@ def test_every_workload_plans_with_expected_shape(name):
         "conv2d_in_div_n128_bf16": (128, 128, 126, 126),
         "convt2d_gelu_gn_n128_bf16": (128, 64, 258, 258),
         "convt2d_gelu_gn_n128_bf16x3": (128, 64, 258, 258),
+        "convt2d_s2_gelu_gn_n128_bf16x3": (128, 64, 256, 256),
     }[name]
     assert plan.out_shape == exp
     assert "family=" in plan.describe()
@@ -282,9 +283,9 @@ def test_sixteen_bit_inputs_plan_on_the_general_family(monkeypatch):
 
 def test_f32_math_option():
     """f32_math: NATIVE or BF16X3, anything else is an invalid descriptor; the
-    split form is named only where the plan's kernel has it (the single-write
-    grouped transposed conv with fp32 inputs), every other plan contracts fp32
-    natively and says nothing."""
+    split form is named only where the plan's kernel has it (the two
+    single-write grouped transposed convs with fp32 inputs), every other plan
+    contracts fp32 natively and says nothing."""
     d = _desc("convt2d_gelu_gn_n128")
     d.f32_math = 2
     assert cnf.cnf_plan_create_status(d) == cnf.CNF_ERR_INVALID_DESC
@@ -297,7 +298,9 @@ def test_f32_math_option():
     assert "contraction=" not in native.describe()
     # the same kernel and workspace either way
     assert split.workspace_bytes == native.workspace_bytes
-    for name, over in (("conv2d_in_div_n128", {}), ("convt2d_s2_gelu_gn_n128", {}),
+    up = cnf.Plan(_desc("convt2d_s2_gelu_gn_n128", f32_math="bf16x3"))
+    assert "family=convt2d_s2_grouped8_gn_fused" in up.describe() and "contraction=bf16x3" in up.describe()
+    for name, over in (("conv2d_in_div_n128", {}), ("conv3d_softmax_pool_n128", {}),
                        ("convt2d_gelu_gn_n128", dict(dtype="bf16")),
                        ("convt2d_gelu_gn_n128", dict(in_dims=(1, 64, 200)))):
         p = cnf.Plan(_desc(name, f32_math="bf16x3", **over))
@@ -314,6 +317,7 @@ def test_family_routing():
     # on the general family
     special = {"convt2d_gelu_gn_n128_bf16": "family=convt2d_grouped8_gn_fused",
                "convt2d_gelu_gn_n128_bf16x3": "family=convt2d_grouped8_gn_fused",
+               "convt2d_s2_gelu_gn_n128_bf16x3": "family=convt2d_s2_grouped8_gn_fused",
                "convt2d_s2_gelu_gn_n128": "family=convt2d_s2_grouped8_gn_fused",
                "conv2d_s2p1_in_div_n128": "family=conv2d_igemm",
                "conv2d_in_div_n128_bf16": "family=conv2d_igemm16"}

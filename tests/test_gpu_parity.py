@@ -177,6 +177,7 @@ FULL_SUBSET = {
     "conv2d_in_div_n128_bf16": 4 + 2,
     "convt2d_gelu_gn_n128_bf16": 4 + 2,
     "convt2d_gelu_gn_n128_bf16x3": 8 + 2,
+    "convt2d_s2_gelu_gn_n128_bf16x3": 4 + 2,
 }
 
 
@@ -464,22 +465,27 @@ UPS2_FUSED = [
 
 
 @pytest.mark.parametrize("over", UPS2_FUSED)
-def test_upsample_single_write_every_element(over):
-    wl = cnf_inputs.workload("convt2d_s2_gelu_gn_n128", **over)
-    _say(f"[ups2-fused] {over}")
+@pytest.mark.parametrize("f32_math", ["native", "bf16x3"])
+def test_upsample_single_write_every_element(over, f32_math):
+    # native: the conv on the vector unit; bf16x3: on the MFMA, fp32 operands as
+    # three bf16 pieces
+    wl = cnf_inputs.workload("convt2d_s2_gelu_gn_n128", f32_math=f32_math, **over)
+    _say(f"[ups2-fused] {over} {f32_math}")
     x = cnf_inputs.gen_x(wl)
     p = cnf_inputs.gen_params(wl)
     plan, out, _ = run_gpu(wl, x, p)
     assert "convt2d_s2_grouped8_gn_fused" in plan.describe(), plan.describe()
+    assert ("contraction=bf16x3" in plan.describe()) == (f32_math == "bf16x3")
     ref, _ = oracle.forward(wl, x, **p)
     err = check_close(out.cpu().numpy(), ref, f"upsample fused {over}")
     _say(f"    max_abs_err={err:.3e}")
 
 
-def test_upsample_single_write_many_rounds(monkeypatch):
+@pytest.mark.parametrize("f32_math", ["native", "bf16x3"])
+def test_upsample_single_write_many_rounds(monkeypatch, f32_math):
     # two units per round: 12 rounds, the bank rotation and ring hand-over across them
     monkeypatch.setenv("CNF_TEST_FUSED_MAX_UNITS_PER_ROUND", "2")
-    _case("convt2d_s2_gelu_gn_n128", N=3, in_dims=(1, 32, 128))
+    _case("convt2d_s2_gelu_gn_n128", N=3, in_dims=(1, 32, 128), f32_math=f32_math)
 
 
 def test_upsample_single_write_waits(monkeypatch):
@@ -507,10 +513,11 @@ def test_upsample_single_write_forced_fallback(monkeypatch):
     _case("convt2d_s2_gelu_gn_n128", N=2, in_dims=(1, 16, 128))
 
 
+@pytest.mark.parametrize("f32_math", ["native", "bf16x3"])
 @pytest.mark.parametrize("offset_floats", [4, 20])
-def test_upsample_output_off_line_boundary(offset_floats):
+def test_upsample_output_off_line_boundary(offset_floats, f32_math):
     import convolution_normalization_forward_amd as cnf
-    wl = cnf_inputs.workload("convt2d_s2_gelu_gn_n128", N=2, in_dims=(1, 24, 128))
+    wl = cnf_inputs.workload("convt2d_s2_gelu_gn_n128", N=2, in_dims=(1, 24, 128), f32_math=f32_math)
     _say(f"[ups2 off-line] offset {offset_floats} floats")
     x = cnf_inputs.gen_x(wl)
     p = cnf_inputs.gen_params(wl)

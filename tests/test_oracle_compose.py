@@ -106,6 +106,7 @@ SMALL = {
                                       num_groups=8),
     "convt2d_gelu_gn_n128_bf16x3": dict(N=2, C_in=16, C_out=16, in_dims=(1, 9, 10), groups=8,
                                         num_groups=8),
+    "convt2d_s2_gelu_gn_n128_bf16x3": dict(N=2, C_in=16, C_out=16, in_dims=(1, 6, 7)),
 }
 
 

@@ -25,7 +25,14 @@
 //     2*wn + 1 as 2 x 2 tiles of v_mfma_f32_32x32x2f32 (channel half x row).
 //     32-column tiles keep the padding of the last column tile small for
 //     widths just past a multiple of 64 (258 = 4 * 64 + 2 wasted a quarter of
-//     the MFMA work with 64-column tiles).
+//     the MFMA work with 64-column tiles).  At stride 1, widths 1 or 2 past a
+//     multiple of 32 (258 again) leave those last columns to column-strip
+//     tiles, whose 32 MFMA columns are 16 rows x 2 columns (32 NR rows per
+//     tile), instead of tiles with 1 or 2 live columns in 32; heights 1 or 2
+//     past a multiple of TR leave those last rows to row-strip tiles of 2 rows
+//     x 32 NR columns, instead of tiles in which one wave has live rows.  On a
+//     258 x 258 output this drops the tiles from 153 to 131 per sample and the
+//     MFMA work from 1.18x to 1.00x the live positions.
 //   * Stride s = 1 or 2: output position (r, c) reads input rows s r + kh and
 //     columns s c + kw of the (padded) input, so a tile's halo is
 //     (TR - 1) s + 3 rows of 31 s + 3 columns.
@@ -53,6 +60,10 @@ constexpr int THREADS = 512;
 constexpr int NWAVES = THREADS / 64;
 constexpr int MAX_CC = 4;                // input channels per K chunk at stride 1
 
+// Padding that makes a block of `base` floats end `m` floats past a multiple
+// of 64 (the next block then starts m floats into a 64-bank row).
+constexpr int pad_to(int base, int m) { return base + ((m - base % 64) + 64) % 64; }
+
 // Tile geometry for CO output channels (128 or 64) and stride SD: 64 channels x
 // 64 columns (two rows of 32) per wave, so NR = 8 waves / (CO / 64) waves along
 // the rows and TR = 2 * NR output rows per tile.  At stride 1 the halo row
@@ -60,16 +71,16 @@ constexpr int MAX_CC = 4;                // input channels per K chunk at stride
 // the two K rows of an operand (lane halves) read disjoint banks; at stride 2 a
 // lane half reads every other float of a row, so the channel block starts an
 // odd number of floats in and the two halves take the even and the odd banks.
-template <int CO, int SD>
+template <int CO_, int SD_>
 struct Geo {
+    static constexpr int CO = CO_, SD = SD_;
     static constexpr int CC = SD == 1 ? MAX_CC : 2;
     static constexpr int KC = 9 * CC;
     static constexpr int WM = CO / 64, NR = NWAVES / WM, TR = 2 * NR;
     static constexpr int HR = (TR - 1) * SD + 3, HC = (TC - 1) * SD + 3;  // halo rows, columns
     static constexpr int PITCH = SD == 1 ? 36 : 68;
-    static constexpr int CS_BASE = HR * PITCH;
-    static constexpr int CS = SD == 1 ? CS_BASE + ((32 - CS_BASE % 64) + 64) % 64  // == 32 mod 64
-                                      : CS_BASE + ((33 - CS_BASE % 64) + 64) % 64; // == 33 mod 64
+    static constexpr int BJ = SD * PITCH;  // LDS offset from a wave's first output row to its second
+    static constexpr int CS = pad_to(HR * PITCH, SD == 1 ? 32 : 33);
     static constexpr int WPITCH = CO + 32;                                // == 32 mod 64
     static constexpr int XS_FLOATS = (CC * CS + 3) / 4 * 4;             // float4-aligned weights after it
     static constexpr int WS_FLOATS = KC * WPITCH;
@@ -81,6 +92,52 @@ struct Geo {
     static_assert(HC <= PITCH, "halo row fits its pitch");
     static_assert(NR * WM == NWAVES, "one 64-channel x 64-position block per wave");
     static_assert(2 * BUF_FLOATS * 4 <= 80 * 1024, "two workgroups per CU");
+};
+
+// Column strip (stride 1): when Wo mod 32 is 1 or 2, a tile of 32 columns would
+// hold 1 or 2 live ones, so those last columns get tiles of their own in which
+// a wave's two 32-column MFMA blocks are 16 rows x 2 columns each (lane i of a
+// half: row i / 2, column i % 2).  A wave covers 32 rows and a tile TR = 32 NR
+// rows; its halo is TR + 2 rows of 4 columns (pitch 4).  A lane half reads
+// columns {0, 1} + kw of every fourth float, so a channel block starts 2 floats
+// past a multiple of 64 and the two halves take the banks 4 j + {0, 1} and
+// 4 j + {2, 3}.  Two input channels per K chunk keep the halo and the weights
+// inside the main tile's staging buffers (the same LDS layout).
+template <int CO_>
+struct GeoStrip {
+    static constexpr int CO = CO_, SD = 1;
+    static constexpr int CC = 2, KC = 9 * CC;
+    static constexpr int WM = CO / 64, NR = NWAVES / WM, TR = 32 * NR;
+    static constexpr int HR = TR + 2, HC = 4, PITCH = 4;
+    static constexpr int BJ = 16 * PITCH;
+    static constexpr int CS = pad_to(HR * PITCH, 2);
+    static constexpr int WPITCH = Geo<CO, 1>::WPITCH;
+    static constexpr int XS_FLOATS = Geo<CO, 1>::XS_FLOATS, BUF_FLOATS = Geo<CO, 1>::BUF_FLOATS;
+    static constexpr int XIN = CC * HR * HC;
+    static constexpr int XPF = (XIN + THREADS - 1) / THREADS;
+    static constexpr int WPF = (KC * CO / 4 + THREADS - 1) / THREADS;
+    static_assert(CC * CS <= XS_FLOATS, "strip halo fits the main tile's halo buffer");
+    static_assert(KC * WPITCH <= Geo<CO, 1>::WS_FLOATS, "strip weights fit the main tile's buffer");
+};
+
+// Row strip (stride 1): when Ho mod TR is 1 or 2, those last rows get tiles of
+// 2 rows x 32 NR columns (wave wn: both rows, columns 32 wn .. + 31) instead of
+// tiles in which one wave in NR has live rows.  Halo: 4 rows of 32 NR + 2
+// columns; two input channels per K chunk, as in the column strip.
+template <int CO_>
+struct GeoRow {
+    static constexpr int CO = CO_, SD = 1;
+    static constexpr int CC = 2, KC = 9 * CC;
+    static constexpr int WM = CO / 64, NR = NWAVES / WM, TW = 32 * NR;  // tile columns
+    static constexpr int HR = 4, HC = TW + 2, PITCH = HC, BJ = PITCH;
+    static constexpr int CS = pad_to(HR * PITCH, 32);
+    static constexpr int WPITCH = Geo<CO, 1>::WPITCH;
+    static constexpr int XS_FLOATS = Geo<CO, 1>::XS_FLOATS, BUF_FLOATS = Geo<CO, 1>::BUF_FLOATS;
+    static constexpr int XIN = CC * HR * HC;
+    static constexpr int XPF = (XIN + THREADS - 1) / THREADS;
+    static constexpr int WPF = (KC * CO / 4 + THREADS - 1) / THREADS;
+    static_assert(CC * CS <= XS_FLOATS, "row-strip halo fits the main tile's halo buffer");
+    static_assert(KC * WPITCH <= Geo<CO, 1>::WS_FLOATS, "row-strip weights fit the main tile's buffer");
 };
 
 // Conv: w[co][ci][kh][kw] -> wt[ci][tap][co].  Transposed conv (weights
@@ -96,95 +153,155 @@ __global__ void conv2d_weight_transpose_kernel(const float *__restrict__ w, floa
     wt[i] = transposed ? w[((size_t)ci * CO + co) * 9 + (8 - tap)] : w[(size_t)co * C_in * 9 + rest];
 }
 
-template <int CO, int SD, int XPF = Geo<CO, SD>::XPF, int WPF = Geo<CO, SD>::WPF>
+// Per-thread staging slots of geometry G for the tile at (row0, col0): halo
+// element e = tid + u*THREADS (clamped so every load is in bounds; out-of-image
+// or surplus slots carry 0), and float4 e of the chunk's [ci][tap][co] weight rows.
+template <class G>
+__device__ __forceinline__ void igemm_tables(int tid, int row0, int col0, int H, int W, int pad,
+                                             int (&xoff)[G::XPF], bool (&xok)[G::XPF],
+                                             int (&xdst)[G::XPF], int (&wdst)[G::WPF])
+{
+#pragma unroll
+    for (int u = 0; u < G::XPF; ++u) {
+        const int e = tid + u * THREADS;
+        const int ec = e < G::XIN ? e : G::XIN - 1;
+        const int cc = ec % G::HC, rest = ec / G::HC;
+        const int rr = rest % G::HR, c = rest / G::HR;
+        // input row / column of the (zero-padded by pad) halo element
+        const int gr = G::SD * row0 + rr - pad, gc = G::SD * col0 + cc - pad;
+        xok[u] = e < G::XIN && gr >= 0 && gr < H && gc >= 0 && gc < W;
+        xoff[u] = xok[u] ? (c * H + gr) * W + gc : 0;
+        xdst[u] = e < G::XIN ? c * G::CS + rr * G::PITCH + cc : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < G::WPF; ++u) {
+        const int e = tid + u * THREADS;
+        const int co4 = e % (G::CO / 4), r = e / (G::CO / 4);  // r = c * 9 + tap
+        const int c = r / 9, tap = r % 9;
+        wdst[u] = e < G::KC * G::CO / 4 ? (tap * G::CC + c) * G::WPITCH + co4 * 4 : -1;
+    }
+}
+
+template <class G>
 __device__ __forceinline__ void igemm_fetch(const float *__restrict__ xn, const float *__restrict__ wt,
                                             int chunk, int H, int W, int tid,
-                                            const int (&xoff)[XPF], const bool (&xok)[XPF],
-                                            float (&xpf)[XPF], v4f (&wpf)[WPF])
+                                            const int (&xoff)[G::XPF], const bool (&xok)[G::XPF],
+                                            float (&xpf)[G::XPF], v4f (&wpf)[G::WPF])
 {
-    constexpr int CC = Geo<CO, SD>::CC, KC = Geo<CO, SD>::KC;
-    const float *xc = xn + (size_t)chunk * CC * H * W;
+    const float *xc = xn + (size_t)chunk * G::CC * H * W;
 #pragma unroll
-    for (int u = 0; u < XPF; ++u) {
+    for (int u = 0; u < G::XPF; ++u) {
         const float v = xc[xoff[u]];
         xpf[u] = xok[u] ? v : 0.0f;
     }
-    const v4f *src = reinterpret_cast<const v4f *>(wt + (size_t)chunk * CC * 9 * CO);
+    const v4f *src = reinterpret_cast<const v4f *>(wt + (size_t)chunk * G::CC * 9 * G::CO);
 #pragma unroll
-    for (int u = 0; u < WPF; ++u) {
+    for (int u = 0; u < G::WPF; ++u) {
         const int e = tid + u * THREADS;
-        wpf[u] = src[e < KC * CO / 4 ? e : 0];
+        wpf[u] = src[e < G::KC * G::CO / 4 ? e : 0];
     }
 }
 
-template <int CO, int SD, int XPF = Geo<CO, SD>::XPF, int WPF = Geo<CO, SD>::WPF>
-__device__ __forceinline__ void igemm_stash(float *lds, int buf, const int (&xdst)[XPF],
-                                            const int (&wdst)[WPF], const float (&xpf)[XPF],
-                                            const v4f (&wpf)[WPF])
+template <class G>
+__device__ __forceinline__ void igemm_stash(float *lds, int buf, const int (&xdst)[G::XPF],
+                                            const int (&wdst)[G::WPF], const float (&xpf)[G::XPF],
+                                            const v4f (&wpf)[G::WPF])
 {
-    float *xs = lds + buf * Geo<CO, SD>::BUF_FLOATS;
-    float *ws = xs + Geo<CO, SD>::XS_FLOATS;
+    float *xs = lds + buf * G::BUF_FLOATS;
+    float *ws = xs + G::XS_FLOATS;
 #pragma unroll
-    for (int u = 0; u < XPF; ++u)
+    for (int u = 0; u < G::XPF; ++u)
         if (xdst[u] >= 0) xs[xdst[u]] = xpf[u];
 #pragma unroll
-    for (int u = 0; u < WPF; ++u)
+    for (int u = 0; u < G::WPF; ++u)
         if (wdst[u] >= 0) *reinterpret_cast<v4f *>(ws + wdst[u]) = wpf[u];
 }
 
-template <int CO, int ACT, int SD>
+// The K loop of one tile of geometry G: chunks of CC input channels staged in
+// double-buffered LDS, the next chunk fetched into registers while the current
+// one is multiplied.  xlane: LDS offset of this lane's first B operand in a
+// channel block; active: false for a wave whose output rows all lie past the
+// output (it still stages, but skips the MFMAs).
+template <class G>
+__device__ __forceinline__ void igemm_loop(const float *__restrict__ xn, const float *__restrict__ wt,
+                                           float *lds, int C_in, int H, int W, int pad, int row0,
+                                           int col0, int tid, int xlane, bool active, v16f (&acc)[2][2])
+{
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / G::NR, h = lane >> 5, i32 = lane & 31;
+    int xoff[G::XPF], xdst[G::XPF], wdst[G::WPF];
+    bool xok[G::XPF];
+    igemm_tables<G>(tid, row0, col0, H, W, pad, xoff, xok, xdst, wdst);
+    float xpf[G::XPF];
+    v4f wpf[G::WPF];
+
+    const int nchunks = C_in / G::CC;
+    igemm_fetch<G>(xn, wt, 0, H, W, tid, xoff, xok, xpf, wpf);
+    igemm_stash<G>(lds, 0, xdst, wdst, xpf, wpf);
+    __syncthreads();
+    for (int ch = 0; ch < nchunks; ++ch) {
+        const int buf = ch & 1;
+        if (ch + 1 < nchunks) igemm_fetch<G>(xn, wt, ch + 1, H, W, tid, xoff, xok, xpf, wpf);
+        const float *xs = lds + buf * G::BUF_FLOATS;
+        const float *ws = xs + G::XS_FLOATS;
+        const float *wa = ws + h * G::WPITCH + 64 * wm + i32;
+        const float *xb = xs + h * G::CS + xlane;
+        if (active) {
+#pragma unroll
+            for (int tap = 0; tap < 9; ++tap) {
+                const int kh = tap / 3, kw = tap % 3;
+#pragma unroll
+                for (int p = 0; p < G::CC / 2; ++p) {
+                    const int s = tap * (G::CC / 2) + p;
+                    const float a0 = wa[2 * s * G::WPITCH];
+                    const float a1 = wa[2 * s * G::WPITCH + 32];
+                    const float b0 = xb[2 * p * G::CS + kh * G::PITCH + kw];
+                    const float b1 = xb[2 * p * G::CS + G::BJ + kh * G::PITCH + kw];
+                    acc[0][0] = mfma_32x32x2(a0, b0, acc[0][0]);
+                    acc[0][1] = mfma_32x32x2(a0, b1, acc[0][1]);
+                    acc[1][0] = mfma_32x32x2(a1, b0, acc[1][0]);
+                    acc[1][1] = mfma_32x32x2(a1, b1, acc[1][1]);
+                }
+            }
+        }
+        if (ch + 1 < nchunks)  // buf^1 was last read in iteration ch-1
+            igemm_stash<G>(lds, buf ^ 1, xdst, wdst, xpf, wpf);
+        __syncthreads();
+    }
+}
+
+// EDGE (stride 1 only): a sample's tiles are tiles_w x tiles_h row-major
+// 32-column tiles, then `row_strips` row-strip tiles of the last Ho - TR tiles_h
+// rows (0 unless that is 1 or 2), then column-strip tiles of the last Wo - 32
+// tiles_w columns (none unless that is 1 or 2), which cover every row; and a
+// wave whose output rows all lie past the bottom edge skips its MFMAs.  Without
+// EDGE every tile is a 32-column tile.
+template <int CO, int ACT, int SD, bool EDGE>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(4, 4)))
 void conv2d_igemm_kernel(const float *__restrict__ x, const float *__restrict__ wt,
                          const float *__restrict__ bias, float *__restrict__ y,
                          float *__restrict__ partials, int C_in, int H, int W, int Ho, int Wo,
-                         int pad, int tiles_w, int tiles_per_sample)
+                         int pad, int tiles_w, int tiles_h, int row_strips, int tiles_per_sample)
 {
+    static_assert(!EDGE || SD == 1, "edge strips at stride 1");
     using G = Geo<CO, SD>;
-    constexpr int TR = G::TR, NR = G::NR, CS = G::CS, WPITCH = G::WPITCH, XPF = G::XPF, WPF = G::WPF;
-    constexpr int XIN = G::XIN, BUF_FLOATS = G::BUF_FLOATS, XS_FLOATS = G::XS_FLOATS;
-    constexpr int CC = G::CC, KC = G::KC, PITCH = G::PITCH, HR = G::HR, HC = G::HC;
+    using GS = GeoStrip<CO>;
+    using GR = GeoRow<CO>;
+    constexpr int TR = G::TR, NR = G::NR, BUF_FLOATS = G::BUF_FLOATS;
     __shared__ float lds[2 * BUF_FLOATS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave / NR, wn = wave % NR;
     const int h = lane >> 5, i32 = lane & 31;
-    // XCD-aware tile order: each XCD takes a contiguous run of (n, row tile,
-    // column tile), so vertically adjacent tiles share their halo rows in L2.
-    const int tiles_h = gridDim.y;
-    const int L = blockIdx.x + gridDim.x * (blockIdx.y + tiles_h * blockIdx.z);
-    const int T = xcd_remap(L, gridDim.x * tiles_h * gridDim.z);
-    const int tw = T % tiles_w, th = (T / tiles_w) % tiles_h, n = T / (tiles_w * tiles_h);
-    const int row0 = th * TR, col0 = tw * TC;
+    // XCD-aware tile order: each XCD takes a contiguous run of (n, tile), so
+    // vertically adjacent tiles share their halo rows in L2.
+    const int L = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+    const int T = xcd_remap(L, gridDim.x * gridDim.y * gridDim.z);
+    const int n = T / tiles_per_sample, t = T - n * tiles_per_sample;
+    const int tiles_main = tiles_w * tiles_h;
     const float *xn = x + (size_t)n * C_in * H * W;
 
-    // Per-thread staging slots: halo element e = tid + u*THREADS (clamped so
-    // every load is in bounds; out-of-image or surplus slots carry 0), and
-    // float4 e of the chunk's [ci][tap][co] weight rows.
-    int xoff[XPF], xdst[XPF];
-    bool xok[XPF];
-#pragma unroll
-    for (int u = 0; u < XPF; ++u) {
-        const int e = tid + u * THREADS;
-        const int ec = e < XIN ? e : XIN - 1;
-        const int cc = ec % HC, rest = ec / HC;
-        const int rr = rest % HR, c = rest / HR;
-        // input row / column of the (zero-padded by pad) halo element
-        const int gr = SD * row0 + rr - pad, gc = SD * col0 + cc - pad;
-        xok[u] = e < XIN && gr >= 0 && gr < H && gc >= 0 && gc < W;
-        xoff[u] = xok[u] ? (c * H + gr) * W + gc : 0;
-        xdst[u] = e < XIN ? c * CS + rr * PITCH + cc : -1;
-    }
-    int wdst[WPF];
-#pragma unroll
-    for (int u = 0; u < WPF; ++u) {
-        const int e = tid + u * THREADS;
-        const int co4 = e % (CO / 4), r = e / (CO / 4);  // r = c * 9 + tap
-        const int c = r / 9, tap = r % 9;
-        wdst[u] = e < KC * CO / 4 ? (tap * CC + c) * WPITCH + co4 * 4 : -1;
-    }
-    float xpf[XPF];
-    v4f wpf[WPF];
     v16f acc[2][2];
 #pragma unroll
     for (int a = 0; a < 2; ++a)
@@ -193,50 +310,57 @@ void conv2d_igemm_kernel(const float *__restrict__ x, const float *__restrict__ 
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
-    const int nchunks = C_in / CC;
-    igemm_fetch<CO, SD>(xn, wt, 0, H, W, tid, xoff, xok, xpf, wpf);
-    igemm_stash<CO, SD>(lds, 0, xdst, wdst, xpf, wpf);
-    __syncthreads();
-    for (int ch = 0; ch < nchunks; ++ch) {
-        const int buf = ch & 1;
-        if (ch + 1 < nchunks) igemm_fetch<CO, SD>(xn, wt, ch + 1, H, W, tid, xoff, xok, xpf, wpf);
-        const float *xs = lds + buf * BUF_FLOATS;
-        const float *ws = xs + XS_FLOATS;
-        const float *wa = ws + h * WPITCH + 64 * wm + i32;
-        const float *xb = xs + h * CS + 2 * SD * wn * PITCH + SD * i32;
+    // Register r of acc[bi][bj] holds channel co(bi, r) (fixed per 32-lane half
+    // h) at output row prow[bj], column pcol.  Statistics are taken per 16-lane
+    // row s16 = (lane / 16) % 2 over both bj: mean and then summed squared
+    // deviations (two passes over the registers), giving 2 * NR (count, mean,
+    // M2) partials per channel that one Chan merge per channel folds into the
+    // tile's partial; cnt = the live positions of the lane's 16-lane row.
+    const int s16 = (lane >> 4) & 1;
+    int prow[2], pcol, cnt;
+    if (EDGE && t >= tiles_main + row_strips) {  // block-uniform
+        const int row0 = (t - tiles_main - row_strips) * GS::TR, col0 = tiles_w * TC;
+        const int rw = row0 + 32 * wn;  // the wave's first row
+        igemm_loop<GS>(xn, wt, lds, C_in, H, W, pad, row0, col0, tid,
+                       ((i32 >> 1) + 32 * wn) * GS::PITCH + (i32 & 1), rw < Ho, acc);
+        const int sw = min(Wo - col0, 2);
+        cnt = 0;
 #pragma unroll
-        for (int tap = 0; tap < 9; ++tap) {
-            const int kh = tap / 3, kw = tap % 3;
-#pragma unroll
-            for (int p = 0; p < CC / 2; ++p) {
-                const int s = tap * (CC / 2) + p;
-                const float a0 = wa[2 * s * WPITCH];
-                const float a1 = wa[2 * s * WPITCH + 32];
-                const float b0 = xb[2 * p * CS + kh * PITCH + kw];
-                const float b1 = xb[2 * p * CS + (kh + SD) * PITCH + kw];
-                acc[0][0] = mfma_32x32x2(a0, b0, acc[0][0]);
-                acc[0][1] = mfma_32x32x2(a0, b1, acc[0][1]);
-                acc[1][0] = mfma_32x32x2(a1, b0, acc[1][0]);
-                acc[1][1] = mfma_32x32x2(a1, b1, acc[1][1]);
-            }
+        for (int bj = 0; bj < 2; ++bj) {
+            prow[bj] = rw + 16 * bj + (i32 >> 1);
+            cnt += min(max(Ho - (rw + 16 * bj + 8 * s16), 0), 8) * sw;
         }
-        if (ch + 1 < nchunks)  // buf^1 was last read in iteration ch-1
-            igemm_stash<CO, SD>(lds, buf ^ 1, xdst, wdst, xpf, wpf);
-        __syncthreads();
+        pcol = col0 + (i32 & 1);
+    } else if (EDGE && t >= tiles_main) {
+        // rows TR tiles_h .. Ho - 1; columns of the 32-column tiles only
+        const int row0 = tiles_h * TR, col0 = (t - tiles_main) * GR::TW;
+        const int cw = col0 + 32 * wn;  // the wave's first column
+        const int cend = min(tiles_w * TC, Wo);
+        igemm_loop<GR>(xn, wt, lds, C_in, H, W, pad, row0, col0, tid, 32 * wn + i32, cw < cend, acc);
+        const int live = min(max(cend - (cw + 16 * s16), 0), 16);
+        cnt = 0;
+#pragma unroll
+        for (int bj = 0; bj < 2; ++bj) {
+            prow[bj] = row0 + bj < Ho ? row0 + bj : Ho;  // Ho: not live
+            cnt += row0 + bj < Ho ? live : 0;
+        }
+        pcol = cw + i32 < cend ? cw + i32 : Wo;  // Wo: not live
+    } else {
+        const int th = t / tiles_w, tw = t - th * tiles_w;
+        const int row0 = th * TR, col0 = tw * TC;
+        igemm_loop<G>(xn, wt, lds, C_in, H, W, pad, row0, col0, tid,
+                      2 * SD * wn * G::PITCH + SD * i32, !EDGE || row0 + 2 * wn < Ho, acc);
+        int rem[2];  // live columns of each of the wave's two rows
+#pragma unroll
+        for (int bj = 0; bj < 2; ++bj) {
+            prow[bj] = row0 + 2 * wn + bj;
+            rem[bj] = prow[bj] < Ho ? Wo - col0 : 0;
+        }
+        cnt = min(max(rem[0] - 16 * s16, 0), 16) + min(max(rem[1] - 16 * s16, 0), 16);
+        pcol = col0 + i32;
     }
 
-    // ---- epilogue
-    // Register r of acc[bi][bj] holds channel co(bi, r) (fixed per 32-lane half
-    // h) at row row0 + 2 * wn + bj, column col0 + lane % 32.  Statistics are
-    // taken per 16-lane row s16 = (lane / 16) % 2, which covers the tile columns
-    // 16 * s16 + lane % 16 of both rows: mean and then summed squared deviations
-    // (two passes over the registers), giving 2 * NR (count, mean, M2) partials
-    // per channel that one Chan merge per channel folds into the tile's partial.
-    const int s16 = (lane >> 4) & 1;
-    int rem[2];  // valid columns of each of the wave's two rows
-#pragma unroll
-    for (int bj = 0; bj < 2; ++bj) rem[bj] = row0 + 2 * wn + bj < Ho ? Wo - col0 : 0;
-    const int cnt = min(max(rem[0] - 16 * s16, 0), 16) + min(max(rem[1] - 16 * s16, 0), 16);
+    // ---- epilogue: bias, activation, stores, statistics
     const float rcnt = cnt ? 1.0f / (float)cnt : 0.0f;
     const unsigned plane = (unsigned)Ho * Wo;
     const auto yr = make_rsrc(y + (size_t)n * CO * plane, CO * plane * 4u);
@@ -244,9 +368,8 @@ void conv2d_igemm_kernel(const float *__restrict__ x, const float *__restrict__ 
     unsigned off[2];
 #pragma unroll
     for (int bj = 0; bj < 2; ++bj) {
-        ok[bj] = i32 < rem[bj];
-        off[bj] = ((unsigned)(64 * wm + 4 * h) * plane + (unsigned)(row0 + 2 * wn + bj) * Wo + col0 +
-                   i32) * 4u;
+        ok[bj] = prow[bj] < Ho && pcol < Wo;
+        off[bj] = ((unsigned)(64 * wm + 4 * h) * plane + (unsigned)prow[bj] * Wo + pcol) * 4u;
     }
     float (*red)[2][CO][3] = reinterpret_cast<float (*)[2][CO][3]>(lds);
     static_assert(NR * 2 * CO * 3 <= 2 * BUF_FLOATS, "row partials fit the staging buffers");
@@ -281,8 +404,7 @@ void conv2d_igemm_kernel(const float *__restrict__ x, const float *__restrict__ 
 #pragma unroll
             for (int q = 0; q < 2; ++q)
                 chan_merge(tc, tm, tq, red[k][q][tid][0], red[k][q][tid][1], red[k][q][tid][2]);
-        const size_t tile = (size_t)th * tiles_w + tw;
-        float *pp = partials + (((size_t)n * tiles_per_sample + tile) * CO + tid) * 3;
+        float *pp = partials + (((size_t)n * tiles_per_sample + t) * CO + tid) * 3;
         pp[0] = tc; pp[1] = tm; pp[2] = tq;
     }
 }
@@ -698,6 +820,27 @@ static size_t tiles_of(int C_out, int Ho, int Wo, int dtype)
     return (size_t)((Wo + TC - 1) / TC) * ((Ho + tr - 1) / tr);
 }
 
+// Edge strips (fp32, stride 1): the output columns left to column-strip tiles
+// (Wo mod 32 when that is 1 or 2 and Wo > 32, else 0) and the rows left to
+// row-strip tiles (Ho mod TR when that is 1 or 2 and Ho > TR, else 0).
+struct EdgeTiles {
+    int tiles_w, tiles_h, row_strips, col_strips;
+    int total() const { return tiles_w * tiles_h + row_strips + col_strips; }
+};
+template <int CO>
+static EdgeTiles edge_tiles(int Ho, int Wo, bool edges)
+{
+    constexpr int TR = Geo<CO, 1>::TR;
+    const int rc = Wo % TC, rr = Ho % TR;
+    const bool cs = edges && Wo > TC && (rc == 1 || rc == 2), rs = edges && Ho > TR && (rr == 1 || rr == 2);
+    EdgeTiles e;
+    e.tiles_w = cs ? Wo / TC : (Wo + TC - 1) / TC;
+    e.tiles_h = rs ? Ho / TR : (Ho + TR - 1) / TR;
+    e.row_strips = rs ? (e.tiles_w * TC + GeoRow<CO>::TW - 1) / GeoRow<CO>::TW : 0;
+    e.col_strips = cs ? (Ho + GeoStrip<CO>::TR - 1) / GeoStrip<CO>::TR : 0;
+    return e;
+}
+
 // [N][tiles][C_out][3] Welford partials, the weight copy ([ci][tap][co] fp32,
 // or [ci / 16][tap][co][16] 16-bit), then [N][C_out] (scale, shift) pairs
 static size_t weight_copy_bytes(int C_in, int C_out, int dtype)
@@ -712,18 +855,22 @@ size_t conv2d_igemm_workspace(int N, int C_in, int C_out, int Ho, int Wo, int dt
 }
 
 template <int CO, int ACT>
-static void launch_gemm(const Conv2dIgemmArgs &a, const float *wt, int tiles_w, int tiles_h, int tps,
-                        hipStream_t st)
+static void launch_gemm(const Conv2dIgemmArgs &a, const float *wt, const EdgeTiles &e, hipStream_t st)
 {
     static_assert(Geo<CO, 1>::TR == Geo<CO, 2>::TR, "one tile height per channel count");
     const float *x = static_cast<const float *>(a.x);
-    const dim3 grid(tiles_w, tiles_h, a.N);
+    const int tps = e.total();
+    const dim3 grid(tps, 1, a.N);
+#define CNF_ARGS                                                                                   \
+    grid, dim3(THREADS), 0, st, x, wt, a.b, a.out, a.partials, a.C_in, a.H, a.W, a.Ho, a.Wo, a.pad, \
+        e.tiles_w, e.tiles_h, e.row_strips, tps
     if (a.stride == 2)
-        hipLaunchKernelGGL((conv2d_igemm_kernel<CO, ACT, 2>), grid, dim3(THREADS), 0, st, x, wt, a.b,
-                           a.out, a.partials, a.C_in, a.H, a.W, a.Ho, a.Wo, a.pad, tiles_w, tps);
+        hipLaunchKernelGGL((conv2d_igemm_kernel<CO, ACT, 2, false>), CNF_ARGS);
+    else if (e.row_strips || e.col_strips)
+        hipLaunchKernelGGL((conv2d_igemm_kernel<CO, ACT, 1, true>), CNF_ARGS);
     else
-        hipLaunchKernelGGL((conv2d_igemm_kernel<CO, ACT, 1>), grid, dim3(THREADS), 0, st, x, wt, a.b,
-                           a.out, a.partials, a.C_in, a.H, a.W, a.Ho, a.Wo, a.pad, tiles_w, tps);
+        hipLaunchKernelGGL((conv2d_igemm_kernel<CO, ACT, 1, false>), CNF_ARGS);
+#undef CNF_ARGS
 }
 
 template <int CO, int ACT>
@@ -749,9 +896,16 @@ hipError_t launch_conv2d_igemm(const Conv2dIgemmArgs &a, hipStream_t st)
                     a.C_in % CC16 != 0))
         return hipErrorInvalidValue;
     const int CO = a.C_out, tr = tile_rows(CO, dt);
-    const int tiles_w = (a.Wo + TC - 1) / TC, tiles_h = (a.Ho + tr - 1) / tr;
-    const int tps = tiles_w * tiles_h;
-    float *wt = a.partials + (size_t)a.N * tps * CO * 3;
+    const bool edges = dt == 0 && a.stride == 1;
+    const EdgeTiles et = CO == 128 ? edge_tiles<128>(a.Ho, a.Wo, edges) : edge_tiles<64>(a.Ho, a.Wo, edges);
+    const int tiles_w = (a.Wo + TC - 1) / TC, tiles_h = (a.Ho + tr - 1) / tr;  // (16-bit kernel)
+    const int tps = dt ? tiles_w * tiles_h : et.total();
+    // The strips of a sample never outnumber the 32-column tiles they replace (a
+    // row strip is at least as wide as a tile row, a column strip at least as
+    // tall as a tile column), so the partials fit the space tiles_of sizes.
+    const size_t tps_space = tiles_of(CO, a.Ho, a.Wo, dt);  // the partials conv2d_igemm_workspace sizes
+    if ((size_t)tps > tps_space) return hipErrorInvalidValue;
+    float *wt = a.partials + (size_t)a.N * tps_space * CO * 3;
     {
         const int total = CO * a.C_in * 9;
         if (dt)
@@ -768,7 +922,7 @@ hipError_t launch_conv2d_igemm(const Conv2dIgemmArgs &a, hipStream_t st)
 #define CNF_CASE(C, A)                                                                    \
     if (CO == C && a.act == A) {                                                          \
         if (dt) launch_gemm16<C, A>(a, wt16, tiles_w, tiles_h, tps, st);                  \
-        else launch_gemm<C, A>(a, wt, tiles_w, tiles_h, tps, st);                         \
+        else launch_gemm<C, A>(a, wt, et, st);                                            \
     } else
     CNF_CASE(128, ACT_NONE) CNF_CASE(128, ACT_HARDSWISH) CNF_CASE(128, ACT_GELU_ERF)
     CNF_CASE(128, ACT_GELU_TANH) CNF_CASE(64, ACT_NONE) CNF_CASE(64, ACT_HARDSWISH)

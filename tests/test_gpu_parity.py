@@ -141,6 +141,19 @@ SMALL_CASES = [
     ("convt2d_dense_gelu_gn_n128", dict(N=2, C_in=8, in_dims=(1, 11, 19), padding=1)),
     ("convt2d_dense_gelu_gn_n128", dict(N=1, C_in=8, C_out=128, in_dims=(1, 12, 40), padding=2,
                                         norm="instance")),
+    # edge strips (output widths 1 or 2 past a multiple of 32, heights 1 or 2 past a
+    # multiple of the tile height; stride 1; many cases above have row strips too): two
+    # strip tiles per sample, the second mostly past the bottom edge; GroupNorm and
+    # InstanceNorm merging strip and row-tile partials; strip tiles in which some
+    # waves lie wholly past the bottom edge (padded conv, and a 7-row output)
+    ("convt2d_dense_gelu_gn_n128", dict(N=2, C_in=8, in_dims=(1, 257, 64))),
+    ("conv2d_in_div_n128", dict(N=2, C_in=8, in_dims=(1, 132, 67), norm="group", num_groups=4,
+                                affine=1)),
+    ("conv2d_in_div_n128", dict(N=1, C_in=8, C_out=64, in_dims=(1, 40, 64), padding=2, act="gelu")),
+    ("convt2d_dense_gelu_gn_n128", dict(N=1, C_in=8, C_out=128, in_dims=(1, 5, 95), norm="instance")),
+    # the full-size dense transposed conv's tiling (258 x 258 output: row-major tiles,
+    # one row strip, two column strips) on every element, with fewer input channels
+    ("convt2d_dense_gelu_gn_n128", dict(N=1, C_in=8, in_dims=(1, 256, 256))),
 ]
 
 

@@ -58,10 +58,10 @@ DOMINANT = {
     "conv2d_in_div_n2": ("small_conv_norm_kernel", "k_small_conv_norm.hip", "mfma"),
     "conv3d_softmax_pool_n128": ("conv3d_softmax_pool_kernel", "k_conv3d_softmax_pool.hip", "mfma"),
     "conv3d_hswish_gn_mean_n1024": ("conv3d_k4_gn_mean_kernel", "k_conv3d_gn_mean.hip", "mfma"),
-    "conv2d_in_div_n128": ("conv2d_igemm_kernel<128, 0, 1>", "k_conv2d_igemm.hip", "mfma"),
+    "conv2d_in_div_n128": ("conv2d_igemm_kernel<128, 0, 1, false>", "k_conv2d_igemm.hip", "mfma"),
     "convt2d_gelu_gn_n128": ("convt2d_gn_fused_kernel<2, 0>", "k_convt2d_gn_fused.hip", "hbm"),
-    "convt2d_dense_gelu_gn_n128": ("conv2d_igemm_kernel<64, 2, 1>", "k_conv2d_igemm.hip", "mfma"),
-    "conv2d_s2p1_in_div_n128": ("conv2d_igemm_kernel<128, 0, 2>", "k_conv2d_igemm.hip", "mfma"),
+    "convt2d_dense_gelu_gn_n128": ("conv2d_igemm_kernel<64, 2, 1, true>", "k_conv2d_igemm.hip", "mfma"),
+    "conv2d_s2p1_in_div_n128": ("conv2d_igemm_kernel<128, 0, 2, false>", "k_conv2d_igemm.hip", "mfma"),
     "convt2d_s2_gelu_gn_n128": ("upsample2_gn_fused_kernel<2, false>", "k_convt2d_gn_fused.hip", "hbm"),
     "conv2d_in_div_n128_bf16": ("conv2d_igemm16_kernel<128, 0, 1>", "k_conv2d_igemm.hip", "mfma"),
     "convt2d_gelu_gn_n128_bf16": ("convt2d_gn_fused_kernel<2, 1>", "k_convt2d_gn_fused.hip", "hbm"),
